@@ -1,0 +1,176 @@
+"""Benchmark: prefill TFLOP/s of the fused Q4_K / Q6_K dequant-GEMM at M=1024.
+
+One step = one pass of the prefill hot path over one batch: the seven
+projection GEMMs of one Llama-3.2-3B-shaped decoder layer (Q, K, V, O, gate,
+up in Q4_K, down in Q6_K) at M = 1024 tokens, issued as one grouped launch of
+the library (dmq_gemm_group).  Weights rotate over several independently
+seeded layers (more bytes than the 256 MB Infinity Cache) so every step
+streams its weights from HBM.  Inputs are resident in HBM before timing.
+
+Prints one JSON line (rank 0, one GPU).  Extra keys:
+  roofline      -- the GEMM kernel against the fp16 dense MFMA peak, from HIP
+                   events around every launch on the launch stream;
+  cpu_baseline  -- the CPU oracle on a bounded sample of the same workload;
+  decode        -- the M = 1 decode kernel on one layer (GB/s of weights).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synthetic  # noqa: E402
+
+PEAK_FP16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+M_PREFILL = 1024
+ROTATE_LAYERS = 5              # 5 x 63.1 MB of weights > 256 MB Infinity Cache
+DECODE_ROTATE = 8              # decode: 8 x 63.1 MB
+
+
+def layer_problems(torch, dmq, config, layer, M, xs, ys):
+    probs = []
+    for name, fmt, N, K, wq in synthetic.layer_weights(config, layer):
+        w = torch.from_numpy(wq.reshape(-1)).cuda()
+        probs.append((fmt, xs[name], w, ys[name], M, N, K))
+    return dmq.make_group(probs), probs
+
+
+def flops_of(M):
+    return sum(2.0 * M * N * K for _, _, N, K in synthetic.LAYER_PROJECTIONS)
+
+
+def weight_bytes():
+    size = {"q4k": 144, "q6k": 210}
+    return sum(N * (K // 256) * size[f] for _, f, N, K in synthetic.LAYER_PROJECTIONS)
+
+
+def time_launches(torch, launch, groups, steps, warmup):
+    """Run `launch(group)` over the rotating groups; events bracket every
+    launch on the current (launch) stream.  Returns (total_ms, [per-launch ms])."""
+    for i in range(warmup):
+        launch(groups[i % len(groups)])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        ev[i][0].record()
+        launch(groups[i % len(groups)])
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return t0.elapsed_time(t1), per
+
+
+def cpu_baseline(rows_sample: int):
+    """The oracle (dequant + fp64 matmul) on `rows_sample` rows of every
+    projection of one layer, timed on this host; scaled to TFLOP/s."""
+    import oracle
+    oracle.build()
+    items = []
+    for idx, (name, fmt, N, K, wq) in enumerate(synthetic.layer_weights(2, 0)):
+        x = synthetic.activations(rows_sample, K, seed=synthetic.act_seed(2, 0, idx), unit_rms=True)
+        items.append((fmt, x, wq, N, K))
+    t = time.perf_counter()
+    for fmt, x, wq, N, K in items:
+        oracle.gemm_quant(fmt, x, wq, N, K)
+    dt = time.perf_counter() - t
+    fl = flops_of(rows_sample)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {rows_sample} of {M_PREFILL} rows of all 7 projections of one layer "
+                      f"(exact dequant + fp64 matmul; {fl / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=96, help="rows of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dequant_gemm_q4_amd as dmq
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    M = M_PREFILL
+
+    # activations and outputs (shared by the rotating layers), weights per layer
+    xs, ys = {}, {}
+    for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
+        xs[name] = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(2, 0, idx),
+                                                          unit_rms=True)).cuda()
+        ys[name] = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    # keep (descriptor array, tensors) pairs: the arrays hold raw device pointers
+    layers = [layer_problems(torch, dmq, 2, layer, M, xs, ys) for layer in range(ROTATE_LAYERS)]
+    groups = [g for g, _ in layers]
+    total_ms, per = time_launches(torch, dmq.dmq_gemm_group, groups, args.steps, args.warmup)
+    flops = flops_of(M)
+    value = flops * args.steps / (total_ms / 1e3) / 1e12
+    kern_ms = float(np.mean(per))
+    achieved = flops / (kern_ms / 1e3) / 1e12
+
+    out = {
+        "metric": "prefill TFLOP/s of fused Q4_K dequant-GEMM at M=1024 (% FP16 MFMA peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.2-3B decoder layer prefill: 7 projection GEMMs (Q/K/V/O/gate/up Q4_K, "
+                               "down Q6_K) at M=1024 in one grouped launch, weights rotated over 5 layers",
+                   "M": M, "flop_per_step": flops, "weight_bytes_per_step": weight_bytes(),
+                   "pct_fp16_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel<16,4,false>", "launch_ms": round(kern_ms, 4)},
+    }
+
+    if not args.no_decode:
+        dxs, dys = {}, {}
+        for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
+            dxs[name] = torch.from_numpy(synthetic.activations(1, K, seed=synthetic.act_seed(1, 0, idx))).cuda()
+            dys[name] = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        del groups, layers
+        dlayers = [layer_problems(torch, dmq, 1, layer, 1, dxs, dys) for layer in range(DECODE_ROTATE)]
+        dgroups = [g for g, _ in dlayers]
+        dsteps = max(args.steps, 50)
+        d_total, d_per = time_launches(torch, dmq.dmq_gemm_group, dgroups, dsteps, args.warmup)
+        wb = weight_bytes()
+        d_ms = float(np.mean(d_per))
+        out["decode"] = {"workload": "M=1, one layer's 7 projections in one grouped launch, 8 rotating layers",
+                         "us_per_layer": round(1e3 * d_total / dsteps, 2),
+                         "GB/s": round(wb / (d_total / dsteps / 1e3) / 1e9, 1),
+                         "kernel_GB/s": round(wb / (d_ms / 1e3) / 1e9, 1),
+                         "frac_hbm": round(wb / (d_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

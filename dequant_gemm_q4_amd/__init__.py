@@ -1,0 +1,191 @@
+"""Python binding of libdmq.so (fused Q4_K / Q6_K dequant-GEMM for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libdmq.so.  PyTorch supplies device memory and the current stream.
+The functions carry the names of the C ABI (include/dmq.h) and take torch
+tensors; each checks dtypes, devices, contiguity and byte sizes (the C side
+cannot see buffer sizes) and raises DmqError on a non-zero status.
+
+Importing this package fails loudly when libdmq.so has not been built:
+there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdmq.so")
+
+DMQ_OK = 0
+DMQ_ERR_INVALID_ARG = -1
+DMQ_ERR_ALIGNMENT = -2
+DMQ_ERR_UNSUPPORTED = -3
+DMQ_ERR_HIP = -4
+DMQ_FMT_Q4K = 0
+DMQ_FMT_Q6K = 1
+
+QK = 256
+BLOCK_BYTES = {DMQ_FMT_Q4K: 144, DMQ_FMT_Q6K: 210}
+FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
+
+# Every entry point declared in include/dmq.h.
+EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
+           "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_status_string", "dmq_version")
+
+
+class DmqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class GemmDesc(ctypes.Structure):
+    """Mirror of dmq_gemm_desc."""
+    _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x_f16", ctypes.c_void_p), ("wq", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime with the same SONAME as /opt/rocm's
+    # (libamdhip64.so.7).  Loading torch first makes libdmq.so bind to that
+    # already-loaded runtime, so torch's streams and device pointers are valid
+    # in our calls; loading libdmq.so first would map a second HIP / HSA
+    # runtime into the process.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(or python dequant_gemm_q4_amd/build.py) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.dmq_dequant_q4k.argtypes = [P, P, I64, I64, P]
+    L.dmq_dequant_q6k.argtypes = [P, P, I64, I64, P]
+    L.dmq_gemm_q4k.argtypes = [P, P, P, I64, I64, I64, P]
+    L.dmq_gemm_q6k.argtypes = [P, P, P, I64, I64, I64, P]
+    L.dmq_ffn_swiglu_q4k.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    L.dmq_gemm_group.argtypes = [ctypes.POINTER(GemmDesc), I32, P]
+    for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
+                 "dmq_ffn_swiglu_q4k", "dmq_gemm_group"):
+        getattr(L, name).restype = ctypes.c_int
+    L.dmq_status_string.argtypes = [ctypes.c_int]
+    L.dmq_status_string.restype = ctypes.c_char_p
+    L.dmq_version.argtypes = []
+    L.dmq_version.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.dmq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != DMQ_OK:
+        raise DmqError(status, where)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_tensor(t, dtype, name: str, numel: int):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _wq_bytes(fmt: int, rows: int, k: int) -> int:
+    if k % QK:
+        raise ValueError("K must be a multiple of 256")
+    return rows * (k // QK) * BLOCK_BYTES[fmt]
+
+
+def dmq_dequant_q4k(wq, w_f16, rows: int, k: int, stream=None) -> None:
+    """w_f16[rows, k] (float16) <- exact Q4_K dequant of wq (uint8 blocks)."""
+    import torch
+    pw = _dev_tensor(wq, torch.uint8, "wq", _wq_bytes(DMQ_FMT_Q4K, rows, k))
+    po = _dev_tensor(w_f16, torch.float16, "w_f16", rows * k)
+    _check(lib.dmq_dequant_q4k(pw, po, rows, k, _stream(stream)), "dmq_dequant_q4k")
+
+
+def dmq_dequant_q6k(wq, w_f16, rows: int, k: int, stream=None) -> None:
+    """w_f16[rows, k] (float16) <- exact Q6_K dequant of wq (uint8 blocks)."""
+    import torch
+    pw = _dev_tensor(wq, torch.uint8, "wq", _wq_bytes(DMQ_FMT_Q6K, rows, k))
+    po = _dev_tensor(w_f16, torch.float16, "w_f16", rows * k)
+    _check(lib.dmq_dequant_q6k(pw, po, rows, k, _stream(stream)), "dmq_dequant_q6k")
+
+
+def _gemm(fmt: int, name: str, x, wq, y, M: int, N: int, K: int, stream) -> None:
+    import torch
+    px = _dev_tensor(x, torch.float16, "x", M * K)
+    pw = _dev_tensor(wq, torch.uint8, "wq", _wq_bytes(fmt, N, K))
+    py = _dev_tensor(y, torch.float32, "y", M * N)
+    _check(getattr(lib, name)(px, pw, py, M, N, K, _stream(stream)), name)
+
+
+def dmq_gemm_q4k(x, wq, y, M: int, N: int, K: int, stream=None) -> None:
+    """y[M, N] (float32) <- x[M, K] (float16) * W^T, W in Q4_K (N rows of K/256 blocks)."""
+    _gemm(DMQ_FMT_Q4K, "dmq_gemm_q4k", x, wq, y, M, N, K, stream)
+
+
+def dmq_gemm_q6k(x, wq, y, M: int, N: int, K: int, stream=None) -> None:
+    """y[M, N] (float32) <- x[M, K] (float16) * W^T, W in Q6_K."""
+    _gemm(DMQ_FMT_Q6K, "dmq_gemm_q6k", x, wq, y, M, N, K, stream)
+
+
+def dmq_ffn_swiglu_q4k(x, w_gate_up_q4k, w_down_q6k, h_f16, y, M: int, D: int, F: int,
+                       stream=None) -> None:
+    """h = silu(x Wg^T) * (x Wu^T) (float16 [M, F]); y = h Wd^T (float32 [M, D])."""
+    import torch
+    px = _dev_tensor(x, torch.float16, "x", M * D)
+    pgu = _dev_tensor(w_gate_up_q4k, torch.uint8, "w_gate_up_q4k", _wq_bytes(DMQ_FMT_Q4K, 2 * F, D))
+    pd = _dev_tensor(w_down_q6k, torch.uint8, "w_down_q6k", _wq_bytes(DMQ_FMT_Q6K, D, F))
+    ph = _dev_tensor(h_f16, torch.float16, "h_f16", M * F)
+    py = _dev_tensor(y, torch.float32, "y", M * D)
+    _check(lib.dmq_ffn_swiglu_q4k(px, pgu, pd, ph, py, M, D, F, _stream(stream)), "dmq_ffn_swiglu_q4k")
+
+
+def make_group(problems):
+    """problems: iterable of (format, x, wq, y, M, N, K) with format 'q4k'/'q6k'
+    or DMQ_FMT_*; returns the ctypes dmq_gemm_desc array (sizes checked)."""
+    import torch
+    problems = list(problems)
+    arr = (GemmDesc * len(problems))()
+    for i, (fmt, x, wq, y, M, N, K) in enumerate(problems):
+        fmt = FORMATS.get(fmt, fmt)
+        arr[i].format = fmt
+        arr[i].reserved = 0
+        arr[i].x_f16 = _dev_tensor(x, torch.float16, f"x[{i}]", M * K)
+        arr[i].wq = _dev_tensor(wq, torch.uint8, f"wq[{i}]", _wq_bytes(fmt, N, K))
+        arr[i].y = _dev_tensor(y, torch.float32, f"y[{i}]", M * N)
+        arr[i].M, arr[i].N, arr[i].K = M, N, K
+    return arr
+
+
+def dmq_gemm_group(problems, stream=None) -> None:
+    """Run several independent GEMMs in one launch per kernel kind.
+
+    ``problems`` is a list of (format, x, wq, y, M, N, K) or the array returned
+    by make_group (reusing it avoids re-marshalling in timing loops)."""
+    arr = problems if isinstance(problems, ctypes.Array) else make_group(problems)
+    _check(lib.dmq_gemm_group(arr, len(arr), _stream(stream)), "dmq_gemm_group")
+
+
+def dmq_version() -> int:
+    return int(lib.dmq_version())

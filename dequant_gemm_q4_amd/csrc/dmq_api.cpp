@@ -1,0 +1,191 @@
+// C ABI of libdmq.so: host-side argument checks, dispatch by M, status text.
+// Declarations and the contract of every call are in include/dmq.h.
+//
+// All checks run before the first HIP call, so a rejected call touches no
+// device state (and the checks can be exercised on a machine without a GPU).
+#include "../../include/dmq.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string_view>
+
+#include "dmq_common.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int kMaxGroup = 64;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dim_ok(int64_t v) { return v >= 1 && v <= kMaxDim; }
+
+int check_quant_k(int64_t k) { return (dim_ok(k) && k % 256 == 0) ? DMQ_OK : DMQ_ERR_INVALID_ARG; }
+
+int check_weights(int fmt, const void* wq) {
+  if (!wq) return DMQ_ERR_INVALID_ARG;
+  if (fmt == DMQ_FMT_Q4K) return aligned(wq, 16) ? DMQ_OK : DMQ_ERR_ALIGNMENT;
+  if (fmt == DMQ_FMT_Q6K) return aligned(wq, 2) ? DMQ_OK : DMQ_ERR_ALIGNMENT;
+  return DMQ_ERR_INVALID_ARG;
+}
+
+// Byte size of N rows of K-wide quantised weights (for overflow checks).
+bool weight_bytes_ok(int fmt, int64_t n, int64_t k) {
+  int64_t per_block = fmt == DMQ_FMT_Q4K ? 144 : 210;
+  int64_t blocks = n * (k / 256);                 // n, k < 2^31: no overflow in int64
+  return blocks <= (int64_t(1) << 40) / per_block;
+}
+
+int check_gemm(int fmt, const void* x, const void* wq, const void* y, int64_t M, int64_t N, int64_t K) {
+  if (!x || !y) return DMQ_ERR_INVALID_ARG;
+  if (!dim_ok(M) || !dim_ok(N)) return DMQ_ERR_INVALID_ARG;
+  if (check_quant_k(K) != DMQ_OK) return DMQ_ERR_INVALID_ARG;
+  int w = check_weights(fmt, wq);
+  if (w != DMQ_OK) return w;
+  if (!weight_bytes_ok(fmt, N, K)) return DMQ_ERR_INVALID_ARG;
+  if (M * K > (int64_t(1) << 40) || M * N > (int64_t(1) << 40)) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16)) return DMQ_ERR_ALIGNMENT;
+  return DMQ_OK;
+}
+
+// Device check: the kernels are built for gfx950 only.  Cached per device.
+int check_device() {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DMQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init) {
+    for (int& c : cached) c = 1;   // 1 = unknown
+    init = true;
+  }
+  if (dev < 0 || dev >= 64) return DMQ_ERR_UNSUPPORTED;
+  if (cached[dev] == 1) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DMQ_ERR_UNSUPPORTED;
+    cached[dev] = (prop.gcnArchName[0] && std::string_view(prop.gcnArchName).substr(0, 6) == "gfx950")
+                      ? DMQ_OK : DMQ_ERR_UNSUPPORTED;
+  }
+  return cached[dev];
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DMQ_OK : DMQ_ERR_HIP; }
+
+// The decode kernel stages x in LDS; it takes K up to this size.
+constexpr int64_t kGemvMaxK = 32768;
+
+int run_gemm(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t s) {
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(decode ? dmq::launch_gemv(probs, count, s) : dmq::launch_gemm(probs, count, s));
+}
+
+dmq::GemmProblem make_problem(int fmt, const void* x, const void* wq, void* out, int64_t M, int64_t N, int64_t K,
+                              int swiglu) {
+  dmq::GemmProblem p;
+  p.x = x;
+  p.wq = (const uint8_t*)wq;
+  p.out = out;
+  p.fmt = fmt;
+  p.swiglu = swiglu;
+  p.M = (int32_t)M;
+  p.N = (int32_t)N;
+  p.K = (int32_t)K;
+  return p;
+}
+
+int gemm_one(int fmt, const void* x, const void* wq, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_gemm(fmt, x, wq, y, M, N, K);
+  if (st != DMQ_OK) return st;
+  dmq::GemmProblem p = make_problem(fmt, x, wq, y, M, N, K, 0);
+  bool decode = (M == 1 && K <= kGemvMaxK);
+  return run_gemm(&p, 1, decode, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dmq_version(void) { return 1; }
+
+const char* dmq_status_string(int status) {
+  switch (status) {
+    case DMQ_OK: return "ok";
+    case DMQ_ERR_INVALID_ARG: return "invalid argument (null pointer, size out of range, K not a multiple of 256, or bad format)";
+    case DMQ_ERR_ALIGNMENT: return "misaligned pointer (x, y, h, w_f16 and Q4_K weights need 16 bytes, Q6_K weights 2)";
+    case DMQ_ERR_UNSUPPORTED: return "unsupported device (needs a gfx950 GPU)";
+    case DMQ_ERR_HIP: return "HIP runtime error on launch";
+    default: return "unknown status";
+  }
+}
+
+int dmq_dequant_q4k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* stream) {
+  if (!w_f16 || !dim_ok(rows) || check_quant_k(k) != DMQ_OK) return DMQ_ERR_INVALID_ARG;
+  int w = check_weights(DMQ_FMT_Q4K, wq);
+  if (w != DMQ_OK) return w;
+  if (!weight_bytes_ok(DMQ_FMT_Q4K, rows, k)) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(w_f16, 16)) return DMQ_ERR_ALIGNMENT;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(dmq::launch_dequant_q4k(wq, w_f16, rows, k, (hipStream_t)stream));
+}
+
+int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* stream) {
+  if (!w_f16 || !dim_ok(rows) || check_quant_k(k) != DMQ_OK) return DMQ_ERR_INVALID_ARG;
+  int w = check_weights(DMQ_FMT_Q6K, wq);
+  if (w != DMQ_OK) return w;
+  if (!weight_bytes_ok(DMQ_FMT_Q6K, rows, k)) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(w_f16, 16)) return DMQ_ERR_ALIGNMENT;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(dmq::launch_dequant_q6k(wq, w_f16, rows, k, (hipStream_t)stream));
+}
+
+int dmq_gemm_q4k(const void* x_f16, const void* wq, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_one(DMQ_FMT_Q4K, x_f16, wq, y, M, N, K, stream);
+}
+
+int dmq_gemm_q6k(const void* x_f16, const void* wq, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_one(DMQ_FMT_Q6K, x_f16, wq, y, M, N, K, stream);
+}
+
+int dmq_ffn_swiglu_q4k(const void* x_f16, const void* w_gate_up_q4k, const void* w_down_q6k, void* h_f16, float* y,
+                       int64_t M, int64_t D, int64_t F, void* stream) {
+  if (!h_f16 || !dim_ok(F) || F > kMaxDim / 2) return DMQ_ERR_INVALID_ARG;
+  int st = check_gemm(DMQ_FMT_Q4K, x_f16, w_gate_up_q4k, h_f16, M, 2 * F, D);
+  if (st != DMQ_OK) return st;
+  st = check_gemm(DMQ_FMT_Q6K, h_f16, w_down_q6k, y, M, D, F);
+  if (st != DMQ_OK) return st;
+  bool decode = (M == 1 && D <= kGemvMaxK && F <= kGemvMaxK);
+  dmq::GemmProblem up = make_problem(DMQ_FMT_Q4K, x_f16, w_gate_up_q4k, h_f16, M, 2 * F, D, 1);
+  st = run_gemm(&up, 1, decode, (hipStream_t)stream);
+  if (st != DMQ_OK) return st;
+  dmq::GemmProblem down = make_problem(DMQ_FMT_Q6K, h_f16, w_down_q6k, y, M, D, F, 0);
+  return run_gemm(&down, 1, decode, (hipStream_t)stream);
+}
+
+int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream) {
+  if (!descs || count < 1 || count > kMaxGroup) return DMQ_ERR_INVALID_ARG;
+  dmq::GemmProblem probs[kMaxGroup];
+  int n_decode = 0;
+  for (int i = 0; i < count; ++i) {
+    const dmq_gemm_desc& d = descs[i];
+    if (d.reserved != 0 || (d.format != DMQ_FMT_Q4K && d.format != DMQ_FMT_Q6K)) return DMQ_ERR_INVALID_ARG;
+    int st = check_gemm(d.format, d.x_f16, d.wq, d.y, d.M, d.N, d.K);
+    if (st != DMQ_OK) return st;
+    if (d.M == 1 && d.K <= kGemvMaxK) ++n_decode;
+    probs[i] = make_problem(d.format, d.x_f16, d.wq, d.y, d.M, d.N, d.K, 0);
+  }
+  if (n_decode != 0 && n_decode != count) return DMQ_ERR_INVALID_ARG;   // one kernel kind per call
+  // Longest reduction first: tiles of the deepest K are dispatched first so
+  // they do not trail at the end of the launch.
+  std::stable_sort(probs, probs + count,
+                   [](const dmq::GemmProblem& a, const dmq::GemmProblem& b) { return a.K > b.K; });
+  return run_gemm(probs, count, n_decode == count, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+/*
+ * dmq -- fused Q4_K / Q6_K dequant-GEMM for AMD MI355X (gfx950).
+ *
+ * C ABI of the shared library libdmq.so.  Every entry point takes plain
+ * pointers and sizes, returns an int status (dmq_status), never throws, and
+ * runs asynchronously on the HIP stream it is given.
+ *
+ * What the calls compute comes from the DAMASCUS pages:
+ *  - Overview page, "[02] the pipeline", compartment 09 (Quantization & AMX):
+ *    "Q4_K_M dequant; quantized matmul; fused dequant -> AMX prefill"; and
+ *    "[01] the thesis": the fused path never materialises fp16 weights.
+ *  - Article "Building DAMASCUS", "Read the model, then reproduce its
+ *    operations": the Q4_K and Q6_K dequantizers; and "Prefill and decode need
+ *    different performance questions": decode is matrix-vector work bound by
+ *    streaming the weights, prefill is matrix-matrix work.
+ *  - Same article, layer description: RMSNorm, QKV projections, attention, a
+ *    second RMSNorm and a SwiGLU feed-forward network complete the layer.
+ *
+ * Conventions shared by all calls
+ *  - Pointers named *_f16 point to IEEE binary16 data, y points to fp32 data.
+ *  - Activations x are [M, K] row-major, contiguous.
+ *  - A quantised weight matrix W is [N, K]: N rows, each a contiguous run of
+ *    K/256 super-blocks in GGUF k-quant byte layout (Q4_K: 144 bytes, Q6_K:
+ *    210 bytes per 256 weights); rows follow each other with no padding.
+ *  - Products are y = x * W^T, i.e. y[m][n] = sum_k x[m][k] * W[n][k], [M, N]
+ *    row-major fp32, accumulated in fp32.
+ *  - Every pointer except the stream is DEVICE memory owned by the caller
+ *    (for example a torch tensor's data_ptr()); the library allocates nothing
+ *    on these calls and keeps no state besides cached device properties.
+ *    Passing host memory is undefined behaviour.
+ *  - stream is a hipStream_t passed as void*; NULL means the null stream.  The
+ *    call only enqueues work: results are ready once the stream is
+ *    synchronised.  The device is the caller's current HIP device.
+ *  - Arguments are checked on the host before any HIP call; a rejected call
+ *    enqueues nothing.  Checks: non-NULL pointers, sizes >= 1 and < 2^31,
+ *    K (and D, F) a multiple of 256, x / y / h / w_f16 16-byte aligned, Q4_K
+ *    weights 16-byte aligned, Q6_K weights 2-byte aligned.
+ *  - Output buffers must not overlap inputs.
+ */
+#ifndef DMQ_H
+#define DMQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DMQ_OK = 0,
+  DMQ_ERR_INVALID_ARG = -1,   /* NULL pointer, size out of range, bad format */
+  DMQ_ERR_ALIGNMENT = -2,     /* a pointer breaks the alignment rule above   */
+  DMQ_ERR_UNSUPPORTED = -3,   /* no HIP device / not a gfx950 device         */
+  DMQ_ERR_HIP = -4            /* the HIP runtime reported a launch error     */
+} dmq_status;
+
+/* Weight formats for dmq_gemm_desc.format. */
+#define DMQ_FMT_Q4K 0
+#define DMQ_FMT_Q6K 1
+
+/*
+ * Dequantise a Q4_K matrix to fp16.
+ *   wq    : rows x (k/256) Q4_K blocks (rows*k/256*144 bytes), 16-byte aligned.
+ *   w_f16 : rows x k fp16, row-major (output).
+ * Each weight of sub-block j of a block is w = d*sc_j*q - dmin*m_j (d, dmin the
+ * block's fp16 super-scales, sc_j/m_j its 6-bit scale and min, q the 4-bit
+ * quant), computed exactly and rounded ONCE to fp16 (round to nearest even,
+ * subnormals kept, overflow to inf); an exact zero is +0.  Bit-exact.
+ * Non-finite d/dmin propagate as IEEE arithmetic on (d*sc_j)*q - dmin*m_j.
+ */
+int dmq_dequant_q4k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* stream);
+
+/*
+ * Dequantise a Q6_K matrix to fp16.
+ *   wq    : rows x (k/256) Q6_K blocks (rows*k/256*210 bytes), 2-byte aligned.
+ *   w_f16 : rows x k fp16 (output).
+ * w = d * sc[i/16] * (q - 32), q the 6-bit quant (4 low bits + 2 high bits),
+ * sc the int8 sub-block scale; exact in fp32, rounded once to fp16; exact zero
+ * is +0.  Bit-exact.
+ */
+int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* stream);
+
+/*
+ * y = x * W^T with W in Q4_K, dequantised inside the kernel (no fp16 weight
+ * matrix is ever written to memory).
+ *   x_f16 : [M, K] fp16;  wq : N rows of K/256 Q4_K blocks;  y : [M, N] fp32.
+ * M = 1 runs the decode matrix-vector kernel; small M a skinny MFMA kernel;
+ * large M the tiled MFMA prefill kernel.  Per output, |y - y_exact| stays
+ * within 1e-3 * sum_k |x[m][k] * w[n][k]| + 1e-5 (w the fp16-rounded weight).
+ */
+int dmq_gemm_q4k(const void* x_f16, const void* wq, float* y,
+                 int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Same as dmq_gemm_q4k with W in Q6_K (down projection, tied LM head). */
+int dmq_gemm_q6k(const void* x_f16, const void* wq, float* y,
+                 int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * SwiGLU feed-forward block: h = silu(x*Wg^T) * (x*Wu^T), y = h * Wd^T.
+ *   x_f16         : [M, D] fp16.
+ *   w_gate_up_q4k : 2F rows of D/256 Q4_K blocks; rows 0..F-1 are the gate
+ *                   projection, rows F..2F-1 the up projection.
+ *   w_down_q6k    : D rows of F/256 Q6_K blocks.
+ *   h_f16         : [M, F] fp16 (output, caller-provided): silu(g)*u computed
+ *                   in fp32 from the fp32 accumulators and rounded once to fp16
+ *                   (IEEE: values beyond the fp16 range become +-inf).
+ *                   silu(g) = g / (1 + exp(-g)).
+ *   y             : [M, D] fp32 (output) = h * Wd^T.
+ * g and u are never written to memory; h is written once and read once.
+ */
+int dmq_ffn_swiglu_q4k(const void* x_f16, const void* w_gate_up_q4k,
+                       const void* w_down_q6k, void* h_f16, float* y,
+                       int64_t M, int64_t D, int64_t F, void* stream);
+
+/*
+ * One problem of a grouped GEMM launch.  Each entry is an independent
+ * y = x * W^T with its own format, pointers and sizes, under the same rules
+ * as dmq_gemm_q4k / dmq_gemm_q6k.
+ */
+typedef struct {
+  int32_t format;      /* DMQ_FMT_Q4K or DMQ_FMT_Q6K */
+  int32_t reserved;    /* must be 0 */
+  const void* x_f16;
+  const void* wq;
+  float* y;
+  int64_t M, N, K;
+} dmq_gemm_desc;
+
+/*
+ * Run `count` GEMMs (1 <= count <= 64) as one launch per kernel kind instead
+ * of one launch per GEMM, so that small projections (e.g. the K and V
+ * projections of one layer) share the GPU with the large ones.  descs is a
+ * HOST array; it is read before the call returns.  All problems must use the
+ * same kernel kind: all M = 1 (decode), or all M > 1.  Results are identical
+ * to calling dmq_gemm_q4k / dmq_gemm_q6k for each entry.
+ */
+int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* dmq_status_string(int status);
+
+/* Library ABI version (currently 1). */
+int dmq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMQ_H */

@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/dmq.h, and rejects bad arguments on the host before
+any HIP call (so nothing here touches a device, with or without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_gemm_q4_amd as dmq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmq.h")
+
+A16 = 0x10000          # a 16-byte aligned address that is never dereferenced
+MIS = 0x10008          # 8 mod 16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dmq_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 8, names
+    assert set(names) == set(dmq.EXPORTS)
+    raw = ctypes.CDLL(dmq.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings():
+    assert dmq.dmq_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert dmq.status_string(st) and "unknown" not in dmq.status_string(st)
+    assert "unknown" in dmq.status_string(42)
+
+
+L = dmq.lib
+
+
+@pytest.mark.parametrize("fn", ["dmq_gemm_q4k", "dmq_gemm_q6k"])
+def test_gemm_validation(fn):
+    f = getattr(L, fn)
+    assert f(None, A16, A16, 4, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, None, A16, 4, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, None, 4, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, A16, 0, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, A16, 4, 0, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, A16, 4, 4, 0, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, A16, 4, 4, 300, None) == dmq.DMQ_ERR_INVALID_ARG      # K % 256
+    assert f(A16, A16, A16, -1, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, A16, 1 << 31, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(MIS, A16, A16, 4, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT         # x
+    assert f(A16, A16, MIS, 4, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT         # y
+    assert f(A16, A16 + 1, A16, 4, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT     # odd weights
+
+
+def test_weight_alignment_rules():
+    # Q4_K blocks need 16-byte alignment, Q6_K only 2
+    assert L.dmq_gemm_q4k(A16, A16 + 2, A16, 4, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT
+    assert L.dmq_dequant_q4k(A16 + 8, A16, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT
+    assert L.dmq_dequant_q6k(A16 + 1, A16, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("fn", ["dmq_dequant_q4k", "dmq_dequant_q6k"])
+def test_dequant_validation(fn):
+    f = getattr(L, fn)
+    assert f(None, A16, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, None, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, 0, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, A16, 4, 128, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(A16, MIS, 4, 256, None) == dmq.DMQ_ERR_ALIGNMENT
+
+
+def test_ffn_validation():
+    f = L.dmq_ffn_swiglu_q4k
+    assert f(A16, A16, A16, None, A16, 4, 256, 256, None) == dmq.DMQ_ERR_INVALID_ARG   # h
+    assert f(A16, A16, A16, A16, None, 4, 256, 256, None) == dmq.DMQ_ERR_INVALID_ARG   # y
+    assert f(A16, A16, A16, A16, A16, 4, 300, 256, None) == dmq.DMQ_ERR_INVALID_ARG    # D % 256
+    assert f(A16, A16, A16, A16, A16, 4, 256, 100, None) == dmq.DMQ_ERR_INVALID_ARG    # F % 256
+    assert f(A16, A16, A16, MIS, A16, 4, 256, 256, None) == dmq.DMQ_ERR_ALIGNMENT      # h
+    assert f(A16, A16, A16 + 1, A16, A16, 4, 256, 256, None) == dmq.DMQ_ERR_ALIGNMENT  # down
+
+
+def _desc(fmt=0, M=4, N=4, K=256, x=A16, wq=A16, y=A16, reserved=0):
+    d = dmq.GemmDesc()
+    d.format, d.reserved, d.x_f16, d.wq, d.y, d.M, d.N, d.K = fmt, reserved, x, wq, y, M, N, K
+    return d
+
+
+def test_group_validation():
+    g = L.dmq_gemm_group
+    arr = (dmq.GemmDesc * 2)(_desc(), _desc())
+    assert g(arr, 0, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert g(arr, 65, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert g(None, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.GemmDesc * 1)(_desc(reserved=1))
+    assert g(bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.GemmDesc * 1)(_desc(fmt=7))
+    assert g(bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.GemmDesc * 2)(_desc(), _desc(K=100))
+    assert g(bad, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.GemmDesc * 2)(_desc(), _desc(y=MIS))
+    assert g(bad, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    # decode (M = 1) and prefill problems cannot share one call
+    mixed = (dmq.GemmDesc * 2)(_desc(M=1), _desc(M=8))
+    assert g(mixed, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors_and_bad_sizes():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 256, dtype=torch.float16)
+    w = torch.zeros(4 * 144, dtype=torch.uint8)
+    y = torch.zeros(4, 4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        dmq.dmq_gemm_q4k(x, w, y, 4, 4, 256)          # CPU tensors are refused
+    with pytest.raises(ValueError):
+        dmq.make_group([("q4k", x, w, y, 4, 4, 512)])  # K mismatch is caught first

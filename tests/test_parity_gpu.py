@@ -1,0 +1,403 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (stated per test):
+* dequant: bit-exact fp16, NaN matched as NaN;
+* GEMM / GEMV: per output |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 1e-5, with
+  y_ref and the sum from the oracle's fp64 matmul over its own fp16 weights;
+* SwiGLU h: inside the oracle's interval over g, u +- their GEMM bounds,
+  widened by 2^-20 and rounded outward to fp16 (IEEE overflow to +-inf);
+* FFN down stage: the oracle GEMM applied to the GPU's own h.
+
+Inputs come from `synthetic` (seeded, shaped like the Llama-3.2-3B layer on
+the DAMASCUS overview page, "[06] the target").  Sizes the oracle finishes in
+seconds are checked on every output; the full benchmark sizes are checked on
+sampled rows that hit every 256-row tile, in the grouped launch the benchmark
+times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from _packing import f16_bits, pack_q4k, pack_q6k
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dmq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dequant_gemm_q4_amd
+    return dequant_gemm_q4_amd
+
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def gpu_dequant(dmq, fmt, wq, rows, k):
+    out = torch.empty((rows, k), dtype=torch.float16, device=DEV)
+    fn = dmq.dmq_dequant_q4k if fmt == "q4k" else dmq.dmq_dequant_q6k
+    fn(dev(wq.reshape(-1)), out, rows, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def assert_bits_equal(got, want, what):
+    got = got.reshape(-1)
+    want = want.reshape(-1)
+    nan_w = (want & 0x7C00) == 0x7C00
+    nan_w &= (want & 0x03FF) != 0
+    nan_g = ((got & 0x7C00) == 0x7C00) & ((got & 0x03FF) != 0)
+    assert np.array_equal(nan_g, nan_w), f"{what}: NaN pattern differs"
+    diff = (got != want) & ~nan_w
+    assert not diff.any(), (f"{what}: {int(diff.sum())} of {got.size} weights differ; first at "
+                            f"{int(np.argmax(diff))}: got {got[diff][0]:#06x} want {want[diff][0]:#06x}")
+
+
+def gpu_gemm(dmq, fmt, x, wq, M, N, K):
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    fn = dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k
+    fn(dev(x), dev(wq.reshape(-1)), y, M, N, K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_within(y, ref, s, what):
+    y = y.astype(np.float64)
+    tol = oracle.gemm_tolerance(s)
+    err = np.abs(y - ref)
+    ok = err <= tol
+    ratio = float(np.max(np.where(np.isfinite(err), err / tol, np.inf)))
+    assert ok.all(), f"{what}: {int((~ok).sum())} of {ok.size} outputs outside the bound (worst err/bound {ratio:.3g})"
+    print(f"{what}: max err/bound = {ratio:.3g}")
+    return ratio
+
+
+# --------------------------------------------------------------- dequant ---
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("rows,k", [(64, 3072), (3, 768), (1, 256), (5, 8192)])
+def test_dequant_random_bitexact(dmq, fmt, rows, k):
+    wq = synthetic.weight_blocks(fmt, rows, k, seed=100 + rows + k)
+    assert_bits_equal(gpu_dequant(dmq, fmt, wq, rows, k), oracle.dequant(fmt, wq, rows, k), f"{fmt} {rows}x{k}")
+
+
+def test_dequant_q4k_adversarial_rounding(dmq):
+    # the three hand-found vectors, then a sweep of the region where rounding
+    # through fp32 first would differ: d near the top of its range, dmin in the
+    # lowest binade, large scales and quants
+    blocks = [pack_q4k(d, dm, [sc] * 8, [m] * 8, [q] * 256)
+              for d, sc, q, dm, m in [(0x2458, 63, 15, 0x1423, 11), (0x245A, 63, 15, 0x1517, 7),
+                                      (0x245B, 63, 15, 0x14CF, 33)]]
+    rng = np.random.default_rng(2024)
+    n = 6000
+    sweep = synthetic.random_bytes(n * 144, seed=77).reshape(n, 144).copy()
+    d_bits = rng.integers(f16_bits(0.0169), f16_bits(0.02) + 1, n).astype(np.uint16)
+    dm_bits = rng.integers(0x1400, 0x1800, n).astype(np.uint16)          # [2^-10, 2^-9)
+    sweep[:, 0:2] = d_bits.view(np.uint8).reshape(n, 2)
+    sweep[:, 2:4] = dm_bits.view(np.uint8).reshape(n, 2)
+    # scales >= 50: low 6 bits of bytes 0..3 (j < 4) and the split fields of j >= 4
+    for b in range(n):
+        sc = rng.integers(50, 64, 8)
+        mn = rng.integers(0, 64, 8)
+        q = rng.integers(12, 16, 256)
+        sweep[b] = pack_q4k(int(d_bits[b]), int(dm_bits[b]), sc, mn, q)
+    wq = np.concatenate([np.stack(blocks), sweep]).reshape(-1)
+    rows = len(blocks) + n
+    want = oracle.dequant_q4k(wq, rows, 256)
+    got = gpu_dequant(dmq, "q4k", wq, rows, 256)
+    assert_bits_equal(got, want, "q4k adversarial")
+    assert np.all(want[0] == 0x4C01) and np.all(want[1] == 0x4C03) and np.all(want[2] == 0x4C03)
+    # the sweep must actually contain double-rounding cases to be a test
+    fields = [oracle.q4k_fields(wq[i * 144:(i + 1) * 144]) for i in range(3, 3 + 400)]
+    dr = 0
+    for (d, dmin, sc, mn, q), row in zip(fields, want[3:403]):
+        j = np.arange(256) // 32
+        v32 = (np.float32(d) * sc[j].astype(np.float32) * q.astype(np.float32)
+               - np.float32(dmin) * mn[j].astype(np.float32))
+        dr += int(np.sum(v32.astype(np.float16).view(np.uint16) != row))
+    print(f"double-rounding cases in the first 400 sweep blocks: {dr}")
+    assert dr > 0
+
+
+def test_dequant_special_values(dmq):
+    cases4 = [
+        pack_q4k(0x7C00, 0x3C00, [1] * 8, [1] * 8, [i % 16 for i in range(256)]),   # d = +inf
+        pack_q4k(0x3C00, 0x7E00, [1] * 8, [3] * 8, [1] * 256),                      # dmin = NaN
+        pack_q4k(0xBC00, 0x0000, [5] * 8, [0] * 8, [i % 16 for i in range(256)]),   # d < 0: -0 -> +0
+        pack_q4k(0x0001, 0x0002, [63] * 8, [63] * 8, [i % 16 for i in range(256)]), # subnormal d, dmin
+        pack_q4k(0x7BFF, 0x0000, [63] * 8, [0] * 8, [15] * 256),                    # overflow to inf
+        pack_q4k(0x3C00, 0x3C00, [7] * 8, [7] * 8, [1] * 256),                      # exact zeros
+    ]
+    wq = np.stack(cases4).reshape(-1)
+    assert_bits_equal(gpu_dequant(dmq, "q4k", wq, len(cases4), 256),
+                      oracle.dequant_q4k(wq, len(cases4), 256), "q4k special")
+    cases6 = [
+        pack_q6k(0x3C00, [-(s + 1) for s in range(16)], [32] * 256),                  # all +0
+        pack_q6k(0xFC00, [3] * 16, [(i * 7) % 64 for i in range(256)]),               # d = -inf, q=32 -> NaN
+        pack_q6k(0x0003, [-128] * 16, [(i * 5) % 64 for i in range(256)]),            # subnormal d
+        pack_q6k(0x7BFF, [127] * 16, [0] * 256),                                      # overflow
+    ]
+    wq6 = np.stack(cases6).reshape(-1)
+    assert_bits_equal(gpu_dequant(dmq, "q6k", wq6, len(cases6), 256),
+                      oracle.dequant_q6k(wq6, len(cases6), 256), "q6k special")
+
+
+# ------------------------------------------------------------------ GEMV ---
+
+def test_gemv_config1_every_output(dmq):
+    x = synthetic.activations(1, 3072, seed=synthetic.act_seed(1, 0, 0))
+    hx = synthetic.activations(1, 8192, seed=synthetic.act_seed(1, 0, 6))
+    for name, fmt, N, K, wq in synthetic.layer_weights(1, 0):
+        xin = hx if K == 8192 else x
+        y = gpu_gemm(dmq, fmt, xin, wq, 1, N, K)
+        ref, s = oracle.gemm_quant(fmt, xin, wq, N, K)
+        assert_within(y, ref, s, f"decode {name} {N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("N,K", [(1, 256), (5, 512), (17, 1280), (100, 4096), (33, 2304)])
+def test_gemv_ragged(dmq, fmt, N, K):
+    x = synthetic.activations(1, K, seed=N + K)
+    wq = synthetic.weight_blocks(fmt, N, K, seed=N * 7 + K)
+    y = gpu_gemm(dmq, fmt, x, wq, 1, N, K)
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y, ref, s, f"decode {fmt} {N}x{K}")
+
+
+def test_gemv_group_equals_single_calls(dmq):
+    x = dev(synthetic.activations(1, 3072, seed=5))
+    hx = dev(synthetic.activations(1, 8192, seed=6))
+    probs, singles = [], []
+    for name, fmt, N, K, wq in synthetic.layer_weights(1, 3):
+        w = dev(wq.reshape(-1))
+        xin = hx if K == 8192 else x
+        yg = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        ys = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        probs.append((fmt, xin, w, yg, 1, N, K))
+        singles.append((fmt, xin, w, ys, 1, N, K))
+    dmq.dmq_gemm_group(probs)
+    for fmt, xin, w, ys, M, N, K in singles:
+        (dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k)(xin, w, ys, M, N, K)
+    torch.cuda.synchronize()
+    for (f, _, _, yg, *_), (_, _, _, ys, *_) in zip(probs, singles):
+        assert torch.equal(yg, ys)
+
+
+# ------------------------------------------------------------------ GEMM ---
+
+def test_gemm_config0_every_output(dmq):
+    M, N, K = 16, 3072, 3072
+    x = synthetic.activations(M, K, seed=synthetic.act_seed(0, 0, 0))
+    wq = synthetic.q4k_blocks(N, K, seed=synthetic.weight_seed(0, 0, 0))
+    y = gpu_gemm(dmq, "q4k", x, wq, M, N, K)
+    ref, s = oracle.gemm_quant("q4k", x, wq, N, K)
+    assert_within(y, ref, s, "config0 M=16 q4k")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,N,K", [(2, 64, 256), (17, 100, 512), (65, 333, 768), (300, 1000, 1024),
+                                   (257, 257, 256), (130, 7, 2048), (64, 512, 1536)])
+def test_gemm_ragged_every_output(dmq, fmt, M, N, K):
+    x = synthetic.activations(M, K, seed=M * 31 + N)
+    wq = synthetic.weight_blocks(fmt, N, K, seed=M + N * 3 + K)
+    y = gpu_gemm(dmq, fmt, x, wq, M, N, K)
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y, ref, s, f"gemm {fmt} {M}x{N}x{K}")
+
+
+def test_gemm_adversarial_cancellation(dmq):
+    # every weight is d*sc*q - dmin*m with the two terms equal or nearly
+    # equal: y_ref ~ 0 and S tiny, so the bound is close to 1e-5 absolute
+    rng = np.random.default_rng(9)
+    N, K, M = 64, 512, 48
+    blocks = []
+    for _ in range(N * K // 256):
+        sc = rng.integers(1, 64, 8)
+        q = rng.integers(1, 16, 256)
+        d = f16_bits(0.01)
+        # m = sc * q0 for one q0 per sub-block: weights with q == q0 are exact zeros
+        q0 = rng.integers(1, 4, 8)
+        mn = np.minimum(sc * q0, 63)
+        blocks.append(pack_q4k(d, d, sc, mn, q))
+    wq = np.stack(blocks).reshape(-1)
+    x = synthetic.activations(M, K, seed=10)
+    for m_rows in (M, 1):
+        y = gpu_gemm(dmq, "q4k", x[:m_rows], wq, m_rows, N, K)
+        ref, s = oracle.gemm_quant("q4k", x[:m_rows], wq, N, K)
+        assert_within(y, ref, s, f"cancellation M={m_rows}")
+
+
+def test_gemm_large_k_m1(dmq):
+    # K beyond the decode kernel's LDS staging: M = 1 runs the MFMA kernel
+    M, N, K = 1, 24, 33024
+    x = synthetic.activations(M, K, seed=1)
+    wq = synthetic.q4k_blocks(N, K, seed=2)
+    y = gpu_gemm(dmq, "q4k", x, wq, M, N, K)
+    ref, s = oracle.gemm_quant("q4k", x, wq, N, K)
+    assert_within(y, ref, s, "gemm K=33024 M=1")
+
+
+def _layer_group(dmq, config, layer, M, unit_rms=True):
+    """Inputs and outputs of one layer's 7 projections (O and down get their
+    own activations), as the benchmark builds them."""
+    items = []
+    for idx, (name, fmt, N, K, wq) in enumerate(synthetic.layer_weights(config, layer)):
+        x = synthetic.activations(M, K, seed=synthetic.act_seed(config, layer, idx), unit_rms=unit_rms)
+        items.append((name, fmt, N, K, wq, x))
+    return items
+
+
+def test_gemm_config2_group_sampled(dmq):
+    M = 1024
+    items = _layer_group(dmq, 2, 0, M)
+    # Q, K, V, gate, up share their input in a real layer; here each has its
+    # own seeded input as in the benchmark
+    probs, host = [], []
+    for name, fmt, N, K, wq, x in items:
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        probs.append((fmt, dev(x), dev(wq.reshape(-1)), y, M, N, K))
+        host.append((name, fmt, N, K, wq, x, y))
+    dmq.dmq_gemm_group(probs)
+    torch.cuda.synchronize()
+    rows = synthetic.row_sample(M, 24, seed=3)
+    for name, fmt, N, K, wq, x, y in host:
+        ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
+        assert_within(y.cpu().numpy()[rows], ref, s, f"config2 {name} M={M} (rows {len(rows)})")
+
+
+def test_gemm_group_equals_single_calls(dmq):
+    M = 300
+    items = _layer_group(dmq, 2, 1, M)
+    probs, singles = [], []
+    for name, fmt, N, K, wq, x in items:
+        xd, wd = dev(x), dev(wq.reshape(-1))
+        probs.append((fmt, xd, wd, torch.empty((M, N), dtype=torch.float32, device=DEV), M, N, K))
+        singles.append((fmt, xd, wd, torch.empty((M, N), dtype=torch.float32, device=DEV), M, N, K))
+    dmq.dmq_gemm_group(probs)
+    for fmt, xd, wd, ys, M_, N, K in singles:
+        (dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k)(xd, wd, ys, M_, N, K)
+    torch.cuda.synchronize()
+    for p, s_ in zip(probs, singles):
+        assert torch.equal(p[3], s_[3])
+
+
+@pytest.mark.parametrize("M", [2048, 4096])
+def test_gemm_config4_large_m_sampled(dmq, M):
+    name, fmt, N, K = synthetic.LAYER_PROJECTIONS[0]
+    wq = synthetic.weight_blocks(fmt, N, K, seed=synthetic.weight_seed(4, 27, 0))
+    x = synthetic.activations(M, K, seed=synthetic.act_seed(4, 27, 0), unit_rms=True)
+    y = gpu_gemm(dmq, fmt, x, wq, M, N, K)
+    rows = synthetic.row_sample(M, 40, seed=M)
+    ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
+    assert_within(y[rows], ref, s, f"config4 q M={M}")
+    down = synthetic.LAYER_PROJECTIONS[6]
+    wq6 = synthetic.weight_blocks("q6k", down[2], down[3], seed=synthetic.weight_seed(4, 27, 6))
+    x6 = synthetic.activations(M, down[3], seed=synthetic.act_seed(4, 27, 6), unit_rms=True)
+    y6 = gpu_gemm(dmq, "q6k", x6, wq6, M, down[2], down[3])
+    ref6, s6 = oracle.gemm_quant("q6k", x6[rows], wq6, down[2], down[3])
+    assert_within(y6[rows], ref6, s6, f"config4 down M={M}")
+
+
+def test_lm_head_sampled(dmq):
+    name, fmt, N, K = synthetic.LM_HEAD
+    M = 1024
+    wq = synthetic.lm_head_weights(4)
+    x = synthetic.activations(M, K, seed=synthetic.act_seed(4, 0, synthetic.LM_HEAD_INDEX), unit_rms=True)
+    y = gpu_gemm(dmq, fmt, x, wq, M, N, K)
+    rows = synthetic.row_sample(M, 8, seed=4)
+    # one weight row per 256-row N tile plus the ragged end, dequantised alone
+    rng = np.random.default_rng(8)
+    ncols = np.unique(np.concatenate([np.arange(0, N, 256) + rng.integers(0, 256, (N + 255) // 256),
+                                      [N - 1]]))
+    ncols = ncols[ncols < N]
+    wrow = wq.reshape(N, -1)[ncols]
+    ref, s = oracle.gemm_quant(fmt, x[rows], wrow, len(ncols), K)
+    assert_within(y[np.ix_(rows, ncols)], ref, s, f"lm_head M={M} ({len(rows)}x{len(ncols)} outputs)")
+
+
+# ------------------------------------------------------------------- FFN ---
+
+def run_ffn(dmq, x, wgu, wd, M, D, F):
+    h = torch.empty((M, F), dtype=torch.float16, device=DEV)
+    y = torch.empty((M, D), dtype=torch.float32, device=DEV)
+    dmq.dmq_ffn_swiglu_q4k(dev(x), dev(wgu.reshape(-1)), dev(wd.reshape(-1)), h, y, M, D, F)
+    torch.cuda.synchronize()
+    return h.cpu().numpy(), y.cpu().numpy()
+
+
+def check_ffn(x, wgu, wd, h, y, D, F, rows, what):
+    # stage 1: h against the SwiGLU interval of the oracle's g, u
+    gu, s = oracle.gemm_quant("q4k", x[rows], wgu, 2 * F, D)
+    eg = oracle.gemm_tolerance(s)
+    g, u = gu[:, :F], gu[:, F:]
+    lo, hi = oracle.swiglu_interval(g, u, eg[:, :F], eg[:, F:])
+    hv = h[rows].astype(np.float64)
+    ok = oracle.swiglu_accepts(hv, lo, hi)
+    assert ok.all(), f"{what} h: {int((~ok).sum())} of {ok.size} outside the interval"
+    overflow = float(np.mean(~np.isfinite(hv)))
+    # stage 2: down projection of the GPU's own h
+    ref, sd = oracle.gemm_quant("q6k", h[rows], wd, D, F)
+    yr = y[rows].astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(yr), np.isnan(ref)), f"{what} y: NaN pattern differs"
+    assert np.array_equal(yr[~fin & ~np.isnan(ref)], ref[~fin & ~np.isnan(ref)]), f"{what} y: inf differs"
+    if fin.any():
+        err = np.abs(yr[fin] - ref[fin])
+        tol = oracle.gemm_tolerance(sd[fin])
+        assert np.all(err <= tol), f"{what} y: {int((err > tol).sum())} outputs outside the bound"
+    print(f"{what}: h overflow fraction {overflow:.4f}")
+    return overflow
+
+
+def _ffn_weights(config):
+    D, F = synthetic.HIDDEN, synthetic.FFN
+    wgu = synthetic.q4k_blocks(2 * F, D, seed=synthetic.weight_seed(config, 0, 4))
+    wd = synthetic.q6k_blocks(D, F, seed=synthetic.weight_seed(config, 0, 6))
+    return D, F, wgu, wd
+
+
+@pytest.mark.parametrize("sigma", [1.0, 1.0 / 16])
+def test_ffn_config3_sampled(dmq, sigma):
+    D, F, wgu, wd = _ffn_weights(3)
+    M = 1024
+    x = synthetic.activations(M, D, seed=synthetic.act_seed(3, 0, 0), sigma=sigma)
+    h, y = run_ffn(dmq, x, wgu, wd, M, D, F)
+    rows = synthetic.row_sample(M, 12, seed=5)
+    ov = check_ffn(x, wgu, wd, h, y, D, F, rows, f"config3 sigma={sigma}")
+    if sigma < 1:
+        assert ov == 0.0
+
+
+def test_ffn_decode_m1(dmq):
+    D, F, wgu, wd = _ffn_weights(3)
+    x = synthetic.activations(1, D, seed=12, sigma=1.0 / 16)
+    h, y = run_ffn(dmq, x, wgu, wd, 1, D, F)
+    check_ffn(x, wgu, wd, h, y, D, F, np.array([0]), "ffn decode M=1")
+
+
+@pytest.mark.parametrize("M,D,F", [(2, 256, 512), (40, 512, 768), (300, 768, 256), (1, 512, 1024)])
+def test_ffn_small_every_output(dmq, M, D, F):
+    wgu = synthetic.q4k_blocks(2 * F, D, seed=M + D)
+    wd = synthetic.q6k_blocks(D, F, seed=M + F)
+    x = synthetic.activations(M, D, seed=M * 3, sigma=0.25)
+    h, y = run_ffn(dmq, x, wgu, wd, M, D, F)
+    check_ffn(x, wgu, wd, h, y, D, F, np.arange(M), f"ffn {M}x{D}x{F}")
+
+
+def test_single_hip_runtime_and_native_library(dmq):
+    """The library runs on the same HIP runtime as torch (one libamdhip64 and
+    one libhsa-runtime64 mapped) and is the in-tree build."""
+    torch.zeros(1, device=DEV)
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {l.split()[-1] for l in maps if len(l.split()) >= 6}
+    hip = {p for p in paths if "libamdhip64" in p}
+    hsa = {p for p in paths if "libhsa-runtime64" in p}
+    assert len(hip) == 1, hip
+    assert len(hsa) == 1, hsa
+    assert dmq.LIB_PATH in paths
