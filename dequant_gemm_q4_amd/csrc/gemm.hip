@@ -1,29 +1,37 @@
 // Prefill kernel (M >= 2): y = x * W^T with the Q4_K / Q6_K dequant fused into
-// an MFMA fp16 x fp16 -> fp32 contraction.  Prefill is matrix-matrix work
-// where each weight is reused across all prompt rows (overview page, "[01]
+// an MFMA fp16 x fp16 -> fp32 contraction.  Prefill is matrix-matrix work in
+// which every weight is reused across all prompt rows (overview page, "[01]
 // the thesis": prefill is dense, compute-bound GEMM; article "Building
 // DAMASCUS", "Prefill and decode need different performance questions"), and
 // the fused dequant never writes fp16 weights to memory (overview page, same
 // section, and compartment 09 "fused dequant -> ... prefill").
 //
-// Work decomposition (one workgroup = 4 waves = one BM x BN output tile):
-//  * Each wave owns 16*IB weight rows and all BM = 16*JB activation rows.  It
-//    decodes its raw blocks straight into MFMA A-operand registers, so every
-//    weight is dequantised once per workgroup and no dequantised tile touches
-//    LDS or HBM.
-//  * x is staged in LDS per 64-wide K chunk (double-buffered) and read as the
-//    MFMA B operand by all 4 waves.
-//  * Sub-block scales / mins are decoded once per super-block and row into an
-//    LDS table (double-buffered), so the per-lane work per weight is: build
-//    the fp16 integer q (bit tricks), one fp32 FMA of exact operands
-//    (q*d*sc - dmin*m, v_fma_mix) and one rounding to fp16.
-//  * v_mfma_f32_16x16x32_f16: A = 16 weight rows x 32 k, B = 32 k x 16
-//    activation rows; lane l holds row/col l%16 and k = 8*(l/16) .. +7, and
-//    the accumulator lane holds D[4*(l/16) + r][l%16], r = 0..3.  One
-//    sub-block (32 weights) is exactly one MFMA K step.
-//  * Optional SwiGLU epilogue: a wave's first IB/2 i-blocks are gate rows and
-//    the last IB/2 the matching up rows, so g and u of one output sit in the
-//    same lane and h = silu(g) * u is formed in registers.
+// One workgroup = 4 waves = one BM x BN output tile, BM = 32*JB activation
+// rows, BN = 4 * 32*IB weight rows.
+//  * Each wave owns 32*IB weight rows and all BM activation rows.  It decodes
+//    its raw blocks straight into MFMA A-operand registers: every weight is
+//    dequantised once per workgroup and no dequantised tile touches LDS or
+//    HBM.
+//  * x is staged in LDS per 64-wide K chunk by direct global->LDS loads
+//    (global_load_lds_dwordx4, no VGPR staging), double-buffered, with the
+//    16-byte chunks of each 128-byte row XOR-swizzled by (row & 7) so that
+//    eight consecutive rows read the same column without bank conflicts.
+//  * Sub-block scales / mins are decoded once per super-block and weight row
+//    into an LDS table (double-buffered).  Per weight the lanes then do: mask
+//    and byte-permute the quant into an fp16 integer (1024 + q), subtract
+//    1024 (exact), and one fp32 FMA of exact operands (q*d*sc - dmin*m) with a
+//    single rounding to fp16 (v_fma_mix).
+//  * v_mfma_f32_32x32x16_f16: lane l holds operand row l%32 and k-slots
+//    8*(l/32) .. +7; the accumulator lane holds D[8*(r/4) + 4*(l/32) + r%4]
+//    [l%32], r = 0..15.  The K order inside a 64-wide chunk is permuted (the
+//    same way for both operands) so that each lane's 8 weights of a step come
+//    from 8 consecutive quant bytes: step s, lane half g, slot e covers
+//    k = 32*(s/2) + 16*g + 8*(s%2) + e.
+//  * Dequant of the next K step is issued between the MFMAs of the current
+//    one, so VALU work overlaps the matrix core.
+//  * Optional SwiGLU epilogue: a wave's first i-block holds gate rows, its
+//    second the matching up rows, so g and u of one output sit in the same
+//    lane and h = silu(g) * u is formed in registers.
 #include "dmq_common.h"
 
 namespace dmq {
@@ -43,105 +51,89 @@ struct GemmArgs {
   int32_t count;
 };
 
+typedef float f16x __attribute__((ext_vector_type(16)));
+
 template <int JB, int IB>
 struct TileCfg {
-  static constexpr int BM = 16 * JB;           // activation rows per tile
-  static constexpr int BN = 64 * IB;           // weight rows per tile (4 waves)
-  static constexpr int XSTRIDE = 72;           // halves per LDS x row: 64 + 8 pad
-  static constexpr int XTILE = BM * XSTRIDE;   // halves per x buffer
-  static constexpr int TSTRIDE = 20;           // floats per table row: 16 + 4 pad
-  static constexpr int TAB = BN * TSTRIDE;     // floats per table buffer
-  static constexpr int XLOADS = BM * 8;        // 16-byte x loads per chunk
-  static constexpr int XR = (XLOADS + 255) / 256;
-  static constexpr size_t LDS_BYTES = 2 * XTILE * sizeof(half_t) + 2 * TAB * sizeof(float);
+  static constexpr int BM = 32 * JB;                 // activation rows per tile
+  static constexpr int BN = 128 * IB;                // weight rows per tile
+  static constexpr int XBUF = BM * 128;              // bytes per x buffer (64 fp16 per row)
+  static constexpr int TSTRIDE = 20;                 // floats per table row (16 + 4 pad)
+  static constexpr int TBUF = BN * TSTRIDE * 4;      // bytes per table buffer
+  static constexpr size_t LDS_BYTES = 2 * XBUF + 2 * TBUF;
 };
 
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-// 8 fp16 weights (4 dwords) of the A operand from 8 nibbles-in-bytes.
-// `nib` words hold 4 quants each in the low (mask 0x0f) or, read as 16q, the
-// high (mask 0xf0) half of every byte; w = q * dsc + ndm, exact in fp32,
-// then one rounding to fp16.
+// fp16 pair (q0, q1) -> (fp16(q0*s + c), fp16(q1*s + c)): one fp32 FMA per
+// element with a single rounding to fp16.  Written as one h2 of two fmaf so
+// that the compiler selects v_fma_mixlo/hi_f16 (fp16 inputs, fp32 FMA).
+__device__ __forceinline__ uint32_t fma_mix_pair(uint32_t q, float s, float c) {
+  const h2 v = as_h2(q);
+  const h2 r = {(half_t)__builtin_fmaf((float)v.x, s, c), (half_t)__builtin_fmaf((float)v.y, s, c)};
+  return as_u32(r);
+}
+
+__device__ __forceinline__ uint32_t pk_sub(uint32_t a, uint32_t k) {
+  return as_u32(as_h2(a) - as_h2(k));
+}
+
+// Four quant bytes (each < 64) -> two fp16 pairs of (q - off).
+__device__ __forceinline__ void bytes_to_pairs(uint32_t b, uint32_t koff, uint32_t& p0, uint32_t& p1) {
+  p0 = pk_sub(magic_pair_lo(b), koff);
+  p1 = pk_sub(magic_pair_hi(b), koff);
+}
+
+constexpr uint32_t K1024 = 0x64006400u;   // fp16 pair (1024, 1024)
+constexpr uint32_t K1056 = 0x64206420u;   // fp16 pair (1056, 1056): 1024 + 32
+
+// 8 Q4_K weights (one A fragment) from two quant dwords.
 __device__ __forceinline__ h8 q4k_frag(uint32_t w0, uint32_t w1, uint32_t mask, float dsc, float ndm) {
-  const h2 k1024 = {(half_t)1024.0f, (half_t)1024.0f};
-  uint32_t a = w0 & mask, b = w1 & mask;
-  h2 q[4] = {as_h2(magic_pair_lo(a)) - k1024, as_h2(magic_pair_hi(a)) - k1024,
-             as_h2(magic_pair_lo(b)) - k1024, as_h2(magic_pair_hi(b)) - k1024};
-  h8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[2 * i] = (half_t)__builtin_fmaf((float)q[i].x, dsc, ndm);
-    r[2 * i + 1] = (half_t)__builtin_fmaf((float)q[i].y, dsc, ndm);
-  }
-  return r;
+  uint32_t a0, a1, b0, b1;
+  bytes_to_pairs(w0 & mask, K1024, a0, a1);
+  bytes_to_pairs(w1 & mask, K1024, b0, b1);
+  u32x4 r = {fma_mix_pair(a0, dsc, ndm), fma_mix_pair(a1, dsc, ndm), fma_mix_pair(b0, dsc, ndm),
+             fma_mix_pair(b1, dsc, ndm)};
+  return __builtin_bit_cast(h8, r);
 }
 
-// 8 fp16 weights of a Q6_K quarter t: q = low nibble (shifted by nsh) | two
-// high bits << 4, w = (q - 32) * dsc (exact in fp32, one rounding).
-__device__ __forceinline__ h8 q6k_frag(uint2 ql, uint2 qh, uint32_t nsh, uint32_t hsh, float dsc) {
-  const h2 k1056 = {(half_t)1056.0f, (half_t)1056.0f};
-  uint32_t a = ((ql.x >> nsh) & 0x0f0f0f0fu) | (((qh.x >> hsh) & 0x03030303u) << 4);
-  uint32_t b = ((ql.y >> nsh) & 0x0f0f0f0fu) | (((qh.y >> hsh) & 0x03030303u) << 4);
-  h2 q[4] = {as_h2(magic_pair_lo(a)) - k1056, as_h2(magic_pair_hi(a)) - k1056,
-             as_h2(magic_pair_lo(b)) - k1056, as_h2(magic_pair_hi(b)) - k1056};
-  h8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[2 * i] = (half_t)((float)q[i].x * dsc);
-    r[2 * i + 1] = (half_t)((float)q[i].y * dsc);
-  }
-  return r;
+// 8 Q6_K weights: low nibbles (shifted by nsh) | two high bits (at hsh) << 4.
+__device__ __forceinline__ h8 q6k_frag(uint32_t l0, uint32_t l1, uint32_t h0, uint32_t h1, uint32_t nsh,
+                                       uint32_t hsh, float dsc) {
+  uint32_t q0 = ((l0 >> nsh) & 0x0f0f0f0fu) | (((h0 >> hsh) << 4) & 0x30303030u);
+  uint32_t q1 = ((l1 >> nsh) & 0x0f0f0f0fu) | (((h1 >> hsh) << 4) & 0x30303030u);
+  uint32_t a0, a1, b0, b1;
+  bytes_to_pairs(q0, K1056, a0, a1);
+  bytes_to_pairs(q1, K1056, b0, b1);
+  u32x4 r = {fma_mix_pair(a0, dsc, 0.0f), fma_mix_pair(a1, dsc, 0.0f), fma_mix_pair(b0, dsc, 0.0f),
+             fma_mix_pair(b1, dsc, 0.0f)};
+  return __builtin_bit_cast(h8, r);
 }
 
-// Load / store helpers of the K-chunk pipeline.  Arrays are passed by
-// reference into force-inlined functions with compile-time trip counts so
-// that they stay in registers.
-template <int JB, int IB, int XR>
-__device__ __forceinline__ void x_load(u32x4 (&xr)[XR], const half_t* x, int m0, int M, int K, int ck, int tid) {
-  typedef TileCfg<JB, IB> C;
-#pragma unroll
-  for (int i = 0; i < C::XR; ++i) {
-    int e = tid + 256 * i;
-    if (e < C::XLOADS) {
-      int r = e >> 3;
-      int m = m0 + r < M ? m0 + r : M - 1;      // ragged M: repeat the last row
-      xr[i] = *(const u32x4*)(x + (int64_t)m * K + 64 * ck + 8 * (e & 7));
-    }
-  }
-}
-
-template <int JB, int IB, int XR>
-__device__ __forceinline__ void x_store(const u32x4 (&xr)[XR], half_t* xs, int tid) {
-  typedef TileCfg<JB, IB> C;
-#pragma unroll
-  for (int i = 0; i < C::XR; ++i) {
-    int e = tid + 256 * i;
-    if (e < C::XLOADS) *(u32x4*)(xs + (e >> 3) * C::XSTRIDE + 8 * (e & 7)) = xr[i];
-  }
-}
-
-// Scale-table header of one block: Q4_K bytes 0..15 (d, dmin, 12 scale
-// bytes); Q6_K bytes 192..209 (16 scales, d) read through the enclosing
-// aligned dwords without touching anything past byte 209.
+// Block header for the scale table.  Q4_K: bytes 0..15 (d, dmin, 12 scale
+// bytes).  Q6_K: bytes 192..209 (16 int8 scales, fp16 d), read through the
+// enclosing aligned dwords without touching anything past byte 209.
 template <int FMT>
-__device__ __forceinline__ void hdr_load(const uint8_t* blk, uint4& hdr, uint32_t& hdr4) {
+__device__ __forceinline__ void hdr_load(const uint8_t* blk, u32x4& hdr, uint32_t& hdr4) {
   if constexpr (FMT == 0) {
-    hdr = *(const uint4*)blk;
+    hdr = *(const u32x4*)blk;
   } else {
-    uintptr_t a = (uintptr_t)(blk + 192);
-    const uint32_t* sp = (const uint32_t*)(a & ~(uintptr_t)3);
-    hdr = *(const uint4*)sp;
-    hdr4 = (a & 3) ? sp[4] : (uint32_t)(*(const uint16_t*)(blk + 208)) << 16;
+    const uint8_t* p = blk + 192;
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    const uint32_t* sp = (const uint32_t*)(p - sh);
+    hdr = (u32x4){sp[0], sp[1], sp[2], sp[3]};
+    hdr4 = sh ? sp[4] : (uint32_t)(*(const uint16_t*)(blk + 208)) << 16;
   }
 }
 
-// Decode one row's header into 16 floats of the LDS table.
-// Q4_K: (d*sc_j [/16 for odd j, whose quant is read as 16q], -dmin*m_j) pairs.
-// Q6_K: d*sc_s for the 16 sub-blocks.
+// Decode one header into 16 floats of the table row.
+//  Q4_K: pairs (d*sc_j, -dmin*m_j), with d*sc_j / 16 for odd j (their quant
+//        is read from the high nibble as 16q).
+//  Q6_K: d*sc_s for the 16 sub-blocks.
 template <int FMT>
-__device__ __forceinline__ void tab_store(float* t, const uint4& hdr, uint32_t hdr4, uint32_t sh) {
+__device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t hdr4, uint32_t sh) {
   float v[16];
   if constexpr (FMT == 0) {
     Q4kScales s = unpack_q4k_scales(hdr.y, hdr.z, hdr.w);
@@ -153,7 +145,7 @@ __device__ __forceinline__ void tab_store(float* t, const uint4& hdr, uint32_t h
       v[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
     }
   } else {
-    // sh = block address mod 4 (0 or 2); with sh == 0 d sits in hdr4's high half
+    // sh = block address mod 4; with sh == 0 the d field sits in hdr4's high half
     uint32_t w[4] = {__builtin_amdgcn_alignbyte(hdr.y, hdr.x, sh), __builtin_amdgcn_alignbyte(hdr.z, hdr.y, sh),
                      __builtin_amdgcn_alignbyte(hdr.w, hdr.z, sh), __builtin_amdgcn_alignbyte(hdr4, hdr.w, sh)};
     float d = half_bits_to_float(hdr4 >> 16);
@@ -164,227 +156,330 @@ __device__ __forceinline__ void tab_store(float* t, const uint4& hdr, uint32_t h
   for (int i = 0; i < 4; ++i) ((float4*)t)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
 }
 
-// Raw quant bytes of one 64-wide K chunk for one lane and i-block.
-// Q4_K: 8 quant bytes (k = 8g .. 8g+7 of both sub-blocks of the chunk).
-// Q6_K: low-nibble bytes of quarters t and t+1 and the high-bit bytes; all
-// 8-byte fields at 2-aligned addresses, read by load_u64_a2 inside the block
-// (last byte read <= 196 < 210).
+// 16 consecutive bytes at a 2-aligned address (Q6_K fields), through the
+// enclosing aligned dwords (at most 2 bytes before, 4 after the field).
+__device__ __forceinline__ u32x4 load16_a2(const uint8_t* p) {
+  const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+  const uint32_t* q = (const uint32_t*)(p - sh);
+  uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3], w4 = q[4];
+  return (u32x4){__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
+                 __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh)};
+}
+
+// Raw quant bytes of one lane and i-block.
+//  Q4_K, per 64-wide chunk: quant bytes 32p + 16g .. +16 (p = chunk in block).
+//  Q6_K, per 128-weight half h (two chunks): low-nibble bytes 64h + 16g and
+//  64h + 32 + 16g, high-bit bytes 128 + 32h + 16g (16 each; the last byte
+//  read is at most 176 + 20 = 196 < 210).
+struct RawQ4 { u32x4 q; };
+struct RawQ6 { u32x4 la, lb, hb; };
+template <int FMT> struct RawOf { typedef RawQ4 T; };
+template <> struct RawOf<1> { typedef RawQ6 T; };
+
 template <int FMT>
-__device__ __forceinline__ void raw_load(const uint8_t* wrow, int ck, int g, uint2& a, uint2& b, uint2& c) {
-  const int blk_i = ck >> 2, cc = ck & 3;
+__device__ __forceinline__ void raw_load(const uint8_t* wrow, int ck, int g, typename RawOf<FMT>::T& r) {
+  const int bi = ck >> 2, cc = ck & 3;
   if constexpr (FMT == 0) {
-    a = *(const uint2*)(wrow + (int64_t)blk_i * Q4K_BYTES + 16 + 32 * cc + 8 * g);
+    r.q = *(const u32x4*)(wrow + (int64_t)bi * Q4K_BYTES + 16 + 32 * cc + 16 * g);
   } else {
-    const uint8_t* blk = wrow + (int64_t)blk_i * Q6K_BYTES;
+    const uint8_t* blk = wrow + (int64_t)bi * Q6K_BYTES;
     const int h = cc >> 1;
-    a = load_u64_a2(blk + 64 * h + 8 * g);
-    b = load_u64_a2(blk + 64 * h + 32 + 8 * g);
-    c = load_u64_a2(blk + 128 + 32 * h + 8 * g);
+    r.la = load16_a2(blk + 64 * h + 16 * g);
+    r.lb = load16_a2(blk + 64 * h + 32 + 16 * g);
+    r.hb = load16_a2(blk + 128 + 32 * h + 16 * g);
   }
 }
 
+// A fragment of K step s (0..3) of chunk cc from the raw bytes.
+template <int FMT>
+__device__ __forceinline__ h8 a_frag(const typename RawOf<FMT>::T& r, int s, int cc, const float (&sv)[4]) {
+  if constexpr (FMT == 0) {
+    const uint32_t w0 = (s & 1) ? r.q.z : r.q.x;
+    const uint32_t w1 = (s & 1) ? r.q.w : r.q.y;
+    return s < 2 ? q4k_frag(w0, w1, 0x0f0f0f0fu, sv[0], sv[1]) : q4k_frag(w0, w1, 0xf0f0f0f0u, sv[2], sv[3]);
+  } else {
+    const u32x4& l = (s >> 1) ? r.lb : r.la;
+    const uint32_t l0 = (s & 1) ? l.z : l.x, l1 = (s & 1) ? l.w : l.y;
+    const uint32_t h0 = (s & 1) ? r.hb.z : r.hb.x, h1 = (s & 1) ? r.hb.w : r.hb.y;
+    const uint32_t nsh = (cc & 1) ? 4u : 0u;
+    const uint32_t hsh = 4u * (uint32_t)(cc & 1) + 2u * (uint32_t)(s >> 1);
+    return q6k_frag(l0, l1, h0, h1, nsh, hsh, sv[s >> 1]);
+  }
+}
+
+// Global weight row of local row 32*IB*w + 32*c + i, clamped for a ragged N.
+// SwiGLU (IB == 2): i-block 0 holds gate rows, i-block 1 the matching up rows.
+template <int IB, bool SWIGLU>
+__device__ __forceinline__ int weight_row(int w, int c, int i, int n0, int hb, int F, int N) {
+  int r = SWIGLU ? (c == 0 ? 0 : F) + hb + 32 * w + i : n0 + 32 * IB * w + 32 * c + i;
+  return r < N ? r : N - 1;
+}
+
+// Direct global -> LDS load of one 64-wide x chunk: wave-instruction q (of
+// BM/8) fills LDS rows 8q .. 8q+7 (1 KiB, lane t at byte 16t).
+template <int JB, int IB, int XQ>
+__device__ __forceinline__ void load_x(const half_t* (&xsrc)[XQ], int ck, uint8_t* xd, int wave) {
+#pragma unroll
+  for (int i = 0; i < XQ; ++i) {
+    const int q = 4 * i + wave;
+    if (q < TileCfg<JB, IB>::BM / 8)
+      __builtin_amdgcn_global_load_lds(xsrc[i] + 64 * ck, (__attribute__((address_space(3))) void*)(xd + q * 1024), 16,
+                                       0, 0);
+  }
+}
+
+// x0 / x1 (BM rows x 128 B each) and tab (2 x BN x TSTRIDE floats) are
+// distinct LDS objects: the compiler's wait-count tracking then knows that
+// reading one x buffer does not depend on the direct loads into the other.
 template <int FMT, int JB, int IB, bool SWIGLU>
-__device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, uint8_t* smem) {
+__device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, uint8_t* x0, uint8_t* x1,
+                                          float* tab) {
   typedef TileCfg<JB, IB> C;
+  typedef typename RawOf<FMT>::T Raw;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
-  half_t* xs = (half_t*)smem;
-  float* tab = (float*)(smem + 2 * C::XTILE * sizeof(half_t));
+  constexpr int XQ = (C::BM / 8 + 3) / 4;            // x load instructions per wave per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, g = lane >> 4;
+  const int li = lane & 31, g = lane >> 5;
   const int M = P.M, N = P.N, K = P.K;
   const int nck = K / 64;
   const int64_t row_bytes = (int64_t)(K / QK) * BLOCK_BYTES;
   const int m0 = m_tile * C::BM;
-  const int F = N / 2;                       // SwiGLU: gate rows [0,F), up rows [F,2F)
-  const int hb = n_tile * (C::BN / 2);       // SwiGLU: first h column of the tile
+  const int F = N / 2;                               // SwiGLU: gate rows [0,F), up rows [F,2F)
+  const int hb = n_tile * (C::BN / 2);               // SwiGLU: first h column of the tile
   const int n0 = n_tile * C::BN;
 
-  // weight row of local row lr (0..BN), clamped for a ragged N
   const uint8_t* wrow[IB];
 #pragma unroll
-  for (int c = 0; c < IB; ++c) {
-    int r;
-    if (SWIGLU) {
-      int base = hb + (8 * IB) * wave + li;
-      r = c < IB / 2 ? base + 16 * c : F + base + 16 * (c - IB / 2);
-    } else {
-      r = n0 + 16 * IB * wave + 16 * c + li;
-    }
-    r = r < N ? r : N - 1;
-    wrow[c] = P.wq + (int64_t)r * row_bytes;
-  }
-  // the table row this thread decodes (threads 0..BN-1, local row = tid)
-  const uint8_t* trow;
-  {
-    int lr = tid < C::BN ? tid : 0, r;
-    if (SWIGLU) {
-      int w = lr / (16 * IB), c = (lr / 16) % IB, i = lr & 15;
-      int base = hb + (8 * IB) * w + i;
-      r = c < IB / 2 ? base + 16 * c : F + base + 16 * (c - IB / 2);
-    } else {
-      r = n0 + lr;
-    }
-    r = r < N ? r : N - 1;
-    trow = P.wq + (int64_t)r * row_bytes;
-  }
-  float* my_tab = tab + tid * C::TSTRIDE;
+  for (int c = 0; c < IB; ++c)
+    wrow[c] = P.wq + (int64_t)weight_row<IB, SWIGLU>(wave, c, li, n0, hb, F, N) * row_bytes;
+  const bool tab_thread = tid < C::BN;
+  const int tt = tab_thread ? tid : 0;
+  const uint8_t* trow =
+      P.wq + (int64_t)weight_row<IB, SWIGLU>(tt / (32 * IB), (tt / 32) % IB, tt & 31, n0, hb, F, N) * row_bytes;
+  float* my_tab = tab + tt * C::TSTRIDE;
 
-  f4 acc[JB][IB];
+  // x loader: wave-instruction q (of BM/8) fills LDS rows 8q .. 8q+7; lane t
+  // writes row r = 8q + t/8, slot t%8, which holds 16-byte chunk (t%8)^(r%8).
+  const int xr_row = lane >> 3;
+  const int xr_chunk = (lane & 7) ^ xr_row;
+  const half_t* xsrc[XQ];
+#pragma unroll
+  for (int i = 0; i < XQ; ++i) {
+    int m = m0 + 8 * (4 * i + wave) + xr_row;
+    m = m < M ? m : M - 1;                           // ragged M: repeat the last row
+    xsrc[i] = P.x + (int64_t)m * K + 8 * xr_chunk;
+  }
+
+  f16x acc[JB][IB];
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int c = 0; c < IB; ++c) acc[jb][c] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < IB; ++c) acc[jb][c] = (f16x){};
 
-  u32x4 xr[C::XR];
-  uint4 hdr = make_uint4(0, 0, 0, 0);
+  u32x4 hdr = {0, 0, 0, 0};
   uint32_t hdr4 = 0;
-  uint2 ra[IB], rb[IB], rc[IB];       // raw quant bytes of the current chunk
-  uint2 na[IB], nb[IB], nc[IB];       // ... and of the next one
+  Raw ra[IB], rn[IB];
 
-  x_load<JB, IB>(xr, P.x, m0, M, K, 0, tid);
-  if (tid < C::BN) hdr_load<FMT>(trow, hdr, hdr4);
+  // prologue: chunk 0 of x, table of block 0, raw bytes of chunk 0
+  load_x<JB, IB>(xsrc, 0, x0, wave);
+  if (tab_thread) hdr_load<FMT>(trow, hdr, hdr4);
 #pragma unroll
-  for (int c = 0; c < IB; ++c) raw_load<FMT>(wrow[c], 0, g, ra[c], rb[c], rc[c]);
-  x_store<JB, IB>(xr, xs, tid);
-  if (tid < C::BN) tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + 192) & 3));
+  for (int c = 0; c < IB; ++c) raw_load<FMT>(wrow[c], 0, g, ra[c]);
+  if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + 192) & 3));
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int ck = 0; ck < nck; ++ck) {
+  // B-fragment LDS offsets (bytes) of row li of j-block 0 for the 4 K steps:
+  // 16-byte chunk 4*(s/2) + 2*g + (s%2), swizzled by row & 7 (rows of other
+  // j-blocks differ by multiples of 32, so row & 7 == li & 7).
+  int boff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) boff[s] = li * 128 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ (li & 7));
+
+  // chunks in pairs (nck is a multiple of 4): the even chunk reads x0 while
+  // the next chunk streams into x1, the odd chunk the other way round
+  for (int ck2 = 0; ck2 < nck; ck2 += 2) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int ck = ck2 + half;
+    uint8_t* const xb = half ? x1 : x0;
+    uint8_t* const xnext = half ? x0 : x1;
     const bool has_next = ck + 1 < nck;
     const bool next_block = has_next && ((ck + 1) & 3) == 0;
-    if (has_next) {
-      x_load<JB, IB>(xr, P.x, m0, M, K, ck + 1, tid);
+    const bool next_raw = has_next && (FMT == 0 || ((ck + 1) & 1) == 0);
+    if (has_next) load_x<JB, IB>(xsrc, ck + 1, xnext, wave);
+    if (next_raw) {
 #pragma unroll
-      for (int c = 0; c < IB; ++c) raw_load<FMT>(wrow[c], ck + 1, g, na[c], nb[c], nc[c]);
-      if (next_block && tid < C::BN) hdr_load<FMT>(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES, hdr, hdr4);
+      for (int c = 0; c < IB; ++c) raw_load<FMT>(wrow[c], ck + 1, g, rn[c]);
     }
-    const int tbuf = (ck >> 2) & 1, cc = ck & 3;
-    const half_t* xb = xs + (ck & 1) * C::XTILE + li * C::XSTRIDE + 8 * g;
-    // scale values of this lane's rows for this chunk
+    if (next_block && tab_thread) hdr_load<FMT>(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES, hdr, hdr4);
+
+    const int cc = ck & 3;
+    const float* tb = tab + ((ck >> 2) & 1) * (C::TBUF / 4);
     float sv[IB][4];
 #pragma unroll
     for (int c = 0; c < IB; ++c) {
-      const float* t = tab + tbuf * C::TAB + (16 * IB * wave + 16 * c + li) * C::TSTRIDE;
+      const float* t = tb + (32 * IB * wave + 32 * c + li) * C::TSTRIDE;
       if constexpr (FMT == 0) {
         float4 v = *(const float4*)(t + 4 * cc);     // sub-blocks 2cc, 2cc+1
         sv[c][0] = v.x; sv[c][1] = v.y; sv[c][2] = v.z; sv[c][3] = v.w;
       } else {
-        const int h = cc >> 1, t0 = 2 * (cc & 1);
-        sv[c][0] = t[8 * h + 2 * t0 + (g >> 1)];
-        sv[c][1] = t[8 * h + 2 * (t0 + 1) + (g >> 1)];
+        const int base = 8 * (cc >> 1) + 4 * (cc & 1) + g;   // scale index 8h + 2t + g
+        sv[c][0] = t[base];
+        sv[c][1] = t[base + 2];
         sv[c][2] = 0.0f;
         sv[c][3] = 0.0f;
       }
     }
+    h8 af[IB], bf[JB];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      h8 af[IB];
+    for (int c = 0; c < IB; ++c) af[c] = a_frag<FMT>(ra[c], 0, cc, sv[c]);
 #pragma unroll
-      for (int c = 0; c < IB; ++c) {
-        if constexpr (FMT == 0) {
-          af[c] = ks == 0 ? q4k_frag(ra[c].x, ra[c].y, 0x0f0f0f0fu, sv[c][0], sv[c][1])
-                          : q4k_frag(ra[c].x, ra[c].y, 0xf0f0f0f0u, sv[c][2], sv[c][3]);
-        } else {
-          const int t = 2 * (cc & 1) + ks;
-          af[c] = q6k_frag(ks ? rb[c] : ra[c], rc[c], (cc & 1) ? 4u : 0u, 2u * (uint32_t)t, sv[c][ks]);
-        }
+    for (int jb = 0; jb < JB; ++jb) bf[jb] = *(const h8*)(xb + jb * 32 * 128 + boff[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8 afn[IB], bfn[JB];
+      if (s < 3) {
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(xb + jb * 32 * 128 + boff[s + 1]);
+#pragma unroll
+        for (int c = 0; c < IB; ++c) afn[c] = a_frag<FMT>(ra[c], s + 1, cc, sv[c]);
       }
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) {
-        h8 bf = *(const h8*)(xb + jb * 16 * C::XSTRIDE + 32 * ks);
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int c = 0; c < IB; ++c)
-          acc[jb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[c], bf, acc[jb][c], 0, 0, 0);
+          acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c], bf[jb], acc[jb][c], 0, 0, 0);
+      if (s < 3) {
+#pragma unroll
+        for (int c = 0; c < IB; ++c) af[c] = afn[c];
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
+      }
+      // Schedule of this step: the next step's B-fragment reads go first (their
+      // latency hides behind this step's MFMAs), then each MFMA is followed by
+      // a few VALU ops of the next step's dequant.
+      __builtin_amdgcn_sched_group_barrier(0x100, JB, 0);         // DS reads
+#pragma unroll
+      for (int i = 0; i < JB * IB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);        // VALU
       }
     }
-    if (has_next) {
-      x_store<JB, IB>(xr, xs + ((ck + 1) & 1) * C::XTILE, tid);
-      if (next_block && tid < C::BN)
-        tab_store<FMT>(my_tab + (((ck + 1) >> 2) & 1) * C::TAB, hdr, hdr4,
-                       (uint32_t)((uintptr_t)(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES + 192) & 3));
-    }
+    if (next_block && tab_thread)
+      tab_store<FMT>(my_tab + (((ck + 1) >> 2) & 1) * (C::TBUF / 4), hdr, hdr4,
+                     (uint32_t)((uintptr_t)(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES + 192) & 3));
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (next_raw) {
 #pragma unroll
-    for (int c = 0; c < IB; ++c) {
-      ra[c] = na[c];
-      rb[c] = nb[c];
-      rc[c] = nc[c];
+      for (int c = 0; c < IB; ++c) ra[c] = rn[c];
     }
   }
+  }
 
-  // ---- epilogue ----
+  // ---- epilogue: the lane holds rows 8q + 4g + e (q, e = 0..3) of each i-block ----
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb) {
-    const int m = m0 + 16 * jb + li;
+    const int m = m0 + 32 * jb + li;
     if (m >= M) continue;
     if (SWIGLU) {
-      half_t* h = (half_t*)P.out;
+      half_t* h = (half_t*)P.out + (int64_t)m * F;
+      const f16x& gv = acc[jb][0];
+      const f16x& uv = acc[jb][1];
 #pragma unroll
-      for (int c = 0; c < IB / 2; ++c) {
-        const int col = hb + (8 * IB) * wave + 16 * c + 4 * g;
-        f4 gv = acc[jb][c], uv = acc[jb][c + IB / 2];
-        h2 h01 = {(half_t)(silu_fast(gv[0]) * uv[0]), (half_t)(silu_fast(gv[1]) * uv[1])};
-        h2 h23 = {(half_t)(silu_fast(gv[2]) * uv[2]), (half_t)(silu_fast(gv[3]) * uv[3])};
-        *(uint2*)(h + (int64_t)m * F + col) = make_uint2(as_u32(h01), as_u32(h23));
+      for (int q = 0; q < 4; ++q) {
+        const int col = hb + 32 * wave + 8 * q + 4 * g;
+        h2 h01 = {(half_t)(silu_fast(gv[4 * q]) * uv[4 * q]), (half_t)(silu_fast(gv[4 * q + 1]) * uv[4 * q + 1])};
+        h2 h23 = {(half_t)(silu_fast(gv[4 * q + 2]) * uv[4 * q + 2]),
+                  (half_t)(silu_fast(gv[4 * q + 3]) * uv[4 * q + 3])};
+        *(uint2*)(h + col) = make_uint2(as_u32(h01), as_u32(h23));
       }
     } else {
-      float* y = (float*)P.out;
+      float* yrow = (float*)P.out + (int64_t)m * N;
 #pragma unroll
       for (int c = 0; c < IB; ++c) {
-        const int n = n0 + 16 * IB * wave + 16 * c + 4 * g;
-        float* yp = y + (int64_t)m * N + n;
-        f4 v = acc[jb][c];
-        if ((N & 3) == 0 && n + 3 < N) {
-          *(float4*)yp = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
+        const f16x& v = acc[jb][c];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) yp[r] = v[r];
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + 32 * IB * wave + 32 * c + 8 * q + 4 * g;
+          if ((N & 3) == 0 && n + 3 < N) {
+            *(float4*)(yrow + n) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) yrow[n + e] = v[4 * q + e];
+          }
         }
       }
     }
   }
 }
 
-template <int JB, int IB, bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// Workgroup -> (problem, tile).  Within a problem, tiles go in groups of 8
+// N-tiles x all M-tiles with the N-tile fastest, so workgroups bid, bid+8,
+// bid+16, ... (placed on the same XCD by the dispatcher) share one weight
+// panel in that XCD's L2 while the 8 XCDs work on 8 different panels.
+__device__ __forceinline__ const GemmDesc& tile_of(const GemmArgs& args, int& m_tile, int& n_tile) {
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < GEMM_MAX_GROUP; ++i)
     if (i < args.count && (int)blockIdx.x >= args.d[i].tile_begin) pi = i;
   const GemmDesc& P = args.d[pi];
-  // Tile order within a problem: groups of 8 N-tiles x all M-tiles, with the
-  // N-tile fastest, so workgroups bid, bid+8, bid+16, ... (which the
-  // dispatcher places on the same XCD) share one weight panel in that XCD's
-  // L2 while the 8 XCDs work on 8 different panels.
   const int o = (int)blockIdx.x - P.tile_begin;
   const int mt = P.mt, nt = P.nt;
   const int grp = o / (8 * mt);
   const int u = o - grp * 8 * mt;
   const int nrem = nt - 8 * grp < 8 ? nt - 8 * grp : 8;
-  const int m_tile = u / nrem;
-  const int n_tile = 8 * grp + (u - m_tile * nrem);
+  m_tile = u / nrem;
+  n_tile = 8 * grp + (u - m_tile * nrem);
+  return P;
+}
+
+template <int FMT, int JB, int IB, bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
+  typedef TileCfg<JB, IB> C;
+  __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
+  __shared__ __attribute__((aligned(16))) float tab[2 * C::TBUF / 4];
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+  int m_tile, n_tile;
+  const GemmDesc& P = tile_of(args, m_tile, n_tile);
+  gemm_tile<FMT, JB, IB, SWIGLU>(P, m_tile, n_tile, x0, x1, tab);
+#endif
+}
+
+// Mixed Q4_K / Q6_K groups: one kernel per format would serialise on the
+// stream, so this kernel branches per workgroup (uniformly) on the format.
+template <int JB, int IB>
+__global__ __launch_bounds__(256, 1) void gemm_kernel_mixed(GemmArgs args) {
+  typedef TileCfg<JB, IB> C;
+  __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
+  __shared__ __attribute__((aligned(16))) float tab[2 * C::TBUF / 4];
+#if defined(__HIP_DEVICE_COMPILE__)
+  int m_tile, n_tile;
+  const GemmDesc& P = tile_of(args, m_tile, n_tile);
   if (P.fmt == 0)
-    gemm_tile<0, JB, IB, SWIGLU>(P, m_tile, n_tile, smem);
+    gemm_tile<0, JB, IB, false>(P, m_tile, n_tile, x0, x1, tab);
   else
-    gemm_tile<1, JB, IB, SWIGLU>(P, m_tile, n_tile, smem);
+    gemm_tile<1, JB, IB, false>(P, m_tile, n_tile, x0, x1, tab);
+#endif
+}
+
+template <typename Kern>
+static hipError_t launch_one(Kern k, int tiles, const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k, dim3(tiles), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int JB, int IB, bool SWIGLU>
 static hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t s) {
   typedef TileCfg<JB, IB> C;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<JB, IB, SWIGLU>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   for (int base = 0; base < count; base += GEMM_MAX_GROUP) {
     GemmArgs a{};
     int n = count - base < GEMM_MAX_GROUP ? count - base : GEMM_MAX_GROUP;
-    int tiles = 0;
+    int tiles = 0, fmt_mask = 0;
     for (int i = 0; i < n; ++i) {
       const GemmProblem& p = probs[base + i];
       GemmDesc& d = a.d[i];
@@ -400,10 +495,19 @@ static hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t s)
       d.nt = SWIGLU ? (p.N / 2 + C::BN / 2 - 1) / (C::BN / 2) : (p.N + C::BN - 1) / C::BN;
       d.tile_begin = tiles;
       tiles += d.mt * d.nt;
+      fmt_mask |= 1 << p.fmt;
     }
     a.count = n;
-    hipLaunchKernelGGL((gemm_kernel<JB, IB, SWIGLU>), dim3(tiles), dim3(256), C::LDS_BYTES, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if constexpr (SWIGLU) {
+      e = launch_one(gemm_kernel<0, JB, IB, true>, tiles, a, s);
+    } else if (fmt_mask == 1) {
+      e = launch_one(gemm_kernel<0, JB, IB, false>, tiles, a, s);
+    } else if (fmt_mask == 2) {
+      e = launch_one(gemm_kernel<1, JB, IB, false>, tiles, a, s);
+    } else {
+      e = launch_one(gemm_kernel_mixed<JB, IB>, tiles, a, s);
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -412,15 +516,16 @@ static hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t s)
 // All problems of one call share the tile shape, picked from the largest M.
 hipError_t launch_gemm(const GemmProblem* probs, int count, hipStream_t s) {
   int mmax = 0;
-  bool swiglu = probs[0].swiglu != 0;
+  const bool swiglu = probs[0].swiglu != 0;
   for (int i = 0; i < count; ++i) mmax = probs[i].M > mmax ? probs[i].M : mmax;
   if (swiglu) {
-    if (mmax > 64) return launch_cfg<16, 4, true>(probs, count, s);
-    if (mmax > 16) return launch_cfg<4, 2, true>(probs, count, s);
+    if (mmax > 128) return launch_cfg<8, 2, true>(probs, count, s);
+    if (mmax > 32) return launch_cfg<2, 2, true>(probs, count, s);
     return launch_cfg<1, 2, true>(probs, count, s);
   }
-  if (mmax > 64) return launch_cfg<16, 4, false>(probs, count, s);
-  if (mmax > 16) return launch_cfg<4, 1, false>(probs, count, s);
+  if (mmax > 128) return launch_cfg<8, 2, false>(probs, count, s);
+  if (mmax > 64) return launch_cfg<4, 2, false>(probs, count, s);
+  if (mmax > 32) return launch_cfg<2, 1, false>(probs, count, s);
   return launch_cfg<1, 1, false>(probs, count, s);
 }
 
