@@ -17,6 +17,9 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Reduction length limit of the GEMM kernels: their buffer loads use 32-bit
+// offsets within one tile (256 rows of x, 32 rows of blocks).
+constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int kMaxGroup = 64;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -42,7 +45,7 @@ bool weight_bytes_ok(int fmt, int64_t n, int64_t k) {
 int check_gemm(int fmt, const void* x, const void* wq, const void* y, int64_t M, int64_t N, int64_t K) {
   if (!x || !y) return DMQ_ERR_INVALID_ARG;
   if (!dim_ok(M) || !dim_ok(N)) return DMQ_ERR_INVALID_ARG;
-  if (check_quant_k(K) != DMQ_OK) return DMQ_ERR_INVALID_ARG;
+  if (check_quant_k(K) != DMQ_OK || K > kMaxK) return DMQ_ERR_INVALID_ARG;
   int w = check_weights(fmt, wq);
   if (w != DMQ_OK) return w;
   if (!weight_bytes_ok(fmt, N, K)) return DMQ_ERR_INVALID_ARG;

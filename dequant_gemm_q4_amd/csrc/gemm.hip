@@ -156,37 +156,55 @@ __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t h
   for (int i = 0; i < 4; ++i) ((float4*)t)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
 }
 
-// 16 consecutive bytes at a 2-aligned address (Q6_K fields), through the
-// enclosing aligned dwords (at most 2 bytes before, 4 after the field).
-__device__ __forceinline__ u32x4 load16_a2(const uint8_t* p) {
-  const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
-  const uint32_t* q = (const uint32_t*)(p - sh);
-  uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3], w4 = q[4];
-  return (u32x4){__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
-                 __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh)};
+// Buffer resource (base, byte size) for the raw buffer loads: a 32-bit
+// per-lane offset plus a scalar per-chunk offset, so no 64-bit address math
+// per load, and loads past the end of the described range return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
 // Raw quant bytes of one lane and i-block.
 //  Q4_K, per 64-wide chunk: quant bytes 32p + 16g .. +16 (p = chunk in block).
 //  Q6_K, per 128-weight half h (two chunks): low-nibble bytes 64h + 16g and
-//  64h + 32 + 16g, high-bit bytes 128 + 32h + 16g (16 each; the last byte
-//  read is at most 176 + 20 = 196 < 210).
+//  64h + 32 + 16g, high-bit bytes 128 + 32h + 16g.  Blocks are 210 bytes, so
+//  a field may start 2 mod 4: it is read as the 5 enclosing aligned dwords
+//  (at most 2 bytes before and 4 after the field; the last byte read is at
+//  most 176 + 20 = 196 < 210) and shifted into place.
 struct RawQ4 { u32x4 q; };
 struct RawQ6 { u32x4 la, lb, hb; };
 template <int FMT> struct RawOf { typedef RawQ4 T; };
 template <> struct RawOf<1> { typedef RawQ6 T; };
 
+__device__ __forceinline__ u32x4 load16_a2(rsrc_t r, uint32_t lane_off, uint32_t uni_off) {
+  const uint32_t off = lane_off + uni_off;
+  const uint32_t sh = off & 3u;
+  const uint32_t v = off - sh;                   // aligned down; >= 0 since off >= sh
+  const u32x4 w = buf_load16(r, v, 0);
+  const uint32_t w4 = buf_load4(r, v + 16, 0);
+  return (u32x4){__builtin_amdgcn_alignbyte(w.y, w.x, sh), __builtin_amdgcn_alignbyte(w.z, w.y, sh),
+                 __builtin_amdgcn_alignbyte(w.w, w.z, sh), __builtin_amdgcn_alignbyte(w4, w.w, sh)};
+}
+
+// wr: this i-block's 32 weight rows; roff: li * row_bytes (+ 16 g for Q4_K)
 template <int FMT>
-__device__ __forceinline__ void raw_load(const uint8_t* wrow, int ck, int g, typename RawOf<FMT>::T& r) {
+__device__ __forceinline__ void raw_load(rsrc_t wr, uint32_t roff, int ck, int g, typename RawOf<FMT>::T& r) {
   const int bi = ck >> 2, cc = ck & 3;
   if constexpr (FMT == 0) {
-    r.q = *(const u32x4*)(wrow + (int64_t)bi * Q4K_BYTES + 16 + 32 * cc + 16 * g);
+    r.q = buf_load16(wr, roff, (uint32_t)(bi * Q4K_BYTES + 16 + 32 * cc));
   } else {
-    const uint8_t* blk = wrow + (int64_t)bi * Q6K_BYTES;
-    const int h = cc >> 1;
-    r.la = load16_a2(blk + 64 * h + 16 * g);
-    r.lb = load16_a2(blk + 64 * h + 32 + 16 * g);
-    r.hb = load16_a2(blk + 128 + 32 * h + 16 * g);
+    const uint32_t blk = (uint32_t)(bi * Q6K_BYTES), h = (uint32_t)(cc >> 1);
+    const uint32_t lo = roff + 16u * (uint32_t)g;
+    r.la = load16_a2(wr, lo, blk + 64 * h);
+    r.lb = load16_a2(wr, lo, blk + 64 * h + 32);
+    r.hb = load16_a2(wr, lo, blk + 128 + 32 * h);
   }
 }
 
@@ -207,30 +225,19 @@ __device__ __forceinline__ h8 a_frag(const typename RawOf<FMT>::T& r, int s, int
   }
 }
 
-// Global weight row of local row 32*IB*w + 32*c + i, clamped for a ragged N.
+// First global weight row of i-block c of wave w.
 // SwiGLU (IB == 2): i-block 0 holds gate rows, i-block 1 the matching up rows.
 template <int IB, bool SWIGLU>
-__device__ __forceinline__ int weight_row(int w, int c, int i, int n0, int hb, int F, int N) {
-  int r = SWIGLU ? (c == 0 ? 0 : F) + hb + 32 * w + i : n0 + 32 * IB * w + 32 * c + i;
-  return r < N ? r : N - 1;
-}
-
-// Direct global -> LDS load of one 64-wide x chunk: wave-instruction q (of
-// BM/8) fills LDS rows 8q .. 8q+7 (1 KiB, lane t at byte 16t).
-template <int JB, int IB, int XQ>
-__device__ __forceinline__ void load_x(const half_t* (&xsrc)[XQ], int ck, uint8_t* xd, int wave) {
-#pragma unroll
-  for (int i = 0; i < XQ; ++i) {
-    const int q = 4 * i + wave;
-    if (q < TileCfg<JB, IB>::BM / 8)
-      __builtin_amdgcn_global_load_lds(xsrc[i] + 64 * ck, (__attribute__((address_space(3))) void*)(xd + q * 1024), 16,
-                                       0, 0);
-  }
+__device__ __forceinline__ int iblock_row0(int w, int c, int n0, int hb, int F) {
+  return SWIGLU ? (c == 0 ? 0 : F) + hb + 32 * w : n0 + 32 * IB * w + 32 * c;
 }
 
 // x0 / x1 (BM rows x 128 B each) and tab (2 x BN x TSTRIDE floats) are
 // distinct LDS objects: the compiler's wait-count tracking then knows that
 // reading one x buffer does not depend on the direct loads into the other.
+// x rows are stored with their 16-byte chunks XOR-swizzled by (row >> 1) & 7:
+// a ds_read_b128 of one column by 16 consecutive rows then covers all 64
+// banks once (two rows share one 256-byte bank line).
 template <int FMT, int JB, int IB, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, uint8_t* x0, uint8_t* x1,
                                           float* tab) {
@@ -238,7 +245,8 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   typedef typename RawOf<FMT>::T Raw;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
   constexpr int XQ = (C::BM / 8 + 3) / 4;            // x load instructions per wave per chunk
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int M = P.M, N = P.N, K = P.K;
   const int nck = K / 64;
@@ -248,27 +256,42 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   const int hb = n_tile * (C::BN / 2);               // SwiGLU: first h column of the tile
   const int n0 = n_tile * C::BN;
 
-  const uint8_t* wrow[IB];
+  // weight rows: one buffer per 32-row i-block; rows past N read as zero
+  rsrc_t wr[IB];
 #pragma unroll
-  for (int c = 0; c < IB; ++c)
-    wrow[c] = P.wq + (int64_t)weight_row<IB, SWIGLU>(wave, c, li, n0, hb, F, N) * row_bytes;
+  for (int c = 0; c < IB; ++c) {
+    const int r0 = iblock_row0<IB, SWIGLU>(wave, c, n0, hb, F);
+    const int nrows = N - r0 < 32 ? N - r0 : 32;
+    wr[c] = make_rsrc(P.wq + (int64_t)r0 * row_bytes, (int64_t)nrows * row_bytes);
+  }
+  const uint32_t roff = (uint32_t)(li * row_bytes) + (FMT == 0 ? 16u * (uint32_t)g : 0u);
+  // table thread tt decodes local row tt = 32*IB*w + 32*c + i (clamped to a valid row)
   const bool tab_thread = tid < C::BN;
   const int tt = tab_thread ? tid : 0;
-  const uint8_t* trow =
-      P.wq + (int64_t)weight_row<IB, SWIGLU>(tt / (32 * IB), (tt / 32) % IB, tt & 31, n0, hb, F, N) * row_bytes;
+  int trow_i = iblock_row0<IB, SWIGLU>(tt / (32 * IB), (tt / 32) % IB, n0, hb, F) + (tt & 31);
+  trow_i = trow_i < N ? trow_i : N - 1;
+  const uint8_t* trow = P.wq + (int64_t)trow_i * row_bytes;
   float* my_tab = tab + tt * C::TSTRIDE;
 
-  // x loader: wave-instruction q (of BM/8) fills LDS rows 8q .. 8q+7; lane t
-  // writes row r = 8q + t/8, slot t%8, which holds 16-byte chunk (t%8)^(r%8).
-  const int xr_row = lane >> 3;
-  const int xr_chunk = (lane & 7) ^ xr_row;
-  const half_t* xsrc[XQ];
+  // x: one buffer over this tile's rows (rows past M read as zero).  Wave
+  // instruction q (of BM/8) fills LDS rows 8q .. 8q+7; lane t writes row
+  // r = 8q + t/8, slot t%8, which holds 16-byte chunk (t%8) ^ ((r>>1)&7).
+  const rsrc_t xr = make_rsrc(P.x + (int64_t)m0 * K, (int64_t)(M - m0) * K * 2);
+  uint32_t xoff[XQ];
 #pragma unroll
   for (int i = 0; i < XQ; ++i) {
-    int m = m0 + 8 * (4 * i + wave) + xr_row;
-    m = m < M ? m : M - 1;                           // ragged M: repeat the last row
-    xsrc[i] = P.x + (int64_t)m * K + 8 * xr_chunk;
+    const int r = 8 * (4 * i + wave) + (lane >> 3);
+    xoff[i] = (uint32_t)r * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
+  auto load_x = [&](int ck, uint8_t* xd) {
+#pragma unroll
+    for (int i = 0; i < XQ; ++i) {
+      const int q = 4 * i + wave;
+      if (q < C::BM / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xd + q * 1024), 16,
+                                                 xoff[i], (uint32_t)(128 * ck), 0, 0);
+    }
+  };
 
   f16x acc[JB][IB];
 #pragma unroll
@@ -281,101 +304,95 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   Raw ra[IB], rn[IB];
 
   // prologue: chunk 0 of x, table of block 0, raw bytes of chunk 0
-  load_x<JB, IB>(xsrc, 0, x0, wave);
+  load_x(0, x0);
   if (tab_thread) hdr_load<FMT>(trow, hdr, hdr4);
 #pragma unroll
-  for (int c = 0; c < IB; ++c) raw_load<FMT>(wrow[c], 0, g, ra[c]);
+  for (int c = 0; c < IB; ++c) raw_load<FMT>(wr[c], roff, 0, g, ra[c]);
   if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + 192) & 3));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // B-fragment LDS offsets (bytes) of row li of j-block 0 for the 4 K steps:
-  // 16-byte chunk 4*(s/2) + 2*g + (s%2), swizzled by row & 7 (rows of other
-  // j-blocks differ by multiples of 32, so row & 7 == li & 7).
-  int boff[4];
+  // B-fragment LDS addresses of row li of j-block 0 for the 4 K steps and the
+  // two buffers: 16-byte chunk 4*(s/2) + 2*g + (s%2), swizzled by the row
+  // (rows of other j-blocks differ by multiples of 32: same swizzle).
+  const uint8_t* bp[2][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) boff[s] = li * 128 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ (li & 7));
+  for (int s = 0; s < 4; ++s) {
+    const int off = li * 128 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ ((li >> 1) & 7));
+    bp[0][s] = x0 + off;
+    bp[1][s] = x1 + off;
+  }
 
   // chunks in pairs (nck is a multiple of 4): the even chunk reads x0 while
   // the next chunk streams into x1, the odd chunk the other way round
   for (int ck2 = 0; ck2 < nck; ck2 += 2) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int ck = ck2 + half;
-    uint8_t* const xb = half ? x1 : x0;
-    uint8_t* const xnext = half ? x0 : x1;
-    const bool has_next = ck + 1 < nck;
-    const bool next_block = has_next && ((ck + 1) & 3) == 0;
-    const bool next_raw = has_next && (FMT == 0 || ((ck + 1) & 1) == 0);
-    if (has_next) load_x<JB, IB>(xsrc, ck + 1, xnext, wave);
-    if (next_raw) {
+    for (int half = 0; half < 2; ++half) {
+      const int ck = ck2 + half;
+      uint8_t* const xnext = half ? x0 : x1;
+      const bool has_next = ck + 1 < nck;
+      const bool next_block = has_next && ((ck + 1) & 3) == 0;
+      const bool next_raw = has_next && (FMT == 0 || ((ck + 1) & 1) == 0);
+      if (has_next) load_x(ck + 1, xnext);
+      if (next_raw) {
 #pragma unroll
-      for (int c = 0; c < IB; ++c) raw_load<FMT>(wrow[c], ck + 1, g, rn[c]);
-    }
-    if (next_block && tab_thread) hdr_load<FMT>(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES, hdr, hdr4);
+        for (int c = 0; c < IB; ++c) raw_load<FMT>(wr[c], roff, ck + 1, g, rn[c]);
+      }
+      if (next_block && tab_thread) hdr_load<FMT>(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES, hdr, hdr4);
 
-    const int cc = ck & 3;
-    const float* tb = tab + ((ck >> 2) & 1) * (C::TBUF / 4);
-    float sv[IB][4];
+      const int cc = ck & 3;
+      const float* tb = tab + ((ck >> 2) & 1) * (C::TBUF / 4);
+      float sv[IB][4];
 #pragma unroll
-    for (int c = 0; c < IB; ++c) {
-      const float* t = tb + (32 * IB * wave + 32 * c + li) * C::TSTRIDE;
-      if constexpr (FMT == 0) {
-        float4 v = *(const float4*)(t + 4 * cc);     // sub-blocks 2cc, 2cc+1
-        sv[c][0] = v.x; sv[c][1] = v.y; sv[c][2] = v.z; sv[c][3] = v.w;
-      } else {
-        const int base = 8 * (cc >> 1) + 4 * (cc & 1) + g;   // scale index 8h + 2t + g
-        sv[c][0] = t[base];
-        sv[c][1] = t[base + 2];
-        sv[c][2] = 0.0f;
-        sv[c][3] = 0.0f;
+      for (int c = 0; c < IB; ++c) {
+        const float* t = tb + (32 * IB * wave + 32 * c + li) * C::TSTRIDE;
+        if constexpr (FMT == 0) {
+          float4 v = *(const float4*)(t + 4 * cc);   // sub-blocks 2cc, 2cc+1
+          sv[c][0] = v.x; sv[c][1] = v.y; sv[c][2] = v.z; sv[c][3] = v.w;
+        } else {
+          const int base = 8 * (cc >> 1) + 4 * (cc & 1) + g;   // scale index 8h + 2t + g
+          sv[c][0] = t[base];
+          sv[c][1] = t[base + 2];
+          sv[c][2] = 0.0f;
+          sv[c][3] = 0.0f;
+        }
+      }
+      h8 af[IB], bf[JB];
+#pragma unroll
+      for (int c = 0; c < IB; ++c) af[c] = a_frag<FMT>(ra[c], 0, cc, sv[c]);
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) bf[jb] = *(const h8*)(bp[half][0] + jb * 32 * 128);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        h8 afn[IB], bfn[JB];
+        if (s < 3) {
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(bp[half][s + 1] + jb * 32 * 128);
+#pragma unroll
+          for (int c = 0; c < IB; ++c) afn[c] = a_frag<FMT>(ra[c], s + 1, cc, sv[c]);
+        }
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+          for (int c = 0; c < IB; ++c)
+            acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c], bf[jb], acc[jb][c], 0, 0, 0);
+        if (s < 3) {
+#pragma unroll
+          for (int c = 0; c < IB; ++c) af[c] = afn[c];
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
+        }
+      }
+      if (next_block && tab_thread)
+        tab_store<FMT>(my_tab + (((ck + 1) >> 2) & 1) * (C::TBUF / 4), hdr, hdr4,
+                       (uint32_t)((uintptr_t)(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES + 192) & 3));
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (next_raw) {
+#pragma unroll
+        for (int c = 0; c < IB; ++c) ra[c] = rn[c];
       }
     }
-    h8 af[IB], bf[JB];
-#pragma unroll
-    for (int c = 0; c < IB; ++c) af[c] = a_frag<FMT>(ra[c], 0, cc, sv[c]);
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) bf[jb] = *(const h8*)(xb + jb * 32 * 128 + boff[0]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      h8 afn[IB], bfn[JB];
-      if (s < 3) {
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(xb + jb * 32 * 128 + boff[s + 1]);
-#pragma unroll
-        for (int c = 0; c < IB; ++c) afn[c] = a_frag<FMT>(ra[c], s + 1, cc, sv[c]);
-      }
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int c = 0; c < IB; ++c)
-          acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c], bf[jb], acc[jb][c], 0, 0, 0);
-      if (s < 3) {
-#pragma unroll
-        for (int c = 0; c < IB; ++c) af[c] = afn[c];
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
-      }
-      // Schedule of this step: the next step's B-fragment reads go first (their
-      // latency hides behind this step's MFMAs), then each MFMA is followed by
-      // a few VALU ops of the next step's dequant.
-      __builtin_amdgcn_sched_group_barrier(0x100, JB, 0);         // DS reads
-#pragma unroll
-      for (int i = 0; i < JB * IB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);        // VALU
-      }
-    }
-    if (next_block && tab_thread)
-      tab_store<FMT>(my_tab + (((ck + 1) >> 2) & 1) * (C::TBUF / 4), hdr, hdr4,
-                     (uint32_t)((uintptr_t)(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES + 192) & 3));
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (next_raw) {
-#pragma unroll
-      for (int c = 0; c < IB; ++c) ra[c] = rn[c];
-    }
-  }
   }
 
   // ---- epilogue: the lane holds rows 8q + 4g + e (q, e = 0..3) of each i-block ----

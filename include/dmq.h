@@ -33,8 +33,9 @@
  *    synchronised.  The device is the caller's current HIP device.
  *  - Arguments are checked on the host before any HIP call; a rejected call
  *    enqueues nothing.  Checks: non-NULL pointers, sizes >= 1 and < 2^31,
- *    K (and D, F) a multiple of 256, x / y / h / w_f16 16-byte aligned, Q4_K
- *    weights 16-byte aligned, Q6_K weights 2-byte aligned.
+ *    K (and D, F) a multiple of 256 and, for the GEMM calls, at most 2^20,
+ *    x / y / h / w_f16 16-byte aligned, Q4_K weights 16-byte aligned, Q6_K
+ *    weights 2-byte aligned.
  *  - Output buffers must not overlap inputs.
  */
 #ifndef DMQ_H

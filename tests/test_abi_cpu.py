@@ -119,3 +119,9 @@ def test_binding_rejects_host_tensors_and_bad_sizes():
         dmq.dmq_gemm_q4k(x, w, y, 4, 4, 256)          # CPU tensors are refused
     with pytest.raises(ValueError):
         dmq.make_group([("q4k", x, w, y, 4, 4, 512)])  # K mismatch is caught first
+
+
+def test_gemm_k_limit():
+    # the GEMM kernels take K up to 2^20
+    assert L.dmq_gemm_q4k(A16, A16, A16, 4, 4, (1 << 20) + 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert L.dmq_gemm_q6k(A16, A16, A16, 1, 4, (1 << 20) + 256, None) == dmq.DMQ_ERR_INVALID_ARG
