@@ -98,7 +98,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-rows", type=int, default=96, help="rows of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU-oracle sample (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,7 +146,7 @@ def main():
                    "pct_fp16_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_kernel<16,4,false>", "launch_ms": round(kern_ms, 4)},
+                     "kernel": "dmq::gemm_kernel_mixed (grouped Q4_K/Q6_K prefill launch)", "launch_ms": round(kern_ms, 4)},
     }
 
     if not args.no_decode:

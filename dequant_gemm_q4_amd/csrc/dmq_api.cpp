@@ -54,26 +54,30 @@ int check_gemm(int fmt, const void* x, const void* wq, const void* y, int64_t M,
   return DMQ_OK;
 }
 
-// Device check: the kernels are built for gfx950 only.  Cached per device.
+// Device check: the kernels are built for gfx950 only.  Cached per device,
+// together with the compute-unit count used to size launches.
+std::mutex g_dev_mu;
+int g_dev_status[64];
+int g_dev_cus[64];
+bool g_dev_init = false;
+
 int check_device() {
-  static std::mutex mu;
-  static int cached[64];
-  static bool init = false;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DMQ_ERR_UNSUPPORTED;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!init) {
-    for (int& c : cached) c = 1;   // 1 = unknown
-    init = true;
-  }
   if (dev < 0 || dev >= 64) return DMQ_ERR_UNSUPPORTED;
-  if (cached[dev] == 1) {
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_dev_init) {
+    for (int& c : g_dev_status) c = 1;   // 1 = not queried yet
+    g_dev_init = true;
+  }
+  if (g_dev_status[dev] == 1) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DMQ_ERR_UNSUPPORTED;
-    cached[dev] = (prop.gcnArchName[0] && std::string_view(prop.gcnArchName).substr(0, 6) == "gfx950")
-                      ? DMQ_OK : DMQ_ERR_UNSUPPORTED;
+    g_dev_status[dev] = (prop.gcnArchName[0] && std::string_view(prop.gcnArchName).substr(0, 6) == "gfx950")
+                            ? DMQ_OK : DMQ_ERR_UNSUPPORTED;
+    g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   }
-  return cached[dev];
+  return g_dev_status[dev];
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DMQ_OK : DMQ_ERR_HIP; }
@@ -110,6 +114,16 @@ int gemm_one(int fmt, const void* x, const void* wq, float* y, int64_t M, int64_
 }
 
 }  // namespace
+
+namespace dmq {
+// Compute units of the current device (valid after check_device succeeded).
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  return g_dev_init && g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256;
+}
+}  // namespace dmq
 
 extern "C" {
 

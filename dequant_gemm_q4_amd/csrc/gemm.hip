@@ -468,7 +468,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
 
 // Mixed Q4_K / Q6_K groups: one kernel per format would serialise on the
 // stream, so this kernel branches per workgroup (uniformly) on the format.
-template <int JB, int IB>
+// Q6_K problems run with JB6 <= JB j-blocks per tile: in a layer the Q6_K
+// down projection has the longest reduction (K = 8192), and shorter tiles
+// spread it over more CUs so it does not set the end of the launch.
+template <int JB, int IB, int JB6>
 __global__ __launch_bounds__(256, 1) void gemm_kernel_mixed(GemmArgs args) {
   typedef TileCfg<JB, IB> C;
   __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel_mixed(GemmArgs args) {
   if (P.fmt == 0)
     gemm_tile<0, JB, IB, false>(P, m_tile, n_tile, x0, x1, tab);
   else
-    gemm_tile<1, JB, IB, false>(P, m_tile, n_tile, x0, x1, tab);
+    gemm_tile<1, JB6, IB, false>(P, m_tile, n_tile, x0, x1, tab);
 #endif
 }
 
@@ -490,60 +493,117 @@ static hipError_t launch_one(Kern k, int tiles, const GemmArgs& a, hipStream_t s
   return hipGetLastError();
 }
 
-template <int JB, int IB, bool SWIGLU>
+// Tile counts of one problem for BM = 32*jb rows and BN = 128*ib weight rows.
+static void set_tiles(GemmDesc& d, const GemmProblem& p, int jb, int ib, bool swiglu) {
+  const int bm = 32 * jb, bn = 128 * ib;
+  d.x = (const half_t*)p.x;
+  d.wq = p.wq;
+  d.out = p.out;
+  d.fmt = p.fmt;
+  d.swiglu = p.swiglu;
+  d.M = p.M;
+  d.N = p.N;
+  d.K = p.K;
+  d.mt = (p.M + bm - 1) / bm;
+  d.nt = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
+}
+
+// JB: j-blocks per tile for Q4_K (and single-format) problems; JB6 for Q6_K
+// problems of a mixed group.
+template <int JB, int IB, bool SWIGLU, int JB6 = JB>
 static hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t s) {
-  typedef TileCfg<JB, IB> C;
   for (int base = 0; base < count; base += GEMM_MAX_GROUP) {
     GemmArgs a{};
     int n = count - base < GEMM_MAX_GROUP ? count - base : GEMM_MAX_GROUP;
-    int tiles = 0, fmt_mask = 0;
+    int fmt_mask = 0;
+    for (int i = 0; i < n; ++i) fmt_mask |= 1 << probs[base + i].fmt;
+    const bool mixed = !SWIGLU && fmt_mask == 3;
+    int tiles = 0;
     for (int i = 0; i < n; ++i) {
       const GemmProblem& p = probs[base + i];
       GemmDesc& d = a.d[i];
-      d.x = (const half_t*)p.x;
-      d.wq = p.wq;
-      d.out = p.out;
-      d.fmt = p.fmt;
-      d.swiglu = p.swiglu;
-      d.M = p.M;
-      d.N = p.N;
-      d.K = p.K;
-      d.mt = (p.M + C::BM - 1) / C::BM;
-      d.nt = SWIGLU ? (p.N / 2 + C::BN / 2 - 1) / (C::BN / 2) : (p.N + C::BN - 1) / C::BN;
+      set_tiles(d, p, (mixed && p.fmt == 1) ? JB6 : JB, IB, SWIGLU);
       d.tile_begin = tiles;
       tiles += d.mt * d.nt;
-      fmt_mask |= 1 << p.fmt;
     }
     a.count = n;
     hipError_t e;
     if constexpr (SWIGLU) {
       e = launch_one(gemm_kernel<0, JB, IB, true>, tiles, a, s);
-    } else if (fmt_mask == 1) {
-      e = launch_one(gemm_kernel<0, JB, IB, false>, tiles, a, s);
-    } else if (fmt_mask == 2) {
-      e = launch_one(gemm_kernel<1, JB, IB, false>, tiles, a, s);
     } else {
-      e = launch_one(gemm_kernel_mixed<JB, IB>, tiles, a, s);
+      if (fmt_mask == 1)
+        e = launch_one(gemm_kernel<0, JB, IB, false>, tiles, a, s);
+      else if (fmt_mask == 2)
+        e = launch_one(gemm_kernel<1, JB, IB, false>, tiles, a, s);
+      else
+        e = launch_one(gemm_kernel_mixed<JB, IB, JB6>, tiles, a, s);
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-// All problems of one call share the tile shape, picked from the largest M.
-hipError_t launch_gemm(const GemmProblem* probs, int count, hipStream_t s) {
-  int mmax = 0;
-  const bool swiglu = probs[0].swiglu != 0;
-  for (int i = 0; i < count; ++i) mmax = probs[i].M > mmax ? probs[i].M : mmax;
-  if (swiglu) {
-    if (mmax > 128) return launch_cfg<8, 2, true>(probs, count, s);
-    if (mmax > 32) return launch_cfg<2, 2, true>(probs, count, s);
-    return launch_cfg<1, 2, true>(probs, count, s);
+// Relative time of a launch with tiles of jb j-blocks (32 activation rows
+// each) and ib i-blocks per wave (32 weight rows each).  Workgroups run in
+// rounds of one tile per CU; per K chunk a tile costs the dequant of its
+// weight panel (~ 2 MFMA j-blocks per i-block) plus jb * ib MFMA j-blocks.
+static double launch_cost(const GemmProblem* probs, int count, int jb, int ib, bool swiglu, int ncu) {
+  int64_t tiles = 0, kmax = 0;
+  double work = 0.0;
+  for (int i = 0; i < count; ++i) {
+    GemmDesc d;
+    set_tiles(d, probs[i], jb, ib, swiglu);
+    tiles += (int64_t)d.mt * d.nt;
+    work += (double)d.mt * d.nt * probs[i].K;
+    kmax = probs[i].K > kmax ? probs[i].K : kmax;
   }
-  if (mmax > 128) return launch_cfg<8, 2, false>(probs, count, s);
-  if (mmax > 64) return launch_cfg<4, 2, false>(probs, count, s);
-  if (mmax > 32) return launch_cfg<2, 1, false>(probs, count, s);
-  return launch_cfg<1, 1, false>(probs, count, s);
+  const double per_chunk = ib * (2.0 + 0.5 * jb);
+  const double rounds = (double)((tiles + ncu - 1) / ncu);
+  // full rounds of the mean tile, but never less than the longest tile
+  double t = rounds * (work / (double)tiles);
+  if (t < (double)kmax) t = (double)kmax;
+  return t * per_chunk;
+}
+
+hipError_t launch_gemm(const GemmProblem* probs, int count, hipStream_t s) {
+  int mmax = 0, fmt_mask = 0;
+  const bool swiglu = probs[0].swiglu != 0;
+  for (int i = 0; i < count; ++i) {
+    mmax = probs[i].M > mmax ? probs[i].M : mmax;
+    fmt_mask |= 1 << probs[i].fmt;
+  }
+  const int ncu = device_cu_count();
+  // candidate tile shapes (jb, ib); SwiGLU needs ib == 2 (gate + up)
+  static const int cand[6][2] = {{8, 2}, {4, 2}, {2, 2}, {1, 2}, {2, 1}, {1, 1}};
+  int best_jb = 1, best_ib = 2;
+  double best = 0.0;
+  for (const auto& c : cand) {
+    const int jb = c[0], ib = c[1];
+    if (swiglu && ib != 2) continue;
+    if (jb > 1 && 32 * (jb / 2) >= mmax) continue;          // taller than needed
+    const double t = launch_cost(probs, count, jb, ib, swiglu, ncu);
+    if (best == 0.0 || t < best * 0.97) {
+      best = t;
+      best_jb = jb;
+      best_ib = ib;
+    }
+  }
+  if (swiglu) {
+    switch (best_jb) {
+      case 8: return launch_cfg<8, 2, true>(probs, count, s);
+      case 4: return launch_cfg<4, 2, true>(probs, count, s);
+      case 2: return launch_cfg<2, 2, true>(probs, count, s);
+      default: return launch_cfg<1, 2, true>(probs, count, s);
+    }
+  }
+  const bool mixed = fmt_mask == 3;
+  if (best_ib == 1) return best_jb == 2 ? launch_cfg<2, 1, false>(probs, count, s) : launch_cfg<1, 1, false>(probs, count, s);
+  switch (best_jb) {
+    case 8: return mixed ? launch_cfg<8, 2, false, 4>(probs, count, s) : launch_cfg<8, 2, false>(probs, count, s);
+    case 4: return mixed ? launch_cfg<4, 2, false, 2>(probs, count, s) : launch_cfg<4, 2, false>(probs, count, s);
+    case 2: return launch_cfg<2, 2, false>(probs, count, s);
+    default: return launch_cfg<1, 2, false>(probs, count, s);
+  }
 }
 
 }  // namespace dmq
