@@ -4,7 +4,7 @@
 // the thesis": prefill is dense, compute-bound GEMM; article "Building
 // DAMASCUS", "Prefill and decode need different performance questions"), and
 // the fused dequant never writes fp16 weights to memory (overview page, same
-// section, and compartment 09 "fused dequant -> ... prefill").
+// section, and compartment 09 of "[02] the pipeline").
 //
 // One workgroup = 4 waves = one BM x BN output tile, BM = 32*JB activation
 // rows, BN = 4 * 32*IB weight rows.

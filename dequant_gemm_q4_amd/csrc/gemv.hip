@@ -1,6 +1,6 @@
 // Decode (M = 1) kernel: y[n] = sum_k x[k] * W[n][k] with W in Q4_K or Q6_K.
 //
-// Decode processes one token at a time and is bound by streaming the weights
+// Decode handles a single token per step and is bound by streaming the weights
 // from memory (overview page, "[01] the thesis" and "[04] one decode step";
 // article "Building DAMASCUS", "Prefill and decode need different performance
 // questions").  The kernel is therefore built around the HBM stream:

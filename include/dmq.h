@@ -6,15 +6,16 @@
  * runs asynchronously on the HIP stream it is given.
  *
  * What the calls compute comes from the DAMASCUS pages:
- *  - Overview page, "[02] the pipeline", compartment 09 (Quantization & AMX):
- *    "Q4_K_M dequant; quantized matmul; fused dequant -> AMX prefill"; and
- *    "[01] the thesis": the fused path never materialises fp16 weights.
+ *  - Overview page, "[02] the pipeline", compartment 09 (Quantization & AMX),
+ *    which lists the Q4_K_M dequantizer, the quantised matmul and a prefill
+ *    kernel with fused dequant; and "[01] the thesis": that fused path never
+ *    materialises fp16 weights.
  *  - Article "Building DAMASCUS", "Read the model, then reproduce its
- *    operations": the Q4_K and Q6_K dequantizers; and "Prefill and decode need
- *    different performance questions": decode is matrix-vector work bound by
- *    streaming the weights, prefill is matrix-matrix work.
- *  - Same article, layer description: RMSNorm, QKV projections, attention, a
- *    second RMSNorm and a SwiGLU feed-forward network complete the layer.
+ *    operations": the Q4_K and Q6_K dequantizers; and "Prefill and decode
+ *    need different performance questions": decode is matrix-vector work
+ *    bound by streaming the weights, prefill is matrix-matrix work.
+ *  - Same article, layer description: each decoder layer ends with a second
+ *    RMSNorm followed by a SwiGLU feed-forward network.
  *
  * Conventions shared by all calls
  *  - Pointers named *_f16 point to IEEE binary16 data, y points to fp32 data.

@@ -12,9 +12,9 @@ the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 Sources (DAMASCUS pages): the dequantisers and the quantised matmul are the
 overview page's compartment 09 ("[02] the pipeline") and the article's
 section "Read the model, then reproduce its operations"; the SwiGLU FFN is
-compartment 05/06 and the article's layer description ("A second RMSNorm and
-a SwiGLU feed-forward network complete the layer"); comparing against the same
-dequantised blocks is the article's "same-weights oracle".  The per-output
+compartment 05/06 and the article's layer description (a second RMSNorm and
+a SwiGLU feed-forward network end each layer); comparing against the same
+dequantised blocks is the article's same-weights oracle idea.  The per-output
 acceptance bound |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 1e-5 replaces the
 pages' own 1e-3 absolute logit threshold (article, same section).
 

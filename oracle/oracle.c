@@ -8,22 +8,23 @@
  * What it computes, and where that is defined:
  *
  *  - Dequantisation of the two k-quant super-block formats the DAMASCUS pages
- *    name (project overview page, "[02] the pipeline", compartment 09
- *    "Q4_K_M dequant"; article "Building DAMASCUS", section "Read the model,
- *    then reproduce its operations": "The Q4_K and Q6_K dequantizers").  The
+ *    name (project overview page, "[02] the pipeline", compartment 09, which
+ *    lists the Q4_K_M dequantizer; article "Building DAMASCUS", section "Read
+ *    the model, then reproduce its operations", which checks the Q4_K and
+ *    Q6_K dequantizers before their output is used).  The
  *    pages name the formats but do not define their bytes; the byte layout is
  *    the public GGUF k-quant layout (restated in the comments below).  Each
  *    weight is computed exactly in fp64 and then rounded once to fp16 with
  *    round-to-nearest-even; an exact zero is returned as +0.
  *
- *  - The quantised matmul (overview page, compartment 09 "quantized matmul";
+ *  - The quantised matmul (overview page, compartment 09;
  *    section "[01] the thesis": prefill is dense GEMM, decode is GEMV) as the
  *    plain definition y[m][n] = sum_k x[m][k] * w[n][k] over the fp16 inputs
  *    and the oracle's own fp16 weights, accumulated in fp64 in ascending k,
  *    together with S[m][n] = sum_k |x[m][k] * w[n][k]|, the scale of the
- *    acceptance bound.  Comparing against the same dequantised weights is the
- *    "same-weights oracle" idea of the article's section "A same-weights
- *    oracle makes the comparison useful".
+ *    acceptance bound.  Comparing against the same dequantised weights, so
+ *    that quantisation error does not mix with implementation error, is the
+ *    idea of the article's same-weights oracle section.
  *
  * Loops are plain and sequential per output; OpenMP only spreads independent
  * outputs over host cores.

@@ -8,9 +8,9 @@ draw their inputs from here, and nothing else is shared between the two.
 Shapes follow the target model named on the DAMASCUS project overview page,
 section "[06] the target": 28 layers, hidden 3072, FFN 8192, 24 heads with
 8 KV heads of dim 128, vocabulary 128256, tied embeddings.  The quantised
-formats are the GGUF k-quant super-blocks the pages name ("Q4_K_M",
-"Q4_K and Q6_K dequantizers", article "Building DAMASCUS", section "Read the
-model, then reproduce its operations"):
+formats are the GGUF k-quant super-blocks the pages name (the Q4_K_M model
+file and its Q4_K and Q6_K dequantizers, article "Building DAMASCUS", section
+"Read the model, then reproduce its operations"):
 
 * Q4_K: 144 bytes per 256 weights -- fp16 ``d`` at byte 0, fp16 ``dmin`` at
   byte 2, 12 bytes of packed 6-bit scales/mins at byte 4, 128 bytes of 4-bit
