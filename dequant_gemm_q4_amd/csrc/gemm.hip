@@ -59,8 +59,8 @@ struct TileCfg {
   static constexpr int BN = 128 * IB;                // weight rows per tile
   static constexpr int XBUF = BM * 128;              // bytes per x buffer (64 fp16 per row)
   static constexpr int TSTRIDE = 20;                 // floats per table row (16 + 4 pad)
-  static constexpr int TBUF = BN * TSTRIDE * 4;      // bytes per table buffer
-  static constexpr size_t LDS_BYTES = 2 * XBUF + 2 * TBUF;
+  static constexpr int TBUF = BN * TSTRIDE * 4;      // bytes of the scale table
+  static constexpr size_t LDS_BYTES = 4 * XBUF + TBUF;
 };
 
 __device__ __forceinline__ float silu_fast(float g) {
@@ -76,62 +76,68 @@ __device__ __forceinline__ uint32_t fma_mix_pair(uint32_t q, float s, float c) {
   return as_u32(r);
 }
 
-__device__ __forceinline__ uint32_t pk_sub(uint32_t a, uint32_t k) {
-  return as_u32(as_h2(a) - as_h2(k));
+// Quant bytes (each < 1024 after masking) -> fp16 pairs whose bit patterns
+// are the bytes themselves: the subnormal values b * 2^-24, exact.  Byte
+// selector 0x0c of v_perm_b32 yields 0x00.
+__device__ __forceinline__ uint32_t sub_pair_lo(uint32_t b) {   // (b.byte0, b.byte1)
+  return __builtin_amdgcn_perm(0u, b, 0x0c010c00u);
+}
+__device__ __forceinline__ uint32_t sub_pair_hi(uint32_t b) {   // (b.byte2, b.byte3)
+  return __builtin_amdgcn_perm(0u, b, 0x0c030c02u);
 }
 
-// Four quant bytes (each < 64) -> two fp16 pairs of (q - off).
-__device__ __forceinline__ void bytes_to_pairs(uint32_t b, uint32_t koff, uint32_t& p0, uint32_t& p1) {
-  p0 = pk_sub(magic_pair_lo(b), koff);
-  p1 = pk_sub(magic_pair_hi(b), koff);
-}
-
-constexpr uint32_t K1024 = 0x64006400u;   // fp16 pair (1024, 1024)
-constexpr uint32_t K1056 = 0x64206420u;   // fp16 pair (1056, 1056): 1024 + 32
-
-// 8 Q4_K weights (one A fragment) from two quant dwords.
+// 8 Q4_K weights (one A fragment) from two quant dwords.  The nibbles are
+// masked in place (low: q, high: 16 q) and read as fp16 subnormals; the
+// table scale s carries the matching 2^24 or 2^20 factor, so q*2^-24 * s is
+// exactly q*d*sc and the FMA with -dmin*m rounds once.
 __device__ __forceinline__ h8 q4k_frag(uint32_t w0, uint32_t w1, uint32_t mask, float dsc, float ndm) {
-  uint32_t a0, a1, b0, b1;
-  bytes_to_pairs(w0 & mask, K1024, a0, a1);
-  bytes_to_pairs(w1 & mask, K1024, b0, b1);
-  u32x4 r = {fma_mix_pair(a0, dsc, ndm), fma_mix_pair(a1, dsc, ndm), fma_mix_pair(b0, dsc, ndm),
-             fma_mix_pair(b1, dsc, ndm)};
+  const uint32_t a = w0 & mask, b = w1 & mask;
+  u32x4 r = {fma_mix_pair(sub_pair_lo(a), dsc, ndm), fma_mix_pair(sub_pair_hi(a), dsc, ndm),
+             fma_mix_pair(sub_pair_lo(b), dsc, ndm), fma_mix_pair(sub_pair_hi(b), dsc, ndm)};
   return __builtin_bit_cast(h8, r);
 }
 
-// 8 Q6_K weights: low nibbles (shifted by nsh) | two high bits (at hsh) << 4.
+// 8 Q6_K weights: q = low nibbles (shifted by nsh) | two high bits (at hsh)
+// << 4, read as subnormals q*2^-24; dsc24 = d*sc*2^24, off = -32*d*sc.
 __device__ __forceinline__ h8 q6k_frag(uint32_t l0, uint32_t l1, uint32_t h0, uint32_t h1, uint32_t nsh,
-                                       uint32_t hsh, float dsc) {
+                                       uint32_t hsh, float dsc24, float off) {
   uint32_t q0 = ((l0 >> nsh) & 0x0f0f0f0fu) | (((h0 >> hsh) << 4) & 0x30303030u);
   uint32_t q1 = ((l1 >> nsh) & 0x0f0f0f0fu) | (((h1 >> hsh) << 4) & 0x30303030u);
-  uint32_t a0, a1, b0, b1;
-  bytes_to_pairs(q0, K1056, a0, a1);
-  bytes_to_pairs(q1, K1056, b0, b1);
-  u32x4 r = {fma_mix_pair(a0, dsc, 0.0f), fma_mix_pair(a1, dsc, 0.0f), fma_mix_pair(b0, dsc, 0.0f),
-             fma_mix_pair(b1, dsc, 0.0f)};
+  u32x4 r = {fma_mix_pair(sub_pair_lo(q0), dsc24, off), fma_mix_pair(sub_pair_hi(q0), dsc24, off),
+             fma_mix_pair(sub_pair_lo(q1), dsc24, off), fma_mix_pair(sub_pair_hi(q1), dsc24, off)};
   return __builtin_bit_cast(h8, r);
 }
 
 // Block header for the scale table.  Q4_K: bytes 0..15 (d, dmin, 12 scale
 // bytes).  Q6_K: bytes 192..209 (16 int8 scales, fp16 d), read through the
 // enclosing aligned dwords without touching anything past byte 209.
+// The dword at byte 206 of a Q6_K block (halfwords 206 and 208; 2-byte
+// aligned, which the hardware's unaligned global loads handle).
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
+
 template <int FMT>
 __device__ __forceinline__ void hdr_load(const uint8_t* blk, u32x4& hdr, uint32_t& hdr4) {
   if constexpr (FMT == 0) {
     hdr = *(const u32x4*)blk;
   } else {
+    // Q6_K: the aligned dwords from byte 192 (or 190) and the dword at 206,
+    // all inside the block.  Nothing here combines the values: that waits
+    // until the decode, so the loads' latency stays hidden.
     const uint8_t* p = blk + 192;
     const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
     const uint32_t* sp = (const uint32_t*)(p - sh);
     hdr = (u32x4){sp[0], sp[1], sp[2], sp[3]};
-    hdr4 = sh ? sp[4] : (uint32_t)(*(const uint16_t*)(blk + 208)) << 16;
+    hdr4 = *(const u32_a2*)(blk + 206);
   }
 }
 
 // Decode one header into 16 floats of the table row.
-//  Q4_K: pairs (d*sc_j, -dmin*m_j), with d*sc_j / 16 for odd j (their quant
-//        is read from the high nibble as 16q).
-//  Q6_K: d*sc_s for the 16 sub-blocks.
+//  Q4_K: pairs (d*sc_j*2^24, -dmin*m_j), with 2^20 instead of 2^24 for odd j
+//        (their quant is read from the high nibble as 16q); quants enter the
+//        FMA as fp16 subnormals q*2^-24.
+//  Q6_K: d*sc_s*2^24 for the 16 sub-blocks, even s first (s = 0, 2, .., 14
+//        in floats 0..7), then odd s (floats 8..15): a lane only needs the
+//        sub-blocks of one parity.
 template <int FMT>
 __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t hdr4, uint32_t sh) {
   float v[16];
@@ -141,16 +147,18 @@ __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t h
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float dsc = d * (float)q4k_sc(s, j);
-      v[2 * j] = (j & 1) ? dsc * 0.0625f : dsc;
+      v[2 * j] = dsc * ((j & 1) ? 1048576.0f : 16777216.0f);
       v[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
     }
   } else {
-    // sh = block address mod 4; with sh == 0 the d field sits in hdr4's high half
+    // sh = (block address + 192) mod 4: the 20 bytes from byte 192 - sh are
+    // hdr and, for sh = 2, hdr4 (the dword at 206); d is hdr4's high half
     uint32_t w[4] = {__builtin_amdgcn_alignbyte(hdr.y, hdr.x, sh), __builtin_amdgcn_alignbyte(hdr.z, hdr.y, sh),
                      __builtin_amdgcn_alignbyte(hdr.w, hdr.z, sh), __builtin_amdgcn_alignbyte(hdr4, hdr.w, sh)};
     float d = half_bits_to_float(hdr4 >> 16);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) v[s] = d * (float)(int)(int8_t)((w[s >> 2] >> (8 * (s & 3))) & 0xffu);
+    for (int s = 0; s < 16; ++s)
+      v[(s >> 1) + 8 * (s & 1)] = d * (float)(int)(int8_t)((w[s >> 2] >> (8 * (s & 3))) & 0xffu) * 16777216.0f;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) ((float4*)t)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -175,54 +183,59 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t 
 //  Q4_K, per 64-wide chunk: quant bytes 32p + 16g .. +16 (p = chunk in block).
 //  Q6_K, per 128-weight half h (two chunks): low-nibble bytes 64h + 16g and
 //  64h + 32 + 16g, high-bit bytes 128 + 32h + 16g.  Blocks are 210 bytes, so
-//  a field may start 2 mod 4: it is read as the 5 enclosing aligned dwords
+//  a field may start 2 mod 4: it is loaded as the 5 enclosing aligned dwords
 //  (at most 2 bytes before and 4 after the field; the last byte read is at
-//  most 176 + 20 = 196 < 210) and shifted into place.
+//  most 176 + 20 = 196 < 210) and shifted into place only when first used,
+//  so that the load's latency is not exposed where it is issued.
 struct RawQ4 { u32x4 q; };
-struct RawQ6 { u32x4 la, lb, hb; };
+struct Win { u32x4 w; uint32_t w4; };                  // 20-byte aligned window
+struct RawQ6 { Win la, lb, hb; uint32_t sh; };         // sh: field start mod 4
+struct Q6Fields { u32x4 la, lb, hb; };                 // realigned 16-byte fields
 template <int FMT> struct RawOf { typedef RawQ4 T; };
 template <> struct RawOf<1> { typedef RawQ6 T; };
 
-__device__ __forceinline__ u32x4 load16_a2(rsrc_t r, uint32_t lane_off, uint32_t uni_off) {
-  const uint32_t off = lane_off + uni_off;
-  const uint32_t sh = off & 3u;
-  const uint32_t v = off - sh;                   // aligned down; >= 0 since off >= sh
-  const u32x4 w = buf_load16(r, v, 0);
-  const uint32_t w4 = buf_load4(r, v + 16, 0);
-  return (u32x4){__builtin_amdgcn_alignbyte(w.y, w.x, sh), __builtin_amdgcn_alignbyte(w.z, w.y, sh),
-                 __builtin_amdgcn_alignbyte(w.w, w.z, sh), __builtin_amdgcn_alignbyte(w4, w.w, sh)};
+__device__ __forceinline__ void load_win(rsrc_t r, uint32_t aligned_off, Win& w) {
+  w.w = buf_load16(r, aligned_off, 0);
+  w.w4 = buf_load4(r, aligned_off + 16, 0);
+}
+__device__ __forceinline__ u32x4 realign(const Win& w, uint32_t sh) {
+  return (u32x4){__builtin_amdgcn_alignbyte(w.w.y, w.w.x, sh), __builtin_amdgcn_alignbyte(w.w.z, w.w.y, sh),
+                 __builtin_amdgcn_alignbyte(w.w.w, w.w.z, sh), __builtin_amdgcn_alignbyte(w.w4, w.w.w, sh)};
 }
 
-// wr: this i-block's 32 weight rows; roff: li * row_bytes (+ 16 g for Q4_K)
-template <int FMT>
-__device__ __forceinline__ void raw_load(rsrc_t wr, uint32_t roff, int ck, int g, typename RawOf<FMT>::T& r) {
-  const int bi = ck >> 2, cc = ck & 3;
-  if constexpr (FMT == 0) {
-    r.q = buf_load16(wr, roff, (uint32_t)(bi * Q4K_BYTES + 16 + 32 * cc));
-  } else {
-    const uint32_t blk = (uint32_t)(bi * Q6K_BYTES), h = (uint32_t)(cc >> 1);
-    const uint32_t lo = roff + 16u * (uint32_t)g;
-    r.la = load16_a2(wr, lo, blk + 64 * h);
-    r.lb = load16_a2(wr, lo, blk + 64 * h + 32);
-    r.hb = load16_a2(wr, lo, blk + 128 + 32 * h);
-  }
+// Q4_K raw bytes of chunk ck (wr: this i-block's 32 rows; roff: li * row_bytes + 16 g)
+__device__ __forceinline__ void raw_load_q4(rsrc_t wr, uint32_t roff, int ck, RawQ4& r) {
+  r.q = buf_load16(wr, roff, (uint32_t)((ck >> 2) * Q4K_BYTES + 16 + 32 * (ck & 3)));
+}
+// Q6_K raw bytes of half h of block bi (roff: li * row_bytes)
+__device__ __forceinline__ void raw_load_q6(rsrc_t wr, uint32_t roff, int bi, int h, int g, RawQ6& r) {
+  const uint32_t lo = roff + (uint32_t)(bi * Q6K_BYTES) + 16u * (uint32_t)g;   // lane's field offset, before h
+  r.sh = lo & 3u;                                      // same for the three fields (offsets differ by 32/64)
+  const uint32_t base = lo - r.sh;
+  load_win(wr, base + 64u * (uint32_t)h, r.la);
+  load_win(wr, base + 64u * (uint32_t)h + 32u, r.lb);
+  load_win(wr, base + 128u + 32u * (uint32_t)h, r.hb);
+}
+__device__ __forceinline__ Q6Fields q6_fields(const RawQ6& r) {
+  return Q6Fields{realign(r.la, r.sh), realign(r.lb, r.sh), realign(r.hb, r.sh)};
 }
 
-// A fragment of K step s (0..3) of chunk cc from the raw bytes.
-template <int FMT>
-__device__ __forceinline__ h8 a_frag(const typename RawOf<FMT>::T& r, int s, int cc, const float (&sv)[4]) {
-  if constexpr (FMT == 0) {
-    const uint32_t w0 = (s & 1) ? r.q.z : r.q.x;
-    const uint32_t w1 = (s & 1) ? r.q.w : r.q.y;
-    return s < 2 ? q4k_frag(w0, w1, 0x0f0f0f0fu, sv[0], sv[1]) : q4k_frag(w0, w1, 0xf0f0f0f0u, sv[2], sv[3]);
-  } else {
-    const u32x4& l = (s >> 1) ? r.lb : r.la;
-    const uint32_t l0 = (s & 1) ? l.z : l.x, l1 = (s & 1) ? l.w : l.y;
-    const uint32_t h0 = (s & 1) ? r.hb.z : r.hb.x, h1 = (s & 1) ? r.hb.w : r.hb.y;
-    const uint32_t nsh = (cc & 1) ? 4u : 0u;
-    const uint32_t hsh = 4u * (uint32_t)(cc & 1) + 2u * (uint32_t)(s >> 1);
-    return q6k_frag(l0, l1, h0, h1, nsh, hsh, sv[s >> 1]);
-  }
+// A fragment of K step s (0..3) of chunk cc (0..3 within the block).
+// sv: Q4_K (d*sc*2^24 and -dmin*m of the chunk's even and odd sub-block);
+// Q6_K (d*sc*2^24 of the lane's two sub-blocks of the chunk).
+__device__ __forceinline__ h8 a_frag_q4(const RawQ4& r, int s, const float (&sv)[4]) {
+  const uint32_t w0 = (s & 1) ? r.q.z : r.q.x;
+  const uint32_t w1 = (s & 1) ? r.q.w : r.q.y;
+  return s < 2 ? q4k_frag(w0, w1, 0x0f0f0f0fu, sv[0], sv[1]) : q4k_frag(w0, w1, 0xf0f0f0f0u, sv[2], sv[3]);
+}
+__device__ __forceinline__ h8 a_frag_q6(const Q6Fields& f, int s, int cc, const float (&sv)[4]) {
+  const u32x4& l = (s >> 1) ? f.lb : f.la;
+  const uint32_t l0 = (s & 1) ? l.z : l.x, l1 = (s & 1) ? l.w : l.y;
+  const uint32_t h0 = (s & 1) ? f.hb.z : f.hb.x, h1 = (s & 1) ? f.hb.w : f.hb.y;
+  const uint32_t nsh = (cc & 1) ? 4u : 0u;
+  const uint32_t hsh = 4u * (uint32_t)(cc & 1) + 2u * (uint32_t)(s >> 1);
+  const float dsc24 = sv[s >> 1];
+  return q6k_frag(l0, l1, h0, h1, nsh, hsh, dsc24, dsc24 * -0x1p-19f);
 }
 
 // First global weight row of i-block c of wave w.
@@ -232,25 +245,52 @@ __device__ __forceinline__ int iblock_row0(int w, int c, int n0, int hb, int F) 
   return SWIGLU ? (c == 0 ? 0 : F) + hb + 32 * w : n0 + 32 * IB * w + 32 * c;
 }
 
-// x0 / x1 (BM rows x 128 B each) and tab (2 x BN x TSTRIDE floats) are
-// distinct LDS objects: the compiler's wait-count tracking then knows that
-// reading one x buffer does not depend on the direct loads into the other.
+// s_waitcnt vmcnt(n) lgkmcnt(0) followed by a workgroup barrier, as one asm
+// statement with a memory clobber: the compiler neither moves memory
+// accesses across it nor adds a full vmcnt(0) drain (as a fence would).
+template <int n>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
+// One BM x BN output tile.  The reduction runs over 64-wide K chunks, four per
+// super-block, as a software pipeline:
+//  * x chunk ck is staged by direct global->LDS loads into buffer ck % 4,
+//    issued three chunks ahead (x0..x3 are distinct LDS objects, so the
+//    compiler's wait-count tracking knows that reading one buffer does not
+//    depend on the direct loads into another);
+//  * raw quant bytes go to registers, issued three chunks ahead (Q4_K, four
+//    register sets) or half a block ahead (Q6_K, two sets);
+//  * every chunk has one barrier, before its last K step, after which the
+//    next chunk's x buffer and (at a block boundary) the next scale table are
+//    visible; the last step's MFMAs then overlap the next chunk's first
+//    dequant and B-fragment reads, so no chunk starts with an exposed
+//    prologue;
+//  * within a step, the B fragments of the next step are requested first and
+//    the next step's dequant (VALU) is interleaved with this step's MFMAs.
+// The scale table holds one super-block: per weight row, decoded by one
+// thread, from a header loaded a block ahead; each lane copies its rows'
+// entries to registers once per block.
 // x rows are stored with their 16-byte chunks XOR-swizzled by (row >> 1) & 7:
 // a ds_read_b128 of one column by 16 consecutive rows then covers all 64
 // banks once (two rows share one 256-byte bank line).
 template <int FMT, int JB, int IB, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, uint8_t* x0, uint8_t* x1,
-                                          float* tab) {
+                                          uint8_t* x2, uint8_t* x3, float* tab) {
   typedef TileCfg<JB, IB> C;
   typedef typename RawOf<FMT>::T Raw;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
-  constexpr int XQ = (C::BM / 8 + 3) / 4;            // x load instructions per wave per chunk
+  constexpr int XQ = JB;                             // x load instructions per wave per chunk (BM/8 row groups / 4 waves)
+  constexpr int NRAW = FMT == 0 ? IB : 6 * IB;       // VMEM instructions of one raw load round
+  constexpr int NSC = FMT == 0 ? 16 : 8;             // scale floats per row a lane keeps
+  uint8_t* const xb[4] = {x0, x1, x2, x3};
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int M = P.M, N = P.N, K = P.K;
-  const int nck = K / 64;
-  const int64_t row_bytes = (int64_t)(K / QK) * BLOCK_BYTES;
+  const int nb = K / QK;
+  const int64_t row_bytes = (int64_t)nb * BLOCK_BYTES;
   const int m0 = m_tile * C::BM;
   const int F = N / 2;                               // SwiGLU: gate rows [0,F), up rows [F,2F)
   const int hb = n_tile * (C::BN / 2);               // SwiGLU: first h column of the tile
@@ -285,13 +325,16 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   }
   auto load_x = [&](int ck, uint8_t* xd) {
 #pragma unroll
-    for (int i = 0; i < XQ; ++i) {
-      const int q = 4 * i + wave;
-      if (q < C::BM / 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xd + q * 1024), 16,
-                                                 xoff[i], (uint32_t)(128 * ck), 0, 0);
-    }
+    for (int i = 0; i < XQ; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xd + (4 * i + wave) * 1024),
+                                               16, xoff[i], (uint32_t)(128 * ck), 0, 0);
   };
+  // B-fragment offsets of row li (j-block 0) in an x buffer for the 4 K
+  // steps: 16-byte chunk 4*(s/2) + 2*g + (s%2), swizzled by the row (rows of
+  // other j-blocks differ by multiples of 32: same swizzle).
+  uint32_t boff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) boff[s] = (uint32_t)(li * 128 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ ((li >> 1) & 7)));
 
   f16x acc[JB][IB];
 #pragma unroll
@@ -301,99 +344,179 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
 
   u32x4 hdr = {0, 0, 0, 0};
   uint32_t hdr4 = 0;
-  Raw ra[IB], rn[IB];
+  constexpr int NSET = FMT == 0 ? 4 : 2;
+  Raw rs[NSET][IB];          // raw quant sets: Q4_K chunk mod 4, Q6_K block half
+  float scl[IB][NSC];        // this block's scale-table entries of the lane's rows
+  float sv[IB][4];           // scales of the current chunk
+  h8 af[IB], bf[JB];
 
-  // prologue: chunk 0 of x, table of block 0, raw bytes of chunk 0
-  load_x(0, x0);
+  auto read_scales = [&]() {
+#pragma unroll
+    for (int c = 0; c < IB; ++c) {
+      const float* t = tab + (32 * IB * wave + 32 * c + li) * C::TSTRIDE + (FMT == 0 ? 0 : 8 * g);
+#pragma unroll
+      for (int i = 0; i < NSC / 4; ++i) {
+        const float4 v = ((const float4*)t)[i];
+        scl[c][4 * i] = v.x; scl[c][4 * i + 1] = v.y; scl[c][4 * i + 2] = v.z; scl[c][4 * i + 3] = v.w;
+      }
+    }
+  };
+  // chunk cc's scales (Q6_K: scale index 8h + 2t + g, t = 2(cc&1) + s/2, is
+  // entry 4(cc>>1) + 2(cc&1) + s/2 of the lane's parity list)
+  auto chunk_scales = [&](int cc, float (&o)[IB][4]) {
+#pragma unroll
+    for (int c = 0; c < IB; ++c) {
+      if constexpr (FMT == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[c][e] = scl[c][4 * cc + e];
+      } else {
+        const int e0 = 4 * (cc >> 1) + 2 * (cc & 1);
+        o[c][0] = scl[c][e0];
+        o[c][1] = scl[c][e0 + 1];
+        o[c][2] = 0.0f;
+        o[c][3] = 0.0f;
+      }
+    }
+  };
+  auto frag = [&](const Raw& r, int s, int cc, const float (&v)[4]) -> h8 {
+    if constexpr (FMT == 0) {
+      return a_frag_q4(r, s, v);
+    } else {
+      return a_frag_q6(q6_fields(r), s, cc, v);
+    }
+  };
+  auto mfma_step = [&](const h8 (&a)[IB], const h8 (&bm)[JB]) {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int c = 0; c < IB; ++c)
+        acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], bm[jb], acc[jb][c], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+    // spread the VALU work of the next fragment between this step's MFMAs
+#pragma unroll
+    for (int i = 0; i < JB * IB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+
+  // ---- prologue: block 0's table, x and raw bytes of the first chunks
   if (tab_thread) hdr_load<FMT>(trow, hdr, hdr4);
 #pragma unroll
-  for (int c = 0; c < IB; ++c) raw_load<FMT>(wr[c], roff, 0, g, ra[c]);
-  if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + 192) & 3));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // B-fragment LDS addresses of row li of j-block 0 for the 4 K steps and the
-  // two buffers: 16-byte chunk 4*(s/2) + 2*g + (s%2), swizzled by the row
-  // (rows of other j-blocks differ by multiples of 32: same swizzle).
-  const uint8_t* bp[2][4];
+  for (int c = 0; c < IB; ++c) {
+    if constexpr (FMT == 0) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int off = li * 128 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ ((li >> 1) & 7));
-    bp[0][s] = x0 + off;
-    bp[1][s] = x1 + off;
+      for (int k = 0; k < 3; ++k) raw_load_q4(wr[c], roff, k, rs[k][c]);
+    } else {
+      raw_load_q6(wr[c], roff, 0, 0, g, rs[0][c]);
+      raw_load_q6(wr[c], roff, 0, 1, g, rs[1][c]);
+    }
   }
+  load_x(0, x0);
+  load_x(1, x1);
+  load_x(2, x2);
+  if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + 192) & 3));
+  wait_vm_barrier<0>();
+  read_scales();
+  chunk_scales(0, sv);
+#pragma unroll
+  for (int c = 0; c < IB; ++c) af[c] = frag(rs[0][c], 0, 0, sv[c]);
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) bf[jb] = *(const h8*)(x0 + boff[0] + jb * 32 * 128);
 
-  // chunks in pairs (nck is a multiple of 4): the even chunk reads x0 while
-  // the next chunk streams into x1, the odd chunk the other way round
-  for (int ck2 = 0; ck2 < nck; ck2 += 2) {
+  for (int b = 0; b < nb; ++b) {
+    const bool more = b + 1 < nb;
+    // header of the next block (decoded into the table during chunk 3).
+    // Loads are issued unconditionally (past the end they re-read the last
+    // block or chunk into buffers nobody reads), so every iteration issues
+    // the same VMEM instructions and the wait counts below are exact.
+    const int bnext = more ? b + 1 : b;
+    if (tab_thread) hdr_load<FMT>(trow + (int64_t)bnext * BLOCK_BYTES, hdr, hdr4);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int ck = ck2 + half;
-      uint8_t* const xnext = half ? x0 : x1;
-      const bool has_next = ck + 1 < nck;
-      const bool next_block = has_next && ((ck + 1) & 3) == 0;
-      const bool next_raw = has_next && (FMT == 0 || ((ck + 1) & 1) == 0);
-      if (has_next) load_x(ck + 1, xnext);
-      if (next_raw) {
+    for (int j = 0; j < 4; ++j) {
+      const int ck = 4 * b + j;
+      const uint8_t* const xc = xb[j];
+      const uint8_t* const xn = xb[(j + 1) & 3];
+      const bool pf1 = j < 3 || more;     // chunk ck + 1 exists
+      const int cur = FMT == 0 ? j : (j >> 1);                    // raw set of chunk ck
+      const int nxt = FMT == 0 ? ((j + 1) & 3) : (((j + 1) & 3) >> 1);
+      // x (and Q4_K raw bytes) of chunk ck+3, into the buffers chunk ck-1 used
+      const int ck3 = ck + 3 < 4 * nb ? ck + 3 : 4 * nb - 1;
+      load_x(ck3, xb[(j + 3) & 3]);
+      if constexpr (FMT == 0) {
 #pragma unroll
-        for (int c = 0; c < IB; ++c) raw_load<FMT>(wr[c], roff, ck + 1, g, rn[c]);
+        for (int c = 0; c < IB; ++c) raw_load_q4(wr[c], roff, ck3, rs[(j + 3) & 3][c]);
       }
-      if (next_block && tab_thread) hdr_load<FMT>(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES, hdr, hdr4);
 
-      const int cc = ck & 3;
-      const float* tb = tab + ((ck >> 2) & 1) * (C::TBUF / 4);
-      float sv[IB][4];
+      // K steps 0..2
 #pragma unroll
-      for (int c = 0; c < IB; ++c) {
-        const float* t = tb + (32 * IB * wave + 32 * c + li) * C::TSTRIDE;
-        if constexpr (FMT == 0) {
-          float4 v = *(const float4*)(t + 4 * cc);   // sub-blocks 2cc, 2cc+1
-          sv[c][0] = v.x; sv[c][1] = v.y; sv[c][2] = v.z; sv[c][3] = v.w;
-        } else {
-          const int base = 8 * (cc >> 1) + 4 * (cc & 1) + g;   // scale index 8h + 2t + g
-          sv[c][0] = t[base];
-          sv[c][1] = t[base + 2];
-          sv[c][2] = 0.0f;
-          sv[c][3] = 0.0f;
-        }
-      }
-      h8 af[IB], bf[JB];
-#pragma unroll
-      for (int c = 0; c < IB; ++c) af[c] = a_frag<FMT>(ra[c], 0, cc, sv[c]);
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb) bf[jb] = *(const h8*)(bp[half][0] + jb * 32 * 128);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 3; ++s) {
         h8 afn[IB], bfn[JB];
-        if (s < 3) {
 #pragma unroll
-          for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(bp[half][s + 1] + jb * 32 * 128);
+        for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(xc + boff[s + 1] + jb * 32 * 128);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int c = 0; c < IB; ++c) afn[c] = a_frag<FMT>(ra[c], s + 1, cc, sv[c]);
-        }
+        for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
+        if (j == 3 && s == 0 && more && tab_thread)
+          tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + (int64_t)(b + 1) * BLOCK_BYTES + 192) & 3));
+        mfma_step(af, bf);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
+        for (int c = 0; c < IB; ++c) af[c] = afn[c];
 #pragma unroll
-          for (int c = 0; c < IB; ++c)
-            acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c], bf[jb], acc[jb][c], 0, 0, 0);
-        if (s < 3) {
-#pragma unroll
-          for (int c = 0; c < IB; ++c) af[c] = afn[c];
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
-        }
+        for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
       }
-      if (next_block && tab_thread)
-        tab_store<FMT>(my_tab + (((ck + 1) >> 2) & 1) * (C::TBUF / 4), hdr, hdr4,
-                       (uint32_t)((uintptr_t)(trow + (int64_t)((ck + 1) >> 2) * BLOCK_BYTES + 192) & 3));
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (next_raw) {
+
+      // K step 3: wait for chunk ck+1's x and raw bytes and, at a block
+      // boundary, the new table; the loads of later chunks stay in flight
+      // (counts: VMEM instructions issued after the last one needed here)
+      if constexpr (FMT == 0) {
+        wait_vm_barrier<2 * (XQ + NRAW)>();
+      } else {
+        if (j == 0 || j == 2) wait_vm_barrier<2 * XQ + NRAW>();
+        else wait_vm_barrier<2 * XQ>();
+      }
+      h8 afn[IB], bfn[JB];
+      float svn[IB][4];
+      if (pf1) {
+        if (j == 3) read_scales();
+        chunk_scales((j + 1) & 3, svn);
 #pragma unroll
-        for (int c = 0; c < IB; ++c) ra[c] = rn[c];
+        for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(xn + boff[0] + jb * 32 * 128);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (pf1) {
+#pragma unroll
+        for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
+      }
+      mfma_step(af, bf);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      if (pf1) {
+#pragma unroll
+        for (int c = 0; c < IB; ++c) {
+          af[c] = afn[c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
+        }
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
+      }
+      // Q6_K raw bytes ahead: the next block's half j/2 once this block's
+      // half is used up
+      if constexpr (FMT == 1) {
+        if (j & 1) {
+#pragma unroll
+          for (int c = 0; c < IB; ++c) raw_load_q6(wr[c], roff, bnext, j >> 1, g, rs[j >> 1][c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
+  // no direct-to-LDS load may still be in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: the lane holds rows 8q + 4g + e (q, e = 0..3) of each i-block ----
 #pragma unroll
@@ -458,11 +581,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
   typedef TileCfg<JB, IB> C;
   __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
-  __shared__ __attribute__((aligned(16))) float tab[2 * C::TBUF / 4];
+  __shared__ __attribute__((aligned(16))) uint8_t x2[C::XBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t x3[C::XBUF];
+  __shared__ __attribute__((aligned(16))) float tab[C::TBUF / 4];
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   int m_tile, n_tile;
   const GemmDesc& P = tile_of(args, m_tile, n_tile);
-  gemm_tile<FMT, JB, IB, SWIGLU>(P, m_tile, n_tile, x0, x1, tab);
+  gemm_tile<FMT, JB, IB, SWIGLU>(P, m_tile, n_tile, x0, x1, x2, x3, tab);
 #endif
 }
 
@@ -476,14 +601,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel_mixed(GemmArgs args) {
   typedef TileCfg<JB, IB> C;
   __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
-  __shared__ __attribute__((aligned(16))) float tab[2 * C::TBUF / 4];
+  __shared__ __attribute__((aligned(16))) uint8_t x2[C::XBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t x3[C::XBUF];
+  __shared__ __attribute__((aligned(16))) float tab[C::TBUF / 4];
 #if defined(__HIP_DEVICE_COMPILE__)
   int m_tile, n_tile;
   const GemmDesc& P = tile_of(args, m_tile, n_tile);
   if (P.fmt == 0)
-    gemm_tile<0, JB, IB, false>(P, m_tile, n_tile, x0, x1, tab);
+    gemm_tile<0, JB, IB, false>(P, m_tile, n_tile, x0, x1, x2, x3, tab);
   else
-    gemm_tile<1, JB6, IB, false>(P, m_tile, n_tile, x0, x1, tab);
+    gemm_tile<1, JB6, IB, false>(P, m_tile, n_tile, x0, x1, x2, x3, tab);
 #endif
 }
 
