@@ -29,11 +29,42 @@ import numpy as np  # noqa: E402
 
 import synthetic  # noqa: E402
 
+import hashlib  # noqa: E402
+
 PEAK_FP16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 M_PREFILL = 1024
 ROTATE_LAYERS = 5              # 5 x 63.1 MB of weights > 256 MB Infinity Cache
 DECODE_ROTATE = 8              # decode: 8 x 63.1 MB
+
+
+# HBM bytes per launch of the grouped prefill kernel, from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE passes scaled by the same counters' reading for a plain copy
+# of known size (profiles/gemm_kernel_mixed_layer_m1024_traffic.md).  Valid
+# only for the kernel sources they were taken with: a changed source reports
+# traffic as null until the counters are taken again.
+TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
+TRAFFIC = {"sources_sha256": None, "bytes_per_launch": None}
+COPY_PROBE_BYTES = 256 << 20
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_probe(torch, reps=3):
+    """A plain device-to-device copy of COPY_PROBE_BYTES (for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters: it reads and writes exactly that much)."""
+    src = torch.randint(0, 255, (COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "reps": reps}), flush=True)
 
 
 def layer_problems(torch, dmq, config, layer, M, xs, ys):
@@ -100,6 +131,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU-oracle sample (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain copy of known size (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -110,6 +143,9 @@ def main():
     import dequant_gemm_q4_amd as dmq
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     M = M_PREFILL
 
     # activations and outputs (shared by the rotating layers), weights per layer
@@ -145,7 +181,8 @@ def main():
                    "M": M, "flop_per_step": flops, "weight_bytes_per_step": weight_bytes(),
                    "pct_fp16_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": (TRAFFIC["bytes_per_launch"] if TRAFFIC["sources_sha256"] == sources_sha256() else None),
                      "kernel": "dmq::gemm_kernel_mixed (grouped Q4_K/Q6_K prefill launch)", "launch_ms": round(kern_ms, 4)},
     }
 

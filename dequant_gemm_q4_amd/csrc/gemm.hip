@@ -556,10 +556,12 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   }
 }
 
-// Workgroup -> (problem, tile).  Within a problem, tiles go in groups of 8
-// N-tiles x all M-tiles with the N-tile fastest, so workgroups bid, bid+8,
-// bid+16, ... (placed on the same XCD by the dispatcher) share one weight
-// panel in that XCD's L2 while the 8 XCDs work on 8 different panels.
+// Workgroup -> (problem, tile).  Within a problem the M-tile runs fastest:
+// the dispatcher places workgroup bid on XCD bid % 8, so with mt dividing 8
+// each XCD keeps seeing the same one or two activation panels (they stay in
+// that XCD's L2) while its compute units stream different weight panels,
+// each once per M-tile.  (N-tile-fastest order would instead stream every
+// activation panel through every XCD once per N-tile.)
 __device__ __forceinline__ const GemmDesc& tile_of(const GemmArgs& args, int& m_tile, int& n_tile) {
   int pi = 0;
 #pragma unroll
@@ -567,12 +569,8 @@ __device__ __forceinline__ const GemmDesc& tile_of(const GemmArgs& args, int& m_
     if (i < args.count && (int)blockIdx.x >= args.d[i].tile_begin) pi = i;
   const GemmDesc& P = args.d[pi];
   const int o = (int)blockIdx.x - P.tile_begin;
-  const int mt = P.mt, nt = P.nt;
-  const int grp = o / (8 * mt);
-  const int u = o - grp * 8 * mt;
-  const int nrem = nt - 8 * grp < 8 ? nt - 8 * grp : 8;
-  m_tile = u / nrem;
-  n_tile = 8 * grp + (u - m_tile * nrem);
+  n_tile = o / P.mt;
+  m_tile = o - n_tile * P.mt;
   return P;
 }
 
