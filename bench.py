@@ -44,7 +44,7 @@ DECODE_ROTATE = 8              # decode: 8 x 63.1 MB
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": None, "bytes_per_launch": None}
+TRAFFIC = {"sources_sha256": "0e0110f76c668ee09a06986421ec53e9625bf2dc3f887ef74d3f15d29de37ca4", "bytes_per_launch": 592736739}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -58,13 +58,69 @@ def sources_sha256():
 
 def copy_probe(torch, reps=3):
     """A plain device-to-device copy of COPY_PROBE_BYTES (for calibrating the
-    FETCH_SIZE / WRITE_SIZE counters: it reads and writes exactly that much)."""
+    FETCH_SIZE / WRITE_SIZE counters: it reads and writes exactly that much),
+    then timed copies of 64 MiB and 256 MiB as a plain-bandwidth reference."""
     src = torch.randint(0, 255, (COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "reps": reps}), flush=True)
+    out = {"copy_probe_bytes": COPY_PROBE_BYTES, "reps": reps}
+    for n in (64 << 20, 256 << 20):
+        a, b = src[:n], dst[:n]
+        for _ in range(3):
+            b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        out[f"copy_{n >> 20}MiB_read_plus_write_GBps"] = round(2 * n / ms / 1e6, 1)
+    print(json.dumps(out), flush=True)
+
+
+def vendor_gemm_probe(torch):
+    """Dense fp16 GEMMs through torch.matmul (the vendor BLAS) on the layer's
+    shapes at M = 1024: a reference for what a dense, dequant-free fp16 GEMM
+    reaches on this GPU (fp16 output, fp32 accumulation)."""
+    out = {}
+    M = M_PREFILL
+    tot_fl, tot_ms = 0.0, 0.0
+    for name, fmt, N, K in synthetic.LAYER_PROJECTIONS:
+        a = torch.randn(M, K, device="cuda", dtype=torch.float16)
+        w = torch.randn(N, K, device="cuda", dtype=torch.float16)
+        wt = w.t()
+        f = lambda: torch.matmul(a, wt)   # noqa: E731
+        for _ in range(5):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        fl = 2.0 * M * N * K
+        out[f"{name}_{N}x{K}_TFLOPs"] = round(fl / ms / 1e9, 1)
+        tot_fl += fl
+        tot_ms += ms
+    out["layer_sequential_TFLOPs"] = round(tot_fl / tot_ms / 1e9, 1)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+    for _ in range(3):
+        torch.matmul(a, a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["square_8192_fp16_out_TFLOPs"] = round(2 * 8192 ** 3 / (e0.elapsed_time(e1) / 10) / 1e9, 1)
+    print(json.dumps({"vendor_gemm_probe": out}), flush=True)
 
 
 def layer_problems(torch, dmq, config, layer, M, xs, ys):
@@ -133,6 +189,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of known size (counter calibration) and exit")
+    ap.add_argument("--vendor-gemm-probe", action="store_true",
+                    help="only time dense fp16 torch.matmul on the layer shapes (reference) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -145,6 +203,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.vendor_gemm_probe:
+        vendor_gemm_probe(torch)
         return
     M = M_PREFILL
 
