@@ -13,14 +13,14 @@
 //    dequantised once per workgroup and no dequantised tile touches LDS or
 //    HBM.
 //  * x is staged in LDS per 64-wide K chunk by direct global->LDS loads
-//    (global_load_lds_dwordx4, no VGPR staging), double-buffered, with the
-//    16-byte chunks of each 128-byte row XOR-swizzled by (row & 7) so that
-//    eight consecutive rows read the same column without bank conflicts.
+//    (buffer_load ... lds, no VGPR staging) into four buffers, three chunks
+//    ahead, with the 16-byte chunks of each 128-byte row XOR-swizzled by the
+//    row so that B-fragment reads are free of bank conflicts.
 //  * Sub-block scales / mins are decoded once per super-block and weight row
-//    into an LDS table (double-buffered).  Per weight the lanes then do: mask
-//    and byte-permute the quant into an fp16 integer (1024 + q), subtract
-//    1024 (exact), and one fp32 FMA of exact operands (q*d*sc - dmin*m) with a
-//    single rounding to fp16 (v_fma_mix).
+//    into an LDS table.  Per weight the lanes then do: mask the nibble in
+//    place, convert the byte to fp32 (v_cvt_f32_ubyteN, exact), one fp32 FMA
+//    of exact operands (q*d*sc - dmin*m) and a round-to-nearest-even pack of
+//    two results to fp16 (v_cvt_pk_f16_f32).
 //  * v_mfma_f32_32x32x16_f16: lane l holds operand row l%32 and k-slots
 //    8*(l/32) .. +7; the accumulator lane holds D[8*(r/4) + 4*(l/32) + r%4]
 //    [l%32], r = 0..15.  The K order inside a 64-wide chunk is permuted (the
@@ -28,7 +28,7 @@
 //    from 8 consecutive quant bytes: step s, lane half g, slot e covers
 //    k = 32*(s/2) + 16*g + 8*(s%2) + e.
 //  * Dequant of the next K step is issued between the MFMAs of the current
-//    one, so VALU work overlaps the matrix core.
+//    one.
 //  * Optional SwiGLU epilogue: a wave's first i-block holds gate rows, its
 //    second the matching up rows, so g and u of one output sit in the same
 //    lane and h = silu(g) * u is formed in registers.
@@ -67,44 +67,45 @@ __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-// fp16 pair (q0, q1) -> (fp16(q0*s + c), fp16(q1*s + c)): one fp32 FMA per
-// element with a single rounding to fp16.  Written as one h2 of two fmaf so
-// that the compiler selects v_fma_mixlo/hi_f16 (fp16 inputs, fp32 FMA).
-__device__ __forceinline__ uint32_t fma_mix_pair(uint32_t q, float s, float c) {
-  const h2 v = as_h2(q);
-  const h2 r = {(half_t)__builtin_fmaf((float)v.x, s, c), (half_t)__builtin_fmaf((float)v.y, s, c)};
-  return as_u32(r);
-}
+typedef float f2 __attribute__((ext_vector_type(2)));
 
-// Quant bytes (each < 1024 after masking) -> fp16 pairs whose bit patterns
-// are the bytes themselves: the subnormal values b * 2^-24, exact.  Byte
-// selector 0x0c of v_perm_b32 yields 0x00.
-__device__ __forceinline__ uint32_t sub_pair_lo(uint32_t b) {   // (b.byte0, b.byte1)
-  return __builtin_amdgcn_perm(0u, b, 0x0c010c00u);
-}
-__device__ __forceinline__ uint32_t sub_pair_hi(uint32_t b) {   // (b.byte2, b.byte3)
-  return __builtin_amdgcn_perm(0u, b, 0x0c030c02u);
+// Four quant bytes b0..b3 -> the fp16 pairs (w0, w1), (w2, w3) with
+// w_i = fp16(b_i * s + c): v_cvt_f32_ubyteN (exact), one fp32 FMA of exact
+// operands, and v_cvt_pk_f16_f32 (round to nearest even).  All three are
+// full-rate VALU instructions on gfx950, where v_fma_mix runs at about half
+// rate.  The empty asm hides the masks applied by the caller, so that the
+// compiler converts byte N directly instead of extracting it first.
+__device__ __forceinline__ void bytes_fma_pairs(uint32_t b, float s, float c, uint32_t& p0, uint32_t& p1) {
+  asm("" : "+v"(b));
+  const f2 v0 = {__builtin_fmaf((float)(b & 0xffu), s, c), __builtin_fmaf((float)((b >> 8) & 0xffu), s, c)};
+  const f2 v1 = {__builtin_fmaf((float)((b >> 16) & 0xffu), s, c), __builtin_fmaf((float)(b >> 24), s, c)};
+  p0 = as_u32(__builtin_convertvector(v0, h2));
+  p1 = as_u32(__builtin_convertvector(v1, h2));
 }
 
 // 8 Q4_K weights (one A fragment) from two quant dwords.  The nibbles are
-// masked in place (low: q, high: 16 q) and read as fp16 subnormals; the
-// table scale s carries the matching 2^24 or 2^20 factor, so q*2^-24 * s is
-// exactly q*d*sc and the FMA with -dmin*m rounds once.
+// masked in place (low: q, high: 16 q); the table scale s is d*sc (d*sc/16
+// for high nibbles, exact), so b*s is exactly q*d*sc and the FMA with
+// -dmin*m rounds once.
 __device__ __forceinline__ h8 q4k_frag(uint32_t w0, uint32_t w1, uint32_t mask, float dsc, float ndm) {
-  const uint32_t a = w0 & mask, b = w1 & mask;
-  u32x4 r = {fma_mix_pair(sub_pair_lo(a), dsc, ndm), fma_mix_pair(sub_pair_hi(a), dsc, ndm),
-             fma_mix_pair(sub_pair_lo(b), dsc, ndm), fma_mix_pair(sub_pair_hi(b), dsc, ndm)};
+  uint32_t r0, r1, r2, r3;
+  bytes_fma_pairs(w0 & mask, dsc, ndm, r0, r1);
+  bytes_fma_pairs(w1 & mask, dsc, ndm, r2, r3);
+  const u32x4 r = {r0, r1, r2, r3};
   return __builtin_bit_cast(h8, r);
 }
 
 // 8 Q6_K weights: q = low nibbles (shifted by nsh) | two high bits (at hsh)
-// << 4, read as subnormals q*2^-24; dsc24 = d*sc*2^24, off = -32*d*sc.
+// << 4; w = q*dsc - 32*dsc with dsc = d*sc.
 __device__ __forceinline__ h8 q6k_frag(uint32_t l0, uint32_t l1, uint32_t h0, uint32_t h1, uint32_t nsh,
-                                       uint32_t hsh, float dsc24, float off) {
-  uint32_t q0 = ((l0 >> nsh) & 0x0f0f0f0fu) | (((h0 >> hsh) << 4) & 0x30303030u);
-  uint32_t q1 = ((l1 >> nsh) & 0x0f0f0f0fu) | (((h1 >> hsh) << 4) & 0x30303030u);
-  u32x4 r = {fma_mix_pair(sub_pair_lo(q0), dsc24, off), fma_mix_pair(sub_pair_hi(q0), dsc24, off),
-             fma_mix_pair(sub_pair_lo(q1), dsc24, off), fma_mix_pair(sub_pair_hi(q1), dsc24, off)};
+                                       uint32_t hsh, float dsc) {
+  const uint32_t q0 = ((l0 >> nsh) & 0x0f0f0f0fu) | (((h0 >> hsh) << 4) & 0x30303030u);
+  const uint32_t q1 = ((l1 >> nsh) & 0x0f0f0f0fu) | (((h1 >> hsh) << 4) & 0x30303030u);
+  const float off = dsc * -32.0f;
+  uint32_t r0, r1, r2, r3;
+  bytes_fma_pairs(q0, dsc, off, r0, r1);
+  bytes_fma_pairs(q1, dsc, off, r2, r3);
+  const u32x4 r = {r0, r1, r2, r3};
   return __builtin_bit_cast(h8, r);
 }
 
@@ -132,10 +133,9 @@ __device__ __forceinline__ void hdr_load(const uint8_t* blk, u32x4& hdr, uint32_
 }
 
 // Decode one header into 16 floats of the table row.
-//  Q4_K: pairs (d*sc_j*2^24, -dmin*m_j), with 2^20 instead of 2^24 for odd j
-//        (their quant is read from the high nibble as 16q); quants enter the
-//        FMA as fp16 subnormals q*2^-24.
-//  Q6_K: d*sc_s*2^24 for the 16 sub-blocks, even s first (s = 0, 2, .., 14
+//  Q4_K: pairs (d*sc_j, -dmin*m_j), with d*sc_j/16 for odd j (their quant
+//        is read from the high nibble as 16q).
+//  Q6_K: d*sc_s for the 16 sub-blocks, even s first (s = 0, 2, .., 14
 //        in floats 0..7), then odd s (floats 8..15): a lane only needs the
 //        sub-blocks of one parity.
 template <int FMT>
@@ -147,7 +147,7 @@ __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t h
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float dsc = d * (float)q4k_sc(s, j);
-      v[2 * j] = dsc * ((j & 1) ? 1048576.0f : 16777216.0f);
+      v[2 * j] = (j & 1) ? dsc * 0.0625f : dsc;
       v[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
     }
   } else {
@@ -158,7 +158,7 @@ __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t h
     float d = half_bits_to_float(hdr4 >> 16);
 #pragma unroll
     for (int s = 0; s < 16; ++s)
-      v[(s >> 1) + 8 * (s & 1)] = d * (float)(int)(int8_t)((w[s >> 2] >> (8 * (s & 3))) & 0xffu) * 16777216.0f;
+      v[(s >> 1) + 8 * (s & 1)] = d * (float)(int)(int8_t)((w[s >> 2] >> (8 * (s & 3))) & 0xffu);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) ((float4*)t)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -221,8 +221,8 @@ __device__ __forceinline__ Q6Fields q6_fields(const RawQ6& r) {
 }
 
 // A fragment of K step s (0..3) of chunk cc (0..3 within the block).
-// sv: Q4_K (d*sc*2^24 and -dmin*m of the chunk's even and odd sub-block);
-// Q6_K (d*sc*2^24 of the lane's two sub-blocks of the chunk).
+// sv: Q4_K (d*sc and -dmin*m of the chunk's even and odd sub-block, d*sc/16
+// for the odd one); Q6_K (d*sc of the lane's two sub-blocks of the chunk).
 __device__ __forceinline__ h8 a_frag_q4(const RawQ4& r, int s, const float (&sv)[4]) {
   const uint32_t w0 = (s & 1) ? r.q.z : r.q.x;
   const uint32_t w1 = (s & 1) ? r.q.w : r.q.y;
@@ -234,8 +234,7 @@ __device__ __forceinline__ h8 a_frag_q6(const Q6Fields& f, int s, int cc, const 
   const uint32_t h0 = (s & 1) ? f.hb.z : f.hb.x, h1 = (s & 1) ? f.hb.w : f.hb.y;
   const uint32_t nsh = (cc & 1) ? 4u : 0u;
   const uint32_t hsh = 4u * (uint32_t)(cc & 1) + 2u * (uint32_t)(s >> 1);
-  const float dsc24 = sv[s >> 1];
-  return q6k_frag(l0, l1, h0, h1, nsh, hsh, dsc24, dsc24 * -0x1p-19f);
+  return q6k_frag(l0, l1, h0, h1, nsh, hsh, sv[s >> 1]);
 }
 
 // First global weight row of i-block c of wave w.
