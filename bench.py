@@ -123,6 +123,92 @@ def vendor_gemm_probe(torch):
     print(json.dumps({"vendor_gemm_probe": out}), flush=True)
 
 
+def _timed(torch, fn, reps=20, warm=5):
+    """Mean ms of fn() over reps launches (HIP events on the current stream)."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sweep(torch, dmq):
+    """The other configurations of the scope table, one JSON line each:
+    config 0 (one Q projection at M=16), config 3 (fused SwiGLU FFN at
+    M=1024, x ~ N(0,1) and the sigma=1/16 companion), config 4 (one layer's
+    seven GEMMs at M = 1024 / 2048 / 4096, weights rotated over 5 layers,
+    and the Q6_K LM head on 1024 rows)."""
+    dev = "cuda"
+    # config 0: one Q projection, M = 16, weights rotated (64 copies > 256 MB cache)
+    M, N, K = 16, 3072, 3072
+    x = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(0, 0, 0))).to(dev)
+    ws = [torch.from_numpy(synthetic.q4k_blocks(N, K, seed=synthetic.weight_seed(0, layer, 0)).reshape(-1)).to(dev)
+          for layer in range(64)]
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    it = [0]
+
+    def c0():
+        dmq.dmq_gemm_q4k(x, ws[it[0] % 64], y, M, N, K)
+        it[0] += 1
+    ms = _timed(torch, c0, reps=64)
+    wbytes = N * (K // 256) * 144
+    print(json.dumps({"sweep": "config0 Q4_K GEMM M=16 N=K=3072, 64 rotating weight copies",
+                      "us": round(ms * 1e3, 2), "TFLOP/s": round(2 * M * N * K / ms / 1e9, 2),
+                      "weight_GB/s": round(wbytes / ms / 1e6, 1)}), flush=True)
+    del ws
+
+    # config 3: fused FFN, M = 1024, D = 3072, F = 8192
+    M, D, F = 1024, 3072, 8192
+    wgu = torch.from_numpy(synthetic.q4k_blocks(2 * F, D, seed=synthetic.weight_seed(3, 0, 4)).reshape(-1)).to(dev)
+    wd = torch.from_numpy(synthetic.q6k_blocks(D, F, seed=synthetic.weight_seed(3, 0, 6)).reshape(-1)).to(dev)
+    h = torch.empty((M, F), dtype=torch.float16, device=dev)
+    yf = torch.empty((M, D), dtype=torch.float32, device=dev)
+    for sigma in (1.0, 1.0 / 16):
+        xf = torch.from_numpy(synthetic.activations(M, D, seed=synthetic.act_seed(3, 0, 4), sigma=sigma)).to(dev)
+        ms = _timed(torch, lambda: dmq.dmq_ffn_swiglu_q4k(xf, wgu, wd, h, yf, M, D, F))
+        hf = h.float()
+        fl = 2.0 * M * (2 * F * D + D * F)
+        print(json.dumps({"sweep": f"config3 SwiGLU FFN M=1024 D=3072 F=8192 x~N(0,{sigma:g}^2)",
+                          "us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
+                          "h_overflow_fraction": round(float((~torch.isfinite(hf)).float().mean()), 4)}), flush=True)
+    del wgu, wd, h, yf
+
+    # config 4: one layer's seven GEMMs at M = 1024, 2048, 4096 (grouped launch)
+    for M in (1024, 2048, 4096):
+        xs, ys = {}, {}
+        for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
+            xs[name] = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(4, 0, idx),
+                                                              unit_rms=True)).to(dev)
+            ys[name] = torch.empty((M, N), dtype=torch.float32, device=dev)
+        layers = [layer_problems(torch, dmq, 4, layer, M, xs, ys) for layer in range(ROTATE_LAYERS)]
+        it = [0]
+
+        def c4():
+            dmq.dmq_gemm_group(layers[it[0] % ROTATE_LAYERS][0])
+            it[0] += 1
+        ms = _timed(torch, c4)
+        print(json.dumps({"sweep": f"config4 layer GEMMs M={M} (grouped launch, 5 rotating layers)",
+                          "ms": round(ms, 4), "TFLOP/s": round(flops_of(M) / ms / 1e9, 1),
+                          "pct_fp16_peak": round(100 * flops_of(M) / ms / 1e9 / PEAK_FP16_TFLOPS, 2)}), flush=True)
+        del layers, xs, ys
+
+    # config 4: tied LM head, Q6_K 3072 -> 128256 on 1024 rows
+    name, fmt, N, K = synthetic.LM_HEAD
+    M = 1024
+    wl = torch.from_numpy(synthetic.lm_head_weights(4).reshape(-1)).to(dev)
+    xl = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(4, 0, synthetic.LM_HEAD_INDEX),
+                                                unit_rms=True)).to(dev)
+    yl = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ms = _timed(torch, lambda: dmq.dmq_gemm_q6k(xl, wl, yl, M, N, K), reps=10, warm=2)
+    print(json.dumps({"sweep": "config4 LM head Q6_K N=128256 K=3072 M=1024",
+                      "ms": round(ms, 4), "TFLOP/s": round(2.0 * M * N * K / ms / 1e9, 1)}), flush=True)
+
+
 def layer_problems(torch, dmq, config, layer, M, xs, ys):
     probs = []
     for name, fmt, N, K, wq in synthetic.layer_weights(config, layer):
@@ -189,6 +275,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of known size (counter calibration) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only measure the other configurations (M=16, FFN, M sweep, LM head) and exit")
     ap.add_argument("--vendor-gemm-probe", action="store_true",
                     help="only time dense fp16 torch.matmul on the layer shapes (reference) and exit")
     args = ap.parse_args()
@@ -206,6 +294,10 @@ def main():
         return
     if args.vendor_gemm_probe:
         vendor_gemm_probe(torch)
+        return
+    if args.sweep:
+        import dequant_gemm_q4_amd as dmq
+        sweep(torch, dmq)
         return
     M = M_PREFILL
 
