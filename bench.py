@@ -336,7 +336,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": (TRAFFIC["bytes_per_launch"] if TRAFFIC["sources_sha256"] == sources_sha256() else None),
-                     "kernel": "dmq::gemm_kernel_mixed (grouped Q4_K/Q6_K prefill launch)", "launch_ms": round(kern_ms, 4)},
+                     "kernel": "dmq::gemm_kernel<3,8,4,false> (grouped Q4_K/Q6_K prefill launch)", "launch_ms": round(kern_ms, 4)},
     }
 
     if not args.no_decode:

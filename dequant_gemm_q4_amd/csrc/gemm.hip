@@ -34,20 +34,34 @@
 //    lane and h = silu(g) * u is formed in registers.
 #include "dmq_common.h"
 
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace dmq {
 
-constexpr int GEMM_MAX_GROUP = 8;
+constexpr int GEMM_MAX_GROUP = 8;              // problems per launch
+constexpr int GEMM_MAX_SEG = 2 * GEMM_MAX_GROUP;   // segments per launch
 
+// One segment of a launch: the tiles of n-tiles [n_begin, n_begin + nt) of
+// one problem, all of one tile height (alt = 0: the kernel's tall height,
+// 1: its short one), workgroups tile_begin .. tile_begin + ks*mt*nt - 1.
+// With ks > 1 the reduction is split: piece s covers K blocks [s*kbs,
+// (s+1)*kbs) and writes its fp32 partial sums to out + s*out_stride floats
+// (a workspace that a second kernel sums in piece order).
 struct GemmDesc {
   const half_t* x;
   const uint8_t* wq;
   void* out;
+  int64_t out_stride;
   int32_t fmt, swiglu, M, N, K;
-  int32_t tile_begin, mt, nt;
+  int32_t tile_begin, mt, nt, n_begin, alt, ks, kbs;
 };
 
 struct GemmArgs {
-  GemmDesc d[GEMM_MAX_GROUP];
+  GemmDesc d[GEMM_MAX_SEG];
   int32_t count;
 };
 
@@ -275,8 +289,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // a ds_read_b128 of one column by 16 consecutive rows then covers all 64
 // banks once (two rows share one 256-byte bank line).
 template <int FMT, int JB, int IB, bool SWIGLU>
-__device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, uint8_t* x0, uint8_t* x1,
-                                          uint8_t* x2, uint8_t* x3, float* tab) {
+__device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, int kb0, int nbk, void* out,
+                                          uint8_t* x0, uint8_t* x1, uint8_t* x2, uint8_t* x3, float* tab) {
   typedef TileCfg<JB, IB> C;
   typedef typename RawOf<FMT>::T Raw;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
@@ -288,8 +302,9 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
   const int M = P.M, N = P.N, K = P.K;
-  const int nb = K / QK;
-  const int64_t row_bytes = (int64_t)nb * BLOCK_BYTES;
+  const int nb = nbk;                                // K blocks of this piece, from block kb0
+  const int64_t row_bytes = (int64_t)(K / QK) * BLOCK_BYTES;
+  const int64_t kb_bytes = (int64_t)kb0 * BLOCK_BYTES;
   const int m0 = m_tile * C::BM;
   const int F = N / 2;                               // SwiGLU: gate rows [0,F), up rows [F,2F)
   const int hb = n_tile * (C::BN / 2);               // SwiGLU: first h column of the tile
@@ -301,7 +316,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   for (int c = 0; c < IB; ++c) {
     const int r0 = iblock_row0<IB, SWIGLU>(wave, c, n0, hb, F);
     const int nrows = N - r0 < 32 ? N - r0 : 32;
-    wr[c] = make_rsrc(P.wq + (int64_t)r0 * row_bytes, (int64_t)nrows * row_bytes);
+    wr[c] = make_rsrc(P.wq + (int64_t)r0 * row_bytes + kb_bytes, (int64_t)nrows * row_bytes - kb_bytes);
   }
   const uint32_t roff = (uint32_t)(li * row_bytes) + (FMT == 0 ? 16u * (uint32_t)g : 0u);
   // table thread tt decodes local row tt = 32*IB*w + 32*c + i (clamped to a valid row)
@@ -309,13 +324,13 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   const int tt = tab_thread ? tid : 0;
   int trow_i = iblock_row0<IB, SWIGLU>(tt / (32 * IB), (tt / 32) % IB, n0, hb, F) + (tt & 31);
   trow_i = trow_i < N ? trow_i : N - 1;
-  const uint8_t* trow = P.wq + (int64_t)trow_i * row_bytes;
+  const uint8_t* trow = P.wq + (int64_t)trow_i * row_bytes + kb_bytes;
   float* my_tab = tab + tt * C::TSTRIDE;
 
   // x: one buffer over this tile's rows (rows past M read as zero).  Wave
   // instruction q (of BM/8) fills LDS rows 8q .. 8q+7; lane t writes row
   // r = 8q + t/8, slot t%8, which holds 16-byte chunk (t%8) ^ ((r>>1)&7).
-  const rsrc_t xr = make_rsrc(P.x + (int64_t)m0 * K, (int64_t)(M - m0) * K * 2);
+  const rsrc_t xr = make_rsrc(P.x + (int64_t)m0 * K + kb0 * QK, (int64_t)(M - m0) * K * 2 - kb0 * QK * 2);
   uint32_t xoff[XQ];
 #pragma unroll
   for (int i = 0; i < XQ; ++i) {
@@ -523,7 +538,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
     const int m = m0 + 32 * jb + li;
     if (m >= M) continue;
     if (SWIGLU) {
-      half_t* h = (half_t*)P.out + (int64_t)m * F;
+      half_t* h = (half_t*)out + (int64_t)m * F;
       const f16x& gv = acc[jb][0];
       const f16x& uv = acc[jb][1];
 #pragma unroll
@@ -535,7 +550,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         *(uint2*)(h + col) = make_uint2(as_u32(h01), as_u32(h23));
       }
     } else {
-      float* yrow = (float*)P.out + (int64_t)m * N;
+      float* yrow = (float*)out + (int64_t)m * N;
 #pragma unroll
       for (int c = 0; c < IB; ++c) {
         const f16x& v = acc[jb][c];
@@ -555,179 +570,464 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   }
 }
 
-// Workgroup -> (problem, tile).  Within a problem the M-tile runs fastest:
+// Workgroup -> (segment, tile).  Within a segment the M-tile runs fastest:
 // the dispatcher places workgroup bid on XCD bid % 8, so with mt dividing 8
 // each XCD keeps seeing the same one or two activation panels (they stay in
 // that XCD's L2) while its compute units stream different weight panels,
 // each once per M-tile.  (N-tile-fastest order would instead stream every
 // activation panel through every XCD once per N-tile.)
-__device__ __forceinline__ const GemmDesc& tile_of(const GemmArgs& args, int& m_tile, int& n_tile) {
+// Split pieces run slowest: all tiles of piece 0, then of piece 1, ...
+__device__ __forceinline__ const GemmDesc& tile_of(const GemmArgs& args, int& m_tile, int& n_tile, int& piece) {
   int pi = 0;
 #pragma unroll
-  for (int i = 1; i < GEMM_MAX_GROUP; ++i)
+  for (int i = 1; i < GEMM_MAX_SEG; ++i)
     if (i < args.count && (int)blockIdx.x >= args.d[i].tile_begin) pi = i;
   const GemmDesc& P = args.d[pi];
+  const int per = P.mt * P.nt;
   const int o = (int)blockIdx.x - P.tile_begin;
-  n_tile = o / P.mt;
-  m_tile = o - n_tile * P.mt;
+  piece = o / per;
+  const int r = o - piece * per;
+  const int nl = r / P.mt;
+  m_tile = r - nl * P.mt;
+  n_tile = P.n_begin + nl;
   return P;
 }
 
-template <int FMT, int JB, int IB, bool SWIGLU>
+template <int FMT, int JBA, int JBB, bool SWIGLU>
+__device__ __forceinline__ void run_tile(const GemmDesc& P, int m_tile, int n_tile, int piece, uint8_t* x0,
+                                         uint8_t* x1, uint8_t* x2, uint8_t* x3, float* tab) {
+  const int kb0 = piece * P.kbs;
+  const int left = P.K / QK - kb0;
+  const int nbk = left < P.kbs ? left : P.kbs;
+  void* out = SWIGLU ? P.out : (void*)((float*)P.out + piece * P.out_stride);
+  if constexpr (JBA == JBB) {
+    gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+  } else {
+    if (P.alt)
+      gemm_tile<FMT, JBB, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+    else
+      gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+  }
+}
+
+// One workgroup = one tile of 32*JBA or 32*JBB activation rows (per
+// segment) by 256 weight rows.  FMT_MASK: bit 0 Q4_K, bit 1 Q6_K; with both,
+// the kernel branches per workgroup (uniformly) on the segment's format, so
+// a group of mixed-format problems is one launch rather than one per format
+// serialised on the stream.
+template <int FMT_MASK, int JBA, int JBB, bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
-  typedef TileCfg<JB, IB> C;
+  typedef TileCfg<JBA, 2> C;   // LDS sized for the taller tile
   __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x2[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x3[C::XBUF];
   __shared__ __attribute__((aligned(16))) float tab[C::TBUF / 4];
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-  int m_tile, n_tile;
-  const GemmDesc& P = tile_of(args, m_tile, n_tile);
-  gemm_tile<FMT, JB, IB, SWIGLU>(P, m_tile, n_tile, x0, x1, x2, x3, tab);
+  int m_tile, n_tile, piece;
+  const GemmDesc& P = tile_of(args, m_tile, n_tile, piece);
+  if constexpr (FMT_MASK == 1) {
+    run_tile<0, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+  } else if constexpr (FMT_MASK == 2) {
+    run_tile<1, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+  } else {
+    if (P.fmt == 0)
+      run_tile<0, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+    else
+      run_tile<1, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+  }
+#else
+  (void)args, (void)x0, (void)x1, (void)x2, (void)x3, (void)tab;
 #endif
 }
 
-// Mixed Q4_K / Q6_K groups: one kernel per format would serialise on the
-// stream, so this kernel branches per workgroup (uniformly) on the format.
-// Q6_K problems run with JB6 <= JB j-blocks per tile: in a layer the Q6_K
-// down projection has the longest reduction (K = 8192), and shorter tiles
-// spread it over more CUs so it does not set the end of the launch.
-template <int JB, int IB, int JB6>
-__global__ __launch_bounds__(256, 1) void gemm_kernel_mixed(GemmArgs args) {
-  typedef TileCfg<JB, IB> C;
-  __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t x2[C::XBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t x3[C::XBUF];
-  __shared__ __attribute__((aligned(16))) float tab[C::TBUF / 4];
-#if defined(__HIP_DEVICE_COMPILE__)
-  int m_tile, n_tile;
-  const GemmDesc& P = tile_of(args, m_tile, n_tile);
-  if (P.fmt == 0)
-    gemm_tile<0, JB, IB, false>(P, m_tile, n_tile, x0, x1, x2, x3, tab);
-  else
-    gemm_tile<1, JB6, IB, false>(P, m_tile, n_tile, x0, x1, x2, x3, tab);
-#endif
+// Split-K combine: y = sum over pieces s = 0 .. ks-1 of part[s], added in
+// piece order, so a result does not depend on which piece finished first.
+struct ReduceDesc {
+  const float* part;   // ks slices of n floats, stride floats apart
+  float* y;            // n floats
+  int64_t n, stride;   // n = M * N; stride = n rounded up to a multiple of 4
+  int32_t ks;
+};
+struct ReduceArgs {
+  ReduceDesc d[GEMM_MAX_GROUP];
+  int64_t begin[GEMM_MAX_GROUP + 1];   // float4 index where each problem starts
+  int32_t count;
+};
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
+  const int64_t total = a.begin[a.count];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    int pi = 0;
+    for (int k = 1; k < a.count; ++k)
+      if (i >= a.begin[k]) pi = k;
+    const ReduceDesc& d = a.d[pi];
+    const int64_t e = 4 * (i - a.begin[pi]);   // first float of this thread's group of 4
+    if (e + 4 <= d.n) {
+      float4 acc = *(const float4*)(d.part + e);
+      for (int s = 1; s < d.ks; ++s) {
+        const float4 v = *(const float4*)(d.part + s * d.stride + e);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      *(float4*)(d.y + e) = acc;
+    } else {
+      for (int64_t f = e; f < d.n; ++f) {
+        float acc = d.part[f];
+        for (int s = 1; s < d.ks; ++s) acc += d.part[s * d.stride + f];
+        d.y[f] = acc;
+      }
+    }
+  }
 }
 
-template <typename Kern>
-static hipError_t launch_one(Kern k, int tiles, const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k, dim3(tiles), dim3(256), 0, s, a);
+// ------------------------------------------------------------ launch plan ---
+//
+// Workgroups hold one CU each (the LDS of one tile exceeds half a CU's) and
+// the dispatcher hands them to CUs in index order as CUs fall free, so a
+// launch is a greedy list schedule of its tiles.  When the tiles do not
+// fill whole rounds, or a long-K problem's tiles outlast the rest, CUs idle
+// at the end of the launch.  The plan picks, per group of problems, the tile
+// height pair (tall, short), which height each problem uses, and how many of
+// the last problem's n-tile columns to run at the short height, by
+// simulating that schedule with per-tile times measured on gfx950.
+
+// Time of one tile (arbitrary units, measured on MI355X with the launch
+// full of tiles of one shape): fixed part + part per 256-wide K block.
+// Q6_K tiles are scaled by 1.3 and Q4_K ones by 1.15, what they measured
+// inside a mixed Q4_K/Q6_K launch.
+static double tile_cost(int fmt, int jb, int nb) {
+  static const double a4[4] = {313, 393, 874, 1270}, b4[4] = {275, 324, 466, 808};
+  static const double a6[4] = {278, 492, 781, 802}, b6[4] = {488, 526, 690, 1069};
+  const int i = jb == 1 ? 0 : jb == 2 ? 1 : jb == 4 ? 2 : 3;
+  return fmt == 0 ? 1.15 * (a4[i] + b4[i] * nb) : 1.3 * (a6[i] + b6[i] * nb);
+}
+
+struct Seg {
+  int prob, alt, n_begin, nt, ks, kbs;
+};
+struct Plan {
+  int jba = 1, jbb = 1, nseg = 0, fmt_mask = 0;
+  bool swiglu = false;
+  Seg seg[GEMM_MAX_SEG];
+};
+
+static int m_tiles(const GemmProblem& p, int jb) { return (p.M + 32 * jb - 1) / (32 * jb); }
+static int n_tiles(const GemmProblem& p) {
+  return p.swiglu ? (p.N / 2 + 127) / 128 : (p.N + 255) / 256;   // SwiGLU: 128 gate + 128 up rows per tile
+}
+
+// Time of the split-K combine (same units as tile_cost): a launch plus
+// reading ks partial slices and writing y at about 4 TB/s.
+static double reduce_cost(const Plan& pl, const GemmProblem* probs) {
+  double bytes = 0.0;
+  bool any = false;
+  for (int i = 0; i < pl.nseg; ++i) {
+    const Seg& sg = pl.seg[i];
+    if (sg.ks == 1) continue;
+    any = true;
+    bytes += 4.0 * (sg.ks + 1) * probs[sg.prob].M * (double)probs[sg.prob].N;
+  }
+  return any ? 300.0 + bytes / 40000.0 : 0.0;
+}
+
+// Greedy dispatch of the segments' tiles, in order, over ncu CUs (plus the
+// split-K combine): the time the last CU falls idle.  The tiles of one
+// segment cost the same, so the CU free times they produce come out in
+// increasing order: a sorted array plus a FIFO replace a heap.
+static double simulate(const Plan& pl, const GemmProblem* probs, int ncu, std::vector<double>& buf) {
+  buf.assign(3 * (size_t)ncu, 0.0);
+  double* cur = buf.data();              // sorted free times of the CUs not yet used by this segment
+  double* fifo = buf.data() + ncu;       // ring of free times produced by this segment
+  double* tmp = buf.data() + 2 * ncu;
+  for (int i = 0; i < pl.nseg; ++i) {
+    const Seg& sg = pl.seg[i];
+    const GemmProblem& p = probs[sg.prob];
+    const int jb = sg.alt ? pl.jbb : pl.jba;
+    const double c = tile_cost(p.fmt, jb, sg.kbs);
+    const int64_t n = (int64_t)m_tiles(p, jb) * sg.nt * sg.ks;
+    int a = 0, head = 0, len = 0;
+    for (int64_t t = 0; t < n; ++t) {
+      double f;
+      if (len > 0 && (a == ncu || fifo[head] < cur[a])) {
+        f = fifo[head];
+        head = head + 1 == ncu ? 0 : head + 1;
+        --len;
+      } else {
+        f = cur[a++];
+      }
+      int tail = head + len;
+      fifo[tail >= ncu ? tail - ncu : tail] = f + c;
+      ++len;
+    }
+    // merge the untouched CUs with the segment's output (both sorted)
+    int o = 0;
+    while (a < ncu || len > 0) {
+      if (len > 0 && (a == ncu || fifo[head] < cur[a])) {
+        tmp[o++] = fifo[head];
+        head = head + 1 == ncu ? 0 : head + 1;
+        --len;
+      } else {
+        tmp[o++] = cur[a++];
+      }
+    }
+    std::copy(tmp, tmp + ncu, cur);
+  }
+  return cur[ncu - 1] + reduce_cost(pl, probs);
+}
+
+// Piece length in K blocks for a split into about ks pieces (Q6_K pieces
+// start on even blocks, keeping the weight rows' 4-byte alignment).
+static int piece_blocks(const GemmProblem& p, int ks) {
+  const int nb = p.K / QK;
+  int kbs = (nb + ks - 1) / ks;
+  if (p.fmt == 1 && (kbs & 1) && kbs < nb) ++kbs;
+  return kbs;
+}
+
+static Plan make_plan(const GemmProblem* probs, int count, int ncu) {
+  int mmax = 0, kmax = 0, fmt_mask = 0;
+  for (int i = 0; i < count; ++i) {
+    mmax = probs[i].M > mmax ? probs[i].M : mmax;
+    kmax = probs[i].K > kmax ? probs[i].K : kmax;
+    fmt_mask |= 1 << probs[i].fmt;
+  }
+  const bool swiglu = probs[0].swiglu != 0;
+  static const int pairs[4][2] = {{8, 4}, {4, 2}, {2, 1}, {1, 1}};
+  static const int splits[8] = {1, 2, 3, 4, 6, 8, 12, 16};
+  std::vector<double> heap;
+
+  // Phase 1: tile heights, which problems run short tiles, and the split of
+  // the deepest-K problems; no tail.
+  struct Cand {
+    Plan pl;
+    double t;
+  };
+  std::vector<Cand> cands;
+  for (const auto& hp : pairs) {
+    const int jba = hp[0], jbb = hp[1];
+    if (jba > 1 && 32 * (jba / 2) >= mmax) continue;   // taller than needed
+    // which problems run short tiles: none, Q6_K ones (mixed groups), all
+    for (int short_set = 0; short_set < 3; ++short_set) {
+      if (jba == jbb && short_set) break;
+      if (short_set == 1 && fmt_mask != 3) continue;
+      for (int ks : splits) {
+        if (ks > 1 && (swiglu || ks > kmax / QK)) break;
+        Plan pl;
+        pl.jba = jba;
+        pl.jbb = jbb;
+        pl.fmt_mask = fmt_mask;
+        pl.swiglu = swiglu;
+        bool ok = true;
+        int order[GEMM_MAX_GROUP];
+        Seg sg[GEMM_MAX_GROUP];
+        for (int i = 0; i < count; ++i) {
+          const GemmProblem& p = probs[i];
+          const int alt = short_set == 2 || (short_set == 1 && p.fmt == 1) ? 1 : 0;
+          const int kbs = p.K == kmax ? piece_blocks(p, ks) : p.K / QK;
+          const int pks = (p.K / QK + kbs - 1) / kbs;
+          // the partial sums must fit a bounded workspace
+          if (pks > 1 && (double)pks * p.M * (double)p.N * 4.0 > (double)(512 << 20)) ok = false;
+          sg[i] = Seg{i, alt, 0, n_tiles(p), pks, kbs};
+          order[i] = i;
+        }
+        if (!ok) continue;
+        // longest tiles first
+        auto cost_of = [&](int i) { return tile_cost(probs[i].fmt, sg[i].alt ? jbb : jba, sg[i].kbs); };
+        std::stable_sort(order, order + count, [&](int a, int b) { return cost_of(a) > cost_of(b); });
+        for (int i = 0; i < count; ++i) pl.seg[pl.nseg++] = sg[order[i]];
+        cands.push_back(Cand{pl, simulate(pl, probs, ncu, heap)});
+      }
+    }
+  }
+  std::stable_sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b) { return a.t < b.t; });
+
+  // Phase 2, for every candidate within 25% of the best: the last k n-tile
+  // columns of the last tall, unsplit segment at the short height.
+  Plan best = cands[0].pl;
+  double best_t = cands[0].t;
+  for (const Cand& cd : cands) {
+    if (cd.t > 1.25 * cands[0].t) break;
+    const Plan& pl = cd.pl;
+    const Seg last = pl.seg[pl.nseg - 1];
+    const int kmx = (pl.jba != pl.jbb && !last.alt && last.ks == 1) ? last.nt : 0;
+    const int kstep = kmx > 32 ? (kmx + 31) / 32 : 1;
+    for (int k = kstep; k <= kmx; k += kstep) {
+      Plan q = pl;
+      q.seg[q.nseg - 1].nt = last.nt - k;
+      q.seg[q.nseg++] = Seg{last.prob, 1, last.nt - k, k, 1, last.kbs};
+      if (k == last.nt) q.seg[q.nseg - 2] = q.seg[q.nseg - 1], --q.nseg;
+      const double t = simulate(q, probs, ncu, heap);
+      if (t < best_t * 0.995) {
+        best_t = t;
+        best = q;
+      }
+    }
+  }
+  return best;
+}
+
+// Plans are cached by the problems' shapes (a serving loop repeats a few).
+struct PlanKey {
+  int count;
+  int32_t shape[GEMM_MAX_GROUP][5];
+  bool operator==(const PlanKey& o) const {
+    return count == o.count && std::memcmp(shape, o.shape, sizeof(int32_t) * 5 * count) == 0;
+  }
+};
+
+static Plan get_plan(const GemmProblem* probs, int count) {
+  static std::mutex mu;
+  static std::vector<std::pair<PlanKey, Plan>> cache;
+  PlanKey key{};
+  key.count = count;
+  for (int i = 0; i < count; ++i) {
+    const GemmProblem& p = probs[i];
+    key.shape[i][0] = p.fmt;
+    key.shape[i][1] = p.swiglu;
+    key.shape[i][2] = p.M;
+    key.shape[i][3] = p.N;
+    key.shape[i][4] = p.K;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.first == key) return e.second;
+  Plan pl = make_plan(probs, count, device_cu_count());
+  if (cache.size() >= 256) cache.erase(cache.begin());
+  cache.emplace_back(key, pl);
+  return pl;
+}
+
+template <int FMT_MASK, int JBA, int JBB, bool SWIGLU>
+static hipError_t launch_k(int tiles, const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<FMT_MASK, JBA, JBB, SWIGLU>), dim3(tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// Tile counts of one problem for BM = 32*jb rows and BN = 128*ib weight rows.
-static void set_tiles(GemmDesc& d, const GemmProblem& p, int jb, int ib, bool swiglu) {
-  const int bm = 32 * jb, bn = 128 * ib;
-  d.x = (const half_t*)p.x;
-  d.wq = p.wq;
-  d.out = p.out;
-  d.fmt = p.fmt;
-  d.swiglu = p.swiglu;
-  d.M = p.M;
-  d.N = p.N;
-  d.K = p.K;
-  d.mt = (p.M + bm - 1) / bm;
-  d.nt = swiglu ? (p.N / 2 + bn / 2 - 1) / (bn / 2) : (p.N + bn - 1) / bn;
+template <int JBA, int JBB>
+static hipError_t launch_pair(const Plan& pl, int tiles, const GemmArgs& a, hipStream_t s) {
+  if (pl.swiglu) return launch_k<1, JBA, JBB, true>(tiles, a, s);
+  switch (pl.fmt_mask) {
+    case 1: return launch_k<1, JBA, JBB, false>(tiles, a, s);
+    case 2: return launch_k<2, JBA, JBB, false>(tiles, a, s);
+    default: return launch_k<3, JBA, JBB, false>(tiles, a, s);
+  }
 }
 
-// JB: j-blocks per tile for Q4_K (and single-format) problems; JB6 for Q6_K
-// problems of a mixed group.
-template <int JB, int IB, bool SWIGLU, int JB6 = JB>
-static hipError_t launch_cfg(const GemmProblem* probs, int count, hipStream_t s) {
-  for (int base = 0; base < count; base += GEMM_MAX_GROUP) {
-    GemmArgs a{};
-    int n = count - base < GEMM_MAX_GROUP ? count - base : GEMM_MAX_GROUP;
-    int fmt_mask = 0;
-    for (int i = 0; i < n; ++i) fmt_mask |= 1 << probs[base + i].fmt;
-    const bool mixed = !SWIGLU && fmt_mask == 3;
-    int tiles = 0;
-    for (int i = 0; i < n; ++i) {
-      const GemmProblem& p = probs[base + i];
-      GemmDesc& d = a.d[i];
-      set_tiles(d, p, (mixed && p.fmt == 1) ? JB6 : JB, IB, SWIGLU);
-      d.tile_begin = tiles;
-      tiles += d.mt * d.nt;
-    }
-    a.count = n;
+// Split-K workspace: one buffer per (device, stream), grown on demand and
+// kept until the process ends.  Calls on one stream are ordered, so they
+// may share it; calls on different streams get different buffers.
+static float* splitk_workspace(hipStream_t s, size_t bytes, hipError_t& err) {
+  static std::mutex mu;
+  struct Ws {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+  };
+  static std::vector<Ws> pool;
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  for (auto& w : pool) {
+    if (w.dev != dev || w.stream != s) continue;
+    if (w.bytes >= bytes) return (float*)w.ptr;
+    // earlier launches on this stream may still read the old buffer
+    err = hipStreamSynchronize(s);
+    if (err == hipSuccess) err = hipFree(w.ptr);
+    if (err != hipSuccess) return nullptr;
+    w.ptr = nullptr;
+    w.bytes = 0;
+    err = hipMalloc(&w.ptr, bytes);
+    if (err != hipSuccess) return nullptr;
+    w.bytes = bytes;
+    return (float*)w.ptr;
+  }
+  void* p = nullptr;
+  err = hipMalloc(&p, bytes);
+  if (err != hipSuccess) return nullptr;
+  pool.push_back(Ws{dev, s, p, bytes});
+  return (float*)p;
+}
+
+static hipError_t launch_chunk(const GemmProblem* probs, int count, hipStream_t s) {
+  const Plan pl = get_plan(probs, count);
+  // workspace slices of the split problems (slice stride rounded to 4 floats)
+  int64_t ws_floats = 0;
+  int64_t ws_at[GEMM_MAX_SEG];
+  for (int i = 0; i < pl.nseg; ++i) {
+    const Seg& sg = pl.seg[i];
+    ws_at[i] = ws_floats;
+    if (sg.ks > 1) ws_floats += sg.ks * ((((int64_t)probs[sg.prob].M * probs[sg.prob].N) + 3) & ~(int64_t)3);
+  }
+  float* ws = nullptr;
+  if (ws_floats > 0) {
     hipError_t e;
-    if constexpr (SWIGLU) {
-      e = launch_one(gemm_kernel<0, JB, IB, true>, tiles, a, s);
+    ws = splitk_workspace(s, (size_t)ws_floats * 4, e);
+    if (!ws) return e;
+  }
+  GemmArgs a{};
+  ReduceArgs r{};
+  int tiles = 0;
+  for (int i = 0; i < pl.nseg; ++i) {
+    const Seg& sg = pl.seg[i];
+    const GemmProblem& p = probs[sg.prob];
+    GemmDesc& d = a.d[i];
+    d.x = (const half_t*)p.x;
+    d.wq = p.wq;
+    d.fmt = p.fmt;
+    d.swiglu = p.swiglu;
+    d.M = p.M;
+    d.N = p.N;
+    d.K = p.K;
+    d.mt = m_tiles(p, sg.alt ? pl.jbb : pl.jba);
+    d.nt = sg.nt;
+    d.n_begin = sg.n_begin;
+    d.alt = sg.alt;
+    d.ks = sg.ks;
+    d.kbs = sg.kbs;
+    d.tile_begin = tiles;
+    if (sg.ks > 1) {
+      const int64_t n = (int64_t)p.M * p.N;
+      d.out = ws + ws_at[i];
+      d.out_stride = (n + 3) & ~(int64_t)3;
+      ReduceDesc& rd = r.d[r.count];
+      rd.part = ws + ws_at[i];
+      rd.y = (float*)p.out;
+      rd.n = n;
+      rd.stride = d.out_stride;
+      rd.ks = sg.ks;
+      r.begin[r.count + 1] = r.begin[r.count] + (n + 3) / 4;
+      ++r.count;
     } else {
-      if (fmt_mask == 1)
-        e = launch_one(gemm_kernel<0, JB, IB, false>, tiles, a, s);
-      else if (fmt_mask == 2)
-        e = launch_one(gemm_kernel<1, JB, IB, false>, tiles, a, s);
-      else
-        e = launch_one(gemm_kernel_mixed<JB, IB, JB6>, tiles, a, s);
+      d.out = p.out;
+      d.out_stride = 0;
     }
-    if (e != hipSuccess) return e;
+    tiles += d.ks * d.mt * d.nt;
   }
-  return hipSuccess;
-}
-
-// Relative time of a launch with tiles of jb j-blocks (32 activation rows
-// each) and ib i-blocks per wave (32 weight rows each).  Workgroups run in
-// rounds of one tile per CU; per K chunk a tile costs the dequant of its
-// weight panel (~ 2 MFMA j-blocks per i-block) plus jb * ib MFMA j-blocks.
-static double launch_cost(const GemmProblem* probs, int count, int jb, int ib, bool swiglu, int ncu) {
-  int64_t tiles = 0, kmax = 0;
-  double work = 0.0;
-  for (int i = 0; i < count; ++i) {
-    GemmDesc d;
-    set_tiles(d, probs[i], jb, ib, swiglu);
-    tiles += (int64_t)d.mt * d.nt;
-    work += (double)d.mt * d.nt * probs[i].K;
-    kmax = probs[i].K > kmax ? probs[i].K : kmax;
+  a.count = pl.nseg;
+  hipError_t e;
+  switch (pl.jba) {
+    case 8: e = launch_pair<8, 4>(pl, tiles, a, s); break;
+    case 4: e = launch_pair<4, 2>(pl, tiles, a, s); break;
+    case 2: e = launch_pair<2, 1>(pl, tiles, a, s); break;
+    default: e = launch_pair<1, 1>(pl, tiles, a, s); break;
   }
-  const double per_chunk = ib * (2.0 + 0.5 * jb);
-  const double rounds = (double)((tiles + ncu - 1) / ncu);
-  // full rounds of the mean tile, but never less than the longest tile
-  double t = rounds * (work / (double)tiles);
-  if (t < (double)kmax) t = (double)kmax;
-  return t * per_chunk;
+  if (e != hipSuccess || r.count == 0) return e;
+  const int64_t groups = r.begin[r.count];
+  const int64_t blocks = (groups + 255) / 256;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, s, r);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmProblem* probs, int count, hipStream_t s) {
-  int mmax = 0, fmt_mask = 0;
-  const bool swiglu = probs[0].swiglu != 0;
-  for (int i = 0; i < count; ++i) {
-    mmax = probs[i].M > mmax ? probs[i].M : mmax;
-    fmt_mask |= 1 << probs[i].fmt;
+  // A SwiGLU problem runs alone (its epilogue is the kernel's).
+  for (int base = 0; base < count; base += GEMM_MAX_GROUP) {
+    const int n = count - base < GEMM_MAX_GROUP ? count - base : GEMM_MAX_GROUP;
+    const hipError_t e = launch_chunk(probs + base, n, s);
+    if (e != hipSuccess) return e;
   }
-  const int ncu = device_cu_count();
-  // candidate tile shapes (jb, ib); SwiGLU needs ib == 2 (gate + up)
-  static const int cand[6][2] = {{8, 2}, {4, 2}, {2, 2}, {1, 2}, {2, 1}, {1, 1}};
-  int best_jb = 1, best_ib = 2;
-  double best = 0.0;
-  for (const auto& c : cand) {
-    const int jb = c[0], ib = c[1];
-    if (swiglu && ib != 2) continue;
-    if (jb > 1 && 32 * (jb / 2) >= mmax) continue;          // taller than needed
-    const double t = launch_cost(probs, count, jb, ib, swiglu, ncu);
-    if (best == 0.0 || t < best * 0.97) {
-      best = t;
-      best_jb = jb;
-      best_ib = ib;
-    }
-  }
-  if (swiglu) {
-    switch (best_jb) {
-      case 8: return launch_cfg<8, 2, true>(probs, count, s);
-      case 4: return launch_cfg<4, 2, true>(probs, count, s);
-      case 2: return launch_cfg<2, 2, true>(probs, count, s);
-      default: return launch_cfg<1, 2, true>(probs, count, s);
-    }
-  }
-  const bool mixed = fmt_mask == 3;
-  if (best_ib == 1) return best_jb == 2 ? launch_cfg<2, 1, false>(probs, count, s) : launch_cfg<1, 1, false>(probs, count, s);
-  switch (best_jb) {
-    case 8: return mixed ? launch_cfg<8, 2, false, 4>(probs, count, s) : launch_cfg<8, 2, false>(probs, count, s);
-    case 4: return mixed ? launch_cfg<4, 2, false, 2>(probs, count, s) : launch_cfg<4, 2, false>(probs, count, s);
-    case 2: return launch_cfg<2, 2, false>(probs, count, s);
-    default: return launch_cfg<1, 2, false>(probs, count, s);
-  }
+  return hipSuccess;
 }
 
 }  // namespace dmq

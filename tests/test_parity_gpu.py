@@ -271,20 +271,54 @@ def test_gemm_config2_group_sampled(dmq):
         assert_within(y.cpu().numpy()[rows], ref, s, f"config2 {name} M={M} (rows {len(rows)})")
 
 
-def test_gemm_group_equals_single_calls(dmq):
+def test_gemm_group_matches_single_calls(dmq):
+    """A grouped launch and one call per problem may tile (and split K)
+    differently, so their fp32 sums may round differently: both must meet
+    the bar, and repeating a call must give the same bits."""
     M = 300
     items = _layer_group(dmq, 2, 1, M)
-    probs, singles = [], []
+    probs, singles, host = [], [], []
     for name, fmt, N, K, wq, x in items:
         xd, wd = dev(x), dev(wq.reshape(-1))
         probs.append((fmt, xd, wd, torch.empty((M, N), dtype=torch.float32, device=DEV), M, N, K))
         singles.append((fmt, xd, wd, torch.empty((M, N), dtype=torch.float32, device=DEV), M, N, K))
+        host.append((name, fmt, N, K, wq, x))
     dmq.dmq_gemm_group(probs)
     for fmt, xd, wd, ys, M_, N, K in singles:
         (dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k)(xd, wd, ys, M_, N, K)
     torch.cuda.synchronize()
-    for p, s_ in zip(probs, singles):
-        assert torch.equal(p[3], s_[3])
+    first = [p[3].clone() for p in probs]
+    dmq.dmq_gemm_group(probs)
+    torch.cuda.synchronize()
+    rows = synthetic.row_sample(M, 12, seed=5)
+    for p, s_, f, (name, fmt, N, K, wq, x) in zip(probs, singles, first, host):
+        assert torch.equal(p[3], f), f"{name}: repeated grouped launch changed bits"
+        ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
+        assert_within(p[3].cpu().numpy()[rows], ref, s, f"group {name} M={M}")
+        assert_within(s_[3].cpu().numpy()[rows], ref, s, f"single {name} M={M}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,N,K", [(5, 37, 8192), (33, 250, 4864), (16, 3072, 768), (1024, 3072, 8192)])
+def test_gemm_split_k(dmq, fmt, M, N, K):
+    """Too few output tiles to fill the GPU: the launch splits the K blocks
+    into pieces whose fp32 partial sums a second kernel adds in piece order
+    (M*N not a multiple of 4 takes the combine's scalar tail).  Every output
+    is checked (the largest shape, the FFN down projection, on sampled
+    rows), and a second call must give the same bits."""
+    x = synthetic.activations(M, K, seed=M * 7 + K)
+    wq = synthetic.weight_blocks(fmt, N, K, seed=N * 5 + K)
+    xd, wd = dev(x), dev(wq.reshape(-1))
+    fn = dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k
+    y1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    fn(xd, wd, y1, M, N, K)
+    fn(xd, wd, y2, M, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), "split-K result is not reproducible"
+    rows = np.arange(M) if M <= 64 else synthetic.row_sample(M, 24, seed=K)
+    ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
+    assert_within(y1.cpu().numpy()[rows], ref, s, f"split-K {fmt} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M", [2048, 4096])
