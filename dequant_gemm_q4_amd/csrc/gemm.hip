@@ -17,10 +17,12 @@
 //    ahead, with the 16-byte chunks of each 128-byte row XOR-swizzled by the
 //    row so that B-fragment reads are free of bank conflicts.
 //  * Sub-block scales / mins are decoded once per super-block and weight row
-//    into an LDS table.  Per weight the lanes then do: mask the nibble in
-//    place, convert the byte to fp32 (v_cvt_f32_ubyteN, exact), one fp32 FMA
-//    of exact operands (q*d*sc - dmin*m) and a round-to-nearest-even pack of
-//    two results to fp16 (v_cvt_pk_f16_f32).
+//    into an LDS table.  Per weight the lanes then do: isolate the quant in
+//    a byte, convert it to fp32 exactly (Q4_K: the nibble read as an fp8
+//    E4M3 pattern is q * 2^-9, two per v_cvt_pk_f32_fp8, with 2^9 folded
+//    into the scale; Q6_K: v_cvt_f32_ubyteN), one fp32 FMA of exact operands
+//    (q*d*sc - dmin*m) and a round-to-nearest-even pack of two results to
+//    fp16 (v_cvt_pk_f16_f32).
 //  * v_mfma_f32_32x32x16_f16: lane l holds operand row l%32 and k-slots
 //    8*(l/32) .. +7; the accumulator lane holds D[8*(r/4) + 4*(l/32) + r%4]
 //    [l%32], r = 0..15.  The K order inside a 64-wide chunk is permuted (the
@@ -97,14 +99,28 @@ __device__ __forceinline__ void bytes_fma_pairs(uint32_t b, float s, float c, ui
   p1 = as_u32(__builtin_convertvector(v1, h2));
 }
 
-// 8 Q4_K weights (one A fragment) from two quant dwords.  The nibbles are
-// masked in place (low: q, high: 16 q); the table scale s is d*sc (d*sc/16
-// for high nibbles, exact), so b*s is exactly q*d*sc and the FMA with
-// -dmin*m rounds once.
-__device__ __forceinline__ h8 q4k_frag(uint32_t w0, uint32_t w1, uint32_t mask, float dsc, float ndm) {
+// Four nibbles (one per byte, 0..15) -> the fp16 pairs (w0, w1), (w2, w3)
+// with w_i = fp16(q_i * d*sc + c).  v_cvt_pk_f32_fp8 reads byte patterns
+// 0..15 as the fp8 E4M3 values q * 2^-9 exactly, two per instruction, so the
+// scale s512 carries 2^9: the product is exactly q*d*sc and the FMA rounds
+// once, as with an integer q.
+__device__ __forceinline__ void nibbles_fma_pairs(uint32_t b, float s512, float c, uint32_t& p0, uint32_t& p1) {
+  const f2 q01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+  const f2 q23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
+  const f2 v0 = {__builtin_fmaf(q01.x, s512, c), __builtin_fmaf(q01.y, s512, c)};
+  const f2 v1 = {__builtin_fmaf(q23.x, s512, c), __builtin_fmaf(q23.y, s512, c)};
+  p0 = as_u32(__builtin_convertvector(v0, h2));
+  p1 = as_u32(__builtin_convertvector(v1, h2));
+}
+
+// 8 Q4_K weights (one A fragment) from two quant dwords: their low (hi =
+// false) or high nibbles; dsc512 = d*sc*2^9, ndm = -dmin*m.
+__device__ __forceinline__ h8 q4k_frag(uint32_t w0, uint32_t w1, bool hi, float dsc512, float ndm) {
+  const uint32_t b0 = (hi ? w0 >> 4 : w0) & 0x0f0f0f0fu;
+  const uint32_t b1 = (hi ? w1 >> 4 : w1) & 0x0f0f0f0fu;
   uint32_t r0, r1, r2, r3;
-  bytes_fma_pairs(w0 & mask, dsc, ndm, r0, r1);
-  bytes_fma_pairs(w1 & mask, dsc, ndm, r2, r3);
+  nibbles_fma_pairs(b0, dsc512, ndm, r0, r1);
+  nibbles_fma_pairs(b1, dsc512, ndm, r2, r3);
   const u32x4 r = {r0, r1, r2, r3};
   return __builtin_bit_cast(h8, r);
 }
@@ -147,8 +163,8 @@ __device__ __forceinline__ void hdr_load(const uint8_t* blk, u32x4& hdr, uint32_
 }
 
 // Decode one header into 16 floats of the table row.
-//  Q4_K: pairs (d*sc_j, -dmin*m_j), with d*sc_j/16 for odd j (their quant
-//        is read from the high nibble as 16q).
+//  Q4_K: pairs (d*sc_j * 2^9, -dmin*m_j); the nibbles reach fp32 as
+//        q * 2^-9.
 //  Q6_K: d*sc_s for the 16 sub-blocks, even s first (s = 0, 2, .., 14
 //        in floats 0..7), then odd s (floats 8..15): a lane only needs the
 //        sub-blocks of one parity.
@@ -161,7 +177,7 @@ __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t h
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float dsc = d * (float)q4k_sc(s, j);
-      v[2 * j] = (j & 1) ? dsc * 0.0625f : dsc;
+      v[2 * j] = dsc * 512.0f;
       v[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
     }
   } else {
@@ -235,12 +251,12 @@ __device__ __forceinline__ Q6Fields q6_fields(const RawQ6& r) {
 }
 
 // A fragment of K step s (0..3) of chunk cc (0..3 within the block).
-// sv: Q4_K (d*sc and -dmin*m of the chunk's even and odd sub-block, d*sc/16
-// for the odd one); Q6_K (d*sc of the lane's two sub-blocks of the chunk).
+// sv: Q4_K (d*sc*2^9 and -dmin*m of the chunk's even and odd sub-block);
+// Q6_K (d*sc of the lane's two sub-blocks of the chunk).
 __device__ __forceinline__ h8 a_frag_q4(const RawQ4& r, int s, const float (&sv)[4]) {
   const uint32_t w0 = (s & 1) ? r.q.z : r.q.x;
   const uint32_t w1 = (s & 1) ? r.q.w : r.q.y;
-  return s < 2 ? q4k_frag(w0, w1, 0x0f0f0f0fu, sv[0], sv[1]) : q4k_frag(w0, w1, 0xf0f0f0f0u, sv[2], sv[3]);
+  return s < 2 ? q4k_frag(w0, w1, false, sv[0], sv[1]) : q4k_frag(w0, w1, true, sv[2], sv[3]);
 }
 __device__ __forceinline__ h8 a_frag_q6(const Q6Fields& f, int s, int cc, const float (&sv)[4]) {
   const u32x4& l = (s >> 1) ? f.lb : f.la;

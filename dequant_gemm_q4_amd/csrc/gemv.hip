@@ -14,9 +14,11 @@
 //    through LDS in wave order (no atomics, the same result every run);
 //  * every byte of W is read exactly once; Q6_K blocks (210 bytes, so a
 //    field may start 2 mod 4) are read with 2-byte-aligned 16-byte loads;
-//  * each weight is dequantised exactly: the quant byte goes to fp32
-//    (v_cvt_f32_ubyte), one fp32 FMA of exact operands gives q*d*sc - dmin*m
-//    rounded once to fp32, and v_cvt_pk_f16_f32 rounds pairs to fp16; the
+//  * each weight is dequantised exactly: the quant goes to fp32 exactly
+//    (Q4_K: a nibble read as an fp8 E4M3 pattern is q * 2^-9, converted two
+//    per v_cvt_pk_f32_fp8; Q6_K: fp16 magic numbers), one fp32 FMA of exact
+//    operands gives q*d*sc - dmin*m rounded once to fp32, and
+//    v_cvt_pk_f16_f32 rounds pairs to fp16; the
 //    fp16 pairs meet x in v_dot2_f32_f16 with fp32 accumulation.  Factoring
 //    the sub-block scale and min out of the sum would be cheaper, but when
 //    d*sc*q and dmin*m nearly cancel its fp32 rounding error is not bounded
@@ -108,8 +110,11 @@ __device__ __forceinline__ float part_dot(const PartQ4& r, int p, const half_t* 
   const uint32_t sh = (uint32_t)(p & 1) * 16u;
   const float d = half_bits_to_float(r.hdr.x);
   const float dmin = half_bits_to_float(r.hdr.x >> 16);
-  const float dsc0 = d * (float)((scw >> sh) & 0xffu);
-  const float dsc1 = d * (float)((scw >> (sh + 8)) & 0xffu) * 0.0625f;  // high nibble read as 16q
+  // nibbles go to fp32 as q * 2^-9 (fp8 E4M3 patterns 0..15, two per
+  // instruction), so the scales carry 2^9: q*2^-9 * d*sc*2^9 is exactly
+  // q*d*sc and the FMA rounds once, as with an integer q
+  const float dsc0 = d * (float)((scw >> sh) & 0xffu) * 512.0f;
+  const float dsc1 = d * (float)((scw >> (sh + 8)) & 0xffu) * 512.0f;
   const float ndm0 = -(dmin * (float)((mw >> sh) & 0xffu));
   const float ndm1 = -(dmin * (float)((mw >> (sh + 8)) & 0xffu));
   const uint32_t qw[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
@@ -124,20 +129,14 @@ __device__ __forceinline__ float part_dot(const PartQ4& r, int p, const half_t* 
     const uint32_t xb_w[4] = {xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      uint32_t lo = qw[i + u] & 0x0f0f0f0fu;
-      uint32_t hi = qw[i + u] & 0xf0f0f0f0u;
-      // hide the masks from the optimiser: with them known it extracts each
-      // nibble with v_bfe and converts byte 0, instead of one v_cvt_f32_ubyteN
-      asm("" : "+v"(lo));
-      asm("" : "+v"(hi));
-      const h2 wl01 = pack_h2(__builtin_fmaf((float)(lo & 0xffu), dsc0, ndm0),
-                              __builtin_fmaf((float)((lo >> 8) & 0xffu), dsc0, ndm0));
-      const h2 wl23 = pack_h2(__builtin_fmaf((float)((lo >> 16) & 0xffu), dsc0, ndm0),
-                              __builtin_fmaf((float)(lo >> 24), dsc0, ndm0));
-      const h2 wh01 = pack_h2(__builtin_fmaf((float)(hi & 0xffu), dsc1, ndm1),
-                              __builtin_fmaf((float)((hi >> 8) & 0xffu), dsc1, ndm1));
-      const h2 wh23 = pack_h2(__builtin_fmaf((float)((hi >> 16) & 0xffu), dsc1, ndm1),
-                              __builtin_fmaf((float)(hi >> 24), dsc1, ndm1));
+      const int lo = (int)(qw[i + u] & 0x0f0f0f0fu);
+      const int hi = (int)((qw[i + u] >> 4) & 0x0f0f0f0fu);
+      const f2 ql01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), ql23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+      const f2 qh01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), qh23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+      const h2 wl01 = pack_h2(__builtin_fmaf(ql01.x, dsc0, ndm0), __builtin_fmaf(ql01.y, dsc0, ndm0));
+      const h2 wl23 = pack_h2(__builtin_fmaf(ql23.x, dsc0, ndm0), __builtin_fmaf(ql23.y, dsc0, ndm0));
+      const h2 wh01 = pack_h2(__builtin_fmaf(qh01.x, dsc1, ndm1), __builtin_fmaf(qh01.y, dsc1, ndm1));
+      const h2 wh23 = pack_h2(__builtin_fmaf(qh23.x, dsc1, ndm1), __builtin_fmaf(qh23.y, dsc1, ndm1));
       acc0 = __builtin_amdgcn_fdot2(wl01, as_h2(xa_w[2 * u]), acc0, false);
       acc0 = __builtin_amdgcn_fdot2(wl23, as_h2(xa_w[2 * u + 1]), acc0, false);
       acc1 = __builtin_amdgcn_fdot2(wh01, as_h2(xb_w[2 * u]), acc1, false);
