@@ -40,11 +40,11 @@ DECODE_ROTATE = 8              # decode: 8 x 63.1 MB
 
 # HBM bytes per launch of the grouped prefill kernel, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE passes scaled by the same counters' reading for a plain copy
-# of known size (profiles/gemm_kernel_mixed_layer_m1024_traffic.md).  Valid
+# of known size (profiles/gemm_kernel_layer_m1024_traffic.md).  Valid
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": "0e0110f76c668ee09a06986421ec53e9625bf2dc3f887ef74d3f15d29de37ca4", "bytes_per_launch": 592736739}
+TRAFFIC = {"sources_sha256": "51b5369f85699ab0879ded2f6678672a301e46fa7d16672964903fec25a76bd6", "bytes_per_launch": 617174176}
 COPY_PROBE_BYTES = 256 << 20
 
 
