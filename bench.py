@@ -247,6 +247,33 @@ def time_launches(torch, launch, groups, steps, warmup):
     return t0.elapsed_time(t1), per
 
 
+def time_graph(torch, launch, groups, replays):
+    """Capture one launch per group into a HIP graph and time `replays`
+    replays (kernels back to back, no host launch gaps).  Returns ms per
+    launch."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for g in groups:
+            launch(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for g in groups:
+            launch(g)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (replays * len(groups))
+
+
 def cpu_baseline(rows_sample: int):
     """The oracle (dequant + fp64 matmul) on `rows_sample` rows of every
     projection of one layer, timed on this host; scaled to TFLOP/s."""
@@ -351,11 +378,15 @@ def main():
         d_total, d_per = time_launches(torch, dmq.dmq_gemm_group, dgroups, dsteps, args.warmup)
         wb = weight_bytes()
         d_ms = float(np.mean(d_per))
+        # a decode loop replays its launches from a graph: time that too
+        g_ms = time_graph(torch, dmq.dmq_gemm_group, dgroups, 8)
         out["decode"] = {"workload": "M=1, one layer's 7 projections in one grouped launch, 8 rotating layers",
                          "us_per_layer": round(1e3 * d_total / dsteps, 2),
                          "GB/s": round(wb / (d_total / dsteps / 1e3) / 1e9, 1),
                          "kernel_GB/s": round(wb / (d_ms / 1e3) / 1e9, 1),
-                         "frac_hbm": round(wb / (d_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         "graph_us_per_layer": round(1e3 * g_ms, 2),
+                         "graph_GB/s": round(wb / (g_ms / 1e3) / 1e9, 1),
+                         "frac_hbm": round(wb / (g_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
