@@ -85,10 +85,20 @@ int hip_status(hipError_t e) { return e == hipSuccess ? DMQ_OK : DMQ_ERR_HIP; }
 // The decode kernel stages x in LDS; it takes K up to this size.
 constexpr int64_t kGemvMaxK = 32768;
 
+// Largest M the small-M kernel takes (one 16-row MFMA column group).  At
+// M = 32 the tiled kernel with split-K measured faster (one layer: 45 vs
+// 63 us); at M = 16 the small-M kernel (40 vs 43 us; one 3072x3072 Q4_K
+// projection: 7.8 vs 14.5 us).
+constexpr int kSkinnyMaxM = 16;
+
 int run_gemm(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t s) {
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
-  return hip_status(decode ? dmq::launch_gemv(probs, count, s) : dmq::launch_gemm(probs, count, s));
+  if (decode) return hip_status(dmq::launch_gemv(probs, count, s));
+  bool skinny = true;
+  for (int i = 0; i < count; ++i)
+    if (probs[i].swiglu || probs[i].M > kSkinnyMaxM) skinny = false;
+  return hip_status(skinny ? dmq::launch_skinny(probs, count, s) : dmq::launch_gemm(probs, count, s));
 }
 
 dmq::GemmProblem make_problem(int fmt, const void* x, const void* wq, void* out, int64_t M, int64_t N, int64_t K,

@@ -126,6 +126,9 @@ struct GemmProblem {
 hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s);
 // MFMA kernel (M >= 2).
 hipError_t launch_gemm(const GemmProblem* probs, int count, hipStream_t s);
+// Small-M MFMA kernel (M <= 16, no SwiGLU): the decode kernel's work split
+// with the rows' multiply-adds on v_mfma_f32_16x16x32_f16.
+hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s);
 
 int device_cu_count();
 

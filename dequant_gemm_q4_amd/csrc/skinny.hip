@@ -1,0 +1,319 @@
+// Small-M kernel (2 <= M <= 16): y = x * W^T for a few activation rows.
+//
+// With a handful of rows the work is still a stream of the weights (each
+// weight is used M times, far below the MFMA ridge), so this kernel keeps
+// the decode kernel's shape and hands the per-weight multiply-adds of all
+// M rows to the matrix cores (article "Building DAMASCUS", "Prefill and
+// decode need different performance questions": prefill reuses each weight
+// across the prompt rows; overview page, compartment 09 of "[02] the
+// pipeline": the dequant is fused and fp16 weights are never written):
+//
+//  * a workgroup owns 16 consecutive weight rows; its 4 waves split the
+//    rows' super-blocks into 4 contiguous slices, and a lane works on row
+//    l%16 and part l/16 of every super-block of its wave's slice;
+//  * v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16 and k-slots
+//    8*(l/16) .. +7; B: column l%16, the same k-slots; D: column l%16, rows
+//    4*(l/16) .. +3) takes 8 dequantised weights per lane as the A operand
+//    and the matching 8 x values of activation row l%16 as B (zeros for
+//    rows past M), so every weight is dequantised once and used by all M
+//    rows;
+//  * the K order inside an MFMA is free (A and B use the same one): part p
+//    of a Q4_K block is quant bytes 32p..32p+31 (sub-blocks 2p and 2p+1),
+//    and MFMA step s takes the low (s < 4) or high nibbles of its bytes
+//    8(s%4) .. +7; Q6_K part p is half p/2, 16-weight column p%2 of each
+//    32-weight quarter, and step s covers quarter s/2, weights 8(s%2) .. +7;
+//  * the next block's quant bytes and x fragments are loaded while the
+//    current block is computed; the 4 waves' partial sums are added in
+//    wave order through LDS (the same result every run).
+//
+// Dequant is exact as in the other kernels: Q4_K nibbles reach fp32 as fp8
+// E4M3 patterns (q * 2^-9, scale carrying 2^9), Q6_K quants through
+// v_cvt_f32_ubyte; one fp32 FMA of exact operands; fp16 pairs by RNE.
+#include "dmq_common.h"
+
+#include <utility>
+
+namespace dmq {
+
+constexpr int SKINNY_MAX_GROUP = 8;
+constexpr int SKINNY_ROWS = 16;
+
+struct SkinnyDesc {
+  const half_t* x;
+  const uint8_t* wq;
+  float* y;
+  int32_t fmt, M, N, K;
+  int32_t wg_begin;
+};
+
+struct SkinnyArgs {
+  SkinnyDesc d[SKINNY_MAX_GROUP];
+  int32_t count;
+};
+
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
+typedef uint4 u4_a2 __attribute__((aligned(2)));
+typedef uint2 u2_a2 __attribute__((aligned(2)));
+
+// One lane's bytes of one super-block.  MFMA step s covers the 32 weights
+// k = 32s .. 32s+31 of the block, and part p (= lane / 16) the 8 weights
+// 32s + 8p .. +7, so the 4 parts of a step read one 64-byte piece of each
+// activation row.
+//  Q4_K: sub-block s; its quant bytes 32(s/2) + 8p .. +7, low nibbles for
+//        even s, high for odd s.  A lane loads the 8 bytes 32c + 8p (c =
+//        0..3) and the 16-byte header.
+//  Q6_K: half h = s/4, quarter t = s%4, weights l = 8p .. 8p+7 of the
+//        quarter: low bits in ql byte 64h + 32(t%2) + l (low nibble for
+//        t < 2), high bits 2t..2t+1 of qh byte 32h + l, scale 8h + 2t +
+//        (p >= 2).  A lane loads 8 bytes at 64h + 32u + 8p (h, u = 0..1), 8
+//        bytes at 128 + 32h + 8p, the 16 scales and d.
+struct SkQ4 {
+  uint4 hdr;
+  uint2 q[4];          // quant bytes 32c + 8p .. +7, c = 0..3
+};
+struct SkQ6 {
+  uint2 ql[4];         // index 2h + u
+  uint2 qh[2];         // index h
+  uint4 sc;            // 16 int8 scales
+  uint32_t s206;       // halfwords 206, 208: d in the high half
+};
+template <int FMT> struct SkPart { typedef SkQ4 T; };
+template <> struct SkPart<1> { typedef SkQ6 T; };
+
+__device__ __forceinline__ void sk_load(const uint8_t* blk, int p, SkQ4& r) {
+  r.hdr = *(const uint4*)blk;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.q[c] = *(const uint2*)(blk + 16 + 32 * c + 8 * p);
+}
+// Q6_K blocks are 210 bytes, so a field may start 2 mod 4: 2-byte-aligned
+// loads, which the global memory path serves like aligned ones.
+__device__ __forceinline__ void sk_load(const uint8_t* blk, int p, SkQ6& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.ql[i] = *(const u2_a2*)(blk + 64 * (i >> 1) + 32 * (i & 1) + 8 * p);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) r.qh[h] = *(const u2_a2*)(blk + 128 + 32 * h + 8 * p);
+  r.sc = *(const u4_a2*)(blk + 192);
+  r.s206 = *(const u32_a2*)(blk + 206);
+}
+
+// k offset inside the super-block of the 8 weights of part p, MFMA step s
+__device__ __forceinline__ int sk_kofs(int p, int s) { return 32 * s + 8 * p; }
+
+__device__ __forceinline__ h2 sk_pack(float a, float b) {
+  const f2 v = {a, b};
+  return __builtin_convertvector(v, h2);
+}
+
+// Per-block scale values of a lane.  Q4_K: d*sc_j*2^9 and -dmin*m_j for the
+// 8 sub-blocks; Q6_K: d*sc of the lane's scale in each of the 8 steps.
+struct SkScales {
+  float a[16];
+};
+__device__ __forceinline__ SkScales sk_scales(const SkQ4& r, int p) {
+  (void)p;
+  Q4kScales s = unpack_q4k_scales(r.hdr.y, r.hdr.z, r.hdr.w);
+  const float d = half_bits_to_float(r.hdr.x) * 512.0f;
+  const float dmin = half_bits_to_float(r.hdr.x >> 16);
+  SkScales o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    o.a[2 * j] = d * (float)q4k_sc(s, j);
+    o.a[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
+  }
+  return o;
+}
+__device__ __forceinline__ SkScales sk_scales(const SkQ6& r, int p) {
+  const float d = half_bits_to_float(r.s206 >> 16);
+  const uint32_t sw[4] = {r.sc.x, r.sc.y, r.sc.z, r.sc.w};
+  const uint32_t hi = p >= 2 ? 1u : 0u;
+  SkScales o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    // scale index 8h + 2t + (p >= 2), h = s/4, t = s%4: byte 2s + (p >= 2)
+    const uint32_t w = sw[s >> 1];
+    const int sc = (int)(int8_t)((w >> (16 * (s & 1) + 8 * hi)) & 0xffu);
+    o.a[s] = d * (float)sc;
+  }
+  return o;
+}
+
+// The 8 fp16 weights of MFMA step s (exact dequant, one rounding to fp32,
+// RNE to fp16).
+__device__ __forceinline__ h8 sk_frag(const SkQ4& r, const SkScales& sc, int s) {
+  const uint2 qv = r.q[s >> 1];
+  const bool hi = s & 1;
+  const float m = sc.a[2 * s], c = sc.a[2 * s + 1];
+  const int b0 = (int)((hi ? qv.x >> 4 : qv.x) & 0x0f0f0f0fu);
+  const int b1 = (int)((hi ? qv.y >> 4 : qv.y) & 0x0f0f0f0fu);
+  const f2 q0 = __builtin_amdgcn_cvt_pk_f32_fp8(b0, false), q1 = __builtin_amdgcn_cvt_pk_f32_fp8(b0, true);
+  const f2 q2 = __builtin_amdgcn_cvt_pk_f32_fp8(b1, false), q3 = __builtin_amdgcn_cvt_pk_f32_fp8(b1, true);
+  const h2 w01 = sk_pack(__builtin_fmaf(q0.x, m, c), __builtin_fmaf(q0.y, m, c));
+  const h2 w23 = sk_pack(__builtin_fmaf(q1.x, m, c), __builtin_fmaf(q1.y, m, c));
+  const h2 w45 = sk_pack(__builtin_fmaf(q2.x, m, c), __builtin_fmaf(q2.y, m, c));
+  const h2 w67 = sk_pack(__builtin_fmaf(q3.x, m, c), __builtin_fmaf(q3.y, m, c));
+  return (h8){w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
+}
+__device__ __forceinline__ h8 sk_frag(const SkQ6& r, const SkScales& sc, int s) {
+  const int h = s >> 2, t = s & 3;
+  const uint2 l = r.ql[2 * h + (t & 1)];
+  const uint2 hb = r.qh[h];
+  const uint32_t nsh = t >= 2 ? 4u : 0u;
+  const float dsc = sc.a[s], off = dsc * -32.0f;
+  uint32_t q0 = ((l.x >> nsh) & 0x0f0f0f0fu) | (((hb.x >> (2 * t)) & 0x03030303u) << 4);
+  uint32_t q1 = ((l.y >> nsh) & 0x0f0f0f0fu) | (((hb.y >> (2 * t)) & 0x03030303u) << 4);
+  asm("" : "+v"(q0));   // keep v_cvt_f32_ubyteN on the packed bytes
+  asm("" : "+v"(q1));
+  const h2 w01 = sk_pack(__builtin_fmaf((float)(q0 & 0xffu), dsc, off), __builtin_fmaf((float)((q0 >> 8) & 0xffu), dsc, off));
+  const h2 w23 = sk_pack(__builtin_fmaf((float)((q0 >> 16) & 0xffu), dsc, off), __builtin_fmaf((float)(q0 >> 24), dsc, off));
+  const h2 w45 = sk_pack(__builtin_fmaf((float)(q1 & 0xffu), dsc, off), __builtin_fmaf((float)((q1 >> 8) & 0xffu), dsc, off));
+  const h2 w67 = sk_pack(__builtin_fmaf((float)((q1 >> 16) & 0xffu), dsc, off), __builtin_fmaf((float)(q1 >> 24), dsc, off));
+  return (h8){w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
+}
+
+template <int FMT, int NT>
+__device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, float* red) {
+  typedef typename SkPart<FMT>::T Part;
+  constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rl = lane & 15, p = lane >> 4;
+  const int M = P.M, N = P.N, K = P.K;
+  const int nb = K / QK;
+  const int64_t row_bytes = (int64_t)nb * BLOCK_BYTES;
+  const int n0 = wg_local * SKINNY_ROWS;
+  const int row = n0 + rl < N ? n0 + rl : N - 1;        // ragged tail: clamp, result dropped
+  const int b0 = wave * nb / 4, b1 = (wave + 1) * nb / 4;
+  const uint8_t* wrow = P.wq + (int64_t)row * row_bytes;
+  // x rows of this lane's B operand: rl (group 0) and rl + 16 (group 1)
+  const half_t* xr[NT];
+  bool xv[NT];
+#pragma unroll
+  for (int g = 0; g < NT; ++g) {
+    xv[g] = rl + 16 * g < M;
+    xr[g] = P.x + (int64_t)(xv[g] ? rl + 16 * g : 0) * K;
+  }
+  int kofs[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kofs[s] = sk_kofs(p, s);
+
+  // x fragments of one super-block: activation row rl (+16g) if it exists,
+  // else zeros; the 8 x values of each MFMA step (16 bytes at k offset kofs)
+  auto load_x = [&](int b, uint4 (&xf)[NT][8]) {
+#pragma unroll
+    for (int g = 0; g < NT; ++g)
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        xf[g][s] = xv[g] ? *(const uint4*)(xr[g] + b * QK + kofs[s]) : make_uint4(0, 0, 0, 0);
+  };
+
+  f4 acc[NT];
+#pragma unroll
+  for (int g = 0; g < NT; ++g) acc[g] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const Part& w, const uint4 (&xf)[NT][8]) {
+    const SkScales sc = sk_scales(w, p);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const h8 a = sk_frag(w, sc, s);
+#pragma unroll
+      for (int g = 0; g < NT; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, xf[g][s]), acc[g], 0, 0, 0);
+    }
+  };
+
+  Part w0, w1;
+  uint4 x0[NT][8], x1[NT][8];
+  if (b0 < b1) {
+    sk_load(wrow + (int64_t)b0 * BLOCK_BYTES, p, w0);
+    load_x(b0, x0);
+  }
+  for (int b = b0; b < b1; b += 2) {
+    if (b + 1 < b1) {
+      sk_load(wrow + (int64_t)(b + 1) * BLOCK_BYTES, p, w1);
+      load_x(b + 1, x1);
+    }
+    compute(w0, x0);
+    if (b + 1 < b1) {
+      if (b + 2 < b1) {
+        sk_load(wrow + (int64_t)(b + 2) * BLOCK_BYTES, p, w0);
+        load_x(b + 2, x0);
+      }
+      compute(w1, x1);
+    }
+  }
+
+  // D: lane l holds activation row l%16 (+16g) and weight rows 4(l/16) .. +3
+  // of the tile.  LDS: red[wave][g][activation row][weight row].
+#pragma unroll
+  for (int g = 0; g < NT; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((wave * NT + g) * 16 + rl) * 16 + 4 * p + r] = acc[g][r];
+  __syncthreads();
+  // thread (activation row m, weight row n): consecutive threads write
+  // consecutive n; the 4 waves' sums in wave order
+#pragma unroll
+  for (int g = 0; g < NT; ++g) {
+    const int ml = threadIdx.x >> 4, nl = threadIdx.x & 15;
+    const int m = ml + 16 * g, n = n0 + nl;
+    float v = red[((0 * NT + g) * 16 + ml) * 16 + nl];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + nl];
+    if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs args) {
+  __shared__ float red[4 * NT * 16 * 16];
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < SKINNY_MAX_GROUP; ++i)
+    if (i < args.count && (int)blockIdx.x >= args.d[i].wg_begin) pi = i;
+  const SkinnyDesc& P = args.d[pi];
+  const int wg_local = (int)blockIdx.x - P.wg_begin;
+  if (P.fmt == 0)
+    skinny_tile<0, NT>(P, wg_local, red);
+  else
+    skinny_tile<1, NT>(P, wg_local, red);
+}
+
+// One workgroup per 16 weight rows; problems with the most bytes per
+// workgroup (the deepest K) are dispatched first so they do not trail.
+hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
+  for (int base = 0; base < count; base += SKINNY_MAX_GROUP) {
+    const int n = count - base < SKINNY_MAX_GROUP ? count - base : SKINNY_MAX_GROUP;
+    int order[SKINNY_MAX_GROUP];
+    int mmax = 0;
+    for (int i = 0; i < n; ++i) {
+      order[i] = base + i;
+      mmax = probs[base + i].M > mmax ? probs[base + i].M : mmax;
+    }
+    auto wg_bytes = [&](int i) { return (int64_t)(probs[i].K / QK) * (probs[i].fmt == 0 ? Q4K_BYTES : Q6K_BYTES); };
+    for (int i = 1; i < n; ++i)
+      for (int j = i; j > 0 && wg_bytes(order[j]) > wg_bytes(order[j - 1]); --j) std::swap(order[j], order[j - 1]);
+    SkinnyArgs a{};
+    int wgs = 0;
+    for (int i = 0; i < n; ++i) {
+      const GemmProblem& p = probs[order[i]];
+      SkinnyDesc& d = a.d[i];
+      d.x = (const half_t*)p.x;
+      d.wq = p.wq;
+      d.y = (float*)p.out;
+      d.fmt = p.fmt;
+      d.M = p.M;
+      d.N = p.N;
+      d.K = p.K;
+      d.wg_begin = wgs;
+      wgs += (p.N + SKINNY_ROWS - 1) / SKINNY_ROWS;
+    }
+    a.count = n;
+    if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
+    hipLaunchKernelGGL(skinny_kernel<1>, dim3(wgs), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dmq

@@ -26,9 +26,15 @@
  *  - Products are y = x * W^T, i.e. y[m][n] = sum_k x[m][k] * W[n][k], [M, N]
  *    row-major fp32, accumulated in fp32.
  *  - Every pointer except the stream is DEVICE memory owned by the caller
- *    (for example a torch tensor's data_ptr()); the library allocates nothing
- *    on these calls and keeps no state besides cached device properties.
- *    Passing host memory is undefined behaviour.
+ *    (for example a torch tensor's data_ptr()).  Passing host memory is
+ *    undefined behaviour.  The library keeps cached device properties,
+ *    cached launch plans and, for GEMMs whose plan splits the reduction (see
+ *    dmq_gemm_q4k), one workspace per (device, stream): allocated with
+ *    hipMalloc by the first such call on that stream, grown when a later
+ *    call needs more (after synchronising that stream), kept until the
+ *    process ends.  Nothing else is allocated.  A call made while its stream
+ *    is being captured into a HIP graph must not need a new or larger
+ *    workspace: make the same call once on that stream before capturing.
  *  - stream is a hipStream_t passed as void*; NULL means the null stream.  The
  *    call only enqueues work: results are ready once the stream is
  *    synchronised.  The device is the caller's current HIP device.
@@ -86,9 +92,13 @@ int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* 
  * y = x * W^T with W in Q4_K, dequantised inside the kernel (no fp16 weight
  * matrix is ever written to memory).
  *   x_f16 : [M, K] fp16;  wq : N rows of K/256 Q4_K blocks;  y : [M, N] fp32.
- * M = 1 runs the decode matrix-vector kernel; small M a skinny MFMA kernel;
- * large M the tiled MFMA prefill kernel.  Per output, |y - y_exact| stays
- * within 1e-3 * sum_k |x[m][k] * w[n][k]| + 1e-5 (w the fp16-rounded weight).
+ * M = 1 runs the decode matrix-vector kernel; 2 <= M <= 16 a small-M MFMA
+ * kernel; larger M the tiled MFMA prefill kernel.  When a problem has too
+ * few output tiles to fill the GPU, the tiled kernel splits the K blocks
+ * into pieces whose fp32 partial sums a second kernel adds in piece order
+ * (workspace: see above).  Every path gives the same bits on every run.
+ * Per output, |y - y_exact| stays within 1e-3 * sum_k |x[m][k] * w[n][k]|
+ * + 1e-5 (w the fp16-rounded weight).
  */
 int dmq_gemm_q4k(const void* x_f16, const void* wq, float* y,
                  int64_t M, int64_t N, int64_t K, void* stream);
@@ -133,8 +143,10 @@ typedef struct {
  * of one launch per GEMM, so that small projections (e.g. the K and V
  * projections of one layer) share the GPU with the large ones.  descs is a
  * HOST array; it is read before the call returns.  All problems must use the
- * same kernel kind: all M = 1 (decode), or all M > 1.  Results are identical
- * to calling dmq_gemm_q4k / dmq_gemm_q6k for each entry.
+ * same kernel kind: all M = 1 (decode), or all M > 1.  Results meet the same
+ * bound as dmq_gemm_q4k / dmq_gemm_q6k per entry; they are the same bits as
+ * those calls except where the group's launch plan splits a problem's K
+ * differently (tiled kernel only), which changes the fp32 summation order.
  */
 int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream);
 

@@ -299,7 +299,7 @@ def test_gemm_group_matches_single_calls(dmq):
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
-@pytest.mark.parametrize("M,N,K", [(5, 37, 8192), (33, 250, 4864), (16, 3072, 768), (1024, 3072, 8192)])
+@pytest.mark.parametrize("M,N,K", [(40, 37, 8192), (33, 250, 4864), (48, 3072, 768), (1024, 3072, 8192)])
 def test_gemm_split_k(dmq, fmt, M, N, K):
     """Too few output tiles to fill the GPU: the launch splits the K blocks
     into pieces whose fp32 partial sums a second kernel adds in piece order
@@ -319,6 +319,46 @@ def test_gemm_split_k(dmq, fmt, M, N, K):
     rows = np.arange(M) if M <= 64 else synthetic.row_sample(M, 24, seed=K)
     ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
     assert_within(y1.cpu().numpy()[rows], ref, s, f"split-K {fmt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,N,K", [(2, 16, 256), (5, 37, 4864), (9, 33, 512), (16, 3072, 3072), (16, 48, 8192),
+                                   (17, 100, 1280), (32, 257, 768)])
+def test_gemm_small_m_every_output(dmq, fmt, M, N, K):
+    """M <= 16 runs the small-M kernel (16 weight rows per workgroup, K split
+    over its 4 waves, the rows' products on 16x16x32 MFMAs): every output,
+    ragged N, K blocks not a multiple of 4 (uneven wave slices), and the
+    same bits on a second call.  M = 17 and 32, just past it, run the tiled
+    kernel."""
+    x = synthetic.activations(M, K, seed=M * 11 + N)
+    wq = synthetic.weight_blocks(fmt, N, K, seed=N * 13 + K + M)
+    xd, wd = dev(x), dev(wq.reshape(-1))
+    fn = dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k
+    y1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    fn(xd, wd, y1, M, N, K)
+    fn(xd, wd, y2, M, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), "small-M result is not reproducible"
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y1.cpu().numpy(), ref, s, f"small-M {fmt} {M}x{N}x{K}")
+
+
+def test_gemm_small_m_layer_group(dmq):
+    """The 7 projections of one layer at M = 16 in one grouped launch (mixed
+    Q4_K / Q6_K, K = 3072 and 8192) against the oracle on every output."""
+    M = 16
+    items = _layer_group(dmq, 0, 3, M)
+    probs, host = [], []
+    for name, fmt, N, K, wq, x in items:
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        probs.append((fmt, dev(x), dev(wq.reshape(-1)), y, M, N, K))
+        host.append((name, fmt, N, K, wq, x, y))
+    dmq.dmq_gemm_group(probs)
+    torch.cuda.synchronize()
+    for name, fmt, N, K, wq, x, y in host:
+        ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+        assert_within(y.cpu().numpy(), ref, s, f"small-M group {name} M={M}")
 
 
 @pytest.mark.parametrize("M", [2048, 4096])
