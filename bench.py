@@ -156,10 +156,13 @@ def sweep(torch, dmq):
         dmq.dmq_gemm_q4k(x, ws[it[0] % 64], y, M, N, K)
         it[0] += 1
     ms = _timed(torch, c0, reps=64)
+    # the same 64 launches replayed from a HIP graph: no host launch gaps
+    gms = time_graph(torch, lambda w: dmq.dmq_gemm_q4k(x, w, y, M, N, K), ws, 4)
     wbytes = N * (K // 256) * 144
     print(json.dumps({"sweep": "config0 Q4_K GEMM M=16 N=K=3072, 64 rotating weight copies",
                       "us": round(ms * 1e3, 2), "TFLOP/s": round(2 * M * N * K / ms / 1e9, 2),
-                      "weight_GB/s": round(wbytes / ms / 1e6, 1)}), flush=True)
+                      "weight_GB/s": round(wbytes / ms / 1e6, 1),
+                      "graph_us": round(gms * 1e3, 2), "graph_weight_GB/s": round(wbytes / gms / 1e6, 1)}), flush=True)
     del ws
 
     # config 3: fused FFN, M = 1024, D = 3072, F = 8192
