@@ -246,6 +246,18 @@ __device__ __forceinline__ void raw_load_q6(rsrc_t wr, uint32_t roff, int bi, in
   load_win(wr, base + 64u * (uint32_t)h + 32u, r.lb);
   load_win(wr, base + 128u + 32u * (uint32_t)h, r.hb);
 }
+// One of the six loads of raw_load_q6 (part 0..5: the 16-byte and 4-byte
+// pieces of the la, lb and hb windows), so that they can be spread out.
+__device__ __forceinline__ void raw_load_q6_part(rsrc_t wr, uint32_t roff, int bi, int h, int g, int part, RawQ6& r) {
+  const uint32_t lo = roff + (uint32_t)(bi * Q6K_BYTES) + 16u * (uint32_t)g;
+  r.sh = lo & 3u;
+  const uint32_t base = lo - r.sh;
+  const uint32_t off = part < 2 ? base + 64u * (uint32_t)h : part < 4 ? base + 64u * (uint32_t)h + 32u
+                                                                     : base + 128u + 32u * (uint32_t)h;
+  Win& w = part < 2 ? r.la : part < 4 ? r.lb : r.hb;
+  if (part & 1) w.w4 = buf_load4(wr, off + 16, 0);
+  else w.w = buf_load16(wr, off, 0);
+}
 __device__ __forceinline__ Q6Fields q6_fields(const RawQ6& r) {
   return Q6Fields{realign(r.la, r.sh), realign(r.lb, r.sh), realign(r.hb, r.sh)};
 }
@@ -290,7 +302,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 //    compiler's wait-count tracking knows that reading one buffer does not
 //    depend on the direct loads into another);
 //  * raw quant bytes go to registers, issued three chunks ahead (Q4_K, four
-//    register sets) or half a block ahead (Q6_K, two sets);
+//    register sets) or about half a block ahead (Q6_K, two sets);
+//  * a chunk's loads are spread over its first three K steps, between the
+//    MFMAs: issued as one burst they fill the texture-address FIFO, and the
+//    wave's MFMA issue stalls behind them;
 //  * every chunk has one barrier, before its last K step, after which the
 //    next chunk's x buffer and (at a block boundary) the next scale table are
 //    visible; the last step's MFMAs then overlap the next chunk's first
@@ -313,7 +328,6 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   constexpr int XQ = JB;                             // x load instructions per wave per chunk (BM/8 row groups / 4 waves)
   constexpr int NRAW = FMT == 0 ? IB : 6 * IB;       // VMEM instructions of one raw load round
   constexpr int NSC = FMT == 0 ? 16 : 8;             // scale floats per row a lane keeps
-  uint8_t* const xb[4] = {x0, x1, x2, x3};
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, g = lane >> 5;
@@ -353,6 +367,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
     const int r = 8 * (4 * i + wave) + (lane >> 3);
     xoff[i] = (uint32_t)r * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
+  uint8_t* const xb[4] = {x0, x1, x2, x3};
   auto load_x = [&](int ck, uint8_t* xd) {
 #pragma unroll
     for (int i = 0; i < XQ; ++i)
@@ -422,13 +437,46 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       for (int c = 0; c < IB; ++c)
         acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], bm[jb], acc[jb][c], 0, 0, 0);
   };
-  auto interleave = [&]() {
-    // spread the VALU work of the next fragment between this step's MFMAs
+  // spread the VALU work of the next fragment, and nv VMEM loads, between
+  // this step's MFMAs
+  auto interleave = [&](int nv) {
 #pragma unroll
     for (int i = 0; i < JB * IB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int v = (i + 1) * nv / (JB * IB) - i * nv / (JB * IB);
+#pragma unroll
+      for (int k = 0; k < v; ++k) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
+  };
+  // The VMEM loads chunk j of a block issues for later chunks, spread over its
+  // K steps 0..2 (a burst of them at the chunk start would fill the
+  // texture-address FIFO and stall the wave's MFMA issue behind it):
+  //  Q4_K: x of chunk ck+3 (XQ loads), then its raw quant bytes (IB loads);
+  //  Q6_K: at j = 0 the raw bytes of half 1 of this block, at j = 2 those
+  //  of half 0 of the next block (6*IB loads, issued first), then x of
+  //  chunk ck+3.  Returns the number of loads issued in step s.
+  auto issue_loads = [&](int j, int s, int ck3, int b, int bnext) -> int {
+    constexpr int NR6 = 6 * IB;
+    const int nr = FMT == 0 ? 0 : ((j & 1) ? 0 : NR6);    // raw loads before the x loads
+    const int total = nr + XQ + (FMT == 0 ? IB : 0);
+    const int lo = s * total / 3, hi = (s + 1) * total / 3;
+#pragma unroll
+    for (int t = lo; t < hi; ++t) {
+      if (t < nr) {
+        if constexpr (FMT == 1) {
+          if (j == 0) raw_load_q6_part(wr[t / 6], roff, b, 1, g, t % 6, rs[1][t / 6]);
+          else raw_load_q6_part(wr[t / 6], roff, bnext, 0, g, t % 6, rs[0][t / 6]);
+        }
+      } else if (t < nr + XQ) {
+        const int i = t - nr;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xb[(j + 3) & 3] + (4 * i + wave) * 1024),
+                                                 16, xoff[i], (uint32_t)(128 * ck3), 0, 0);
+      } else if constexpr (FMT == 0) {
+        raw_load_q4(wr[t - nr - XQ], roff, ck3, rs[(j + 3) & 3][t - nr - XQ]);
+      }
+    }
+    return hi - lo;
   };
 
   // ---- prologue: block 0's table, x and raw bytes of the first chunks
@@ -471,13 +519,8 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       const bool pf1 = j < 3 || more;     // chunk ck + 1 exists
       const int cur = FMT == 0 ? j : (j >> 1);                    // raw set of chunk ck
       const int nxt = FMT == 0 ? ((j + 1) & 3) : (((j + 1) & 3) >> 1);
-      // x (and Q4_K raw bytes) of chunk ck+3, into the buffers chunk ck-1 used
+      // x (and raw bytes) of chunk ck+3 go into the buffers chunk ck-1 used
       const int ck3 = ck + 3 < 4 * nb ? ck + 3 : 4 * nb - 1;
-      load_x(ck3, xb[(j + 3) & 3]);
-      if constexpr (FMT == 0) {
-#pragma unroll
-        for (int c = 0; c < IB; ++c) raw_load_q4(wr[c], roff, ck3, rs[(j + 3) & 3][c]);
-      }
 
       // K steps 0..2
 #pragma unroll
@@ -490,8 +533,9 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
         if (j == 3 && s == 0 && more && tab_thread)
           tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + (int64_t)(b + 1) * BLOCK_BYTES + 192) & 3));
+        const int nv = issue_loads(j, s, ck3, b, bnext);
         mfma_step(af, bf);
-        interleave();
+        interleave(nv);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < IB; ++c) af[c] = afn[c];
@@ -522,7 +566,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
       }
       mfma_step(af, bf);
-      interleave();
+      interleave(0);
       __builtin_amdgcn_sched_barrier(0);
       if (pf1) {
 #pragma unroll
@@ -533,15 +577,6 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         }
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
-      }
-      // Q6_K raw bytes ahead: the next block's half j/2 once this block's
-      // half is used up
-      if constexpr (FMT == 1) {
-        if (j & 1) {
-#pragma unroll
-          for (int c = 0; c < IB; ++c) raw_load_q6(wr[c], roff, bnext, j >> 1, g, rs[j >> 1][c]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
