@@ -146,18 +146,16 @@ __device__ __forceinline__ h8 q6k_frag(uint32_t l0, uint32_t l1, uint32_t h0, ui
 // aligned, which the hardware's unaligned global loads handle).
 typedef uint32_t u32_a2 __attribute__((aligned(2)));
 
+typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+
 template <int FMT>
 __device__ __forceinline__ void hdr_load(const uint8_t* blk, u32x4& hdr, uint32_t& hdr4) {
   if constexpr (FMT == 0) {
     hdr = *(const u32x4*)blk;
   } else {
-    // Q6_K: the aligned dwords from byte 192 (or 190) and the dword at 206,
-    // all inside the block.  Nothing here combines the values: that waits
-    // until the decode, so the loads' latency stays hidden.
-    const uint8_t* p = blk + 192;
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
-    const uint32_t* sp = (const uint32_t*)(p - sh);
-    hdr = (u32x4){sp[0], sp[1], sp[2], sp[3]};
+    // Q6_K: the 16 scale bytes (192..207) and the dword at 206 (d in its
+    // high half), both 2-byte aligned, both inside the block
+    hdr = *(const u32x4_a2*)(blk + 192);
     hdr4 = *(const u32_a2*)(blk + 206);
   }
 }
@@ -169,7 +167,7 @@ __device__ __forceinline__ void hdr_load(const uint8_t* blk, u32x4& hdr, uint32_
 //        in floats 0..7), then odd s (floats 8..15): a lane only needs the
 //        sub-blocks of one parity.
 template <int FMT>
-__device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t hdr4, uint32_t sh) {
+__device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t hdr4) {
   float v[16];
   if constexpr (FMT == 0) {
     Q4kScales s = unpack_q4k_scales(hdr.y, hdr.z, hdr.w);
@@ -181,10 +179,7 @@ __device__ __forceinline__ void tab_store(float* t, const u32x4& hdr, uint32_t h
       v[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
     }
   } else {
-    // sh = (block address + 192) mod 4: the 20 bytes from byte 192 - sh are
-    // hdr and, for sh = 2, hdr4 (the dword at 206); d is hdr4's high half
-    uint32_t w[4] = {__builtin_amdgcn_alignbyte(hdr.y, hdr.x, sh), __builtin_amdgcn_alignbyte(hdr.z, hdr.y, sh),
-                     __builtin_amdgcn_alignbyte(hdr.w, hdr.z, sh), __builtin_amdgcn_alignbyte(hdr4, hdr.w, sh)};
+    const uint32_t w[4] = {hdr.x, hdr.y, hdr.z, hdr.w};
     float d = half_bits_to_float(hdr4 >> 16);
 #pragma unroll
     for (int s = 0; s < 16; ++s)
@@ -213,54 +208,33 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t 
 //  Q4_K, per 64-wide chunk: quant bytes 32p + 16g .. +16 (p = chunk in block).
 //  Q6_K, per 128-weight half h (two chunks): low-nibble bytes 64h + 16g and
 //  64h + 32 + 16g, high-bit bytes 128 + 32h + 16g.  Blocks are 210 bytes, so
-//  a field may start 2 mod 4: it is loaded as the 5 enclosing aligned dwords
-//  (at most 2 bytes before and 4 after the field; the last byte read is at
-//  most 176 + 20 = 196 < 210) and shifted into place only when first used,
-//  so that the load's latency is not exposed where it is issued.
+//  a field may start 2 mod 4; the 16-byte buffer loads take such 2-byte
+//  aligned offsets as they are (the memory path splits them), which costs
+//  less than loading the enclosing aligned dwords and shifting.
 struct RawQ4 { u32x4 q; };
-struct Win { u32x4 w; uint32_t w4; };                  // 20-byte aligned window
-struct RawQ6 { Win la, lb, hb; uint32_t sh; };         // sh: field start mod 4
-struct Q6Fields { u32x4 la, lb, hb; };                 // realigned 16-byte fields
+struct RawQ6 { u32x4 la, lb, hb; };
+typedef RawQ6 Q6Fields;
 template <int FMT> struct RawOf { typedef RawQ4 T; };
 template <> struct RawOf<1> { typedef RawQ6 T; };
-
-__device__ __forceinline__ void load_win(rsrc_t r, uint32_t aligned_off, Win& w) {
-  w.w = buf_load16(r, aligned_off, 0);
-  w.w4 = buf_load4(r, aligned_off + 16, 0);
-}
-__device__ __forceinline__ u32x4 realign(const Win& w, uint32_t sh) {
-  return (u32x4){__builtin_amdgcn_alignbyte(w.w.y, w.w.x, sh), __builtin_amdgcn_alignbyte(w.w.z, w.w.y, sh),
-                 __builtin_amdgcn_alignbyte(w.w.w, w.w.z, sh), __builtin_amdgcn_alignbyte(w.w4, w.w.w, sh)};
-}
 
 // Q4_K raw bytes of chunk ck (wr: this i-block's 32 rows; roff: li * row_bytes + 16 g)
 __device__ __forceinline__ void raw_load_q4(rsrc_t wr, uint32_t roff, int ck, RawQ4& r) {
   r.q = buf_load16(wr, roff, (uint32_t)((ck >> 2) * Q4K_BYTES + 16 + 32 * (ck & 3)));
 }
-// Q6_K raw bytes of half h of block bi (roff: li * row_bytes)
-__device__ __forceinline__ void raw_load_q6(rsrc_t wr, uint32_t roff, int bi, int h, int g, RawQ6& r) {
-  const uint32_t lo = roff + (uint32_t)(bi * Q6K_BYTES) + 16u * (uint32_t)g;   // lane's field offset, before h
-  r.sh = lo & 3u;                                      // same for the three fields (offsets differ by 32/64)
-  const uint32_t base = lo - r.sh;
-  load_win(wr, base + 64u * (uint32_t)h, r.la);
-  load_win(wr, base + 64u * (uint32_t)h + 32u, r.lb);
-  load_win(wr, base + 128u + 32u * (uint32_t)h, r.hb);
-}
-// One of the six loads of raw_load_q6 (part 0..5: the 16-byte and 4-byte
-// pieces of the la, lb and hb windows), so that they can be spread out.
+// One of the three loads of the Q6_K raw bytes of half h of block bi (part
+// 0: la, 1: lb, 2: hb; roff: li * row_bytes).
 __device__ __forceinline__ void raw_load_q6_part(rsrc_t wr, uint32_t roff, int bi, int h, int g, int part, RawQ6& r) {
-  const uint32_t lo = roff + (uint32_t)(bi * Q6K_BYTES) + 16u * (uint32_t)g;
-  r.sh = lo & 3u;
-  const uint32_t base = lo - r.sh;
-  const uint32_t off = part < 2 ? base + 64u * (uint32_t)h : part < 4 ? base + 64u * (uint32_t)h + 32u
-                                                                     : base + 128u + 32u * (uint32_t)h;
-  Win& w = part < 2 ? r.la : part < 4 ? r.lb : r.hb;
-  if (part & 1) w.w4 = buf_load4(wr, off + 16, 0);
-  else w.w = buf_load16(wr, off, 0);
+  const uint32_t lo = roff + (uint32_t)(bi * Q6K_BYTES) + 16u * (uint32_t)g;   // lane's field offset, before h
+  const uint32_t off = part == 0 ? lo + 64u * (uint32_t)h : part == 1 ? lo + 64u * (uint32_t)h + 32u
+                                                                      : lo + 128u + 32u * (uint32_t)h;
+  u32x4& w = part == 0 ? r.la : part == 1 ? r.lb : r.hb;
+  w = buf_load16(wr, off, 0);
 }
-__device__ __forceinline__ Q6Fields q6_fields(const RawQ6& r) {
-  return Q6Fields{realign(r.la, r.sh), realign(r.lb, r.sh), realign(r.hb, r.sh)};
+__device__ __forceinline__ void raw_load_q6(rsrc_t wr, uint32_t roff, int bi, int h, int g, RawQ6& r) {
+#pragma unroll
+  for (int part = 0; part < 3; ++part) raw_load_q6_part(wr, roff, bi, h, g, part, r);
 }
+__device__ __forceinline__ const Q6Fields& q6_fields(const RawQ6& r) { return r; }
 
 // A fragment of K step s (0..3) of chunk cc (0..3 within the block).
 // sv: Q4_K (d*sc*2^9 and -dmin*m of the chunk's even and odd sub-block);
@@ -326,7 +300,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   typedef typename RawOf<FMT>::T Raw;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
   constexpr int XQ = JB;                             // x load instructions per wave per chunk (BM/8 row groups / 4 waves)
-  constexpr int NRAW = FMT == 0 ? IB : 6 * IB;       // VMEM instructions of one raw load round
+  constexpr int NRAW = FMT == 0 ? IB : 3 * IB;       // VMEM instructions of one raw load round
   constexpr int NSC = FMT == 0 ? 16 : 8;             // scale floats per row a lane keeps
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -437,16 +411,17 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       for (int c = 0; c < IB; ++c)
         acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], bm[jb], acc[jb][c], 0, 0, 0);
   };
-  // spread the VALU work of the next fragment, and nv VMEM loads, between
-  // this step's MFMAs
-  auto interleave = [&](int nv) {
+  // spread the VALU work of the next fragment (va instructions per MFMA),
+  // and nv VMEM loads, between this step's MFMAs
+  auto interleave = [&](int nv, int va) {
 #pragma unroll
     for (int i = 0; i < JB * IB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       const int v = (i + 1) * nv / (JB * IB) - i * nv / (JB * IB);
 #pragma unroll
       for (int k = 0; k < v; ++k) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+#pragma unroll
+      for (int k = 0; k < va; ++k) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
   };
   // The VMEM loads chunk j of a block issues for later chunks, spread over its
@@ -454,10 +429,10 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   // texture-address FIFO and stall the wave's MFMA issue behind it):
   //  Q4_K: x of chunk ck+3 (XQ loads), then its raw quant bytes (IB loads);
   //  Q6_K: at j = 0 the raw bytes of half 1 of this block, at j = 2 those
-  //  of half 0 of the next block (6*IB loads, issued first), then x of
+  //  of half 0 of the next block (3*IB loads, issued first), then x of
   //  chunk ck+3.  Returns the number of loads issued in step s.
   auto issue_loads = [&](int j, int s, int ck3, int b, int bnext) -> int {
-    constexpr int NR6 = 6 * IB;
+    constexpr int NR6 = 3 * IB;
     const int nr = FMT == 0 ? 0 : ((j & 1) ? 0 : NR6);    // raw loads before the x loads
     const int total = nr + XQ + (FMT == 0 ? IB : 0);
     const int lo = s * total / 3, hi = (s + 1) * total / 3;
@@ -465,8 +440,8 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
     for (int t = lo; t < hi; ++t) {
       if (t < nr) {
         if constexpr (FMT == 1) {
-          if (j == 0) raw_load_q6_part(wr[t / 6], roff, b, 1, g, t % 6, rs[1][t / 6]);
-          else raw_load_q6_part(wr[t / 6], roff, bnext, 0, g, t % 6, rs[0][t / 6]);
+          if (j == 0) raw_load_q6_part(wr[t / 3], roff, b, 1, g, t % 3, rs[1][t / 3]);
+          else raw_load_q6_part(wr[t / 3], roff, bnext, 0, g, t % 3, rs[0][t / 3]);
         }
       } else if (t < nr + XQ) {
         const int i = t - nr;
@@ -494,7 +469,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   load_x(0, x0);
   load_x(1, x1);
   load_x(2, x2);
-  if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + 192) & 3));
+  if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4);
   wait_vm_barrier<0>();
   read_scales();
   chunk_scales(0, sv);
@@ -532,10 +507,12 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
 #pragma unroll
         for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
         if (j == 3 && s == 0 && more && tab_thread)
-          tab_store<FMT>(my_tab, hdr, hdr4, (uint32_t)((uintptr_t)(trow + (int64_t)(b + 1) * BLOCK_BYTES + 192) & 3));
+          tab_store<FMT>(my_tab, hdr, hdr4);
         const int nv = issue_loads(j, s, ck3, b, bnext);
         mfma_step(af, bf);
-        interleave(nv);
+        // the step that also decodes the next block's scale table has more
+        // VALU work to place
+        interleave(nv, j == 3 && s == 0 ? 6 : 3);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < IB; ++c) af[c] = afn[c];
@@ -566,7 +543,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
       }
       mfma_step(af, bf);
-      interleave(0);
+      interleave(0, 3);
       __builtin_amdgcn_sched_barrier(0);
       if (pf1) {
 #pragma unroll
@@ -742,15 +719,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
 // the last problem's n-tile columns to run at the short height, by
 // simulating that schedule with per-tile times measured on gfx950.
 
-// Time of one tile (arbitrary units, measured on MI355X with the launch
-// full of tiles of one shape): fixed part + part per 256-wide K block.
-// Q6_K tiles are scaled by 1.3 and Q4_K ones by 1.15, what they measured
-// inside a mixed Q4_K/Q6_K launch.
+// Time of one tile in shader cycles, measured on MI355X (timestamps of every
+// workgroup in launches full of tiles): a fixed part (prologue, first block,
+// epilogue) plus a part per 256-wide K block, per format and tile height.
 static double tile_cost(int fmt, int jb, int nb) {
-  static const double a4[4] = {313, 393, 874, 1270}, b4[4] = {275, 324, 466, 808};
-  static const double a6[4] = {278, 492, 781, 802}, b6[4] = {488, 526, 690, 1069};
+  static const double a4[4] = {5000, 7700, 14300, 27600}, b4[4] = {5700, 6500, 8430, 12800};
+  static const double a6[4] = {8000, 9000, 17300, 30600}, b6[4] = {9400, 11100, 14000, 17550};
   const int i = jb == 1 ? 0 : jb == 2 ? 1 : jb == 4 ? 2 : 3;
-  return fmt == 0 ? 1.15 * (a4[i] + b4[i] * nb) : 1.3 * (a6[i] + b6[i] * nb);
+  return fmt == 0 ? a4[i] + b4[i] * nb : a6[i] + b6[i] * nb;
 }
 
 struct Seg {
@@ -767,8 +743,8 @@ static int n_tiles(const GemmProblem& p) {
   return p.swiglu ? (p.N / 2 + 127) / 128 : (p.N + 255) / 256;   // SwiGLU: 128 gate + 128 up rows per tile
 }
 
-// Time of the split-K combine (same units as tile_cost): a launch plus
-// reading ks partial slices and writing y at about 4 TB/s.
+// Time of the split-K combine (shader cycles, as tile_cost): a launch plus
+// reading ks partial slices and writing y at about 5.5 TB/s.
 static double reduce_cost(const Plan& pl, const GemmProblem* probs) {
   double bytes = 0.0;
   bool any = false;
@@ -778,7 +754,7 @@ static double reduce_cost(const Plan& pl, const GemmProblem* probs) {
     any = true;
     bytes += 4.0 * (sg.ks + 1) * probs[sg.prob].M * (double)probs[sg.prob].N;
   }
-  return any ? 300.0 + bytes / 40000.0 : 0.0;
+  return any ? 4000.0 + bytes / 2900.0 : 0.0;
 }
 
 // Greedy dispatch of the segments' tiles, in order, over ncu CUs (plus the
