@@ -293,7 +293,14 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // x rows are stored with their 16-byte chunks XOR-swizzled by (row >> 1) & 7:
 // a ds_read_b128 of one column by 16 consecutive rows then covers all 64
 // banks once (two rows share one 256-byte bank line).
-template <int FMT, int JB, int IB, bool SWIGLU>
+// Epilogue staging (fp32 y through LDS): each wave transposes its 32 x 64
+// block of one j-block in its own x buffer, rows padded to 68 floats so that
+// both the fragment writes and the row reads are free of bank conflicts.
+constexpr int EPI_STRIDE = 68;
+constexpr int EPI_BYTES = 32 * EPI_STRIDE * 4;
+
+// XCAP: bytes of each x buffer (the kernel's tallest tile).
+template <int FMT, int JB, int IB, bool SWIGLU, int XCAP>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, int kb0, int nbk, void* out,
                                           uint8_t* x0, uint8_t* x1, uint8_t* x2, uint8_t* x3, float* tab) {
   typedef TileCfg<JB, IB> C;
@@ -561,36 +568,77 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: the lane holds rows 8q + 4g + e (q, e = 0..3) of each i-block ----
+  if constexpr (!SWIGLU && IB == 2 && XCAP >= EPI_BYTES) {
+    // Through LDS, so that every global store writes whole 128-byte lines:
+    // a store instruction covers 4 rows x the wave's 64 columns (256 bytes
+    // each), where writing the accumulator fragments directly would touch
+    // 32 rows x 32 bytes.  Each wave uses its own x buffer; the barrier
+    // waits until every wave has read its last B fragments.
+    __syncthreads();
+    float* const st = (float*)(wave == 0 ? x0 : wave == 1 ? x1 : wave == 2 ? x2 : x3);
+    const int rr = lane >> 4, cc = 4 * (lane & 15);
+    const int n = n0 + 64 * wave + cc;
+    const bool vec = (N & 3) == 0 && n + 3 < N;
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) {
-    const int m = m0 + 32 * jb + li;
-    if (m >= M) continue;
-    if (SWIGLU) {
-      half_t* h = (half_t*)out + (int64_t)m * F;
-      const f16x& gv = acc[jb][0];
-      const f16x& uv = acc[jb][1];
+    for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = hb + 32 * wave + 8 * q + 4 * g;
-        h2 h01 = {(half_t)(silu_fast(gv[4 * q]) * uv[4 * q]), (half_t)(silu_fast(gv[4 * q + 1]) * uv[4 * q + 1])};
-        h2 h23 = {(half_t)(silu_fast(gv[4 * q + 2]) * uv[4 * q + 2]),
-                  (half_t)(silu_fast(gv[4 * q + 3]) * uv[4 * q + 3])};
-        *(uint2*)(h + col) = make_uint2(as_u32(h01), as_u32(h23));
-      }
-    } else {
-      float* yrow = (float*)out + (int64_t)m * N;
-#pragma unroll
-      for (int c = 0; c < IB; ++c) {
-        const f16x& v = acc[jb][c];
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + 32 * IB * wave + 32 * c + 8 * q + 4 * g;
-          if ((N & 3) == 0 && n + 3 < N) {
-            *(float4*)(yrow + n) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-          } else {
+          const f16x& v = acc[jb][c];
+          *(float4*)(st + li * EPI_STRIDE + 32 * c + 8 * q + 4 * g) =
+              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) yrow[n + e] = v[4 * q + e];
+      for (int i = 0; i < 8; ++i) {
+        const int r = rr + 4 * i;
+        const int m = m0 + 32 * jb + r;
+        const float4 v = *(const float4*)(st + r * EPI_STRIDE + cc);
+        if (m < M) {
+          float* yrow = (float*)out + (int64_t)m * N;
+          if (vec) {
+            *(float4*)(yrow + n) = v;
+          } else {
+            const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (n + k < N) yrow[n + k] = e[k];
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int m = m0 + 32 * jb + li;
+      if (m >= M) continue;
+      if (SWIGLU) {
+        half_t* h = (half_t*)out + (int64_t)m * F;
+        const f16x& gv = acc[jb][0];
+        const f16x& uv = acc[jb][1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = hb + 32 * wave + 8 * q + 4 * g;
+          h2 h01 = {(half_t)(silu_fast(gv[4 * q]) * uv[4 * q]), (half_t)(silu_fast(gv[4 * q + 1]) * uv[4 * q + 1])};
+          h2 h23 = {(half_t)(silu_fast(gv[4 * q + 2]) * uv[4 * q + 2]),
+                    (half_t)(silu_fast(gv[4 * q + 3]) * uv[4 * q + 3])};
+          *(uint2*)(h + col) = make_uint2(as_u32(h01), as_u32(h23));
+        }
+      } else {
+        float* yrow = (float*)out + (int64_t)m * N;
+#pragma unroll
+        for (int c = 0; c < IB; ++c) {
+          const f16x& v = acc[jb][c];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + 32 * IB * wave + 32 * c + 8 * q + 4 * g;
+            if ((N & 3) == 0 && n + 3 < N) {
+              *(float4*)(yrow + n) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) yrow[n + e] = v[4 * q + e];
+            }
           }
         }
       }
@@ -629,12 +677,12 @@ __device__ __forceinline__ void run_tile(const GemmDesc& P, int m_tile, int n_ti
   const int nbk = left < P.kbs ? left : P.kbs;
   void* out = SWIGLU ? P.out : (void*)((float*)P.out + piece * P.out_stride);
   if constexpr (JBA == JBB) {
-    gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+    gemm_tile<FMT, JBA, 2, SWIGLU, TileCfg<JBA, 2>::XBUF>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
   } else {
     if (P.alt)
-      gemm_tile<FMT, JBB, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+      gemm_tile<FMT, JBB, 2, SWIGLU, TileCfg<JBA, 2>::XBUF>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
     else
-      gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+      gemm_tile<FMT, JBA, 2, SWIGLU, TileCfg<JBA, 2>::XBUF>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
   }
 }
 
