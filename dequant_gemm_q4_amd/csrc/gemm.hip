@@ -867,7 +867,7 @@ static Plan make_plan(const GemmProblem* probs, int count, int ncu) {
     fmt_mask |= 1 << probs[i].fmt;
   }
   const bool swiglu = probs[0].swiglu != 0;
-  static const int pairs[4][2] = {{8, 4}, {4, 2}, {2, 1}, {1, 1}};
+  static const int pairs[5][2] = {{8, 4}, {8, 2}, {4, 2}, {2, 1}, {1, 1}};
   static const int splits[8] = {1, 2, 3, 4, 6, 8, 12, 16};
   std::vector<double> heap;
 
@@ -1083,7 +1083,7 @@ static hipError_t launch_chunk(const GemmProblem* probs, int count, hipStream_t 
   a.count = pl.nseg;
   hipError_t e;
   switch (pl.jba) {
-    case 8: e = launch_pair<8, 4>(pl, tiles, a, s); break;
+    case 8: e = pl.jbb == 2 ? launch_pair<8, 2>(pl, tiles, a, s) : launch_pair<8, 4>(pl, tiles, a, s); break;
     case 4: e = launch_pair<4, 2>(pl, tiles, a, s); break;
     case 2: e = launch_pair<2, 1>(pl, tiles, a, s); break;
     default: e = launch_pair<1, 1>(pl, tiles, a, s); break;
