@@ -38,13 +38,14 @@ ROTATE_LAYERS = 5              # 5 x 63.1 MB of weights > 256 MB Infinity Cache
 DECODE_ROTATE = 8              # decode: 8 x 63.1 MB
 
 
-# HBM bytes per launch of the grouped prefill kernel, from rocprofv3 FETCH_SIZE
-# and WRITE_SIZE passes scaled by the same counters' reading for a plain copy
-# of known size (profiles/gemm_kernel_layer_m1024_traffic.md).  Valid
+# HBM bytes per launch of the grouped prefill call (the GEMM kernel and the
+# split-K combine), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by
+# the same counters' reading for a plain copy of known size
+# (profiles/gemm_kernel_layer_m1024_traffic.md).  Valid
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": "51b5369f85699ab0879ded2f6678672a301e46fa7d16672964903fec25a76bd6", "bytes_per_launch": 617174176}
+TRAFFIC = {"sources_sha256": "0f45061bfdbfede94d3fc3f8d285b1bfcfc51f5789a1455bee4bd6c1f5ba135a", "bytes_per_launch": 619454993}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -366,7 +367,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": (TRAFFIC["bytes_per_launch"] if TRAFFIC["sources_sha256"] == sources_sha256() else None),
-                     "kernel": "dmq::gemm_kernel<3,8,4,false> (grouped Q4_K/Q6_K prefill launch)", "launch_ms": round(kern_ms, 4)},
+                     "kernel": "dmq::gemm_kernel<3,8,2,false> (grouped Q4_K/Q6_K prefill launch) + "
+                               "dmq::splitk_reduce_kernel (piece-order sum of the split down projection)",
+                     "launch_ms": round(kern_ms, 4)},
     }
 
     if not args.no_decode:
