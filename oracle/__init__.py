@@ -8,12 +8,16 @@ the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
   triple-loop matmul) are plain C in ``oracle.c``, compiled with gcc into
   ``liboracle.so`` and called through ctypes.
 * The SwiGLU check (silu and the acceptance interval) is fp64 numpy here.
+* RMSNorm (fp64, no intermediate rounding) and the GEMM on its fp64 output
+  are C as well; the fp16 acceptance interval of a normalized activation is
+  numpy here.
 
 Sources (DAMASCUS pages): the dequantisers and the quantised matmul are the
 overview page's compartment 09 ("[02] the pipeline") and the article's
 section "Read the model, then reproduce its operations"; the SwiGLU FFN is
 compartment 05/06 and the article's layer description (a second RMSNorm and
-a SwiGLU feed-forward network end each layer); comparing against the same
+a SwiGLU feed-forward network end each layer; RMSNorm also precedes the QKV
+projections, overview "[04] one decode step"); comparing against the same
 dequantised blocks is the article's same-weights oracle idea.  The per-output
 acceptance bound |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 1e-5 replaces the
 pages' own 1e-3 absolute logit threshold (article, same section).
@@ -89,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_f16.restype = ctypes.c_int
         L.oracle_gemm_f16_pairs.argtypes = [P, P, I64, P, P, I64, P, P]
         L.oracle_gemm_f16_pairs.restype = ctypes.c_int
+        L.oracle_rmsnorm.argtypes = [P, P, ctypes.c_double, I64, I64, P]
+        L.oracle_rmsnorm.restype = None
+        L.oracle_gemm_f64x.argtypes = [P, P, I64, I64, I64, P, P]
+        L.oracle_gemm_f64x.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
@@ -304,3 +312,55 @@ def swiglu_accepts(h_gpu: np.ndarray, lo16: np.ndarray, hi16: np.ndarray) -> np.
     """Boolean mask: h_gpu (fp16 values) inside [lo16, hi16]; NaN never accepted."""
     h = np.asarray(h_gpu, np.float64)
     return (h >= lo16) & (h <= hi16)
+
+
+# -------------------------------------------------------------- RMSNorm ---
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of the rows of x (fp16 [M,K]) in fp64: x * g / sqrt(mean(x^2) + eps).
+    g is the per-column weight (read exactly, e.g. fp32 values), eps >= 0."""
+    xb = _c(np.asarray(x, dtype=np.float16).view(np.uint16), np.uint16)
+    M, K = xb.shape
+    gd = _c(np.asarray(g, dtype=np.float64).reshape(-1), np.float64)
+    assert gd.size == K
+    out = np.empty((M, K), np.float64)
+    lib().oracle_rmsnorm(_ptr(xb), _ptr(gd), float(eps), M, K, _ptr(out))
+    return out
+
+
+def gemm_f64x(x: np.ndarray, w_bits: np.ndarray):
+    """y = x W^T and S = sum |x w| in fp64 with fp64 x [M,K] and fp16 W bits [N,K]."""
+    xd = _c(x, np.float64)
+    wb = _c(w_bits, np.uint16)
+    M, K = xd.shape
+    N, K2 = wb.shape
+    assert K == K2
+    y = np.empty((M, N), np.float64)
+    s = np.empty((M, N), np.float64)
+    rc = lib().oracle_gemm_f64x(_ptr(xd), _ptr(wb), M, N, K, _ptr(y), _ptr(s))
+    assert rc == 0
+    return y, s
+
+
+def rmsnorm_gemm_quant(fmt: str, x: np.ndarray, g: np.ndarray, eps: float, wq: np.ndarray, n: int, k: int):
+    """Oracle of RMSNorm followed by the quantised GEMM: the exact normalized
+    activations (fp64, not rounded) times the exactly dequantised fp16 weights."""
+    return gemm_f64x(rmsnorm(x, g, eps), dequant(fmt, wq, n, k))
+
+
+# fp32 arithmetic on the GPU side of a normalized activation: a sum of squares
+# over K terms (per-thread runs of at most K/256 terms, then a tree), a square
+# root and a division, two products.  2^-16 relative covers that with margin
+# for K up to 2^16 and stays below one fp16 ulp (2^-10 relative).
+RMSNORM_REL_SLACK = 2.0 ** -16
+
+
+def rmsnorm_f16_interval(xhat: np.ndarray, rel_slack: float = RMSNORM_REL_SLACK):
+    """Acceptance interval [lo16, hi16] (fp16 values as fp64) for an fp16
+    normalized activation whose exact value is xhat: the fp16 grid points
+    around [xhat - |xhat| rel_slack, xhat + |xhat| rel_slack], rounded
+    outward."""
+    xh = np.asarray(xhat, np.float64)
+    lo = xh - np.abs(xh) * rel_slack
+    hi = xh + np.abs(xh) * rel_slack
+    return _fp16_grid_down(lo), _fp16_grid_up(hi)

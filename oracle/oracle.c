@@ -267,6 +267,56 @@ int oracle_gemm_f16_pairs(const uint16_t* x, const uint16_t* w, int64_t K,
   return 0;
 }
 
+/* ------------------------------------------------------------- RMSNorm --- */
+
+/*
+ * RMSNorm of the rows of x (M x K fp16): out[m][k] = x[m][k] * g[k] / r_m with
+ * r_m = sqrt(sum_k x[m][k]^2 / K + eps), in fp64 (k ascending), no rounding to
+ * fp16.  The layer description on the article page names the operation
+ * (RMSNorm before the QKV projections and before the feed-forward network);
+ * the definition is the standard one: divide by the root mean square of the
+ * row, offset by eps, and scale by the per-column weight g.
+ */
+void oracle_rmsnorm(const uint16_t* x, const double* g, double eps, int64_t M, int64_t K, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    const uint16_t* xr = x + m * K;
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double v = oracle_f16_to_f64(xr[k]);
+      ss += v * v;
+    }
+    double r = sqrt(ss / (double)K + eps);
+    for (int64_t k = 0; k < K; ++k) out[m * K + k] = oracle_f16_to_f64(xr[k]) * g[k] / r;
+  }
+}
+
+/*
+ * y = x W^T and s = sum |x w| with x in fp64 (M x K, e.g. the RMSNorm output
+ * above) and W fp16 (N x K), fp64, k ascending.
+ */
+int oracle_gemm_f64x(const double* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                     double* y, double* s) {
+  double* wd = f16_matrix_to_f64(w, N * K);
+  if (!wd) return -2;
+#pragma omp parallel for schedule(static)
+  for (int64_t mn = 0; mn < M * N; ++mn) {
+    int64_t m = mn / N, n = mn % N;
+    const double* xr = x + m * K;
+    const double* wr = wd + n * K;
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double p = xr[k] * wr[k];
+      acc += p;
+      mag += fabs(p);
+    }
+    y[mn] = acc;
+    if (s) s[mn] = mag;
+  }
+  free(wd);
+  return 0;
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -13,7 +13,11 @@ benchmark must record"), so the oracle is pinned by:
 * numpy's fp16 conversions, exhaustively (P8);
 * the byte count of the model the pages describe against their "1.9 GiB" (P9);
 * numpy's fp64 matmul and exact rational sums for the triple loop (P10);
-* closed forms of silu and the behaviour of the SwiGLU acceptance interval (P11).
+* closed forms of silu and the behaviour of the SwiGLU acceptance interval (P11);
+* RMSNorm (P12): rows with a closed-form root mean square, exact scale
+  invariance under powers of two, linearity in the weight g, the eps offset
+  on a zero row; the fp64-activation GEMM against the fp16 one where the
+  activations are fp16 values, and against numpy's matmul.
 
 The k-quant byte layout is not on the pages; the blocks here are packed by
 ``tests/_packing.py`` from the public GGUF layout, so the layout pins check the
@@ -432,6 +436,90 @@ def test_p11_interval_overflow_and_minimum():
     lo, hi = oracle.swiglu_interval(np.array([-1.0]), np.array([1.0]), np.array([0.5]), np.array([0.0]))
     assert lo[0] <= oracle.SILU_MIN_VAL < hi[0]
     assert lo[0] > oracle.SILU_MIN_VAL - 1e-3
+
+
+# ------------------------------------------------------------------ P12 ----
+
+def test_p12_rmsnorm_closed_forms():
+    K = 256
+    # constant row: the root mean square is |c|, so every value is sign(c) * g
+    x = np.array([[3.0] * K, [-0.25] * K], dtype=np.float16)
+    g = np.ones(K)
+    out = oracle.rmsnorm(x, g, 0.0)
+    assert np.array_equal(out[0], np.ones(K)) and np.array_equal(out[1], -np.ones(K))
+    # +-2 alternating: rms 2, so out = (+-1) * g exactly
+    x = np.array([[2.0, -2.0] * (K // 2)], dtype=np.float16)
+    g = np.arange(K) / 256.0
+    out = oracle.rmsnorm(x, g, 0.0)
+    assert np.array_equal(out[0], np.where(np.arange(K) % 2 == 0, 1.0, -1.0) * g)
+    # one nonzero value a in K = 256: rms = |a| / 16, so out[0] = 16 sign(a) g[0]
+    x = np.zeros((1, K), dtype=np.float16)
+    x[0, 0] = -5.0
+    out = oracle.rmsnorm(x, np.full(K, 0.5), 0.0)
+    assert out[0, 0] == -8.0 and np.all(out[0, 1:] == 0.0)
+    # eps: a zero row stays zero; with eps the rms of a +-1 row is sqrt(1 + eps)
+    x = np.zeros((1, K), dtype=np.float16)
+    assert np.all(oracle.rmsnorm(x, np.ones(K), 1e-5) == 0.0)
+    x = np.array([[1.0, -1.0] * (K // 2)], dtype=np.float16)
+    out = oracle.rmsnorm(x, np.ones(K), 3.0)
+    assert np.allclose(np.abs(out), 0.5, rtol=0, atol=1e-15)
+
+
+def test_p12_rmsnorm_invariants():
+    rng = np.random.default_rng(7)
+    K = 768
+    # magnitudes in [0.05, 3): scaled by 2^-3 or 2^2 they stay normal fp16
+    x = (rng.choice([-1.0, 1.0], (6, K)) * rng.uniform(0.05, 3.0, (6, K))).astype(np.float16)
+    g = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    base = oracle.rmsnorm(x, g, 0.0)
+    # scaling a row by a power of two (exact in fp16) does not change it
+    for j in (-3, 2):
+        xs = (x.astype(np.float64) * 2.0 ** j).astype(np.float16)
+        assert np.array_equal(xs.astype(np.float64), x.astype(np.float64) * 2.0 ** j)
+        assert np.allclose(oracle.rmsnorm(xs, g, 0.0), base, rtol=1e-14, atol=0)
+    # linear in g
+    assert np.allclose(oracle.rmsnorm(x, 2.0 * g.astype(np.float64), 0.0), 2.0 * base, rtol=1e-15, atol=0)
+    # every row has mean square sum(out^2 / g^2) / K = 1 (eps = 0)
+    ms = np.mean((base / g.astype(np.float64)) ** 2, axis=1)
+    assert np.allclose(ms, 1.0, rtol=1e-13)
+    # eps only shrinks: |out(eps)| < |out(0)| where out(0) != 0
+    e = oracle.rmsnorm(x, g, 1e-2)
+    nz = base != 0
+    assert np.all(np.abs(e[nz]) < np.abs(base[nz]))
+
+
+def test_p12_gemm_f64x_matches_f16_gemm_and_numpy():
+    rng = np.random.default_rng(3)
+    wq = synthetic.q4k_blocks(40, 512, seed=31)
+    wb = oracle.dequant("q4k", wq, 40, 512)
+    # fp16-representable activations: both oracles must agree exactly
+    x16 = rng.standard_normal((5, 512)).astype(np.float16)
+    y1, s1 = oracle.gemm_f16(x16, wb)
+    y2, s2 = oracle.gemm_f64x(x16.astype(np.float64), wb)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+    # arbitrary fp64 activations: numpy's matmul in fp64
+    xd = rng.standard_normal((5, 512))
+    y3, s3 = oracle.gemm_f64x(xd, wb)
+    wd = oracle.f16_bits_to_f64(wb)
+    mag = np.abs(xd) @ np.abs(wd).T
+    assert np.all(np.abs(y3 - xd @ wd.T) <= 1e-12 * mag)
+    assert np.allclose(s3, mag, rtol=1e-13)
+
+
+def test_p12_rmsnorm_interval_accepts_rounded_rejects_two_ulps():
+    rng = np.random.default_rng(11)
+    xh = rng.standard_normal(4000) * 3.0
+    lo, hi = oracle.rmsnorm_f16_interval(xh)
+    h = xh.astype(np.float16)
+    hv = h.astype(np.float64)
+    assert np.all((hv >= lo) & (hv <= hi))
+    up2 = np.nextafter(np.nextafter(h, np.float16(np.inf)), np.float16(np.inf)).astype(np.float64)
+    dn2 = np.nextafter(np.nextafter(h, np.float16(-np.inf)), np.float16(-np.inf)).astype(np.float64)
+    assert not np.any((up2 >= lo) & (up2 <= hi))
+    assert not np.any((dn2 >= lo) & (dn2 <= hi))
+    # an exact zero only accepts zero
+    lo, hi = oracle.rmsnorm_f16_interval(np.zeros(3))
+    assert np.all(lo == 0.0) and np.all(hi == 0.0)
 
 
 # -------------------------------------------------------- generators -------
