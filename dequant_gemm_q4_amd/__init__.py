@@ -31,7 +31,8 @@ FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
 
 # Every entry point declared in include/dmq.h.
 EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
-           "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_status_string", "dmq_version")
+           "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_status_string",
+           "dmq_version")
 
 
 class DmqError(RuntimeError):
@@ -45,6 +46,12 @@ class GemmDesc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("x_f16", ctypes.c_void_p), ("wq", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class ProjDesc(ctypes.Structure):
+    """Mirror of dmq_proj_desc."""
+    _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("wq", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
 
 
 def _load() -> ctypes.CDLL:
@@ -65,8 +72,9 @@ def _load() -> ctypes.CDLL:
     L.dmq_gemm_q6k.argtypes = [P, P, P, I64, I64, I64, P]
     L.dmq_ffn_swiglu_q4k.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     L.dmq_gemm_group.argtypes = [ctypes.POINTER(GemmDesc), I32, P]
+    L.dmq_rmsnorm_gemm.argtypes = [P, P, ctypes.c_float, P, I64, I64, ctypes.POINTER(ProjDesc), I32, P]
     for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
-                 "dmq_ffn_swiglu_q4k", "dmq_gemm_group"):
+                 "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm"):
         getattr(L, name).restype = ctypes.c_int
     L.dmq_status_string.argtypes = [ctypes.c_int]
     L.dmq_status_string.restype = ctypes.c_char_p
@@ -185,6 +193,45 @@ def dmq_gemm_group(problems, stream=None) -> None:
     by make_group (reusing it avoids re-marshalling in timing loops)."""
     arr = problems if isinstance(problems, ctypes.Array) else make_group(problems)
     _check(lib.dmq_gemm_group(arr, len(arr), _stream(stream)), "dmq_gemm_group")
+
+
+def make_projs(projs, K: int):
+    """projs: iterable of (format, wq, y, N); returns the ctypes dmq_proj_desc
+    array (sizes checked against K and y's element count / M below)."""
+    import torch
+    projs = list(projs)
+    arr = (ProjDesc * len(projs))()
+    for i, (fmt, wq, y, N) in enumerate(projs):
+        fmt = FORMATS.get(fmt, fmt)
+        arr[i].format = fmt
+        arr[i].reserved = 0
+        arr[i].wq = _dev_tensor(wq, torch.uint8, f"wq[{i}]", _wq_bytes(fmt, N, K))
+        if not isinstance(y, torch.Tensor) or y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous():
+            raise TypeError(f"y[{i}] must be a contiguous float32 GPU tensor")
+        arr[i].y = y.data_ptr()
+        arr[i].N = N
+    return arr
+
+
+def dmq_rmsnorm_gemm(x, g, eps: float, xn, projs, M: int, K: int, stream=None) -> None:
+    """y_i[M, N_i] (float32) <- RMSNorm(x; g, eps) * W_i^T for each projection.
+
+    x: float16 [M, K]; g: float32 [K]; xn: float16 [M, K] output (the
+    normalized activations), or None when M = 1 and K <= 32768 (the decode
+    kernel normalizes while staging x).  ``projs``: list of (format, wq, y, N)
+    or the array returned by make_projs."""
+    import torch
+    px = _dev_tensor(x, torch.float16, "x", M * K)
+    pg = _dev_tensor(g, torch.float32, "g", K)
+    pn = None if xn is None else _dev_tensor(xn, torch.float16, "xn", M * K)
+    arr = projs if isinstance(projs, ctypes.Array) else make_projs(projs, K)
+    for i in range(len(arr)):
+        if not isinstance(projs, ctypes.Array):
+            y = list(projs)[i][2]
+            if y.numel() != M * arr[i].N:
+                raise ValueError(f"y[{i}] has {y.numel()} elements, expected {M * arr[i].N}")
+    _check(lib.dmq_rmsnorm_gemm(px, pg, float(eps), pn, M, K, arr, len(arr), _stream(stream)),
+           "dmq_rmsnorm_gemm")
 
 
 def dmq_version() -> int:

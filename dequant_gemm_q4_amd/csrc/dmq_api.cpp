@@ -112,6 +112,9 @@ dmq::GemmProblem make_problem(int fmt, const void* x, const void* wq, void* out,
   p.M = (int32_t)M;
   p.N = (int32_t)N;
   p.K = (int32_t)K;
+  p.g = nullptr;
+  p.eps = 0.0f;
+  p.xn = nullptr;
   return p;
 }
 
@@ -213,6 +216,40 @@ int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream) {
   std::stable_sort(probs, probs + count,
                    [](const dmq::GemmProblem& a, const dmq::GemmProblem& b) { return a.K > b.K; });
   return run_gemm(probs, count, n_decode == count, (hipStream_t)stream);
+}
+
+int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16, int64_t M, int64_t K,
+                     const dmq_proj_desc* projs, int32_t count, void* stream) {
+  if (!projs || count < 1 || count > kMaxGroup) return DMQ_ERR_INVALID_ARG;
+  if (!x_f16 || !g || !(eps >= 0.0f) || eps > 3.0e38f) return DMQ_ERR_INVALID_ARG;   // rejects NaN too
+  if (!dim_ok(M) || check_quant_k(K) != DMQ_OK || K > kMaxK) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(x_f16, 16) || !aligned(g, 16)) return DMQ_ERR_ALIGNMENT;
+  const bool decode = (M == 1 && K <= kGemvMaxK);
+  if (!decode && !xn_f16) return DMQ_ERR_INVALID_ARG;
+  if (xn_f16) {
+    if (xn_f16 == x_f16) return DMQ_ERR_INVALID_ARG;
+    if (!aligned(xn_f16, 16)) return DMQ_ERR_ALIGNMENT;
+  }
+  dmq::GemmProblem probs[kMaxGroup];
+  for (int i = 0; i < count; ++i) {
+    const dmq_proj_desc& d = projs[i];
+    if (d.reserved != 0 || (d.format != DMQ_FMT_Q4K && d.format != DMQ_FMT_Q6K)) return DMQ_ERR_INVALID_ARG;
+    int st = check_gemm(d.format, decode ? x_f16 : xn_f16, d.wq, d.y, M, d.N, K);
+    if (st != DMQ_OK) return st;
+    probs[i] = make_problem(d.format, decode ? x_f16 : xn_f16, d.wq, d.y, M, d.N, K, 0);
+    if (decode) {
+      probs[i].g = g;
+      probs[i].eps = eps;
+      probs[i].xn = i == 0 ? xn_f16 : nullptr;
+    }
+  }
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  if (!decode) {
+    int st = hip_status(dmq::launch_rmsnorm(x_f16, g, eps, xn_f16, M, K, (hipStream_t)stream));
+    if (st != DMQ_OK) return st;
+  }
+  return run_gemm(probs, count, decode, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -106,11 +106,61 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ------------------------------------------------------------- RMSNorm ---
+// RMSNorm (the layer description on the article page: one before the QKV
+// projections, one before the feed-forward network): x * g / sqrt(mean(x^2)
+// + eps) per row, in fp32, the result rounded once to fp16 for the MFMA / dot
+// operands.
+
+// Sum of squares of 8 fp16 values (one 16-byte chunk), pairwise.
+__device__ __forceinline__ float sumsq8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = as_h2(w[i]);
+    const float a = (float)h.x, b = (float)h.y;
+    p[i] = a * a + b * b;
+  }
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+// 1 / sqrt(mean(x^2) + eps) of one row of K fp16 values, computed by a whole
+// 256-thread workgroup (chunk i = thread + 256 j); red4 is 4 floats of LDS.
+// Every thread of the workgroup must call it (it has a barrier); all get the
+// same value.
+__device__ __forceinline__ float rms_inv(const half_t* row, int K, float eps, float* red4) {
+  const uint4* xr = (const uint4*)row;
+  float ss = 0.0f;
+  for (int i = (int)threadIdx.x; i < K / 8; i += 256) ss += sumsq8(xr[i]);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float t = (red4[0] + red4[1]) + (red4[2] + red4[3]);
+  return 1.0f / __builtin_sqrtf(t / (float)K + eps);
+}
+
+// 8 fp16 values -> fp16(x * g * r), g: the 8 matching weights.
+__device__ __forceinline__ uint4 norm8(uint4 v, const float* g, float r) {
+  const float4 g0 = ((const float4*)g)[0], g1 = ((const float4*)g)[1];
+  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = as_h2(w[i]);
+    const h2 o = {(half_t)(((float)h.x * gv[2 * i]) * r), (half_t)(((float)h.y * gv[2 * i + 1]) * r)};
+    w[i] = as_u32(o);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ------------------------------------------------------------ launchers ---
 // All launchers assume arguments were validated on the host (dmq_api.cpp).
 
 hipError_t launch_dequant_q4k(const void* wq, void* w, int64_t rows, int64_t k, hipStream_t s);
 hipError_t launch_dequant_q6k(const void* wq, void* w, int64_t rows, int64_t k, hipStream_t s);
+// xn[m] = fp16(x[m] * g / sqrt(mean(x[m]^2) + eps)) for each of the M rows.
+hipError_t launch_rmsnorm(const void* x, const float* g, float eps, void* xn, int64_t M, int64_t K, hipStream_t s);
 
 // One GEMM problem as the kernels see it.
 struct GemmProblem {
@@ -120,6 +170,9 @@ struct GemmProblem {
   int32_t fmt;        // 0 = Q4_K, 1 = Q6_K
   int32_t swiglu;     // 1: rows [0,N/2) are gate, [N/2,N) up; out = h
   int32_t M, N, K;
+  const float* g;     // decode kernel only: RMSNorm x with weights g (K floats) ...
+  float eps;          // ... and this eps while staging it; NULL g: no norm
+  void* xn;           // decode kernel, with g: if set, the normalized x (K fp16) is written here
 };
 
 // Decode kernel (M = 1): y[n] = sum_k x[k] w[n][k] for every problem.

@@ -42,6 +42,9 @@ struct GemvDesc {
   const half_t* x;
   const uint8_t* wq;
   void* out;
+  const float* g;     // RMSNorm weights (K floats), or NULL: x is used as it is
+  float eps;
+  half_t* xn;         // with g: workgroup 0 writes the normalized x here (if set)
   int32_t fmt, swiglu, N, K;
   int32_t wg_begin;   // first workgroup of this problem
 };
@@ -196,7 +199,7 @@ __device__ __forceinline__ int part_x_offset(int b, int part) {
 constexpr int GEMV_ROWS = 16;
 
 template <int FMT, bool PAIR>
-__device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_t* xs, float* red) {
+__device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_t* xs, float* red, float* red4) {
   typedef typename PartOf<FMT>::T Part;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
   const int lane = threadIdx.x & 63;
@@ -225,7 +228,16 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
     load_part(wg_ + (int64_t)b0 * BLOCK_BYTES, part, g0);
     if (PAIR) load_part(wu_ + (int64_t)b0 * BLOCK_BYTES, part, u0p);
   }
-  auto xput = [&](int i, const uint4& v) { *(uint4*)((uint8_t*)xs + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v; };
+  // RMSNorm (when P.g is set): the workgroup's sum of squares over the
+  // whole row, then each wave scales its slice as it stages it
+  const float rn = P.g ? rms_inv(P.x, P.K, P.eps, red4) : 1.0f;
+  auto xput = [&](int i, uint4 v) {
+    if (P.g) {
+      v = norm8(v, P.g + 8 * i, rn);
+      if (P.xn && wg_local == 0) ((uint4*)P.xn)[i] = v;
+    }
+    *(uint4*)((uint8_t*)xs + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v;
+  };
   if (xa) xput(b0 * 32 + lane, xra);
   if (xb) xput(b0 * 32 + lane + 64, xrb);
   for (int i = b0 * 32 + lane + 128; i < b1 * 32; i += 64)   // slices of more than 4 blocks
@@ -289,6 +301,7 @@ template <bool PAIRS>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs args) {
   extern __shared__ __attribute__((aligned(16))) half_t xs[];
   __shared__ float red[4 * 2 * GEMV_ROWS];
+  __shared__ float red4[4];
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < GEMV_MAX_GROUP; ++i)
@@ -297,11 +310,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs args) {
   const int wg_local = (int)blockIdx.x - P.wg_begin;
   if (P.fmt == 0) {
     if (PAIRS && P.swiglu)
-      gemv_tile<0, PAIRS>(P, wg_local, xs, red);
+      gemv_tile<0, PAIRS>(P, wg_local, xs, red, red4);
     else
-      gemv_tile<0, false>(P, wg_local, xs, red);
+      gemv_tile<0, false>(P, wg_local, xs, red, red4);
   } else {
-    gemv_tile<1, false>(P, wg_local, xs, red);
+    gemv_tile<1, false>(P, wg_local, xs, red, red4);
   }
 }
 
@@ -325,6 +338,9 @@ hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s) {
       d.x = (const half_t*)p.x;
       d.wq = p.wq;
       d.out = p.out;
+      d.g = p.g;
+      d.eps = p.eps;
+      d.xn = (half_t*)p.xn;
       d.fmt = p.fmt;
       d.swiglu = p.swiglu;
       d.N = p.N;

@@ -150,6 +150,44 @@ typedef struct {
  */
 int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream);
 
+/*
+ * One weight matrix of dmq_rmsnorm_gemm: y = RMSNorm(x) * W^T with W in the
+ * given format (N rows of K/256 blocks) and y [M, N] fp32.
+ */
+typedef struct {
+  int32_t format;      /* DMQ_FMT_Q4K or DMQ_FMT_Q6K */
+  int32_t reserved;    /* must be 0 */
+  const void* wq;
+  float* y;
+  int64_t N;
+} dmq_proj_desc;
+
+/*
+ * RMSNorm of the activations followed by the projections that read them, as
+ * each decoder layer does before its Q|K|V projections and again before its
+ * gate|up projections (article "Building DAMASCUS", layer description;
+ * overview page, "[04] one decode step").
+ *   x_f16  : [M, K] fp16, 16-byte aligned.
+ *   g      : K fp32 RMSNorm weights, 16-byte aligned.
+ *   eps    : >= 0 and finite (Llama-3.2 uses 1e-5).
+ *   xn_f16 : [M, K] fp16 output, 16-byte aligned, not x: the normalized
+ *            activations, xn[m][k] = fp16(x[m][k] * g[k] / sqrt(mean_k x[m][k]^2
+ *            + eps)), computed in fp32 (the row's sum of squares included) and
+ *            rounded once: within one fp16 step of the exact value.  When
+ *            M = 1 (and K <= 32768) the decode kernel normalizes x while it
+ *            stages it; xn is then optional (NULL: not written).
+ *   projs  : 1..64 projections (host array, read before the call returns), all
+ *            with reduction length K.
+ * y_i = xn * W_i^T for each projection with xn as the activations, under the
+ * rules and the per-output bound of dmq_gemm_q4k / dmq_gemm_q6k (one grouped
+ * launch after the normalization).  The fp16 rounding of xn is part of the
+ * operation: where the normalized values are fp16 subnormals (a row of tiny
+ * values under a large eps) it is coarse, and y follows the rounded values.
+ */
+int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
+                     int64_t M, int64_t K, const dmq_proj_desc* projs, int32_t count,
+                     void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* dmq_status_string(int status);
 

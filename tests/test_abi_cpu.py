@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert set(names) == set(dmq.EXPORTS)
     raw = ctypes.CDLL(dmq.LIB_PATH)
     for n in names:
@@ -125,3 +125,40 @@ def test_gemm_k_limit():
     # the GEMM kernels take K up to 2^20
     assert L.dmq_gemm_q4k(A16, A16, A16, 4, 4, (1 << 20) + 256, None) == dmq.DMQ_ERR_INVALID_ARG
     assert L.dmq_gemm_q6k(A16, A16, A16, 1, 4, (1 << 20) + 256, None) == dmq.DMQ_ERR_INVALID_ARG
+
+
+def _proj(fmt=0, N=4, wq=A16, y=A16, reserved=0):
+    d = dmq.ProjDesc()
+    d.format, d.reserved, d.wq, d.y, d.N = fmt, reserved, wq, y, N
+    return d
+
+
+def test_rmsnorm_gemm_validation():
+    f = L.dmq_rmsnorm_gemm
+    p = (dmq.ProjDesc * 2)(_proj(), _proj(fmt=1))
+    X, G, XN = A16, A16 + 0x1000, A16 + 0x2000
+    assert f(X, G, 1e-5, XN, 4, 256, p, 0, None) == dmq.DMQ_ERR_INVALID_ARG      # count
+    assert f(X, G, 1e-5, XN, 4, 256, p, 65, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(X, G, 1e-5, XN, 4, 256, None, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(None, G, 1e-5, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG    # x
+    assert f(X, None, 1e-5, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG    # g
+    assert f(X, G, -1.0, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG       # eps < 0
+    assert f(X, G, float("nan"), XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(X, G, float("inf"), XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(X, G, 1e-5, XN, 4, 300, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG       # K % 256
+    assert f(X, G, 1e-5, XN, 0, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG       # M
+    assert f(X, G, 1e-5, None, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG     # xn needed for M > 1
+    assert f(X, G, 1e-5, X, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG        # xn == x
+    assert f(MIS, G, 1e-5, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    assert f(X, G + 8, 1e-5, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    assert f(X, G, 1e-5, XN + 8, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    bad = (dmq.ProjDesc * 1)(_proj(reserved=1))
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.ProjDesc * 1)(_proj(fmt=5))
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.ProjDesc * 1)(_proj(N=0))
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.ProjDesc * 1)(_proj(y=MIS))
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_ALIGNMENT
+    bad = (dmq.ProjDesc * 1)(_proj(wq=A16 + 2))                # Q4_K weights need 16 bytes
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_ALIGNMENT

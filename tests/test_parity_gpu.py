@@ -475,3 +475,104 @@ def test_single_hip_runtime_and_native_library(dmq):
     assert len(hip) == 1, hip
     assert len(hsa) == 1, hsa
     assert dmq.LIB_PATH in paths
+
+
+# --------------------------------------------------------------- RMSNorm ---
+# dmq_rmsnorm_gemm, checked stage by stage (the reading used for the FFN's h):
+# the normalized activations xn must lie within one fp16 step of the oracle's
+# exact fp64 RMSNorm (interval rounded outward from +-2^-16 relative: fp32 sum
+# of squares, square root, products); y must meet the GEMM bound against the
+# oracle's fp64 product of the GPU's own xn with the exactly dequantised
+# weights.  At M = 1 the decode kernel writes the xn it staged when asked to.
+
+def _norm_weights(K, seed):
+    rng = np.random.default_rng(seed)
+    return rng.uniform(0.5, 1.5, K).astype(np.float32)
+
+
+def _rmsnorm_gemm(dmq, x, g, eps, projs, M, K, want_xn=True):
+    """projs: list of (fmt, wq, N). Returns (xn or None, [y_i])."""
+    xn = torch.empty((M, K), dtype=torch.float16, device=DEV) if want_xn else None
+    ys = [torch.empty((M, N), dtype=torch.float32, device=DEV) for _, _, N in projs]
+    dmq.dmq_rmsnorm_gemm(dev(x), dev(g), eps, xn,
+                         [(fmt, dev(wq.reshape(-1)), y, N) for (fmt, wq, N), y in zip(projs, ys)], M, K)
+    torch.cuda.synchronize()
+    return (None if xn is None else xn.cpu().numpy()), [y.cpu().numpy() for y in ys]
+
+
+def _check_rmsnorm_outputs(x, g, eps, projs, K, xn, ys, what, rows=None):
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    xhat = oracle.rmsnorm(sel(x), g, eps)
+    got = sel(xn)
+    lo, hi = oracle.rmsnorm_f16_interval(xhat)
+    ok = (got.astype(np.float64) >= lo) & (got.astype(np.float64) <= hi)
+    assert ok.all(), f"{what}: xn has {int((~ok).sum())} of {ok.size} values outside the interval"
+    for (fmt, wq, N), y in zip(projs, ys):
+        ref, s = oracle.gemm_quant(fmt, got, wq, N, K)
+        assert_within(sel(y), ref, s, f"{what} {fmt} N={N}")
+
+
+@pytest.mark.parametrize("M,K", [(2, 256), (5, 768), (16, 3072), (40, 512), (300, 1024), (257, 2304)])
+def test_rmsnorm_gemm_every_output(dmq, M, K):
+    x = synthetic.activations(M, K, seed=M * 7 + K, sigma=2.0)
+    g = _norm_weights(K, seed=K)
+    projs = [("q4k", synthetic.q4k_blocks(96, K, seed=M + 1), 96),
+             ("q4k", synthetic.q4k_blocks(37, K, seed=M + 2), 37),
+             ("q6k", synthetic.q6k_blocks(64, K, seed=M + 3), 64)]
+    xn, ys = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, M, K)
+    _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, f"rmsnorm+gemm M={M} K={K}")
+
+
+@pytest.mark.parametrize("K", [256, 3072, 8192])
+def test_rmsnorm_gemv_decode_every_output(dmq, K):
+    # M = 1: the decode kernel normalizes x while staging it
+    x = synthetic.activations(1, K, seed=K + 5, sigma=3.0)
+    g = _norm_weights(K, seed=K + 1)
+    projs = [("q4k", synthetic.q4k_blocks(200, K, seed=K + 2), 200),
+             ("q6k", synthetic.q6k_blocks(33, K, seed=K + 3), 33)]
+    xn, ys = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, 1, K)
+    _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, f"rmsnorm+gemv K={K}")
+    # without xn the results are the same bits
+    _, ys2 = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, 1, K, want_xn=False)
+    for a, b in zip(ys, ys2):
+        assert np.array_equal(a, b)
+
+
+def test_rmsnorm_edge_rows(dmq):
+    # a zero row (eps > 0 keeps it zero), a row of one huge value, a row of
+    # fp16 subnormals (normalized to subnormals again under a large eps), and
+    # a large eps that dominates the mean square
+    M, K = 4, 512
+    x = np.zeros((M, K), dtype=np.float16)
+    x[1, 7] = 60000.0
+    x[2, :] = np.float16(3e-7)
+    x[3, :] = synthetic.activations(1, K, seed=3)[0]
+    g = _norm_weights(K, seed=9)
+    projs = [("q4k", synthetic.q4k_blocks(64, K, seed=4), 64), ("q6k", synthetic.q6k_blocks(40, K, seed=5), 40)]
+    for eps in (1e-5, 4.0):
+        xn, ys = _rmsnorm_gemm(dmq, x, g, eps, projs, M, K)
+        assert np.all(xn[0] == 0) and np.all(ys[0][0] == 0) and np.all(ys[1][0] == 0)
+        _check_rmsnorm_outputs(x, g, eps, projs, K, xn, ys, f"rmsnorm edge rows eps={eps}")
+        # the same rows one at a time through the decode path
+        for m in range(M):
+            xn1, ys1 = _rmsnorm_gemm(dmq, x[m:m + 1], g, eps, projs, 1, K)
+            _check_rmsnorm_outputs(x[m:m + 1], g, eps, projs, K, xn1, ys1, f"rmsnorm edge row {m} decode")
+
+
+def test_rmsnorm_qkv_layer_shapes_sampled(dmq):
+    # the Q|K|V projections of one Llama-3.2-3B-shaped layer behind their
+    # RMSNorm, at M = 1024 (tiled kernel, grouped) and M = 1 (decode kernel)
+    K = 3072
+    g = _norm_weights(K, seed=77)
+    projs = [("q4k", synthetic.q4k_blocks(N, K, seed=synthetic.weight_seed(2, 0, i)), N)
+             for i, N in enumerate((3072, 1024, 1024))]
+    M = 1024
+    x = synthetic.activations(M, K, seed=synthetic.act_seed(2, 0, 0), sigma=1.5)
+    xn, ys = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, M, K)
+    # xn on every row, y on sampled rows that hit every 256-row tile
+    lo, hi = oracle.rmsnorm_f16_interval(oracle.rmsnorm(x, g, 1e-5))
+    assert np.all((xn.astype(np.float64) >= lo) & (xn.astype(np.float64) <= hi))
+    rows = synthetic.row_sample(M, 24, seed=5)
+    _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, "rmsnorm QKV M=1024", rows=rows)
+    xn1, ys1 = _rmsnorm_gemm(dmq, x[:1], g, 1e-5, projs, 1, K)
+    _check_rmsnorm_outputs(x[:1], g, 1e-5, projs, K, xn1, ys1, "rmsnorm QKV M=1")
