@@ -201,6 +201,43 @@ def sweep(torch, dmq):
                           "pct_fp16_peak": round(100 * flops_of(M) / ms / 1e9 / PEAK_FP16_TFLOPS, 2)}), flush=True)
         del layers, xs, ys
 
+    # RMSNorm ahead of the Q|K|V projections (K = 3072): the normalize-then-
+    # GEMM call against the same three GEMMs on already normalized input, at
+    # M = 1024 (norm kernel + grouped GEMM) and M = 1 (norm fused into the
+    # decode kernel's x staging; graph replays over 8 weight copies)
+    K = 3072
+    g = torch.from_numpy(np.random.default_rng(77).uniform(0.5, 1.5, K).astype(np.float32)).to(dev)
+    qkv = [(i, N) for i, N in enumerate((3072, 1024, 1024))]
+    for M in (1024, 1):
+        x = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(2, 0, 0), sigma=1.5)).to(dev)
+        xn = torch.empty((M, K), dtype=torch.float16, device=dev)
+        ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _, N in qkv]
+        nl = 8 if M == 1 else 5
+        ws = [[torch.from_numpy(synthetic.q4k_blocks(N, K, seed=synthetic.weight_seed(2, layer, i)).reshape(-1)).to(dev)
+               for i, N in qkv] for layer in range(nl)]
+        projs = [dmq.make_projs([("q4k", w, y, N) for w, y, (_, N) in zip(wl, ys, qkv)], K) for wl in ws]
+        groups = [dmq.make_group([("q4k", xn, w, y, M, N, K) for w, y, (_, N) in zip(wl, ys, qkv)]) for wl in ws]
+        out_xn = None if M == 1 else xn
+        fused = lambda p: dmq.dmq_rmsnorm_gemm(x, g, 1e-5, out_xn, p, M, K)   # noqa: E731
+        if M == 1:
+            t_norm = time_graph(torch, fused, projs, 8)
+            t_plain = time_graph(torch, dmq.dmq_gemm_group, groups, 8)
+        else:
+            it = [0]
+
+            def run(fn, lst):
+                fn(lst[it[0] % len(lst)])
+                it[0] += 1
+            t_norm = _timed(torch, lambda: run(fused, projs))
+            t_plain = _timed(torch, lambda: run(dmq.dmq_gemm_group, groups))
+        fl = 2.0 * M * K * sum(N for _, N in qkv)
+        print(json.dumps({"sweep": f"RMSNorm + Q|K|V projections M={M} K={K} "
+                                   f"({'graph replay' if M == 1 else 'host-launched'})",
+                          "us_with_norm": round(t_norm * 1e3, 2), "us_gemms_only": round(t_plain * 1e3, 2),
+                          "norm_overhead_us": round((t_norm - t_plain) * 1e3, 2),
+                          "TFLOP/s_with_norm": round(fl / t_norm / 1e9, 1)}), flush=True)
+        del ws, projs, groups
+
     # config 4: tied LM head, Q6_K 3072 -> 128256 on 1024 rows
     name, fmt, N, K = synthetic.LM_HEAD
     M = 1024
