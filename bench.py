@@ -36,6 +36,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 M_PREFILL = 1024
 ROTATE_LAYERS = 5              # 5 x 63.1 MB of weights > 256 MB Infinity Cache
 DECODE_ROTATE = 8              # decode: 8 x 63.1 MB
+SETTLE_MS = 150.0              # untimed GPU work before any timed region (clock settling)
 
 
 # HBM bytes per launch of the grouped prefill call (the GEMM kernel and the
@@ -95,8 +96,7 @@ def vendor_gemm_probe(torch):
         w = torch.randn(N, K, device="cuda", dtype=torch.float16)
         wt = w.t()
         f = lambda: torch.matmul(a, wt)   # noqa: E731
-        for _ in range(5):
-            f()
+        settle(torch, f, 5)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -111,8 +111,7 @@ def vendor_gemm_probe(torch):
         tot_ms += ms
     out["layer_sequential_TFLOPs"] = round(tot_fl / tot_ms / 1e9, 1)
     a = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
-    for _ in range(3):
-        torch.matmul(a, a)
+    settle(torch, lambda: torch.matmul(a, a), 3, chunk=3)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -125,9 +124,9 @@ def vendor_gemm_probe(torch):
 
 
 def _timed(torch, fn, reps=20, warm=5):
-    """Mean ms of fn() over reps launches (HIP events on the current stream)."""
-    for _ in range(warm):
-        fn()
+    """Mean ms of fn() over reps launches (HIP events on the current stream),
+    after at least `warm` untimed calls and SETTLE_MS of GPU time."""
+    settle(torch, fn, warm, chunk=max(1, min(25, warm)))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -267,11 +266,38 @@ def weight_bytes():
     return sum(N * (K // 256) * size[f] for _, f, N, K in synthetic.LAYER_PROJECTIONS)
 
 
+def settle(torch, fn, min_launches, min_ms=SETTLE_MS, chunk=25, cap=20000):
+    """Untimed warm-up: call fn() at least min_launches times and until
+    min_ms of GPU time have run back to back.  From idle, the GPU needs tens
+    of milliseconds of continuous work before its clock settles (the first
+    launches of the M=1024 layer take up to 1.8x the settled time).  Returns
+    (launches run, GPU ms, mean ms of the first min(chunk, n) launches)."""
+    n, ms, first = 0, 0.0, None
+    while (n < min_launches or ms < min_ms) and n < cap:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(chunk):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        if first is None:
+            first = t / chunk
+        n += chunk
+        ms += t
+    return n, ms, first
+
+
 def time_launches(torch, launch, groups, steps, warmup):
     """Run `launch(group)` over the rotating groups; events bracket every
-    launch on the current (launch) stream.  Returns (total_ms, [per-launch ms])."""
-    for i in range(warmup):
-        launch(groups[i % len(groups)])
+    launch on the current (launch) stream.  Returns (total_ms, [per-launch
+    ms], warm-up record)."""
+    it = [0]
+
+    def one():
+        launch(groups[it[0] % len(groups)])
+        it[0] += 1
+    nw, wms, cold = settle(torch, one, warmup)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -285,7 +311,7 @@ def time_launches(torch, launch, groups, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
-    return t0.elapsed_time(t1), per
+    return t0.elapsed_time(t1), per, {"launches": nw, "gpu_ms": round(wms, 1), "first_ms_per_step": round(cold, 4)}
 
 
 def time_graph(torch, launch, groups, replays):
@@ -303,8 +329,7 @@ def time_graph(torch, launch, groups, replays):
     with torch.cuda.graph(graph):
         for g in groups:
             launch(g)
-    graph.replay()
-    torch.cuda.synchronize()
+    settle(torch, graph.replay, 2, chunk=5)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -378,7 +403,7 @@ def main():
     # keep (descriptor array, tensors) pairs: the arrays hold raw device pointers
     layers = [layer_problems(torch, dmq, 2, layer, M, xs, ys) for layer in range(ROTATE_LAYERS)]
     groups = [g for g, _ in layers]
-    total_ms, per = time_launches(torch, dmq.dmq_gemm_group, groups, args.steps, args.warmup)
+    total_ms, per, warm = time_launches(torch, dmq.dmq_gemm_group, groups, args.steps, args.warmup)
     flops = flops_of(M)
     value = flops * args.steps / (total_ms / 1e3) / 1e12
     kern_ms = float(np.mean(per))
@@ -392,6 +417,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(total_ms / args.steps, 4),
+        # the untimed warm-up actually run: at least `warmup` steps and SETTLE_MS
+        # of GPU time; first_ms_per_step is its first 25 steps, from an idle GPU
+        "warmup_run": warm,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -418,7 +446,7 @@ def main():
         dlayers = [layer_problems(torch, dmq, 1, layer, 1, dxs, dys) for layer in range(DECODE_ROTATE)]
         dgroups = [g for g, _ in dlayers]
         dsteps = max(args.steps, 50)
-        d_total, d_per = time_launches(torch, dmq.dmq_gemm_group, dgroups, dsteps, args.warmup)
+        d_total, d_per, _ = time_launches(torch, dmq.dmq_gemm_group, dgroups, dsteps, args.warmup)
         wb = weight_bytes()
         d_ms = float(np.mean(d_per))
         # a decode loop replays its launches from a graph: time that too

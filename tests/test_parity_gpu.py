@@ -321,6 +321,42 @@ def test_gemm_split_k(dmq, fmt, M, N, K):
     assert_within(y1.cpu().numpy()[rows], ref, s, f"split-K {fmt} {M}x{N}x{K}")
 
 
+def test_gemm_split_k_interleaved_shapes(dmq):
+    """Split launches share a per-stream workspace of partial sums: interleave
+    split launches of different piece counts and tile grids on one stream
+    (and one launch on a second stream, with its own workspace), repeat
+    each, and require the bits of its first call."""
+    shapes = [("q6k", 40, 37, 8192), ("q4k", 33, 250, 4864), ("q6k", 1024, 3072, 8192), ("q4k", 48, 3072, 768)]
+    runs = []
+    for fmt, M, N, K in shapes:
+        x = synthetic.activations(M, K, seed=M + 3 * K)
+        wq = synthetic.weight_blocks(fmt, N, K, seed=N + 11 * K)
+        runs.append((fmt, M, N, K, x, wq, dev(x), dev(wq.reshape(-1))))
+    def call(r, stream=None):
+        fmt, M, N, K, _, _, xd, wd = r
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        fn = dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k
+        fn(xd, wd, y, M, N, K, stream=stream)
+        return y
+    first = [call(r) for r in runs]
+    again = [call(r) for r in reversed(runs)][::-1]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        other = call(runs[2], stream=side.cuda_stream)
+    side.synchronize()
+    third = [call(r) for r in runs]
+    torch.cuda.synchronize()
+    for r, a, b, c in zip(runs, first, again, third):
+        assert torch.equal(a, b) and torch.equal(a, c), f"split-K bits changed across launches: {r[:4]}"
+    assert torch.equal(first[2], other), "split-K bits differ on a second stream"
+    for r, y in zip(runs, first):
+        fmt, M, N, K, x, wq = r[:6]
+        rows = np.arange(M) if M <= 64 else synthetic.row_sample(M, 8, seed=K)
+        ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
+        assert_within(y.cpu().numpy()[rows], ref, s, f"interleaved split-K {fmt} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 @pytest.mark.parametrize("M,N,K", [(2, 16, 256), (5, 37, 4864), (9, 33, 512), (16, 3072, 3072), (16, 48, 8192),
                                    (17, 100, 1280), (32, 257, 768)])
