@@ -293,14 +293,12 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // x rows are stored with their 16-byte chunks XOR-swizzled by (row >> 1) & 7:
 // a ds_read_b128 of one column by 16 consecutive rows then covers all 64
 // banks once (two rows share one 256-byte bank line).
-// Epilogue staging (fp32 y through LDS): each wave transposes its 32 x 64
-// block of one j-block in its own x buffer, rows padded to 68 floats so that
-// both the fragment writes and the row reads are free of bank conflicts.
-constexpr int EPI_STRIDE = 68;
-constexpr int EPI_BYTES = 32 * EPI_STRIDE * 4;
-
-// XCAP: bytes of each x buffer (the kernel's tallest tile).
-template <int FMT, int JB, int IB, bool SWIGLU, int XCAP>
+// The x fragment is the MFMA's A operand and the weight fragment its B
+// operand, so an accumulator lane holds one output column n (its lane % 32)
+// and 16 rows m: for a fixed accumulator register the 64 lanes hold 32
+// consecutive columns of two rows, and the epilogue's dword stores write
+// whole 128-byte lines of y straight from the accumulators.
+template <int FMT, int JB, int IB, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, int kb0, int nbk, void* out,
                                           uint8_t* x0, uint8_t* x1, uint8_t* x2, uint8_t* x3, float* tab) {
   typedef TileCfg<JB, IB> C;
@@ -416,7 +414,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
       for (int c = 0; c < IB; ++c)
-        acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], bm[jb], acc[jb][c], 0, 0, 0);
+        acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bm[jb], a[c], acc[jb][c], 0, 0, 0);
   };
   // spread the VALU work of the next fragment (va instructions per MFMA),
   // and nv VMEM loads, between this step's MFMAs
@@ -567,80 +565,49 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   // no direct-to-LDS load may still be in flight when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: the lane holds rows 8q + 4g + e (q, e = 0..3) of each i-block ----
-  if constexpr (!SWIGLU && IB == 2 && XCAP >= EPI_BYTES) {
-    // Through LDS, so that every global store writes whole 128-byte lines:
-    // a store instruction covers 4 rows x the wave's 64 columns (256 bytes
-    // each), where writing the accumulator fragments directly would touch
-    // 32 rows x 32 bytes.  Each wave uses its own x buffer; the barrier
-    // waits until every wave has read its last B fragments.
-    __syncthreads();
-    float* const st = (float*)(wave == 0 ? x0 : wave == 1 ? x1 : wave == 2 ? x2 : x3);
-    const int rr = lane >> 4, cc = 4 * (lane & 15);
-    const int n = n0 + 64 * wave + cc;
-    const bool vec = (N & 3) == 0 && n + 3 < N;
+  // ---- epilogue: register r of acc[jb][c] holds y[m][n], n = the lane's
+  // column of i-block c, m = m0 + 32 jb + 8 (r / 4) + 4 g + r % 4 ----
+  if constexpr (SWIGLU) {
+    // h[m][j] = silu(g) * u, j = hb + 32 w + li: gate in i-block 0, up in 1
+    const int j = hb + 32 * wave + li;
+    if (j < F) {
+      half_t* const hc = (half_t*)out + j;
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f16x& v = acc[jb][c];
-          *(float4*)(st + li * EPI_STRIDE + 32 * c + 8 * q + 4 * g) =
-              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (m < M) hc[(int64_t)m * F] = (half_t)(silu_fast(acc[jb][0][r]) * acc[jb][1][r]);
         }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = rr + 4 * i;
-        const int m = m0 + 32 * jb + r;
-        const float4 v = *(const float4*)(st + r * EPI_STRIDE + cc);
-        if (m < M) {
-          float* yrow = (float*)out + (int64_t)m * N;
-          if (vec) {
-            *(float4*)(yrow + n) = v;
-          } else {
-            const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (n + k < N) yrow[n + k] = e[k];
-          }
-        }
-      }
     }
   } else {
+    // Whole tile inside M and y below 4 GB: buffer stores, a scalar row
+    // offset plus the lane's fixed byte offset, no guard and no per-store
+    // address arithmetic in the lanes.
+    const bool fast = m0 + C::BM <= M && (int64_t)M * N < ((int64_t)1 << 30);
+    const rsrc_t yr = make_rsrc(out, 4 * (int64_t)M * N);
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const int m = m0 + 32 * jb + li;
-      if (m >= M) continue;
-      if (SWIGLU) {
-        half_t* h = (half_t*)out + (int64_t)m * F;
-        const f16x& gv = acc[jb][0];
-        const f16x& uv = acc[jb][1];
+    for (int c = 0; c < IB; ++c) {
+      const int n = n0 + 32 * IB * wave + 32 * c + li;
+      if (n >= N) continue;
+      if (fast) {
+        const uint32_t lo = 4u * (uint32_t)(4 * g * N + n);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = hb + 32 * wave + 8 * q + 4 * g;
-          h2 h01 = {(half_t)(silu_fast(gv[4 * q]) * uv[4 * q]), (half_t)(silu_fast(gv[4 * q + 1]) * uv[4 * q + 1])};
-          h2 h23 = {(half_t)(silu_fast(gv[4 * q + 2]) * uv[4 * q + 2]),
-                    (half_t)(silu_fast(gv[4 * q + 3]) * uv[4 * q + 3])};
-          *(uint2*)(h + col) = make_uint2(as_u32(h01), as_u32(h23));
-        }
-      } else {
-        float* yrow = (float*)out + (int64_t)m * N;
+        for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int c = 0; c < IB; ++c) {
-          const f16x& v = acc[jb][c];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = n0 + 32 * IB * wave + 32 * c + 8 * q + 4 * g;
-            if ((N & 3) == 0 && n + 3 < N) {
-              *(float4*)(yrow + n) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (n + e < N) yrow[n + e] = v[4 * q + e];
-            }
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t so = 4u * (uint32_t)(m0 + 32 * jb + 8 * (r >> 2) + (r & 3)) * (uint32_t)N;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[jb][c][r]), yr, lo, so, 0);
           }
-        }
+      } else {
+        float* const yc = (float*)out + n;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (m < M) yc[(int64_t)m * N] = acc[jb][c][r];
+          }
       }
     }
   }
@@ -677,12 +644,12 @@ __device__ __forceinline__ void run_tile(const GemmDesc& P, int m_tile, int n_ti
   const int nbk = left < P.kbs ? left : P.kbs;
   void* out = SWIGLU ? P.out : (void*)((float*)P.out + piece * P.out_stride);
   if constexpr (JBA == JBB) {
-    gemm_tile<FMT, JBA, 2, SWIGLU, TileCfg<JBA, 2>::XBUF>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+    gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
   } else {
     if (P.alt)
-      gemm_tile<FMT, JBB, 2, SWIGLU, TileCfg<JBA, 2>::XBUF>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+      gemm_tile<FMT, JBB, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
     else
-      gemm_tile<FMT, JBA, 2, SWIGLU, TileCfg<JBA, 2>::XBUF>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+      gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
   }
 }
 
