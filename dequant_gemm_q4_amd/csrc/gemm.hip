@@ -459,23 +459,27 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
     return hi - lo;
   };
 
-  // ---- prologue: block 0's table, x and raw bytes of the first chunks
+  // ---- prologue: block 0's table, x and raw bytes of the first chunks,
+  // issued chunk by chunk; only chunk 0's have to land before the first
+  // step (Q6_K: half 1 of block 0 is loaded by chunk 0 of the loop)
   if (tab_thread) hdr_load<FMT>(trow, hdr, hdr4);
+  if constexpr (FMT == 0) {
 #pragma unroll
-  for (int c = 0; c < IB; ++c) {
-    if constexpr (FMT == 0) {
+    for (int k = 0; k < 3; ++k) {
+      load_x(k, xb[k]);
 #pragma unroll
-      for (int k = 0; k < 3; ++k) raw_load_q4(wr[c], roff, k, rs[k][c]);
-    } else {
-      raw_load_q6(wr[c], roff, 0, 0, g, rs[0][c]);
-      raw_load_q6(wr[c], roff, 0, 1, g, rs[1][c]);
+      for (int c = 0; c < IB; ++c) raw_load_q4(wr[c], roff, k, rs[k][c]);
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < IB; ++c) raw_load_q6(wr[c], roff, 0, 0, g, rs[0][c]);
+    load_x(0, x0);
+    load_x(1, x1);
+    load_x(2, x2);
   }
-  load_x(0, x0);
-  load_x(1, x1);
-  load_x(2, x2);
   if (tab_thread) tab_store<FMT>(my_tab, hdr, hdr4);
-  wait_vm_barrier<0>();
+  if constexpr (FMT == 0) wait_vm_barrier<2 * (XQ + NRAW)>();
+  else wait_vm_barrier<2 * XQ>();
   read_scales();
   chunk_scales(0, sv);
 #pragma unroll
