@@ -17,7 +17,12 @@ benchmark must record"), so the oracle is pinned by:
 * RMSNorm (P12): rows with a closed-form root mean square, exact scale
   invariance under powers of two, linearity in the weight g, the eps offset
   on a zero row; the fp64-activation GEMM against the fp16 one where the
-  activations are fp16 values, and against numpy's matmul.
+  activations are fp16 values, and against numpy's matmul;
+* RoPE and grouped-query attention (P13): rotations with closed-form angles,
+  the identity at position 0, norm keeping, inversion, dependence on the
+  distance only; attention with one visible key, with equal keys, the
+  causal first query, the query-head-to-KV-head grouping, explicit loops,
+  and invariance under a common rotation.
 
 The k-quant byte layout is not on the pages; the blocks here are packed by
 ``tests/_packing.py`` from the public GGUF layout, so the layout pins check the
@@ -520,6 +525,137 @@ def test_p12_rmsnorm_interval_accepts_rounded_rejects_two_ulps():
     # an exact zero only accepts zero
     lo, hi = oracle.rmsnorm_f16_interval(np.zeros(3))
     assert np.all(lo == 0.0) and np.all(hi == 0.0)
+
+
+# ------------------------------------------------------------------ P13 ----
+# RoPE and grouped-query attention (oracle/attention.py).
+
+from oracle import attention as attn  # noqa: E402
+
+
+def test_p13_rope_closed_forms():
+    """Pair 0 has frequency 1: (1, 0) at position p becomes (cos p, sin p);
+    pair i at position p turns by p * theta^(-2i/d); position 0 is the
+    identity; frequency factors divide the angle."""
+    d = 8
+    v = np.zeros((4, 1, d))
+    v[:, 0, 0] = 1.0
+    pos = np.array([0, 1, 2, 3])
+    out = attn.rope(v, pos)
+    for i, p in enumerate(pos):
+        assert out[i, 0, 0] == pytest.approx(np.cos(p), abs=1e-15)
+        assert out[i, 0, 1] == pytest.approx(np.sin(p), abs=1e-15)
+        assert np.all(out[i, 0, 2:] == 0.0)
+    # pair 2 (dims 4, 5): angle p * theta^(-4/8); (0, 1) -> (-sin, cos)
+    v = np.zeros((1, 1, d))
+    v[0, 0, 5] = 1.0
+    a = 7 * 500000.0 ** (-0.5)
+    out = attn.rope(v, np.array([7]))
+    assert out[0, 0, 4] == pytest.approx(-np.sin(a), abs=1e-15)
+    assert out[0, 0, 5] == pytest.approx(np.cos(a), abs=1e-15)
+    rng = np.random.default_rng(1)
+    w = rng.standard_normal((3, 2, 16))
+    assert np.array_equal(attn.rope(w, np.zeros(3)), w)
+    f = rng.uniform(1.0, 8.0, 8)
+    lhs = attn.rope(w[:1], np.array([5.0]), freq_factors=f)
+    # the same rotation without factors, pair by pair, at position 5 / f_i
+    for i in range(8):
+        ref = attn.rope(w[:1], np.array([5.0 / f[i]]))
+        assert np.allclose(lhs[..., 2 * i:2 * i + 2], ref[..., 2 * i:2 * i + 2], atol=1e-13)
+
+
+def test_p13_rope_invariants():
+    """A rotation: pair norms are kept, rotating by -p undoes p, and the dot
+    product of a rotated query and key depends only on their distance."""
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((5, 3, 128))
+    k = rng.standard_normal((5, 3, 128))
+    pos = np.array([0, 1, 17, 1000, 131071])
+    rq = attn.rope(q, pos)
+    assert np.allclose(rq[..., 0::2] ** 2 + rq[..., 1::2] ** 2, q[..., 0::2] ** 2 + q[..., 1::2] ** 2, rtol=1e-12)
+    assert np.allclose(attn.rope(rq, -pos), q, atol=1e-9)
+    for shift in (3, 4096):
+        a = np.einsum("mhd,mhd->mh", attn.rope(q, pos), attn.rope(k, pos[::-1]))
+        b = np.einsum("mhd,mhd->mh", attn.rope(q, pos + shift), attn.rope(k, pos[::-1] + shift))
+        assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+def _attention_loops(q, kc, vc, pos0):
+    """Written out with Python loops and math.exp, for the brute-force pin."""
+    import math
+    m, hq, d = q.shape
+    group = hq // kc.shape[0]
+    out = np.zeros(q.shape)
+    for i in range(m):
+        for h in range(hq):
+            kv = h // group
+            n = pos0 + i + 1
+            s = [sum(q[i, h, e] * kc[kv, t, e] for e in range(d)) / math.sqrt(d) for t in range(n)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            tot = sum(w)
+            for e in range(d):
+                out[i, h, e] = sum(w[t] * vc[kv, t, e] for t in range(n)) / tot
+    return out
+
+
+def test_p13_attention_closed_forms():
+    """One visible key gives its value; equal keys give the mean of the
+    values; a prefill's first query sees only position 0; the query heads of
+    a group read their own KV head (6 query heads over 2 KV heads)."""
+    rng = np.random.default_rng(3)
+    d = 16
+    q = rng.standard_normal((1, 6, d))
+    kc = rng.standard_normal((2, 5, d))
+    vc = rng.standard_normal((2, 5, d))
+    out, _ = attn.attention_gqa(q, kc, vc, 0)
+    for h in range(6):
+        assert np.allclose(out[0, h], vc[h // 3, 0], atol=1e-15)
+    kc_eq = np.repeat(kc[:, :1, :], 5, axis=1)
+    out, _ = attn.attention_gqa(q, kc_eq, vc, 4)
+    for h in range(6):
+        assert np.allclose(out[0, h], vc[h // 3].mean(axis=0), atol=1e-14)
+    qp = rng.standard_normal((5, 6, d))
+    out, mass = attn.attention_gqa(qp, kc, vc, 0)
+    assert np.allclose(out[0], vc[np.arange(6) // 3, 0], atol=1e-15)
+    assert np.all(mass >= np.abs(out) - 1e-12)
+    vconst = np.zeros_like(vc)
+    vconst[0] = 1.0
+    vconst[1] = -2.0
+    out, _ = attn.attention_gqa(qp, kc, vconst, 0)
+    assert np.allclose(out[:, :3], 1.0) and np.allclose(out[:, 3:], -2.0)
+
+
+def test_p13_attention_scale():
+    """The softmax scale is 1/sqrt(d): a query whose score for key 1
+    exceeds that for key 0 by ln 3 after scaling weights them 3 : 1."""
+    d = 128
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = np.sqrt(d) * np.log(3.0)
+    kc = np.zeros((1, 2, d))
+    kc[0, 1, 0] = 1.0
+    vc = np.zeros((1, 2, d))
+    vc[0, 0, :] = 1.0
+    vc[0, 1, :] = 5.0
+    out, _ = attn.attention_gqa(q, kc, vc, 1)
+    assert np.allclose(out[0, 0], (1.0 + 3 * 5.0) / 4, rtol=1e-14)
+
+
+def test_p13_attention_bruteforce_and_shift():
+    """Against explicit loops on a small prefill with a cache offset, and
+    invariant under a common rotation of queries and keys (RoPE of both by
+    the same extra angle keeps every score)."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, 4, 8))
+    kc = rng.standard_normal((2, 9, 8))
+    vc = rng.standard_normal((2, 9, 8))
+    out, _ = attn.attention_gqa(q, kc, vc, 5)
+    assert np.allclose(out, _attention_loops(q, kc, vc, 5), rtol=1e-12, atol=1e-13)
+    s = 11
+    q2 = attn.rope(q, np.full(3, s))
+    kc2 = attn.rope(kc.reshape(18, 1, 8), np.full(18, s)).reshape(2, 9, 8)
+    out2, _ = attn.attention_gqa(q2, kc2, vc, 5)
+    assert np.allclose(out, out2, rtol=1e-10, atol=1e-12)
 
 
 # -------------------------------------------------------- generators -------
