@@ -31,8 +31,9 @@ FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
 
 # Every entry point declared in include/dmq.h.
 EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
-           "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_status_string",
-           "dmq_version")
+           "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
+           "dmq_attention_gqa", "dmq_residual_rmsnorm", "dmq_status_string", "dmq_version")
+HEAD_DIM = 128
 
 
 class DmqError(RuntimeError):
@@ -73,8 +74,12 @@ def _load() -> ctypes.CDLL:
     L.dmq_ffn_swiglu_q4k.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     L.dmq_gemm_group.argtypes = [ctypes.POINTER(GemmDesc), I32, P]
     L.dmq_rmsnorm_gemm.argtypes = [P, P, ctypes.c_float, P, I64, I64, ctypes.POINTER(ProjDesc), I32, P]
+    L.dmq_rope_kv_cache.argtypes = [P, P, P, I64, I64, I32, I32, ctypes.c_double, P, P, P, P, I64, P]
+    L.dmq_attention_gqa.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
+    L.dmq_residual_rmsnorm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, P]
     for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
-                 "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm"):
+                 "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
+                 "dmq_attention_gqa", "dmq_residual_rmsnorm"):
         getattr(L, name).restype = ctypes.c_int
     L.dmq_status_string.argtypes = [ctypes.c_int]
     L.dmq_status_string.restype = ctypes.c_char_p
@@ -232,6 +237,50 @@ def dmq_rmsnorm_gemm(x, g, eps: float, xn, projs, M: int, K: int, stream=None) -
                 raise ValueError(f"y[{i}] has {y.numel()} elements, expected {M * arr[i].N}")
     _check(lib.dmq_rmsnorm_gemm(px, pg, float(eps), pn, M, K, arr, len(arr), _stream(stream)),
            "dmq_rmsnorm_gemm")
+
+
+def dmq_rope_kv_cache(q, k, v, M: int, pos0: int, n_q_heads: int, n_kv_heads: int, q_out, k_cache, v_cache,
+                      cache_len: int, theta: float = 500000.0, freq_factors=None, stream=None) -> None:
+    """RoPE on q [M, Hq*128] and k [M, Hkv*128] (float32, positions pos0..pos0+M-1);
+    q_out float16 [M, Hq*128]; rotated k and v written as float16 into rows
+    pos0..pos0+M-1 of the caches [Hkv, cache_len, 128]."""
+    import torch
+    D = HEAD_DIM
+    pq = _dev_tensor(q, torch.float32, "q", M * n_q_heads * D)
+    pk = _dev_tensor(k, torch.float32, "k", M * n_kv_heads * D)
+    pv = _dev_tensor(v, torch.float32, "v", M * n_kv_heads * D)
+    pf = None if freq_factors is None else _dev_tensor(freq_factors, torch.float32, "freq_factors", D // 2)
+    po = _dev_tensor(q_out, torch.float16, "q_out", M * n_q_heads * D)
+    pkc = _dev_tensor(k_cache, torch.float16, "k_cache", n_kv_heads * cache_len * D)
+    pvc = _dev_tensor(v_cache, torch.float16, "v_cache", n_kv_heads * cache_len * D)
+    _check(lib.dmq_rope_kv_cache(pq, pk, pv, M, pos0, n_q_heads, n_kv_heads, float(theta), pf, po, pkc, pvc,
+                                 cache_len, _stream(stream)), "dmq_rope_kv_cache")
+
+
+def dmq_attention_gqa(q, k_cache, v_cache, out, M: int, pos0: int, n_q_heads: int, n_kv_heads: int,
+                      cache_len: int, stream=None) -> None:
+    """out float16 [M, Hq*128] <- causal grouped-query attention of q (float16,
+    positions pos0..pos0+M-1) over the caches [Hkv, cache_len, 128]."""
+    import torch
+    D = HEAD_DIM
+    pq = _dev_tensor(q, torch.float16, "q", M * n_q_heads * D)
+    pkc = _dev_tensor(k_cache, torch.float16, "k_cache", n_kv_heads * cache_len * D)
+    pvc = _dev_tensor(v_cache, torch.float16, "v_cache", n_kv_heads * cache_len * D)
+    po = _dev_tensor(out, torch.float16, "out", M * n_q_heads * D)
+    _check(lib.dmq_attention_gqa(pq, pkc, pvc, po, M, pos0, n_q_heads, n_kv_heads, cache_len, _stream(stream)),
+           "dmq_attention_gqa")
+
+
+def dmq_residual_rmsnorm(h_in, y, g, eps: float, h_out, xn, M: int, K: int, stream=None) -> None:
+    """h_out = h_in + y (float32 [M, K]); with g (float32 [K]) also
+    xn float16 [M, K] = RMSNorm(h_out; g, eps).  g=None: the add only."""
+    import torch
+    ph = _dev_tensor(h_in, torch.float32, "h_in", M * K)
+    py = _dev_tensor(y, torch.float32, "y", M * K)
+    po = _dev_tensor(h_out, torch.float32, "h_out", M * K)
+    pg = None if g is None else _dev_tensor(g, torch.float32, "g", K)
+    pn = None if g is None else _dev_tensor(xn, torch.float16, "xn", M * K)
+    _check(lib.dmq_residual_rmsnorm(ph, py, pg, float(eps), po, pn, M, K, _stream(stream)), "dmq_residual_rmsnorm")
 
 
 def dmq_version() -> int:

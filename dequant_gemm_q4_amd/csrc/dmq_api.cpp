@@ -12,6 +12,7 @@
 #include <mutex>
 #include <string_view>
 
+#include "attention.h"
 #include "dmq_common.h"
 
 namespace {
@@ -250,6 +251,56 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
     if (st != DMQ_OK) return st;
   }
   return run_gemm(probs, count, decode, (hipStream_t)stream);
+}
+
+static bool heads_ok(int32_t hq, int32_t hkv) {
+  return hq >= 1 && hkv >= 1 && hq <= 1024 && hq % hkv == 0 && hq / hkv <= 8;
+}
+
+// KV-cache geometry: [hkv, cache_len, 128] fp16, positions pos0 .. pos0+M-1 inside it.
+static bool cache_ok(int64_t M, int64_t pos0, int32_t hkv, int64_t cache_len) {
+  return dim_ok(M) && pos0 >= 0 && dim_ok(cache_len) && pos0 + M <= cache_len &&
+         (int64_t)hkv * cache_len * 128 <= (int64_t(1) << 40) && M * 1024 * 128 <= (int64_t(1) << 40);
+}
+
+int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M, int64_t pos0, int32_t n_q_heads,
+                      int32_t n_kv_heads, double theta, const float* freq_factors, void* q_f16, void* k_cache_f16,
+                      void* v_cache_f16, int64_t cache_len, void* stream) {
+  if (!q || !k || !v || !q_f16 || !k_cache_f16 || !v_cache_f16) return DMQ_ERR_INVALID_ARG;
+  if (!heads_ok(n_q_heads, n_kv_heads) || !cache_ok(M, pos0, n_kv_heads, cache_len)) return DMQ_ERR_INVALID_ARG;
+  if (!(theta > 1.0) || theta > 1e30) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_f16, 16) || !aligned(k_cache_f16, 16) ||
+      !aligned(v_cache_f16, 16) || (freq_factors && !aligned(freq_factors, 4)))
+    return DMQ_ERR_ALIGNMENT;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(dmq::launch_rope_kv(q, k, v, freq_factors, q_f16, k_cache_f16, v_cache_f16, theta, cache_len, M,
+                                        pos0, n_q_heads, n_kv_heads, (hipStream_t)stream));
+}
+
+int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16, int64_t M,
+                      int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, void* stream) {
+  if (!q_f16 || !k_cache_f16 || !v_cache_f16 || !out_f16 || out_f16 == q_f16) return DMQ_ERR_INVALID_ARG;
+  if (!heads_ok(n_q_heads, n_kv_heads) || !cache_ok(M, pos0, n_kv_heads, cache_len)) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(q_f16, 16) || !aligned(k_cache_f16, 16) || !aligned(v_cache_f16, 16) || !aligned(out_f16, 16))
+    return DMQ_ERR_ALIGNMENT;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(dmq::launch_attention(q_f16, k_cache_f16, v_cache_f16, out_f16, cache_len, M, pos0, n_q_heads,
+                                          n_kv_heads, (hipStream_t)stream));
+}
+
+int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, float eps, float* h_out, void* xn_f16,
+                         int64_t M, int64_t K, void* stream) {
+  if (!h_in || !y || !h_out || (g && !xn_f16)) return DMQ_ERR_INVALID_ARG;
+  if (g && (!(eps >= 0.0f) || eps > 3.0e38f)) return DMQ_ERR_INVALID_ARG;
+  if (!dim_ok(M) || check_quant_k(K) != DMQ_OK || K > kMaxK || M * K > (int64_t(1) << 40)) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(h_in, 16) || !aligned(y, 16) || !aligned(h_out, 16) || (g && (!aligned(g, 16) || !aligned(xn_f16, 16))))
+    return DMQ_ERR_ALIGNMENT;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(dmq::launch_residual_rmsnorm(h_in, y, g, eps, h_out, g ? xn_f16 : nullptr, M, K,
+                                                 (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -188,6 +188,61 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
                      int64_t M, int64_t K, const dmq_proj_desc* projs, int32_t count,
                      void* stream);
 
+/*
+ * The attention side of a decoder layer (overview page, "[04] one decode step":
+ * RMSNorm -> QKV projection -> RoPE -> attention over the KV cache (GQA) ->
+ * residual add -> RMSNorm -> SwiGLU FFN -> residual add; model table: 24 query
+ * heads, 8 KV heads, head dimension 128, RoPE theta 500000).  The head
+ * dimension is 128 in all three calls.  The KV cache of one layer is two
+ * caller-owned fp16 arrays [n_kv_heads, cache_len, 128]; position p of KV head
+ * h is row h * cache_len + p.
+ */
+
+/*
+ * RoPE on the Q and K projections of M tokens at positions pos0 .. pos0+M-1,
+ * and their K and V rows appended to the cache.
+ *   q, k, v      : fp32 [M, n_q_heads*128], [M, n_kv_heads*128] (the projection
+ *                  outputs y), 16-byte aligned.
+ *   theta        : RoPE base (> 1; 500000 for the pages' model).
+ *   freq_factors : NULL, or 64 floats f_i dividing the angle of pair i.
+ *   q_f16        : [M, n_q_heads*128] fp16 output, the rotated queries.
+ *   k_cache_f16, v_cache_f16 : the layer's cache; rows pos0 .. pos0+M-1 of
+ *                  every KV head are written (K rotated, V as is), nothing else.
+ * Pair i of a head is (dims 2i, 2i+1), turned by pos * theta^(-2i/128) / f_i:
+ * (a, b) -> (a cos - b sin, a sin + b cos).  The angle is formed and reduced in
+ * fp64, the rotation done in fp32 and each result rounded once to fp16.
+ * Requires pos0 >= 0, pos0 + M <= cache_len, n_q_heads a multiple of n_kv_heads
+ * with at most 8 query heads per KV head.
+ */
+int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M, int64_t pos0, int32_t n_q_heads,
+                      int32_t n_kv_heads, double theta, const float* freq_factors, void* q_f16, void* k_cache_f16,
+                      void* v_cache_f16, int64_t cache_len, void* stream);
+
+/*
+ * Causal grouped-query attention of M queries (positions pos0 .. pos0+M-1)
+ * over the cache: query head h reads KV head h / (n_q_heads / n_kv_heads); the
+ * query at position p attends to cache positions 0..p with weights
+ * softmax(q . k / sqrt(128)).
+ *   q_f16   : [M, n_q_heads*128] fp16 (from dmq_rope_kv_cache).
+ *   out_f16 : [M, n_q_heads*128] fp16 output (the O projection's input), not q.
+ * The cache rows 0 .. pos0+M-1 must have been written.  Scores, softmax and
+ * the weighted sum of V are fp32; the output is rounded once to fp16.
+ */
+int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16, int64_t M,
+                      int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, void* stream);
+
+/*
+ * The residual connection, fused with the RMSNorm that follows it:
+ *   h_out = h_in + y (fp32, one rounding per element; h_out may be h_in or y);
+ *   with g: xn_f16 = fp16(h_out * g / sqrt(mean(h_out^2) + eps)), computed in
+ *   fp32 and rounded once, the input of the next projections.  g == NULL: the
+ *   add only (xn_f16 unused).
+ *   h_in, y, h_out : fp32 [M, K], K a multiple of 256; g: K floats; all 16-byte
+ *   aligned.
+ */
+int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, float eps, float* h_out, void* xn_f16,
+                         int64_t M, int64_t K, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* dmq_status_string(int status);
 

@@ -11,6 +11,8 @@ the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 * RMSNorm (fp64, no intermediate rounding) and the GEMM on its fp64 output
   are C as well; the fp16 acceptance interval of a normalized activation is
   numpy here.
+* RoPE, grouped-query attention over a KV cache and the residual add are
+  fp64 numpy in ``attention.py``.
 
 Sources (DAMASCUS pages): the dequantisers and the quantised matmul are the
 overview page's compartment 09 ("[02] the pipeline") and the article's
@@ -353,6 +355,16 @@ def rmsnorm_gemm_quant(fmt: str, x: np.ndarray, g: np.ndarray, eps: float, wq: n
 # root and a division, two products.  2^-16 relative covers that with margin
 # for K up to 2^16 and stays below one fp16 ulp (2^-10 relative).
 RMSNORM_REL_SLACK = 2.0 ** -16
+
+
+def f16_interval(exact: np.ndarray, abs_slack: np.ndarray):
+    """Acceptance interval [lo16, hi16] (fp16 values as fp64) for an fp16
+    result whose exact value is ``exact`` and whose computation before the
+    final rounding may be off by ``abs_slack``: the fp16 grid points around
+    [exact - abs_slack, exact + abs_slack], rounded outward."""
+    e = np.asarray(exact, np.float64)
+    sl = np.asarray(abs_slack, np.float64)
+    return _fp16_grid_down(e - sl), _fp16_grid_up(e + sl)
 
 
 def rmsnorm_f16_interval(xhat: np.ndarray, rel_slack: float = RMSNORM_REL_SLACK):

@@ -81,6 +81,14 @@ def attention_gqa(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos0:
     return out, mass
 
 
+def rmsnorm_f64(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of the rows of x taken as they are (e.g. an fp32 residual
+    stream): x * g / sqrt(mean(x^2) + eps), all in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    return x * g / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
 def residual_add(y: np.ndarray, r: np.ndarray) -> np.ndarray:
     """The residual connection: y + r in fp64."""
     return np.asarray(y, dtype=np.float64) + np.asarray(r, dtype=np.float64)

@@ -641,6 +641,17 @@ def test_p13_attention_scale():
     assert np.allclose(out[0, 0], (1.0 + 3 * 5.0) / 4, rtol=1e-14)
 
 
+def test_p13_rmsnorm_f64_matches_c_oracle_and_closed_forms():
+    """The numpy RMSNorm for fp32 rows equals the C oracle's on rows of fp16
+    values, and a constant row c gives g * sign(c) up to eps."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 512)).astype(np.float16)
+    g = rng.uniform(0.5, 1.5, 512).astype(np.float32)
+    assert np.allclose(attn.rmsnorm_f64(x, g, 1e-5), oracle.rmsnorm(x, g, 1e-5), rtol=1e-14, atol=0)
+    row = np.full((1, 256), -3.0)
+    assert np.allclose(attn.rmsnorm_f64(row, np.ones(256), 0.0), -1.0, rtol=1e-15)
+
+
 def test_p13_attention_bruteforce_and_shift():
     """Against explicit loops on a small prefill with a cache offset, and
     invariant under a common rotation of queries and keys (RoPE of both by

@@ -612,3 +612,245 @@ def test_rmsnorm_qkv_layer_shapes_sampled(dmq):
     _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, "rmsnorm QKV M=1024", rows=rows)
     xn1, ys1 = _rmsnorm_gemm(dmq, x[:1], g, 1e-5, projs, 1, K)
     _check_rmsnorm_outputs(x[:1], g, 1e-5, projs, K, xn1, ys1, "rmsnorm QKV M=1")
+
+
+# -------------------------------------------------------------------------
+# The attention side of a decoder layer: RoPE + KV-cache append, grouped-query
+# attention over the cache, residual add fused with the next RMSNorm.  Each
+# stage is checked against the oracle on the GPU's own inputs to that stage;
+# the layer chain at the end adds an end-to-end comparison with the fp64
+# oracle layer.
+
+from oracle import attention as attn  # noqa: E402
+
+D_HEAD = 128
+
+
+def _rope_case(dmq, M, pos0, hq, hkv, cache_len, seed, freq_factors=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((M, hq * D_HEAD)).astype(np.float32)
+    k = rng.standard_normal((M, hkv * D_HEAD)).astype(np.float32)
+    v = rng.standard_normal((M, hkv * D_HEAD)).astype(np.float32)
+    sentinel = np.float16(7.0)
+    kc = torch.full((hkv, cache_len, D_HEAD), sentinel, dtype=torch.float16, device=DEV)
+    vc = torch.full((hkv, cache_len, D_HEAD), sentinel, dtype=torch.float16, device=DEV)
+    qo = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    ff = None if freq_factors is None else dev(freq_factors.astype(np.float32))
+    dmq.dmq_rope_kv_cache(dev(q), dev(k), dev(v), M, pos0, hq, hkv, qo, kc, vc, cache_len, freq_factors=ff)
+    torch.cuda.synchronize()
+    return q, k, v, qo.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), sentinel
+
+
+def _check_rope(q, k, v, qo, kc, vc, sentinel, M, pos0, hq, hkv, what, freq_factors=None):
+    pos = np.arange(pos0, pos0 + M)
+    for src, got, h in ((q, qo.reshape(M, hq, D_HEAD), hq),
+                        (k, kc[:, pos0:pos0 + M, :].transpose(1, 0, 2), hkv)):
+        x = src.reshape(M, h, D_HEAD).astype(np.float64)
+        exact = attn.rope(x, pos, freq_factors=freq_factors)
+        # fp32 cos/sin (one rounding each) and the fp32 rotation: a few units
+        # of 2^-24 of the pair's magnitude before the final fp16 rounding
+        mag = np.repeat(np.abs(x[..., 0::2]) + np.abs(x[..., 1::2]), 2, axis=-1)
+        lo, hi = oracle.f16_interval(exact, mag * 2.0 ** -21)
+        g64 = got.astype(np.float64)
+        ok = (g64 >= lo) & (g64 <= hi)
+        assert ok.all(), f"{what}: {int((~ok).sum())} of {ok.size} rotated values outside the interval"
+    # V rows: fp16 of the fp32 projection, bit for bit
+    want_v = v.reshape(M, hkv, D_HEAD).astype(np.float16).transpose(1, 0, 2)
+    assert np.array_equal(vc[:, pos0:pos0 + M, :].view(np.uint16), want_v.view(np.uint16)), f"{what}: V rows differ"
+    # nothing outside rows pos0 .. pos0+M-1 is touched
+    for c in (kc, vc):
+        outside = np.concatenate([c[:, :pos0, :].ravel(), c[:, pos0 + M:, :].ravel()])
+        assert np.all(outside == sentinel), f"{what}: cache rows outside the written range changed"
+
+
+@pytest.mark.parametrize("M,pos0,hq,hkv,cache_len", [(1, 0, 24, 8, 8), (1, 1023, 24, 8, 1024), (7, 100, 24, 8, 200),
+                                                     (64, 0, 24, 8, 64), (3, 131000, 6, 2, 131072),
+                                                     (5, 17, 8, 8, 40), (2, 9, 16, 2, 16)])
+def test_rope_kv_cache(dmq, M, pos0, hq, hkv, cache_len):
+    q, k, v, qo, kc, vc, sent = _rope_case(dmq, M, pos0, hq, hkv, cache_len, seed=M * 31 + pos0)
+    _check_rope(q, k, v, qo, kc, vc, sent, M, pos0, hq, hkv, f"rope M={M} pos0={pos0} hq={hq} hkv={hkv}")
+
+
+def test_rope_kv_cache_freq_factors(dmq):
+    # the factors as the kernel receives them (fp32); the oracle takes the same values
+    f = np.random.default_rng(9).uniform(1.0, 32.0, D_HEAD // 2).astype(np.float32)
+    q, k, v, qo, kc, vc, sent = _rope_case(dmq, 4, 5000, 24, 8, 5004, seed=99, freq_factors=f)
+    _check_rope(q, k, v, qo, kc, vc, sent, 4, 5000, 24, 8, "rope with frequency factors", freq_factors=f)
+
+
+def _attention_case(dmq, M, pos0, hq, hkv, cache_len, seed, spread=1.0):
+    rng = np.random.default_rng(seed)
+    n = pos0 + M
+    q = (rng.standard_normal((M, hq * D_HEAD)) * spread).astype(np.float16)
+    kc = np.zeros((hkv, cache_len, D_HEAD), np.float16)
+    vc = np.zeros((hkv, cache_len, D_HEAD), np.float16)
+    kc[:, :n, :] = (rng.standard_normal((hkv, n, D_HEAD)) * spread).astype(np.float16)
+    vc[:, :n, :] = rng.standard_normal((hkv, n, D_HEAD)).astype(np.float16)
+    out = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    dmq.dmq_attention_gqa(dev(q), dev(kc), dev(vc), out, M, pos0, hq, hkv, cache_len)
+    torch.cuda.synchronize()
+    return q, kc, vc, out.cpu().numpy()
+
+
+def _check_attention(q, kc, vc, out, M, pos0, hq, what):
+    q3 = q.reshape(M, hq, D_HEAD).astype(np.float64)
+    ref, mass = attn.attention_gqa(q3, kc, vc, pos0)
+    got = out.reshape(M, hq, D_HEAD).astype(np.float64)
+    # final fp16 rounding (2^-11 relative), fp32 exp / sums (5e-4 of the
+    # output's scale sum p|v|), and the fp32 scores: a 128-term fp32 dot is
+    # off by at most 128 * 2^-24 * sum |q k| / sqrt(128), which moves every
+    # weight by that factor in the exponent (twice the largest such error
+    # times sum p|v| bounds the output change)
+    hkv = kc.shape[0]
+    grp = hq // hkv
+    ds = np.zeros((M, hq, 1))
+    for h in range(hq):
+        kabs = np.abs(kc[h // grp].astype(np.float64))
+        for i in range(M):
+            n = pos0 + i + 1
+            ds[i, h, 0] = 128 * 2.0 ** -24 * np.max(kabs[:n] @ np.abs(q3[i, h])) / np.sqrt(D_HEAD)
+    tol = 2.0 ** -10 * np.abs(ref) + (5e-4 + 2.0 * ds) * mass + 1e-6
+    err = np.abs(got - ref)
+    ok = err <= tol
+    worst = float(np.max(err / tol))
+    assert ok.all(), f"{what}: {int((~ok).sum())} of {ok.size} outputs outside the bound (worst {worst:.3g})"
+    print(f"{what}: max err/bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,pos0,hq,hkv,cache_len", [(1, 0, 24, 8, 16), (1, 1023, 24, 8, 1024), (1, 4096, 24, 8, 5000),
+                                                     (7, 100, 24, 8, 128), (64, 0, 24, 8, 64), (3, 1500, 6, 2, 2048),
+                                                     (33, 600, 8, 8, 700), (5, 511, 16, 2, 600),
+                                                     (4, 20, 4, 4, 32), (2, 7, 5, 1, 9)])
+def test_attention_gqa(dmq, M, pos0, hq, hkv, cache_len):
+    """Decode (M = 1) at several cache lengths, chunk boundaries (512 keys),
+    prefill blocks with and without an offset, and every group size from 1
+    to 8 query heads per KV head."""
+    q, kc, vc, out = _attention_case(dmq, M, pos0, hq, hkv, cache_len, seed=M * 13 + pos0)
+    _check_attention(q, kc, vc, out, M, pos0, hq, f"attention M={M} pos0={pos0} hq={hq} hkv={hkv}")
+
+
+def test_attention_gqa_peaked_scores(dmq):
+    """Large score spread (one key dominates, many weights underflow) and a
+    run of 3 decode steps appending to the same cache."""
+    q, kc, vc, out = _attention_case(dmq, 2, 900, 24, 8, 1024, seed=5, spread=4.0)
+    _check_attention(q, kc, vc, out, 2, 900, 24, "attention peaked")
+
+
+def test_residual_rmsnorm(dmq):
+    rng = np.random.default_rng(21)
+    for M, K in ((1, 3072), (5, 768), (64, 3072)):
+        h = rng.standard_normal((M, K)).astype(np.float32)
+        y = (rng.standard_normal((M, K)) * 3.0).astype(np.float32)
+        g = _norm_weights(K, seed=K + M)
+        ho = torch.empty((M, K), dtype=torch.float32, device=DEV)
+        xn = torch.empty((M, K), dtype=torch.float16, device=DEV)
+        dmq.dmq_residual_rmsnorm(dev(h), dev(y), dev(g), 1e-5, ho, xn, M, K)
+        # in place, add only
+        hin = dev(h)
+        dmq.dmq_residual_rmsnorm(hin, dev(y), None, 0.0, hin, None, M, K)
+        torch.cuda.synchronize()
+        hgot = ho.cpu().numpy()
+        assert np.array_equal(hgot, h + y), f"residual M={M}: h_out is not the fp32 sum"
+        assert np.array_equal(hin.cpu().numpy(), h + y), f"residual M={M}: in-place add differs"
+        xhat = attn.rmsnorm_f64(hgot, g, 1e-5)
+        lo, hi = oracle.rmsnorm_f16_interval(xhat)
+        got = xn.cpu().numpy().astype(np.float64)
+        ok = (got >= lo) & (got <= hi)
+        assert ok.all(), f"residual+rmsnorm M={M}: {int((~ok).sum())} normalized values outside the interval"
+
+
+@pytest.mark.parametrize("M,pos0", [(1, 37), (16, 0), (5, 200)])
+def test_decoder_layer_chain(dmq, M, pos0):
+    """One decoder layer through the library on a small Llama-shaped layer
+    (hidden 768 = 6 query heads x 128, 2 KV heads, FFN 1024): RMSNorm ->
+    Q|K|V -> RoPE + cache -> attention -> O projection -> residual + RMSNorm
+    -> SwiGLU FFN -> residual.  Each new stage is checked on its own GPU
+    inputs, and the layer output against the fp64 oracle layer fed the same
+    weights, inputs and cache (end to end, 1% of the output norm)."""
+    Dm, hq, hkv, F = 768, 6, 2, 1024
+    cache_len = pos0 + M + 3
+    rng = np.random.default_rng(M * 7 + pos0)
+    x = rng.standard_normal((M, Dm)).astype(np.float32)
+    # small RMSNorm weights: the synthetic Q4_K/Q6_K weights are large (up to
+    # ~20), so unit-scale inputs would give scores in the tens of thousands
+    g1 = (0.02 * _norm_weights(Dm, 1)).astype(np.float32)
+    # small FFN input weights: the synthetic Q4_K/Q6_K weights are large (up
+    # to ~20), and the fp16 hidden values must stay finite for the
+    # end-to-end comparison
+    g2 = (0.05 * _norm_weights(Dm, 2)).astype(np.float32)
+    wq_ = synthetic.q4k_blocks(hq * D_HEAD, Dm, seed=11)
+    wk_ = synthetic.q4k_blocks(hkv * D_HEAD, Dm, seed=12)
+    wv_ = synthetic.q6k_blocks(hkv * D_HEAD, Dm, seed=13)
+    wo_ = synthetic.q4k_blocks(Dm, hq * D_HEAD, seed=14)
+    wgu = synthetic.q4k_blocks(2 * F, Dm, seed=15)
+    wd_ = synthetic.q6k_blocks(Dm, F, seed=16)
+    # earlier positions of the cache: rotated keys and values of earlier tokens
+    kc0 = np.zeros((hkv, cache_len, D_HEAD), np.float16)
+    vc0 = np.zeros((hkv, cache_len, D_HEAD), np.float16)
+    kc0[:, :pos0] = (rng.standard_normal((hkv, pos0, D_HEAD)) * 2).astype(np.float16)
+    vc0[:, :pos0] = rng.standard_normal((hkv, pos0, D_HEAD)).astype(np.float16)
+
+    t = lambda a: dev(a)  # noqa: E731
+    xd = t(x)
+    xn1 = torch.empty((M, Dm), dtype=torch.float16, device=DEV)
+    dmq.dmq_residual_rmsnorm(xd, torch.zeros_like(xd), t(g1), 1e-5, torch.empty_like(xd), xn1, M, Dm)
+    yq = torch.empty((M, hq * D_HEAD), dtype=torch.float32, device=DEV)
+    yk = torch.empty((M, hkv * D_HEAD), dtype=torch.float32, device=DEV)
+    yv = torch.empty((M, hkv * D_HEAD), dtype=torch.float32, device=DEV)
+    dmq.dmq_gemm_group([("q4k", xn1, t(wq_.reshape(-1)), yq, M, hq * D_HEAD, Dm),
+                        ("q4k", xn1, t(wk_.reshape(-1)), yk, M, hkv * D_HEAD, Dm),
+                        ("q6k", xn1, t(wv_.reshape(-1)), yv, M, hkv * D_HEAD, Dm)])
+    kc, vc = t(kc0), t(vc0)
+    qr = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    dmq.dmq_rope_kv_cache(yq, yk, yv, M, pos0, hq, hkv, qr, kc, vc, cache_len)
+    att = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    dmq.dmq_attention_gqa(qr, kc, vc, att, M, pos0, hq, hkv, cache_len)
+    yo = torch.empty((M, Dm), dtype=torch.float32, device=DEV)
+    dmq.dmq_gemm_q4k(att, t(wo_.reshape(-1)), yo, M, Dm, hq * D_HEAD)
+    h1 = torch.empty((M, Dm), dtype=torch.float32, device=DEV)
+    xn2 = torch.empty((M, Dm), dtype=torch.float16, device=DEV)
+    dmq.dmq_residual_rmsnorm(xd, yo, t(g2), 1e-5, h1, xn2, M, Dm)
+    hf = torch.empty((M, F), dtype=torch.float16, device=DEV)
+    yd = torch.empty((M, Dm), dtype=torch.float32, device=DEV)
+    dmq.dmq_ffn_swiglu_q4k(xn2, t(wgu.reshape(-1)), t(wd_.reshape(-1)), hf, yd, M, Dm, F)
+    out = torch.empty((M, Dm), dtype=torch.float32, device=DEV)
+    dmq.dmq_residual_rmsnorm(h1, yd, None, 0.0, out, None, M, Dm)
+    torch.cuda.synchronize()
+    cpu = lambda a: a.cpu().numpy()  # noqa: E731
+
+    # stage checks on the GPU's own stage inputs
+    q_, k_, v_ = cpu(yq), cpu(yk), cpu(yv)
+    kc_, vc_ = cpu(kc), cpu(vc)
+    pos = np.arange(pos0, pos0 + M)
+    exact_q = attn.rope(q_.reshape(M, hq, D_HEAD), pos)
+    lo, hi = oracle.f16_interval(exact_q, np.repeat(np.abs(q_.reshape(M, hq, D_HEAD)[..., 0::2])
+                                                    + np.abs(q_.reshape(M, hq, D_HEAD)[..., 1::2]), 2, axis=-1) * 2.0 ** -21)
+    qg = cpu(qr).reshape(M, hq, D_HEAD).astype(np.float64)
+    assert np.all((qg >= lo) & (qg <= hi)), "layer: rotated queries outside the interval"
+    assert np.array_equal(kc_[:, :pos0], kc0[:, :pos0]), "layer: earlier cache rows changed"
+    _check_attention(cpu(qr), kc_, vc_, cpu(att), M, pos0, hq, "layer attention")
+    ref_o, s_o = oracle.gemm_quant("q4k", cpu(att), wo_, Dm, hq * D_HEAD)
+    assert_within(cpu(yo), ref_o, s_o, "layer O projection")
+    assert np.array_equal(cpu(h1), x + cpu(yo)), "layer: first residual is not the fp32 sum"
+    assert np.isfinite(cpu(hf).astype(np.float32)).all(), "layer: fp16 FFN hidden values overflowed"
+    assert np.array_equal(cpu(out), cpu(h1) + cpu(yd)), "layer: second residual is not the fp32 sum"
+
+    # end to end: the fp64 oracle layer on the same weights, input and cache
+    xh1 = attn.rmsnorm_f64(x, g1, 1e-5)
+    W = lambda fmt, wq, n, k: oracle.f16_bits_to_f64(oracle.dequant(fmt, wq, n, k))  # noqa: E731
+    Wq = W("q4k", wq_, hq * D_HEAD, Dm); Wk = W("q4k", wk_, hkv * D_HEAD, Dm); Wv = W("q6k", wv_, hkv * D_HEAD, Dm)  # noqa: E702
+    Wo = W("q4k", wo_, Dm, hq * D_HEAD); Wgu = W("q4k", wgu, 2 * F, Dm); Wd = W("q6k", wd_, Dm, F)  # noqa: E702
+    Q = attn.rope((xh1 @ Wq.T).reshape(M, hq, D_HEAD), pos)
+    Kn = attn.rope((xh1 @ Wk.T).reshape(M, hkv, D_HEAD), pos)
+    Vn = (xh1 @ Wv.T).reshape(M, hkv, D_HEAD)
+    Kc = kc0.astype(np.float64); Vc = vc0.astype(np.float64)  # noqa: E702
+    Kc[:, pos0:pos0 + M] = Kn.transpose(1, 0, 2); Vc[:, pos0:pos0 + M] = Vn.transpose(1, 0, 2)  # noqa: E702
+    A, _ = attn.attention_gqa(Q, Kc, Vc, pos0)
+    H1 = attn.residual_add(x, A.reshape(M, -1) @ Wo.T)
+    xh2 = attn.rmsnorm_f64(H1, g2, 1e-5)
+    G = xh2 @ Wgu[:F].T
+    U = xh2 @ Wgu[F:].T
+    OUT = attn.residual_add(H1, (oracle.silu(G) * U) @ Wd.T)
+    rel = np.linalg.norm(cpu(out) - OUT) / np.linalg.norm(OUT)
+    print(f"layer M={M} pos0={pos0}: end-to-end relative error {rel:.3g}")
+    assert rel < 1e-2, f"layer output differs from the fp64 oracle layer by {rel:.3g} of its norm"
