@@ -249,6 +249,106 @@ def sweep(torch, dmq):
                       "ms": round(ms, 4), "TFLOP/s": round(2.0 * M * N * K / ms / 1e9, 1)}), flush=True)
 
 
+def layer_chain_sweep(torch, dmq):
+    """A whole decoder layer through the library (RMSNorm -> Q|K|V -> RoPE +
+    KV cache -> attention -> O projection -> residual + RMSNorm -> SwiGLU FFN
+    -> residual), Llama-3.2-3B shapes, weights rotated over several seeded
+    layers: the decode step (M = 1, graph replay) at two context lengths and
+    the M = 1024 prefill (host-launched); the attention kernel alone; the
+    decode LM head."""
+    dev = "cuda"
+    D, F, HQ, HKV, HD = synthetic.HIDDEN, synthetic.FFN, synthetic.N_HEADS, synthetic.N_KV_HEADS, synthetic.HEAD_DIM
+    rng = np.random.default_rng(1234)
+    g1 = torch.from_numpy((0.02 * rng.uniform(0.5, 1.5, D)).astype(np.float32)).to(dev)
+    g2 = torch.from_numpy((0.05 * rng.uniform(0.5, 1.5, D)).astype(np.float32)).to(dev)
+
+    def weights(layer):
+        w = {name: (fmt, wq) for name, fmt, N, K, wq in synthetic.layer_weights(4, layer)}
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to(dev)  # noqa: E731
+        return {"q": t(w["q"][1]), "k": t(w["k"][1]), "v": t(w["v"][1]), "o": t(w["o"][1]),
+                "gu": t(np.concatenate([w["gate"][1], w["up"][1]], axis=0)), "down": t(w["down"][1])}
+
+    def buffers(M):
+        e = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+        x = torch.from_numpy(rng.standard_normal((M, D)).astype(np.float32)).to(dev)
+        return {"x": x, "zero": torch.zeros_like(x), "h0": e(M, D), "xn1": e(M, D, dt=torch.float16),
+                "yq": e(M, HQ * HD), "yk": e(M, HKV * HD), "yv": e(M, HKV * HD),
+                "qr": e(M, HQ * HD, dt=torch.float16), "att": e(M, HQ * HD, dt=torch.float16), "yo": e(M, D),
+                "h1": e(M, D), "xn2": e(M, D, dt=torch.float16), "hf": e(M, F, dt=torch.float16), "yd": e(M, D),
+                "out": e(M, D)}
+
+    # one layer of a stack: xn1 = RMSNorm(x) comes from the previous layer's
+    # last call (residual add fused with this layer's input RMSNorm), which
+    # this layer's last call repeats for the next one (in place on x)
+    def step(W, B, kc, vc, M, pos0, L):
+        dmq.dmq_gemm_group(W["qkv"])
+        dmq.dmq_rope_kv_cache(B["yq"], B["yk"], B["yv"], M, pos0, HQ, HKV, B["qr"], kc, vc, L)
+        dmq.dmq_attention_gqa(B["qr"], kc, vc, B["att"], M, pos0, HQ, HKV, L)
+        dmq.dmq_gemm_q4k(B["att"], W["o"], B["yo"], M, D, HQ * HD)
+        dmq.dmq_residual_rmsnorm(B["x"], B["yo"], g2, 1e-5, B["h1"], B["xn2"], M, D)
+        dmq.dmq_ffn_swiglu_q4k(B["xn2"], W["gu"], W["down"], B["hf"], B["yd"], M, D, F)
+        dmq.dmq_residual_rmsnorm(B["h1"], B["yd"], g1, 1e-5, B["x"], B["xn1"], M, D)
+
+    def make(nl, M, L):
+        Ws = [weights(l) for l in range(nl)]
+        B = buffers(M)
+        for W in Ws:
+            W["qkv"] = dmq.make_group([("q4k", B["xn1"], W["q"], B["yq"], M, HQ * HD, D),
+                                       ("q4k", B["xn1"], W["k"], B["yk"], M, HKV * HD, D),
+                                       ("q4k", B["xn1"], W["v"], B["yv"], M, HKV * HD, D)])
+        caches = [(torch.zeros((HKV, L, HD), dtype=torch.float16, device=dev),
+                   torch.zeros((HKV, L, HD), dtype=torch.float16, device=dev)) for _ in range(nl)]
+        for kc, vc in caches:   # earlier tokens' keys and values
+            kc.normal_()
+            vc.normal_()
+        dmq.dmq_residual_rmsnorm(B["x"], B["zero"], g1, 1e-5, B["h0"], B["xn1"], M, D)
+        return Ws, B, caches
+
+    # decode step, 8 rotating layers, graph replay
+    for L in (1024, 4096):
+        pos0 = L - 1
+        Ws, B, caches = make(8, 1, L)
+        items = list(zip(Ws, caches))
+        us = time_graph(torch, lambda it: step(it[0], B, it[1][0], it[1][1], 1, pos0, L), items, 8) * 1e3
+        # the attention kernel alone at this context
+        ua = time_graph(torch, lambda it: dmq.dmq_attention_gqa(B["qr"], it[1][0], it[1][1], B["att"], 1, pos0,
+                                                                HQ, HKV, L), items, 8) * 1e3
+        kv_bytes = 2 * HKV * L * HD * 2
+        print(json.dumps({"sweep": f"decode step, one Llama-3.2-3B layer, all kernels (graph replay, 8 rotating layers), "
+                                   f"context {L}", "us_per_layer": round(us, 2),
+                          "attention_us": round(ua, 2), "attention_kv_GB/s": round(kv_bytes / ua / 1e3, 1)}),
+              flush=True)
+        del Ws, B, caches, items
+    # LM head at M = 1 (decode): 323 MB of Q6_K
+    name, fmt, N, K = synthetic.LM_HEAD
+    wl = torch.from_numpy(synthetic.lm_head_weights(4).reshape(-1)).to(dev)
+    x1 = torch.from_numpy(synthetic.activations(1, K, seed=3)).to(dev)
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    ul = time_graph(torch, lambda w: dmq.dmq_gemm_q6k(x1, w, y1, 1, N, K), [wl], 8) * 1e3
+    print(json.dumps({"sweep": "decode LM head Q6_K 128256x3072, M=1 (graph replay)", "us": round(ul, 2),
+                      "GB/s": round(wl.numel() / ul / 1e3, 1)}), flush=True)
+    del wl
+    # prefill M = 1024 from position 0, 3 rotating layers, host-launched
+    M, L = 1024, 1024
+    Ws, B, caches = make(3, M, L)
+    it = [0]
+
+    def one():
+        W, (kc, vc) = Ws[it[0] % 3], caches[it[0] % 3]
+        it[0] += 1
+        step(W, B, kc, vc, M, 0, L)
+    ms = _timed(torch, one, reps=10, warm=3)
+    it[0] = 0
+    ma = _timed(torch, lambda: dmq.dmq_attention_gqa(B["qr"], caches[0][0], caches[0][1], B["att"], M, 0, HQ, HKV, L),
+                reps=10, warm=2)
+    att_flop = 4.0 * HQ * HD * (M * (M + 1) / 2)
+    gemm_flop = flops_of(M)
+    print(json.dumps({"sweep": "prefill, one Llama-3.2-3B layer, all kernels (host-launched, 3 rotating layers), M=1024",
+                      "ms_per_layer": round(ms, 4), "attention_ms": round(ma, 4),
+                      "attention_TFLOP/s": round(att_flop / ma / 1e9, 2),
+                      "layer_TFLOP/s": round((gemm_flop + att_flop) / ms / 1e9, 1)}), flush=True)
+
+
 def layer_problems(torch, dmq, config, layer, M, xs, ys):
     probs = []
     for name, fmt, N, K, wq in synthetic.layer_weights(config, layer):
@@ -326,7 +426,9 @@ def time_graph(torch, launch, groups, replays):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    # captured on the stream that ran the launches above, so that any
+    # per-stream workspace the library keeps already exists
+    with torch.cuda.graph(graph, stream=side):
         for g in groups:
             launch(g)
     settle(torch, graph.replay, 2, chunk=5)
@@ -370,6 +472,8 @@ def main():
                     help="only run a plain copy of known size (counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="only measure the other configurations (M=16, FFN, M sweep, LM head) and exit")
+    ap.add_argument("--layer", action="store_true",
+                    help="only time whole decoder layers (decode step and prefill) through the library and exit")
     ap.add_argument("--vendor-gemm-probe", action="store_true",
                     help="only time dense fp16 torch.matmul on the layer shapes (reference) and exit")
     args = ap.parse_args()
@@ -391,6 +495,10 @@ def main():
     if args.sweep:
         import dequant_gemm_q4_amd as dmq
         sweep(torch, dmq)
+        layer_chain_sweep(torch, dmq)
+        return
+    if args.layer:
+        layer_chain_sweep(torch, dmq)
         return
     M = M_PREFILL
 

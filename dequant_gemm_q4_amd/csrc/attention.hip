@@ -12,6 +12,9 @@
 
 #include <math.h>
 
+#include <mutex>
+#include <vector>
+
 namespace dmq {
 
 constexpr int HEAD_DIM = 128;
@@ -35,9 +38,13 @@ struct RopeArgs {
   int32_t pos0, hq, hkv;
 };
 
+// grid: (token, unit): units 0 .. ceil(Hq/8)-1 take 8 query heads each, the
+// following ones 8 KV heads (K and V) each.
+constexpr int ROPE_UNIT = 8;
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   __shared__ float cs[HEAD_DIM / 2], sn[HEAD_DIM / 2];
-  const int m = blockIdx.x, tid = threadIdx.x;
+  const int m = blockIdx.x, unit = blockIdx.y, tid = threadIdx.x;
+  const int uq = (a.hq + ROPE_UNIT - 1) / ROPE_UNIT;
   const int64_t pos = (int64_t)a.pos0 + m;
   if (tid < HEAD_DIM / 2) {
     double inv = pow(a.theta, -2.0 * tid / HEAD_DIM);
@@ -56,17 +63,25 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
       ((h2*)dst)[p] = o;
     }
   };
-  rot(a.q + (int64_t)m * a.hq * HEAD_DIM, a.q_out + (int64_t)m * a.hq * HEAD_DIM, a.hq * HEAD_DIM / 2);
+  if (unit < uq) {
+    const int h0 = unit * ROPE_UNIT, nh = a.hq - h0 < ROPE_UNIT ? a.hq - h0 : ROPE_UNIT;
+    const int64_t off = ((int64_t)m * a.hq + h0) * HEAD_DIM;
+    rot(a.q + off, a.q_out + off, nh * HEAD_DIM / 2);
+    return;
+  }
   // K (rotated) and V go to row `pos` of each KV head's cache
-  for (int h = 0; h < a.hkv; ++h) {
-    const int64_t row = ((int64_t)h * a.cache_len + pos) * HEAD_DIM;
-    rot(a.k + ((int64_t)m * a.hkv + h) * HEAD_DIM, a.k_cache + row, HEAD_DIM / 2);
-    const float* vs = a.v + ((int64_t)m * a.hkv + h) * HEAD_DIM;
-    for (int d = tid; d < HEAD_DIM / 2; d += 256) {
-      const float2 x = ((const float2*)vs)[d];
-      const h2 o = {(half_t)x.x, (half_t)x.y};
-      ((h2*)(a.v_cache + row))[d] = o;
-    }
+  const int k0 = (unit - uq) * ROPE_UNIT, k1 = k0 + ROPE_UNIT < a.hkv ? k0 + ROPE_UNIT : a.hkv;
+  for (int p = tid; p < (k1 - k0) * (HEAD_DIM / 2); p += 256) {
+    const int h = k0 + p / (HEAD_DIM / 2), i = p % (HEAD_DIM / 2);
+    const int64_t src = ((int64_t)m * a.hkv + h) * HEAD_DIM + 2 * i;
+    const int64_t row = ((int64_t)h * a.cache_len + pos) * HEAD_DIM + 2 * i;
+    const float2 x = *(const float2*)(a.k + src);
+    const float c = cs[i], sv = sn[i];
+    const h2 ko = {(half_t)(x.x * c - x.y * sv), (half_t)(x.x * sv + x.y * c)};
+    *(h2*)(a.k_cache + row) = ko;
+    const float2 v = *(const float2*)(a.v + src);
+    const h2 vo = {(half_t)v.x, (half_t)v.y};
+    *(h2*)(a.v_cache + row) = vo;
   }
 }
 
@@ -75,7 +90,8 @@ hipError_t launch_rope_kv(const float* q, const float* k, const float* v, const 
                           hipStream_t s) {
   RopeArgs a{q, k, v, ff, (half_t*)q_out, (half_t*)k_cache, (half_t*)v_cache, theta, cache_len,
              (int32_t)pos0, hq, hkv};
-  hipLaunchKernelGGL(rope_kv_kernel, dim3((unsigned)M), dim3(256), 0, s, a);
+  const unsigned units = (unsigned)((hq + ROPE_UNIT - 1) / ROPE_UNIT + (hkv + ROPE_UNIT - 1) / ROPE_UNIT);
+  hipLaunchKernelGGL(rope_kv_kernel, dim3((unsigned)M, units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -93,6 +109,7 @@ hipError_t launch_rope_kv(const float* q, const float* k, const float* v, const 
 //    256 contiguous bytes by 128 threads.
 // The two halves are added at the end and o / sum is rounded to fp16.
 constexpr int ATT_CH = 512;
+constexpr int ATT_SPLIT_MAX_M = 16;   // up to this many queries: the split (decode) path
 
 struct AttnArgs {
   const half_t* q;         // [M, Hq*128] fp16 (after RoPE)
@@ -225,10 +242,242 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
       a.out[((int64_t)m * a.hq + kv * G + g) * HEAD_DIM + d] = (half_t)((o[g] + ohalf[g][d]) / sum[g]);
 }
 
+// Few queries (decode): the positions are split into pieces of SPLIT_S, one
+// workgroup per (piece, KV head, query), so that a decode step has hundreds
+// of workgroups instead of one per KV head.  Each piece writes its partial
+// softmax state (maximum, sum of weights, weighted sum of V) for each query
+// head to a workspace; a second kernel merges the pieces in piece order.
+constexpr int SPLIT_S = 64;
+constexpr int MERGE_MAX_PIECES = 4096;    // pieces the merge stages in LDS (262144 positions)
+constexpr int SPLIT_REC = HEAD_DIM + 2;   // floats per (query head, piece): o[128], max, sum
+
+template <int G>
+__global__ __launch_bounds__(256) void attention_split_kernel(AttnArgs a, float* ws, int nsplit) {
+  __shared__ __attribute__((aligned(16))) float qs[G][HEAD_DIM];
+  __shared__ float ps[G][SPLIT_S];
+  __shared__ float st[G][2];
+  __shared__ float vsl[8][G][HEAD_DIM];
+  const int sp = blockIdx.x, kv = blockIdx.y, m = blockIdx.z, tid = threadIdx.x;
+  const int n = a.pos0 + m + 1;
+  const int c0 = sp * SPLIT_S;
+  if (c0 >= n) return;   // no positions: the merge reads pieces < ceil(n / SPLIT_S) only
+  const int cn = n - c0 < SPLIT_S ? n - c0 : SPLIT_S;
+  const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
+  for (int i = tid; i < G * HEAD_DIM; i += 256)
+    qs[i / HEAD_DIM][i % HEAD_DIM] = (float)a.q[((int64_t)m * a.hq + kv * G) * HEAD_DIM + i] * scale;
+  const half_t* kc = a.k_cache + (int64_t)kv * a.cache_len * HEAD_DIM;
+  const half_t* vc = a.v_cache + (int64_t)kv * a.cache_len * HEAD_DIM;
+  __syncthreads();
+  // scores: 4 threads per position, 32 dimensions each, summed across the quad
+  {
+    const int t = tid >> 2, part = tid & 3;
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = 0.0f;
+    if (t < cn) {
+      const uint4* kr = (const uint4*)(kc + (int64_t)(c0 + t) * HEAD_DIM + 32 * part);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 kw = kr[i];
+        const uint32_t w4[4] = {kw.x, kw.y, kw.z, kw.w};
+        float kf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2 kp = as_h2(w4[e]);
+          kf[2 * e] = (float)kp.x;
+          kf[2 * e + 1] = (float)kp.y;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float* qg = &qs[g][32 * part + 8 * i];
+          float acc = s[g];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qg[e], kf[e], acc);
+          s[g] = acc;
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s[g] += __shfl_xor(s[g], 1, 64);
+      s[g] += __shfl_xor(s[g], 2, 64);
+      if (part == 0 && t < cn) ps[g][t] = s[g];
+    }
+  }
+  __syncthreads();
+  // the piece's softmax state per head: wave 0, one lane per position
+  if (tid < 64) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float v = tid < cn ? ps[g][tid] : -INFINITY;
+      float mx = v;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      const float p = tid < cn ? __expf(v - mx) : 0.0f;
+      float sum = p;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      if (tid < cn) ps[g][tid] = p;
+      if (tid == 0) {
+        st[g][0] = mx;
+        st[g][1] = sum;
+      }
+    }
+  }
+  __syncthreads();
+  // weighted sum of V: thread (slice, q4) takes dims 4 q4 .. +3 of positions
+  // slice, slice + 8, ... (8 loads in flight), the 8 slices summed in order
+  const int q4 = tid & 31, slice = tid >> 5;
+  float o[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[g][e] = 0.0f;
+  uint2 vr[SPLIT_S / 8];
+#pragma unroll
+  for (int u = 0; u < SPLIT_S / 8; ++u) {
+    const int t = slice + 8 * u;
+    vr[u] = t < cn ? *(const uint2*)(vc + (int64_t)(c0 + t) * HEAD_DIM + 4 * q4) : make_uint2(0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < SPLIT_S / 8; ++u) {
+    const int t = slice + 8 * u;
+    if (t < cn) {
+      const h2 v01 = as_h2(vr[u].x), v23 = as_h2(vr[u].y);
+      const float vv[4] = {(float)v01.x, (float)v01.y, (float)v23.x, (float)v23.y};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = ps[g][t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[g][e] = __builtin_fmaf(p, vv[e], o[g][e]);
+      }
+    }
+  }
+  __syncthreads();   // ps no longer read: reuse ohalf as the slices' staging
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vsl[slice][g][4 * q4 + e] = o[g][e];
+  __syncthreads();
+  for (int i = tid; i < G * HEAD_DIM; i += 256) {
+    const int g = i / HEAD_DIM, dd = i % HEAD_DIM;
+    float acc = vsl[0][g][dd];
+#pragma unroll
+    for (int sl = 1; sl < 8; ++sl) acc += vsl[sl][g][dd];
+    float* rec = ws + (((int64_t)m * a.hq + kv * G + g) * nsplit + sp) * SPLIT_REC;
+    rec[dd] = acc;
+    if (dd == 0) {
+      rec[HEAD_DIM] = st[g][0];
+      rec[HEAD_DIM + 1] = st[g][1];
+    }
+  }
+}
+
+// Merge of the pieces of one (query, query head), in piece order: rescale
+// each piece's sums to the overall maximum and divide.  The pieces' maxima
+// and sums are read in parallel into LDS first; the weighted sums of V are
+// then read 8 pieces at a time, so the loads overlap.
+__global__ __launch_bounds__(128) void attention_merge_kernel(AttnArgs a, const float* ws, int nsplit) {
+  __shared__ float fac[MERGE_MAX_PIECES];
+  __shared__ float red[2];
+  const int h = blockIdx.x, m = blockIdx.y, d = threadIdx.x;
+  const int n = a.pos0 + m + 1;
+  const int np = (n + SPLIT_S - 1) / SPLIT_S;
+  const float* rec = ws + ((int64_t)m * a.hq + h) * nsplit * SPLIT_REC;
+  float mx = -INFINITY;
+  for (int i = d; i < np; i += 128) {
+    fac[i] = rec[i * SPLIT_REC + HEAD_DIM];
+    mx = fmaxf(mx, fac[i]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  for (int i = d; i < np; i += 128) fac[i] = __expf(fac[i] - mx);   // the thread's own entries
+  __syncthreads();
+  float sum = 0.0f, o = 0.0f;
+  int i = 0;
+  for (; i + 8 <= np; i += 8) {
+    float ov[8], sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ov[u] = rec[(i + u) * SPLIT_REC + d];
+      sv[u] = rec[(i + u) * SPLIT_REC + HEAD_DIM + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sum = __builtin_fmaf(sv[u], fac[i + u], sum);
+      o = __builtin_fmaf(ov[u], fac[i + u], o);
+    }
+  }
+  for (; i < np; ++i) {
+    sum = __builtin_fmaf(rec[i * SPLIT_REC + HEAD_DIM + 1], fac[i], sum);
+    o = __builtin_fmaf(rec[i * SPLIT_REC + d], fac[i], o);
+  }
+  a.out[((int64_t)m * a.hq + h) * HEAD_DIM + d] = (half_t)(o / sum);
+}
+
+// Workspace of the split path: one buffer per (device, stream), grown on
+// demand and kept until the process ends (as the GEMMs' split-K workspace).
+static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) {
+  static std::mutex mu;
+  struct Ws {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+  };
+  static std::vector<Ws> pool;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  for (auto& w : pool) {
+    if (w.dev != dev || w.stream != s) continue;
+    if (w.bytes < bytes) {
+      if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;   // earlier launches may still use it
+      if ((err = hipFree(w.ptr)) != hipSuccess) return err;
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if ((err = hipMalloc(&w.ptr, bytes)) != hipSuccess) return err;
+      w.bytes = bytes;
+    }
+    *out = (float*)w.ptr;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  if ((err = hipMalloc(&p, bytes)) != hipSuccess) return err;
+  pool.push_back(Ws{dev, s, p, bytes});
+  *out = (float*)p;
+  return hipSuccess;
+}
+
 hipError_t launch_attention(const void* q, const void* k_cache, const void* v_cache, void* out, int64_t cache_len,
                             int64_t M, int64_t pos0, int hq, int hkv, hipStream_t s) {
   AttnArgs a{(const half_t*)q, (const half_t*)k_cache, (const half_t*)v_cache, (half_t*)out, cache_len,
              (int32_t)pos0, hq, hkv};
+  const int64_t nsplit64 = (pos0 + M + SPLIT_S - 1) / SPLIT_S;
+  if (M <= ATT_SPLIT_MAX_M && nsplit64 <= MERGE_MAX_PIECES) {
+    const int nsplit = (int)nsplit64;
+    float* ws = nullptr;
+    hipError_t e = attention_workspace(s, (size_t)M * hq * nsplit * SPLIT_REC * sizeof(float), &ws);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)nsplit, (unsigned)hkv, (unsigned)M);
+    switch (hq / hkv) {
+      case 1: hipLaunchKernelGGL(attention_split_kernel<1>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      case 2: hipLaunchKernelGGL(attention_split_kernel<2>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      case 3: hipLaunchKernelGGL(attention_split_kernel<3>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      case 4: hipLaunchKernelGGL(attention_split_kernel<4>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      case 5: hipLaunchKernelGGL(attention_split_kernel<5>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      case 6: hipLaunchKernelGGL(attention_split_kernel<6>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      case 7: hipLaunchKernelGGL(attention_split_kernel<7>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+      default: hipLaunchKernelGGL(attention_split_kernel<8>, grid, dim3(256), 0, s, a, ws, nsplit); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)hq, (unsigned)M), dim3(HEAD_DIM), 0, s, a, ws, nsplit);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)M, (unsigned)hkv);
   switch (hq / hkv) {
     case 1: hipLaunchKernelGGL(attention_kernel<1>, grid, dim3(256), 0, s, a); break;

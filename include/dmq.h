@@ -227,6 +227,11 @@ int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M,
  *   out_f16 : [M, n_q_heads*128] fp16 output (the O projection's input), not q.
  * The cache rows 0 .. pos0+M-1 must have been written.  Scores, softmax and
  * the weighted sum of V are fp32; the output is rounded once to fp16.
+ * With M <= 16 (decode) the positions are split into pieces of 64 over many
+ * workgroups whose partial softmax states a second kernel merges in piece
+ * order; the states go to a workspace the library keeps per (device, stream),
+ * allocated and grown like the GEMMs' split-K workspace (same rule under
+ * graph capture).  Every path gives the same bits on every run.
  */
 int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16, int64_t M,
                       int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, void* stream);
