@@ -453,6 +453,168 @@ static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) 
   return hipSuccess;
 }
 
+// Many queries (prefill): MFMA flash attention.  One workgroup = 4 waves =
+// 128 consecutive queries of one query head; wave w owns queries
+// 32w .. 32w+31 of the block and keeps them as MFMA operands for the whole
+// key loop.  Keys go in blocks of 32, staged in LDS by the workgroup (K row-
+// major with 16-byte chunks XOR-swizzled by the key, V transposed to
+// [dim][key]) and double-buffered.  Per key block and wave, with
+// v_mfma_f32_32x32x16_f16 (D = A B^T):
+//  * S^T = K Q^T (A = K rows, B = Q rows, 8 MFMAs over the 128 dims): an
+//    accumulator lane holds one query (its lane % 32) and 16 of the 32 keys,
+//    the lane 32 away the other 16, so a query's maximum and sum need one
+//    exchange between the two lanes;
+//  * online softmax in fp32 on exp2 with log2(e)/sqrt(128) folded into the
+//    scores; keys past a query's position are masked to -inf;
+//  * O^T += V^T P^T (A = V^T rows, B = P rows, 2 key steps x 4 dim blocks):
+//    the key order inside a 16-key step is permuted the same way for both
+//    operands so that P's B fragment is 8 consecutive accumulator registers,
+//    converted to fp16.
+// The 128 dims of O^T stay in 64 accumulator registers per lane; at the end
+// O / sum is rounded to fp16 and stored.
+constexpr int FA_KB = 32;                 // keys per block
+constexpr int FA_QB = 128;                // queries per workgroup
+constexpr int FA_VT_STRIDE = 40;          // halves per V^T row (32 keys + pad)
+
+typedef float f16acc __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, int nqb) {
+  __shared__ __attribute__((aligned(16))) half_t ks[2][FA_KB * HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) half_t vt[2][HEAD_DIM * FA_VT_STRIDE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, g = lane >> 5;
+  const int qb = nqb - 1 - (int)blockIdx.x;   // the longest (latest) query blocks first
+  const int h = blockIdx.y;
+  const int G = a.hq / a.hkv;
+  const int kvh = h / G;
+  const int q0 = qb * FA_QB;                  // first query (row of q) of the block
+  const int qw = q0 + 32 * wave;              // first query of this wave
+  const int64_t pos_q = (int64_t)a.pos0 + qw + li;   // this lane's query position
+  const half_t* kc = a.k_cache + (int64_t)kvh * a.cache_len * HEAD_DIM;
+  const half_t* vc = a.v_cache + (int64_t)kvh * a.cache_len * HEAD_DIM;
+
+  // Q fragments (B operand of S^T): query qw + li, dims 16 kk + 8 g .. +7
+  h8 qf[HEAD_DIM / 16];
+  {
+    const bool ok = qw + li < M;
+    const half_t* qr = a.q + ((int64_t)(qw + li) * a.hq + h) * HEAD_DIM + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < HEAD_DIM / 16; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ok) v = *(const uint4*)(qr + 16 * kk);
+      qf[kk] = __builtin_bit_cast(h8, v);
+    }
+  }
+  // keys needed: positions 0 .. last query position of the workgroup
+  const int qlast = (q0 + FA_QB < M ? q0 + FA_QB : M) - 1;
+  const int64_t nkeys = (int64_t)a.pos0 + qlast + 1;
+  const int nkb = (int)((nkeys + FA_KB - 1) / FA_KB);
+  // a wave is done with key blocks past its last query
+  const int qwl = (qw + 31 < M ? qw + 31 : M - 1);
+  const int64_t wave_last_pos = (int64_t)a.pos0 + qwl;
+
+  // staging of key block kb into buffer b: thread t takes 16-byte chunks t
+  // and t + 256 of the block's K and V (32 keys x 128 dims)
+  auto stage = [&](int kb, int b) {
+    const int64_t k0 = (int64_t)kb * FA_KB;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cidx = tid + 256 * u;
+      const int key = cidx >> 4, ch = cidx & 15;
+      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+      if (k0 + key < nkeys) {
+        kv4 = *(const uint4*)(kc + (k0 + key) * HEAD_DIM + 8 * ch);
+        vv4 = *(const uint4*)(vc + (k0 + key) * HEAD_DIM + 8 * ch);
+      }
+      *(uint4*)(&ks[b][key * HEAD_DIM + 8 * (ch ^ (key & 15))]) = kv4;
+      const half_t* vh = (const half_t*)&vv4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[b][(8 * ch + e) * FA_VT_STRIDE + key] = vh[e];
+    }
+  };
+
+  f16acc o[HEAD_DIM / 32];
+#pragma unroll
+  for (int db = 0; db < HEAD_DIM / 32; ++db) o[db] = (f16acc){};
+  float mrun = -INFINITY, lrun = 0.0f;
+  const float c = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
+
+  stage(0, 0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int b = kb & 1;
+    if (kb + 1 < nkb) stage(kb + 1, b ^ 1);   // the other buffer was released by the last barrier
+    const int64_t k0 = (int64_t)kb * FA_KB;
+    if (k0 <= wave_last_pos) {
+      // S^T = K Q^T
+      f16acc sacc = (f16acc){};
+#pragma unroll
+      for (int kk = 0; kk < HEAD_DIM / 16; ++kk) {
+        const int ch = 2 * kk + g;
+        const h8 kf = *(const h8*)(&ks[b][li * HEAD_DIM + 8 * (ch ^ (li & 15))]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
+      }
+      // scores, causal mask, block maximum of this lane's query
+      float sv[16];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float v = key <= pos_q ? sacc[r] * c : -INFINITY;
+        sv[r] = v;
+        bm = fmaxf(bm, v);
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mnew = fmaxf(mrun, bm);
+      // a query with no key in this block yet (mnew = -inf) keeps its state
+      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+      float ps = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = mnew == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - mnew);
+        sv[r] = p;
+        ps += p;
+      }
+      ps += __shfl_xor(ps, 32, 64);
+      lrun = lrun * alpha + ps;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < HEAD_DIM / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      // O^T += V^T P^T, two 16-key steps
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        h8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (half_t)sv[8 * kk + e];
+#pragma unroll
+        for (int db = 0; db < HEAD_DIM / 32; ++db) {
+          const half_t* vr = &vt[b][(32 * db + li) * FA_VT_STRIDE + 16 * kk + 4 * g];
+          const uint2 lo = *(const uint2*)vr;         // keys 16kk + 4g + 0..3
+          const uint2 hi = *(const uint2*)(vr + 8);   // keys 16kk + 8 + 4g + 0..3
+          const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, w), pf, o[db], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();   // buffer b is free, buffer b^1 is staged
+  }
+  // O = O^T / sum: lane holds query qw + li, dims 32 db + 8 (r/4) + 4 g + r % 4
+  if (qw + li < M) {
+    const float inv = 1.0f / lrun;
+    half_t* orow = a.out + ((int64_t)(qw + li) * a.hq + h) * HEAD_DIM;
+#pragma unroll
+    for (int db = 0; db < HEAD_DIM / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const h2 x01 = {(half_t)(o[db][4 * q4] * inv), (half_t)(o[db][4 * q4 + 1] * inv)};
+        const h2 x23 = {(half_t)(o[db][4 * q4 + 2] * inv), (half_t)(o[db][4 * q4 + 3] * inv)};
+        *(uint2*)(orow + 32 * db + 8 * q4 + 4 * g) = make_uint2(as_u32(x01), as_u32(x23));
+      }
+  }
+}
+
 hipError_t launch_attention(const void* q, const void* k_cache, const void* v_cache, void* out, int64_t cache_len,
                             int64_t M, int64_t pos0, int hq, int hkv, hipStream_t s) {
   AttnArgs a{(const half_t*)q, (const half_t*)k_cache, (const half_t*)v_cache, (half_t*)out, cache_len,
@@ -476,6 +638,11 @@ hipError_t launch_attention(const void* q, const void* k_cache, const void* v_ca
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)hq, (unsigned)M), dim3(HEAD_DIM), 0, s, a, ws, nsplit);
+    return hipGetLastError();
+  }
+  if (M > ATT_SPLIT_MAX_M) {
+    const int nqb = (int)((M + FA_QB - 1) / FA_QB);
+    hipLaunchKernelGGL(attention_mfma_kernel, dim3((unsigned)nqb, (unsigned)hq), dim3(256), 0, s, a, (int)M, nqb);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)M, (unsigned)hkv);

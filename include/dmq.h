@@ -227,6 +227,9 @@ int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M,
  *   out_f16 : [M, n_q_heads*128] fp16 output (the O projection's input), not q.
  * The cache rows 0 .. pos0+M-1 must have been written.  Scores, softmax and
  * the weighted sum of V are fp32; the output is rounded once to fp16.
+ * With M > 16 (prefill) an MFMA flash-attention kernel takes 128 queries of
+ * one head per workgroup over 32-key blocks (online softmax in fp32, P
+ * rounded to fp16 for the P V product).
  * With M <= 16 (decode) the positions are split into pieces of 64 over many
  * workgroups whose partial softmax states a second kernel merges in piece
  * order; the states go to a workspace the library keeps per (device, stream),

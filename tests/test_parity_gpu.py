@@ -729,6 +729,28 @@ def test_attention_gqa(dmq, M, pos0, hq, hkv, cache_len):
     _check_attention(q, kc, vc, out, M, pos0, hq, f"attention M={M} pos0={pos0} hq={hq} hkv={hkv}")
 
 
+@pytest.mark.parametrize("M,pos0,hq,hkv", [(17, 0, 24, 8), (300, 50, 24, 8), (129, 1000, 6, 2), (200, 3, 8, 1)])
+def test_attention_gqa_prefill_mfma(dmq, M, pos0, hq, hkv):
+    """More than 16 queries run the MFMA kernel (128 queries per workgroup,
+    32-key blocks): ragged query blocks, a cache offset, the causal diagonal
+    inside blocks, group sizes 3, 1 and 8."""
+    q, kc, vc, out = _attention_case(dmq, M, pos0, hq, hkv, pos0 + M + 5, seed=M + pos0)
+    _check_attention(q, kc, vc, out, M, pos0, hq, f"attention prefill M={M} pos0={pos0} hq={hq} hkv={hkv}")
+
+
+def test_attention_gqa_prefill_full_size_sampled(dmq):
+    """The Llama-3.2-3B prefill shape (1024 queries from position 0, 24 query
+    heads over 8 KV heads), every output of a sample of query rows that
+    covers every 128-query block and both ends."""
+    M, hq, hkv = 1024, 24, 8
+    q, kc, vc, out = _attention_case(dmq, M, 0, hq, hkv, M, seed=77)
+    rows = synthetic.row_sample(M, 24, seed=3, tile=128)
+    # the oracle on the sampled rows: each row's attention depends only on its
+    # own query and the cache
+    for r in rows:
+        _check_attention(q[r:r + 1], kc, vc, out[r:r + 1], 1, int(r), hq, f"attention prefill 1024 row {r}")
+
+
 def test_attention_gqa_peaked_scores(dmq):
     """Large score spread (one key dominates, many weights underflow) and a
     run of 3 decode steps appending to the same cache."""
