@@ -46,7 +46,7 @@ SETTLE_MS = 150.0              # untimed GPU work before any timed region (clock
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": "ed69830a2146fd2de13ea918c077f85df33afb32f619b25d88d632ff2d93ee3a", "bytes_per_launch": 619415092}
+TRAFFIC = {"sources_sha256": "1305205177e265fb316edb8a106ba9f6e02b8e76551184af473b45adf1d6f132", "bytes_per_launch": 619831867}
 COPY_PROBE_BYTES = 256 << 20
 
 
