@@ -21,6 +21,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-source additions.  attention.hip: keep MFMA accumulators in VGPRs; the
+# flash-attention loop rescales its output accumulators with VALU ops, and in
+# AGPRs each rescale costs a copy out and back (and pushes the kernel past 256
+# registers, one wave per SIMD).
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -30,7 +37,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -474,13 +474,15 @@ static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) 
 // O / sum is rounded to fp16 and stored.
 constexpr int FA_KB = 32;                 // keys per block
 constexpr int FA_QB = 128;                // queries per workgroup
-constexpr int FA_VT_STRIDE = 40;          // halves per V^T row (32 keys + pad)
+constexpr int FA_VT_WORDS = 18;           // 32-bit words per V^T row (16 key pairs + pad)
+// V^T word swizzle: rows 32..63 and 96..127 swap the two 8-word halves
+__device__ __forceinline__ int fa_vt_swz(int row) { return 8 * ((row >> 5) & 1); }
 
 typedef float f16acc __attribute__((ext_vector_type(16)));
 
 __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, int nqb) {
   __shared__ __attribute__((aligned(16))) half_t ks[2][FA_KB * HEAD_DIM];
-  __shared__ __attribute__((aligned(16))) half_t vt[2][HEAD_DIM * FA_VT_STRIDE];
+  __shared__ __attribute__((aligned(16))) half_t vt[2][HEAD_DIM * 2 * FA_VT_WORDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, g = lane >> 5;
   const int qb = nqb - 1 - (int)blockIdx.x;   // the longest (latest) query blocks first
@@ -513,23 +515,49 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
   const int qwl = (qw + 31 < M ? qw + 31 : M - 1);
   const int64_t wave_last_pos = (int64_t)a.pos0 + qwl;
 
-  // staging of key block kb into buffer b: thread t takes 16-byte chunks t
-  // and t + 256 of the block's K and V (32 keys x 128 dims)
-  auto stage = [&](int kb, int b) {
+  // staging of a key block (32 keys x 128 dims of K and of V).  K: thread t
+  // holds 16-byte chunks t and t + 256 (key = chunk / 16, dims 8 (chunk % 16)
+  // ..+7).  V: thread t holds keys 2 jp, 2 jp + 1 at dims 8 cv .. +7 and
+  // writes them as 8 key pairs (one 32-bit word per dim) of V^T; a wave's
+  // lanes take 8 key pairs x 8 dim chunks, which the row stride of 18 words and
+  // the swizzle keep on 64 distinct banks.  The loads of block kb+1 are issued
+  // before block kb's compute and written to LDS after it; they are
+  // unconditional (rows past the last key re-read the last one and are zeroed
+  // when stored), so no branch makes the compiler wait for them early.
+  uint4 kr0, kr1, va, vb;
+  const int ck0 = tid >> 4, ck1 = (tid + 256) >> 4, cch = tid & 15;
+  const int jp = (tid & 7) + 8 * ((tid >> 6) & 1), cv = ((tid >> 3) & 7) + 8 * (tid >> 7);
+  auto load_block = [&](int kb) {
     const int64_t k0 = (int64_t)kb * FA_KB;
+    const int64_t r0 = k0 + ck0 < nkeys ? k0 + ck0 : nkeys - 1;
+    const int64_t r1 = k0 + ck1 < nkeys ? k0 + ck1 : nkeys - 1;
+    const int64_t ra = k0 + 2 * jp < nkeys ? k0 + 2 * jp : nkeys - 1;
+    const int64_t rb = k0 + 2 * jp + 1 < nkeys ? k0 + 2 * jp + 1 : nkeys - 1;
+    kr0 = *(const uint4*)(kc + r0 * HEAD_DIM + 8 * cch);
+    kr1 = *(const uint4*)(kc + r1 * HEAD_DIM + 8 * cch);
+    va = *(const uint4*)(vc + ra * HEAD_DIM + 8 * cv);
+    vb = *(const uint4*)(vc + rb * HEAD_DIM + 8 * cv);
+  };
+  auto store_block = [&](int kb, int b) {
+    const int64_t k0 = (int64_t)kb * FA_KB;
+    // component-wise masks: a select of whole uint4 values goes through scratch
+    const uint32_t m0 = k0 + ck0 < nkeys ? 0xffffffffu : 0u;
+    const uint32_t m1 = k0 + ck1 < nkeys ? 0xffffffffu : 0u;
+    const uint32_t ma = k0 + 2 * jp < nkeys ? 0xffffffffu : 0u;
+    const uint32_t mb = k0 + 2 * jp + 1 < nkeys ? 0xffffffffu : 0u;
+    *(uint4*)(&ks[b][ck0 * HEAD_DIM + 8 * (cch ^ (ck0 & 15))]) =
+        make_uint4(kr0.x & m0, kr0.y & m0, kr0.z & m0, kr0.w & m0);
+    *(uint4*)(&ks[b][ck1 * HEAD_DIM + 8 * (cch ^ (ck1 & 15))]) =
+        make_uint4(kr1.x & m1, kr1.y & m1, kr1.z & m1, kr1.w & m1);
+    const uint32_t wa[4] = {va.x & ma, va.y & ma, va.z & ma, va.w & ma};
+    const uint32_t wb[4] = {vb.x & mb, vb.y & mb, vb.z & mb, vb.w & mb};
+    uint32_t* vrow = (uint32_t*)vt[b];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int cidx = tid + 256 * u;
-      const int key = cidx >> 4, ch = cidx & 15;
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (k0 + key < nkeys) {
-        kv4 = *(const uint4*)(kc + (k0 + key) * HEAD_DIM + 8 * ch);
-        vv4 = *(const uint4*)(vc + (k0 + key) * HEAD_DIM + 8 * ch);
-      }
-      *(uint4*)(&ks[b][key * HEAD_DIM + 8 * (ch ^ (key & 15))]) = kv4;
-      const half_t* vh = (const half_t*)&vv4;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[b][(8 * ch + e) * FA_VT_STRIDE + key] = vh[e];
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * cv + e;
+      const uint32_t x = wa[e >> 1], y = wb[e >> 1];
+      const uint32_t pair = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+      vrow[row * FA_VT_WORDS + (jp ^ fa_vt_swz(row))] = pair;
     }
   };
 
@@ -539,11 +567,12 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
   float mrun = -INFINITY, lrun = 0.0f;
   const float c = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
 
-  stage(0, 0);
+  load_block(0);
+  store_block(0, 0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int b = kb & 1;
-    if (kb + 1 < nkb) stage(kb + 1, b ^ 1);   // the other buffer was released by the last barrier
+    load_block(kb + 1 < nkb ? kb + 1 : kb);   // in flight during this block's compute
     const int64_t k0 = (int64_t)kb * FA_KB;
     if (k0 <= wave_last_pos) {
       // S^T = K Q^T
@@ -578,10 +607,12 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
       ps += __shfl_xor(ps, 32, 64);
       lrun = lrun * alpha + ps;
       mrun = mnew;
+      if (__any(alpha != 1.0f)) {   // once the maxima settle, most blocks leave O as it is
 #pragma unroll
-      for (int db = 0; db < HEAD_DIM / 32; ++db)
+        for (int db = 0; db < HEAD_DIM / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
       // O^T += V^T P^T, two 16-key steps
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -590,14 +621,18 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
         for (int e = 0; e < 8; ++e) pf[e] = (half_t)sv[8 * kk + e];
 #pragma unroll
         for (int db = 0; db < HEAD_DIM / 32; ++db) {
-          const half_t* vr = &vt[b][(32 * db + li) * FA_VT_STRIDE + 16 * kk + 4 * g];
-          const uint2 lo = *(const uint2*)vr;         // keys 16kk + 4g + 0..3
-          const uint2 hi = *(const uint2*)(vr + 8);   // keys 16kk + 8 + 4g + 0..3
+          const int row = 32 * db + li;
+          const uint32_t* vr = (const uint32_t*)vt[b] + row * FA_VT_WORDS;
+          const int sw = fa_vt_swz(row);
+          const uint2 lo = *(const uint2*)(vr + ((8 * kk + 2 * g) ^ sw));       // keys 16kk + 4g + 0..3
+          const uint2 hi = *(const uint2*)(vr + ((8 * kk + 4 + 2 * g) ^ sw));   // keys 16kk + 8 + 4g + 0..3
           const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, w), pf, o[db], 0, 0, 0);
         }
       }
     }
+    // the other buffer was released by the previous iteration's barrier
+    if (kb + 1 < nkb) store_block(kb + 1, b ^ 1);
     __syncthreads();   // buffer b is free, buffer b^1 is staged
   }
   // O = O^T / sum: lane holds query qw + li, dims 32 db + 8 (r/4) + 4 g + r % 4
