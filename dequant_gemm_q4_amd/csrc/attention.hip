@@ -453,19 +453,25 @@ static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) 
   return hipSuccess;
 }
 
-// Many queries (prefill): MFMA flash attention.  One workgroup = 4 waves =
-// 128 consecutive queries of one query head; wave w owns queries
-// 32w .. 32w+31 of the block and keeps them as MFMA operands for the whole
-// key loop.  Keys go in blocks of 32, staged in LDS by the workgroup (K row-
-// major with 16-byte chunks XOR-swizzled by the key, V transposed to
-// [dim][key]) and double-buffered.  Per key block and wave, with
-// v_mfma_f32_32x32x16_f16 (D = A B^T):
+// Many queries (prefill): MFMA flash attention.  One workgroup = 8 waves =
+// 128 consecutive queries of one query head, in two halves of 4 waves that
+// take the even and the odd key blocks and merge their softmax states in LDS
+// at the end (two independent chains per SIMD).  Wave w of a half owns
+// queries 32w .. 32w+31 of the block and keeps them as MFMA operands for the
+// whole key loop.  Keys go in blocks of 32, staged in LDS by each half (K
+// row-major with 16-byte chunks XOR-swizzled by the key; V transposed to
+// [dim][key pair], packed 32-bit words on conflict-free banks), double-
+// buffered, the next block's global loads in flight during the current
+// block's compute.  Per key block and wave, with v_mfma_f32_32x32x16_f16
+// (D = A B^T):
 //  * S^T = K Q^T (A = K rows, B = Q rows, 8 MFMAs over the 128 dims): an
 //    accumulator lane holds one query (its lane % 32) and 16 of the 32 keys,
 //    the lane 32 away the other 16, so a query's maximum and sum need one
 //    exchange between the two lanes;
 //  * online softmax in fp32 on exp2 with log2(e)/sqrt(128) folded into the
-//    scores; keys past a query's position are masked to -inf;
+//    exponent; keys past a query's position are masked to -inf (only in
+//    blocks that cross the wave's diagonal); the reference maximum moves
+//    lazily (only by more than 2^8), so O is rarely rescaled;
 //  * O^T += V^T P^T (A = V^T rows, B = P rows, 2 key steps x 4 dim blocks):
 //    the key order inside a 16-key step is permuted the same way for both
 //    operands so that P's B fragment is 8 consecutive accumulator registers,
@@ -474,21 +480,37 @@ static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) 
 // O / sum is rounded to fp16 and stored.
 constexpr int FA_KB = 32;                 // keys per block
 constexpr int FA_QB = 128;                // queries per workgroup
+constexpr float FA_RESCALE = 8.0f;        // log2 headroom of the lazy softmax rescale
+constexpr int FA_MERGE_STRIDE = HEAD_DIM / 2 + 4;   // floats per lane in the merge: O^T, m, l, pad
 constexpr int FA_VT_WORDS = 18;           // 32-bit words per V^T row (16 key pairs + pad)
 // V^T word swizzle: rows 32..63 and 96..127 swap the two 8-word halves
 __device__ __forceinline__ int fa_vt_swz(int row) { return 8 * ((row >> 5) & 1); }
 
 typedef float f16acc __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, int nqb) {
-  __shared__ __attribute__((aligned(16))) half_t ks[2][FA_KB * HEAD_DIM];
-  __shared__ __attribute__((aligned(16))) half_t vt[2][HEAD_DIM * 2 * FA_VT_WORDS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(512) void attention_mfma_kernel(AttnArgs a, int M, int nqb) {
+  // per half: K double buffer, V^T double buffer; reused for the final merge
+  constexpr int KS_BYTES = 2 * FA_KB * HEAD_DIM * 2, VT_BYTES = 2 * HEAD_DIM * FA_VT_WORDS * 4;
+  constexpr int HALF_BYTES = KS_BYTES + VT_BYTES;
+  static_assert(2 * HALF_BYTES >= 4 * 64 * FA_MERGE_STRIDE * 4, "merge staging must fit");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * HALF_BYTES];
+  const int hf = threadIdx.x >> 8;            // half: key blocks hf, hf + 2, hf + 4, ...
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+  half_t (*ks)[FA_KB * HEAD_DIM] = (half_t (*)[FA_KB * HEAD_DIM])(lds + hf * HALF_BYTES);
+  half_t (*vt)[HEAD_DIM * 2 * FA_VT_WORDS] = (half_t (*)[HEAD_DIM * 2 * FA_VT_WORDS])(lds + hf * HALF_BYTES + KS_BYTES);
   const int li = lane & 31, g = lane >> 5;
-  const int qb = nqb - 1 - (int)blockIdx.x;   // the longest (latest) query blocks first
-  const int h = blockIdx.y;
+  // work item t = (KV head, query block from the last, query head of the
+  // group).  Workgroups are dealt to the 8 XCDs round-robin; XCD x takes the
+  // items x*per .. x*per+per-1, so the queries of one KV head share an L2 and
+  // its K and V are read from HBM about once.  Longest blocks first.
   const int G = a.hq / a.hkv;
-  const int kvh = h / G;
+  const int nitems = nqb * a.hq, per = (nitems + 7) / 8;
+  const int t = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+  if (t >= nitems) return;
+  const int kvh = t / (nqb * G);
+  const int rem = t - kvh * nqb * G;
+  const int qb = nqb - 1 - rem / G;
+  const int h = kvh * G + rem % G;
   const int q0 = qb * FA_QB;                  // first query (row of q) of the block
   const int qw = q0 + 32 * wave;              // first query of this wave
   const int64_t pos_q = (int64_t)a.pos0 + qw + li;   // this lane's query position
@@ -514,6 +536,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
   // a wave is done with key blocks past its last query
   const int qwl = (qw + 31 < M ? qw + 31 : M - 1);
   const int64_t wave_last_pos = (int64_t)a.pos0 + qwl;
+  const int64_t wave_first_pos = (int64_t)a.pos0 + qw;
 
   // staging of a key block (32 keys x 128 dims of K and of V).  K: thread t
   // holds 16-byte chunks t and t + 256 (key = chunk / 16, dims 8 (chunk % 16)
@@ -567,14 +590,22 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
   float mrun = -INFINITY, lrun = 0.0f;
   const float c = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
 
-  load_block(0);
-  store_block(0, 0);
+  // both halves run the same number of iterations (the barriers are shared);
+  // a half whose block index is past the last block only waits
+  const int niter = (nkb + 1) / 2;
+  const int kb_last = nkb - 1 - ((nkb - 1 - hf) & 1);   // this half's last block (may be < 0)
+  if (hf < nkb) {
+    load_block(hf);
+    store_block(hf, 0);
+  }
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int b = kb & 1;
-    load_block(kb + 1 < nkb ? kb + 1 : kb);   // in flight during this block's compute
+  for (int it = 0; it < niter; ++it) {
+    const int b = it & 1;
+    const int kb = 2 * it + hf;
+    const int kbn = kb + 2 <= kb_last ? kb + 2 : kb_last;
+    if (kb_last >= 0) load_block(kbn);   // in flight during this block's compute
     const int64_t k0 = (int64_t)kb * FA_KB;
-    if (k0 <= wave_last_pos) {
+    if (kb < nkb && k0 <= wave_last_pos) {
       // S^T = K Q^T
       f16acc sacc = (f16acc){};
 #pragma unroll
@@ -583,31 +614,41 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
         const h8 kf = *(const h8*)(&ks[b][li * HEAD_DIM + 8 * (ch ^ (li & 15))]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
       }
-      // scores, causal mask, block maximum of this lane's query
-      float sv[16];
-      float bm = -INFINITY;
+      // causal mask, only in blocks that reach past the wave's first query
+      // (a wave-uniform test: most blocks lie wholly below the diagonal)
+      if (k0 + FA_KB - 1 > wave_first_pos) {
+        const int d = (int)(pos_q - k0) - 4 * g;   // key k0 + 4g + j is visible iff j <= d
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float v = key <= pos_q ? sacc[r] * c : -INFINITY;
-        sv[r] = v;
-        bm = fmaxf(bm, v);
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > d) sacc[r] = -INFINITY;
       }
+      // block maximum of this lane's query (raw scores; the scale c > 0 keeps the order)
+      float bm = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[r]);
       bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      const float mnew = fmaxf(mrun, bm);
-      // a query with no key in this block yet (mnew = -inf) keeps its state
-      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+      // lazy rescaling: the reference m of the running sums moves only when
+      // the block maximum exceeds it by more than FA_RESCALE (so p <= 2^8 in
+      // fp16), which after the first blocks is rare; O and l share m, so
+      // the result does not depend on it.  A query with no visible key yet
+      // keeps m = -inf, l = 0, O = 0 (reference point 0: p = 0).
+      const float bmc = bm * c;
+      const bool move = bmc > mrun + FA_RESCALE;
+      const float mnew = move ? bmc : mrun;
+      const float mref = mnew == -INFINITY ? 0.0f : mnew;
+      const float alpha = move ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
+      float sv[16];
       float ps = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = mnew == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - mnew);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mref));
         sv[r] = p;
         ps += p;
       }
       ps += __shfl_xor(ps, 32, 64);
       lrun = lrun * alpha + ps;
       mrun = mnew;
-      if (__any(alpha != 1.0f)) {   // once the maxima settle, most blocks leave O as it is
+      if (__any(move)) {
 #pragma unroll
         for (int db = 0; db < HEAD_DIM / 32; ++db)
 #pragma unroll
@@ -632,8 +673,41 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a, int M, 
       }
     }
     // the other buffer was released by the previous iteration's barrier
-    if (kb + 1 < nkb) store_block(kb + 1, b ^ 1);
+    if (kb + 2 < nkb) store_block(kb + 2, b ^ 1);
     __syncthreads();   // buffer b is free, buffer b^1 is staged
+  }
+  // merge of the two halves' softmax states: half 1 leaves its running
+  // maximum, sum and O^T in LDS (staging memory, free after the last
+  // barrier), half 0 rescales both to the common maximum
+  float* mo = (float*)lds + (wave * 64 + lane) * FA_MERGE_STRIDE;
+  if (hf == 1) {
+#pragma unroll
+    for (int db = 0; db < HEAD_DIM / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4)
+        *(float4*)(mo + 16 * db + r) = make_float4(o[db][r], o[db][r + 1], o[db][r + 2], o[db][r + 3]);
+    mo[HEAD_DIM / 2] = mrun;
+    mo[HEAD_DIM / 2 + 1] = lrun;
+  }
+  __syncthreads();
+  if (hf == 1) return;
+  {
+    const float m1 = mo[HEAD_DIM / 2], l1 = mo[HEAD_DIM / 2 + 1];
+    const float mx = fmaxf(mrun, m1);
+    // a half without keys for this query has m = -inf and contributes nothing
+    const float f0 = mrun == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mrun - mx);
+    const float f1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+    lrun = lrun * f0 + l1 * f1;
+#pragma unroll
+    for (int db = 0; db < HEAD_DIM / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const float4 w = *(const float4*)(mo + 16 * db + r);
+        o[db][r] = o[db][r] * f0 + w.x * f1;
+        o[db][r + 1] = o[db][r + 1] * f0 + w.y * f1;
+        o[db][r + 2] = o[db][r + 2] * f0 + w.z * f1;
+        o[db][r + 3] = o[db][r + 3] * f0 + w.w * f1;
+      }
   }
   // O = O^T / sum: lane holds query qw + li, dims 32 db + 8 (r/4) + 4 g + r % 4
   if (qw + li < M) {
@@ -677,7 +751,8 @@ hipError_t launch_attention(const void* q, const void* k_cache, const void* v_ca
   }
   if (M > ATT_SPLIT_MAX_M) {
     const int nqb = (int)((M + FA_QB - 1) / FA_QB);
-    hipLaunchKernelGGL(attention_mfma_kernel, dim3((unsigned)nqb, (unsigned)hq), dim3(256), 0, s, a, (int)M, nqb);
+    const int per = (nqb * hq + 7) / 8;   // work items per XCD
+    hipLaunchKernelGGL(attention_mfma_kernel, dim3(8u * (unsigned)per), dim3(512), 0, s, a, (int)M, nqb);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)M, (unsigned)hkv);
