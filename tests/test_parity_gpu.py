@@ -758,6 +758,27 @@ def test_attention_gqa_peaked_scores(dmq):
     _check_attention(q, kc, vc, out, 2, 900, 24, "attention peaked")
 
 
+@pytest.mark.parametrize("M,pos0,hq,hkv", [(300, 20, 24, 8), (150, 0, 6, 2)])
+def test_attention_gqa_prefill_rising_scores(dmq, M, pos0, hq, hkv):
+    """Prefill (MFMA path) with scores that rise along the keys by about 45
+    in natural units: every query's running maximum moves many times, by
+    more and by less than 2^8 in the exp2 domain, and a large spread case
+    (one key dominates, most weights underflow)."""
+    rng = np.random.default_rng(M + hq)
+    n = pos0 + M
+    u = rng.standard_normal(D_HEAD)
+    q = (rng.standard_normal((M, hq, D_HEAD)) * 0.5 + 2.0 * u).astype(np.float16).reshape(M, hq * D_HEAD)
+    ramp = 2.0 * np.arange(n) / n
+    kc = (rng.standard_normal((hkv, n, D_HEAD)) * 0.5 + ramp[None, :, None] * u).astype(np.float16)
+    vc = rng.standard_normal((hkv, n, D_HEAD)).astype(np.float16)
+    out = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    dmq.dmq_attention_gqa(dev(q), dev(kc), dev(vc), out, M, pos0, hq, hkv, n)
+    torch.cuda.synchronize()
+    _check_attention(q, kc, vc, out.cpu().numpy(), M, pos0, hq, f"attention rising M={M} pos0={pos0}")
+    q2, kc2, vc2, out2 = _attention_case(dmq, M, pos0, hq, hkv, n, seed=M * 7, spread=4.0)
+    _check_attention(q2, kc2, vc2, out2, M, pos0, hq, f"attention prefill peaked M={M}")
+
+
 def test_residual_rmsnorm(dmq):
     rng = np.random.default_rng(21)
     for M, K in ((1, 3072), (5, 768), (64, 3072)):
