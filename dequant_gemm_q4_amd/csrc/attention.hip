@@ -533,9 +533,6 @@ __global__ __launch_bounds__(512) void attention_mfma_kernel(AttnArgs a, int M, 
   const int qlast = (q0 + FA_QB < M ? q0 + FA_QB : M) - 1;
   const int64_t nkeys = (int64_t)a.pos0 + qlast + 1;
   const int nkb = (int)((nkeys + FA_KB - 1) / FA_KB);
-  // a wave is done with key blocks past its last query
-  const int qwl = (qw + 31 < M ? qw + 31 : M - 1);
-  const int64_t wave_last_pos = (int64_t)a.pos0 + qwl;
   const int64_t wave_first_pos = (int64_t)a.pos0 + qw;
 
   // staging of a key block (32 keys x 128 dims of K and of V).  K: thread t
@@ -550,28 +547,34 @@ __global__ __launch_bounds__(512) void attention_mfma_kernel(AttnArgs a, int M, 
   uint4 kr0, kr1, va, vb;
   const int ck0 = tid >> 4, ck1 = (tid + 256) >> 4, cch = tid & 15;
   const int jp = (tid & 7) + 8 * ((tid >> 6) & 1), cv = ((tid >> 3) & 7) + 8 * (tid >> 7);
-  auto load_block = [&](int kb) {
+  auto load_k = [&](int kb) {
     const int64_t k0 = (int64_t)kb * FA_KB;
     const int64_t r0 = k0 + ck0 < nkeys ? k0 + ck0 : nkeys - 1;
     const int64_t r1 = k0 + ck1 < nkeys ? k0 + ck1 : nkeys - 1;
-    const int64_t ra = k0 + 2 * jp < nkeys ? k0 + 2 * jp : nkeys - 1;
-    const int64_t rb = k0 + 2 * jp + 1 < nkeys ? k0 + 2 * jp + 1 : nkeys - 1;
     kr0 = *(const uint4*)(kc + r0 * HEAD_DIM + 8 * cch);
     kr1 = *(const uint4*)(kc + r1 * HEAD_DIM + 8 * cch);
+  };
+  auto load_v = [&](int kb) {
+    const int64_t k0 = (int64_t)kb * FA_KB;
+    const int64_t ra = k0 + 2 * jp < nkeys ? k0 + 2 * jp : nkeys - 1;
+    const int64_t rb = k0 + 2 * jp + 1 < nkeys ? k0 + 2 * jp + 1 : nkeys - 1;
     va = *(const uint4*)(vc + ra * HEAD_DIM + 8 * cv);
     vb = *(const uint4*)(vc + rb * HEAD_DIM + 8 * cv);
   };
-  auto store_block = [&](int kb, int b) {
+  // component-wise masks: a select of whole uint4 values goes through scratch
+  auto store_k = [&](int kb, int b) {
     const int64_t k0 = (int64_t)kb * FA_KB;
-    // component-wise masks: a select of whole uint4 values goes through scratch
     const uint32_t m0 = k0 + ck0 < nkeys ? 0xffffffffu : 0u;
     const uint32_t m1 = k0 + ck1 < nkeys ? 0xffffffffu : 0u;
-    const uint32_t ma = k0 + 2 * jp < nkeys ? 0xffffffffu : 0u;
-    const uint32_t mb = k0 + 2 * jp + 1 < nkeys ? 0xffffffffu : 0u;
     *(uint4*)(&ks[b][ck0 * HEAD_DIM + 8 * (cch ^ (ck0 & 15))]) =
         make_uint4(kr0.x & m0, kr0.y & m0, kr0.z & m0, kr0.w & m0);
     *(uint4*)(&ks[b][ck1 * HEAD_DIM + 8 * (cch ^ (ck1 & 15))]) =
         make_uint4(kr1.x & m1, kr1.y & m1, kr1.z & m1, kr1.w & m1);
+  };
+  auto store_v = [&](int kb, int b) {
+    const int64_t k0 = (int64_t)kb * FA_KB;
+    const uint32_t ma = k0 + 2 * jp < nkeys ? 0xffffffffu : 0u;
+    const uint32_t mb = k0 + 2 * jp + 1 < nkeys ? 0xffffffffu : 0u;
     const uint32_t wa[4] = {va.x & ma, va.y & ma, va.z & ma, va.w & ma};
     const uint32_t wb[4] = {vb.x & mb, vb.y & mb, vb.z & mb, vb.w & mb};
     uint32_t* vrow = (uint32_t*)vt[b];
@@ -590,91 +593,142 @@ __global__ __launch_bounds__(512) void attention_mfma_kernel(AttnArgs a, int M, 
   float mrun = -INFINITY, lrun = 0.0f;
   const float c = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
 
-  // both halves run the same number of iterations (the barriers are shared);
-  // a half whose block index is past the last block only waits
-  const int niter = (nkb + 1) / 2;
-  const int kb_last = nkb - 1 - ((nkb - 1 - hf) & 1);   // this half's last block (may be < 0)
-  if (hf < nkb) {
-    load_block(hf);
-    store_block(hf, 0);
-  }
-  __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    const int b = it & 1;
-    const int kb = 2 * it + hf;
-    const int kbn = kb + 2 <= kb_last ? kb + 2 : kb_last;
-    if (kb_last >= 0) load_block(kbn);   // in flight during this block's compute
-    const int64_t k0 = (int64_t)kb * FA_KB;
-    if (kb < nkb && k0 <= wave_last_pos) {
-      // S^T = K Q^T
-      f16acc sacc = (f16acc){};
+  // S^T = K Q^T of the key block in K buffer kbuf
+  auto scores = [&](int kbuf) {
+    f16acc sacc = (f16acc){};
 #pragma unroll
-      for (int kk = 0; kk < HEAD_DIM / 16; ++kk) {
-        const int ch = 2 * kk + g;
-        const h8 kf = *(const h8*)(&ks[b][li * HEAD_DIM + 8 * (ch ^ (li & 15))]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
-      }
-      // causal mask, only in blocks that reach past the wave's first query
-      // (a wave-uniform test: most blocks lie wholly below the diagonal)
-      if (k0 + FA_KB - 1 > wave_first_pos) {
-        const int d = (int)(pos_q - k0) - 4 * g;   // key k0 + 4g + j is visible iff j <= d
+    for (int kk = 0; kk < HEAD_DIM / 16; ++kk) {
+      const int ch = 2 * kk + g;
+      const h8 kf = *(const h8*)(&ks[kbuf][li * HEAD_DIM + 8 * (ch ^ (li & 15))]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
+    }
+    return sacc;
+  };
+  // causal mask of the block at key k0, only where it reaches past the
+  // wave's first query (a wave-uniform test: most blocks lie wholly below
+  // the diagonal); a block wholly past the wave's queries masks to -inf and
+  // then adds nothing
+  auto mask = [&](f16acc& sacc, int64_t k0) {
+    if (k0 + FA_KB - 1 > wave_first_pos) {
+      const int64_t dd = pos_q - k0 - 4 * g;   // key k0 + 4g + j is visible iff j <= dd
+      const int d = dd < -1 ? -1 : (dd > FA_KB ? FA_KB : (int)dd);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + (r & 3) > d) sacc[r] = -INFINITY;
-      }
-      // block maximum of this lane's query (raw scores; the scale c > 0 keeps the order)
-      float bm = sacc[0];
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > d) sacc[r] = -INFINITY;
+    }
+  };
+  // online softmax of one block's scores: P (fp16, as the MFMA operand),
+  // the rescale factor alpha and whether any lane's reference moved
+  auto softmax = [&](const f16acc& sacc, h8 (&pf)[2], float& alpha, bool& move) {
+    // block maximum of this lane's query (raw scores; the scale c > 0 keeps the order)
+    float bm = sacc[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[r]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      // lazy rescaling: the reference m of the running sums moves only when
-      // the block maximum exceeds it by more than FA_RESCALE (so p <= 2^8 in
-      // fp16), which after the first blocks is rare; O and l share m, so
-      // the result does not depend on it.  A query with no visible key yet
-      // keeps m = -inf, l = 0, O = 0 (reference point 0: p = 0).
-      const float bmc = bm * c;
-      const bool move = bmc > mrun + FA_RESCALE;
-      const float mnew = move ? bmc : mrun;
-      const float mref = mnew == -INFINITY ? 0.0f : mnew;
-      const float alpha = move ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
-      float sv[16];
-      float ps = 0.0f;
+    for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[r]);
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    // lazy rescaling: the reference m of the running sums moves only when
+    // the block maximum exceeds it by more than FA_RESCALE (so p <= 2^8 in
+    // fp16), which after the first blocks is rare; O and l share m, so the
+    // result does not depend on it.  A query with no visible key yet keeps
+    // m = -inf, l = 0, O = 0 (reference point 0: p = 0).
+    const float bmc = bm * c;
+    move = bmc > mrun + FA_RESCALE;
+    const float mnew = move ? bmc : mrun;
+    const float mref = mnew == -INFINITY ? 0.0f : mnew;
+    alpha = move ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
+    float sv[16];
+    float ps = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mref));
-        sv[r] = p;
-        ps += p;
-      }
-      ps += __shfl_xor(ps, 32, 64);
-      lrun = lrun * alpha + ps;
-      mrun = mnew;
-      if (__any(move)) {
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mref));
+      sv[r] = p;
+      ps += p;
+    }
+    ps += __shfl_xor(ps, 32, 64);
+    lrun = lrun * alpha + ps;
+    mrun = mnew;
 #pragma unroll
-        for (int db = 0; db < HEAD_DIM / 32; ++db)
+    for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (half_t)sv[e];
+  };
+  // O^T = alpha O^T + V^T P^T with V^T from buffer vbuf
+  auto update = [&](const h8 (&pf)[2], float alpha, bool move, int vbuf) {
+    if (__any(move)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      // O^T += V^T P^T, two 16-key steps
+      for (int db = 0; db < HEAD_DIM / 32; ++db)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        h8 pf;
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    // O^T += V^T P^T, two 16-key steps
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (half_t)sv[8 * kk + e];
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int db = 0; db < HEAD_DIM / 32; ++db) {
-          const int row = 32 * db + li;
-          const uint32_t* vr = (const uint32_t*)vt[b] + row * FA_VT_WORDS;
-          const int sw = fa_vt_swz(row);
-          const uint2 lo = *(const uint2*)(vr + ((8 * kk + 2 * g) ^ sw));       // keys 16kk + 4g + 0..3
-          const uint2 hi = *(const uint2*)(vr + ((8 * kk + 4 + 2 * g) ^ sw));   // keys 16kk + 8 + 4g + 0..3
-          const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, w), pf, o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < HEAD_DIM / 32; ++db) {
+        const int row = 32 * db + li;
+        const uint32_t* vr = (const uint32_t*)vt[vbuf] + row * FA_VT_WORDS;
+        const int sw = fa_vt_swz(row);
+        const uint2 lo = *(const uint2*)(vr + ((8 * kk + 2 * g) ^ sw));       // keys 16kk + 4g + 0..3
+        const uint2 hi = *(const uint2*)(vr + ((8 * kk + 4 + 2 * g) ^ sw));   // keys 16kk + 8 + 4g + 0..3
+        const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, w), pf[kk], o[db], 0, 0, 0);
       }
     }
-    // the other buffer was released by the previous iteration's barrier
-    if (kb + 2 < nkb) store_block(kb + 2, b ^ 1);
-    __syncthreads();   // buffer b is free, buffer b^1 is staged
+  };
+
+  // Software pipeline over this half's blocks j = 0, 1, ... (key blocks
+  // 2j + hf): iteration j computes the scores of block j+1 while it runs
+  // block j's softmax and O update, so the MFMA pipe and the VALU overlap.
+  // K is staged two blocks ahead (buffer j&1 is free once block j's scores
+  // exist), V one block ahead.  Both halves run the same number of
+  // iterations: the barriers are shared.
+  const int nloc = hf < nkb ? (nkb - hf + 1) / 2 : 0;
+  const int niter = (nkb + 1) / 2;
+  if (nloc > 0) {
+    load_k(hf);
+    load_v(hf);
+    store_k(hf, 0);
+    store_v(hf, 0);
+  }
+  if (nloc > 1) {
+    load_k(2 + hf);
+    store_k(2 + hf, 1);
+  }
+  __syncthreads();
+  f16acc scur = (f16acc){};
+  if (nloc > 0) {
+    scur = scores(0);
+    mask(scur, (int64_t)hf * FA_KB);
+  }
+  __syncthreads();   // K buffer 0 is rewritten in iteration 0
+  for (int j = 0; j < niter; ++j) {
+    if (j + 1 < nloc) {
+      const int jk = j + 2 < nloc ? j + 2 : nloc - 1;   // clamped: the loads stay unconditional
+      load_k(2 * jk + hf);
+      load_v(2 * (j + 1) + hf);
+      f16acc snext = scores((j + 1) & 1);
+      h8 pf[2];
+      float alpha;
+      bool move;
+      softmax(scur, pf, alpha, move);
+      // interleave: each MFMA of the next block's scores followed by this
+      // block's softmax VALU work, which runs while the MFMA executes
+#pragma unroll
+      for (int i = 0; i < HEAD_DIM / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read (K fragment)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+      }
+      update(pf, alpha, move, j & 1);
+      if (j + 2 < nloc) store_k(2 * (j + 2) + hf, j & 1);
+      store_v(2 * (j + 1) + hf, (j + 1) & 1);
+      mask(snext, (int64_t)(2 * (j + 1) + hf) * FA_KB);
+      scur = snext;
+    } else if (j < nloc) {
+      h8 pf[2];
+      float alpha;
+      bool move;
+      softmax(scur, pf, alpha, move);
+      update(pf, alpha, move, j & 1);
+    }
+    __syncthreads();
   }
   // merge of the two halves' softmax states: half 1 leaves its running
   // maximum, sum and O^T in LDS (staging memory, free after the last
