@@ -289,6 +289,19 @@ def layer_chain_sweep(torch, dmq):
         dmq.dmq_ffn_swiglu_q4k(B["xn2"], W["gu"], W["down"], B["hf"], B["yd"], M, D, F)
         dmq.dmq_residual_rmsnorm(B["h1"], B["yd"], g1, 1e-5, B["x"], B["xn1"], M, D)
 
+    # the same layer with the residual adds fused into the projections that
+    # follow them (dmq_residual_rmsnorm_gemm): at M = 1 the decode kernel
+    # forms h = h_in + y and its RMSNorm while it stages x.  The residual
+    # stream alternates between x and h1; this layer's first call adds the
+    # previous layer's FFN output.
+    def step_fused(W, B, kc, vc, M, pos0, L):
+        dmq.dmq_residual_rmsnorm_gemm(B["h1"], B["yd"], g1, 1e-5, B["x"], None, W["qkv_p"], M, D)
+        dmq.dmq_rope_kv_cache(B["yq"], B["yk"], B["yv"], M, pos0, HQ, HKV, B["qr"], kc, vc, L)
+        dmq.dmq_attention_gqa(B["qr"], kc, vc, B["att"], M, pos0, HQ, HKV, L)
+        dmq.dmq_gemm_q4k(B["att"], W["o"], B["yo"], M, D, HQ * HD)
+        dmq.dmq_residual_rmsnorm_gemm(B["x"], B["yo"], g2, 1e-5, B["h1"], None, W["gu_p"], M, D)
+        dmq.dmq_gemm_q6k(B["hf"], W["down"], B["yd"], M, D, F)
+
     def make(nl, M, L):
         Ws = [weights(l) for l in range(nl)]
         B = buffers(M)
@@ -296,6 +309,9 @@ def layer_chain_sweep(torch, dmq):
             W["qkv"] = dmq.make_group([("q4k", B["xn1"], W["q"], B["yq"], M, HQ * HD, D),
                                        ("q4k", B["xn1"], W["k"], B["yk"], M, HKV * HD, D),
                                        ("q4k", B["xn1"], W["v"], B["yv"], M, HKV * HD, D)])
+            W["qkv_p"] = dmq.make_projs([("q4k", W["q"], B["yq"], HQ * HD), ("q4k", W["k"], B["yk"], HKV * HD),
+                                         ("q4k", W["v"], B["yv"], HKV * HD)], D)
+            W["gu_p"] = dmq.make_projs([("q4k", W["gu"], B["hf"], 2 * F, "swiglu")], D)
         caches = [(torch.zeros((HKV, L, HD), dtype=torch.float16, device=dev),
                    torch.zeros((HKV, L, HD), dtype=torch.float16, device=dev)) for _ in range(nl)]
         for kc, vc in caches:   # earlier tokens' keys and values
@@ -310,12 +326,16 @@ def layer_chain_sweep(torch, dmq):
         Ws, B, caches = make(8, 1, L)
         items = list(zip(Ws, caches))
         us = time_graph(torch, lambda it: step(it[0], B, it[1][0], it[1][1], 1, pos0, L), items, 8) * 1e3
+        B["h1"].copy_(B["x"])
+        B["yd"].zero_()
+        uf = time_graph(torch, lambda it: step_fused(it[0], B, it[1][0], it[1][1], 1, pos0, L), items, 8) * 1e3
         # the attention kernel alone at this context
         ua = time_graph(torch, lambda it: dmq.dmq_attention_gqa(B["qr"], it[1][0], it[1][1], B["att"], 1, pos0,
                                                                 HQ, HKV, L), items, 8) * 1e3
         kv_bytes = 2 * HKV * L * HD * 2
         print(json.dumps({"sweep": f"decode step, one Llama-3.2-3B layer, all kernels (graph replay, 8 rotating layers), "
                                    f"context {L}", "us_per_layer": round(us, 2),
+                          "fused_residual_us_per_layer": round(uf, 2),
                           "attention_us": round(ua, 2), "attention_kv_GB/s": round(kv_bytes / ua / 1e3, 1)}),
               flush=True)
         del Ws, B, caches, items

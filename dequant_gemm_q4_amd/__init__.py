@@ -32,7 +32,8 @@ FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
 # Every entry point declared in include/dmq.h.
 EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
            "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
-           "dmq_attention_gqa", "dmq_residual_rmsnorm", "dmq_status_string", "dmq_version")
+           "dmq_attention_gqa", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm", "dmq_status_string",
+           "dmq_version")
 HEAD_DIM = 128
 
 
@@ -51,7 +52,7 @@ class GemmDesc(ctypes.Structure):
 
 class ProjDesc(ctypes.Structure):
     """Mirror of dmq_proj_desc."""
-    _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("format", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("wq", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
 
 
@@ -77,9 +78,11 @@ def _load() -> ctypes.CDLL:
     L.dmq_rope_kv_cache.argtypes = [P, P, P, I64, I64, I32, I32, ctypes.c_double, P, P, P, P, I64, P]
     L.dmq_attention_gqa.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
     L.dmq_residual_rmsnorm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, P]
+    L.dmq_residual_rmsnorm_gemm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, ctypes.POINTER(ProjDesc),
+                                            I32, P]
     for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
                  "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
-                 "dmq_attention_gqa", "dmq_residual_rmsnorm"):
+                 "dmq_attention_gqa", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm"):
         getattr(L, name).restype = ctypes.c_int
     L.dmq_status_string.argtypes = [ctypes.c_int]
     L.dmq_status_string.restype = ctypes.c_char_p
@@ -200,22 +203,39 @@ def dmq_gemm_group(problems, stream=None) -> None:
     _check(lib.dmq_gemm_group(arr, len(arr), _stream(stream)), "dmq_gemm_group")
 
 
+PROJ_SWIGLU = 1
+
+
 def make_projs(projs, K: int):
-    """projs: iterable of (format, wq, y, N); returns the ctypes dmq_proj_desc
-    array (sizes checked against K and y's element count / M below)."""
+    """projs: iterable of (format, wq, y, N) or (format, wq, h, N, "swiglu")
+    (a Q4_K gate|up pair whose output is h = silu(gate) * up, float16
+    [M, N/2]); returns the ctypes dmq_proj_desc array (sizes checked against
+    K and the output's element count / M below)."""
     import torch
     projs = list(projs)
     arr = (ProjDesc * len(projs))()
-    for i, (fmt, wq, y, N) in enumerate(projs):
+    for i, pr in enumerate(projs):
+        fmt, wq, y, N = pr[:4]
+        swiglu = len(pr) > 4 and pr[4] == "swiglu"
         fmt = FORMATS.get(fmt, fmt)
         arr[i].format = fmt
-        arr[i].reserved = 0
+        arr[i].flags = PROJ_SWIGLU if swiglu else 0
         arr[i].wq = _dev_tensor(wq, torch.uint8, f"wq[{i}]", _wq_bytes(fmt, N, K))
-        if not isinstance(y, torch.Tensor) or y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous():
-            raise TypeError(f"y[{i}] must be a contiguous float32 GPU tensor")
+        want = torch.float16 if swiglu else torch.float32
+        if not isinstance(y, torch.Tensor) or y.dtype != want or not y.is_cuda or not y.is_contiguous():
+            raise TypeError(f"y[{i}] must be a contiguous {want} GPU tensor")
         arr[i].y = y.data_ptr()
         arr[i].N = N
     return arr
+
+
+def _check_proj_outputs(projs, arr, M: int) -> None:
+    if isinstance(projs, ctypes.Array):
+        return
+    for i, pr in enumerate(list(projs)):
+        n_out = arr[i].N // 2 if arr[i].flags & PROJ_SWIGLU else arr[i].N
+        if pr[2].numel() != M * n_out:
+            raise ValueError(f"y[{i}] has {pr[2].numel()} elements, expected {M * n_out}")
 
 
 def dmq_rmsnorm_gemm(x, g, eps: float, xn, projs, M: int, K: int, stream=None) -> None:
@@ -230,13 +250,25 @@ def dmq_rmsnorm_gemm(x, g, eps: float, xn, projs, M: int, K: int, stream=None) -
     pg = _dev_tensor(g, torch.float32, "g", K)
     pn = None if xn is None else _dev_tensor(xn, torch.float16, "xn", M * K)
     arr = projs if isinstance(projs, ctypes.Array) else make_projs(projs, K)
-    for i in range(len(arr)):
-        if not isinstance(projs, ctypes.Array):
-            y = list(projs)[i][2]
-            if y.numel() != M * arr[i].N:
-                raise ValueError(f"y[{i}] has {y.numel()} elements, expected {M * arr[i].N}")
+    _check_proj_outputs(projs, arr, M)
     _check(lib.dmq_rmsnorm_gemm(px, pg, float(eps), pn, M, K, arr, len(arr), _stream(stream)),
            "dmq_rmsnorm_gemm")
+
+
+def dmq_residual_rmsnorm_gemm(h_in, y_add, g, eps: float, h_out, xn, projs, M: int, K: int, stream=None) -> None:
+    """h_out <- h_in + y_add (float32 [M, K], h_out a separate buffer), then
+    y_i <- RMSNorm(h_out; g, eps) * W_i^T as in dmq_rmsnorm_gemm.  xn: float16
+    [M, K] or None when M = 1 and K <= 32768 (one decode launch)."""
+    import torch
+    ph = _dev_tensor(h_in, torch.float32, "h_in", M * K)
+    pa = _dev_tensor(y_add, torch.float32, "y_add", M * K)
+    pg = _dev_tensor(g, torch.float32, "g", K)
+    po = _dev_tensor(h_out, torch.float32, "h_out", M * K)
+    pn = None if xn is None else _dev_tensor(xn, torch.float16, "xn", M * K)
+    arr = projs if isinstance(projs, ctypes.Array) else make_projs(projs, K)
+    _check_proj_outputs(projs, arr, M)
+    _check(lib.dmq_residual_rmsnorm_gemm(ph, pa, pg, float(eps), po, pn, M, K, arr, len(arr), _stream(stream)),
+           "dmq_residual_rmsnorm_gemm")
 
 
 def dmq_rope_kv_cache(q, k, v, M: int, pos0: int, n_q_heads: int, n_kv_heads: int, q_out, k_cache, v_cache,

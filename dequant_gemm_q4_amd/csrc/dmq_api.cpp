@@ -13,6 +13,7 @@
 #include <string_view>
 
 #include "attention.h"
+#include "gemv.h"
 #include "dmq_common.h"
 
 namespace {
@@ -219,9 +220,58 @@ int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream) {
   return run_gemm(probs, count, n_decode == count, (hipStream_t)stream);
 }
 
+namespace {
+
+// The projections of dmq_rmsnorm_gemm / dmq_residual_rmsnorm_gemm as problems
+// with activations x; with DMQ_PROJ_SWIGLU a Q4_K gate|up pair (N/2 a
+// multiple of 256) whose output is h = silu(gate) * up in fp16 [M, N/2].
+int proj_problems(const dmq_proj_desc* projs, int32_t count, const void* x, int64_t M, int64_t K,
+                  dmq::GemmProblem* probs) {
+  if (!projs || count < 1 || count > kMaxGroup) return DMQ_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    const dmq_proj_desc& d = projs[i];
+    if ((d.flags & ~DMQ_PROJ_SWIGLU) != 0 || (d.format != DMQ_FMT_Q4K && d.format != DMQ_FMT_Q6K))
+      return DMQ_ERR_INVALID_ARG;
+    const int swiglu = (d.flags & DMQ_PROJ_SWIGLU) ? 1 : 0;
+    if (swiglu && (d.format != DMQ_FMT_Q4K || d.N % 512 != 0)) return DMQ_ERR_INVALID_ARG;
+    int st = check_gemm(d.format, x, d.wq, d.y, M, d.N, K);
+    if (st != DMQ_OK) return st;
+    probs[i] = make_problem(d.format, x, d.wq, d.y, M, d.N, K, swiglu);
+  }
+  return DMQ_OK;
+}
+
+// Projections of one activation matrix: the decode kernel takes a mixed
+// group; the MFMA kernels take SwiGLU pairs one per launch (the epilogue is
+// the launch's), the plain projections together.
+int run_projs(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t s) {
+  if (decode) return run_gemm(probs, count, true, s);
+  dmq::GemmProblem plain[kMaxGroup];
+  int np = 0;
+  for (int i = 0; i < count; ++i)
+    if (!probs[i].swiglu) plain[np++] = probs[i];
+  if (np > 0) {
+    int st = run_gemm(plain, np, false, s);
+    if (st != DMQ_OK) return st;
+  }
+  for (int i = 0; i < count; ++i)
+    if (probs[i].swiglu) {
+      int st = run_gemm(&probs[i], 1, false, s);
+      if (st != DMQ_OK) return st;
+    }
+  return DMQ_OK;
+}
+
+// [p, p + n) and [q, q + n) share a byte
+bool overlap(const void* p, const void* q, int64_t n) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)n && b < a + (uintptr_t)n;
+}
+
+}  // namespace
+
 int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16, int64_t M, int64_t K,
                      const dmq_proj_desc* projs, int32_t count, void* stream) {
-  if (!projs || count < 1 || count > kMaxGroup) return DMQ_ERR_INVALID_ARG;
   if (!x_f16 || !g || !(eps >= 0.0f) || eps > 3.0e38f) return DMQ_ERR_INVALID_ARG;   // rejects NaN too
   if (!dim_ok(M) || check_quant_k(K) != DMQ_OK || K > kMaxK) return DMQ_ERR_INVALID_ARG;
   if (!aligned(x_f16, 16) || !aligned(g, 16)) return DMQ_ERR_ALIGNMENT;
@@ -232,13 +282,10 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
     if (!aligned(xn_f16, 16)) return DMQ_ERR_ALIGNMENT;
   }
   dmq::GemmProblem probs[kMaxGroup];
-  for (int i = 0; i < count; ++i) {
-    const dmq_proj_desc& d = projs[i];
-    if (d.reserved != 0 || (d.format != DMQ_FMT_Q4K && d.format != DMQ_FMT_Q6K)) return DMQ_ERR_INVALID_ARG;
-    int st = check_gemm(d.format, decode ? x_f16 : xn_f16, d.wq, d.y, M, d.N, K);
-    if (st != DMQ_OK) return st;
-    probs[i] = make_problem(d.format, decode ? x_f16 : xn_f16, d.wq, d.y, M, d.N, K, 0);
-    if (decode) {
+  int st = proj_problems(projs, count, decode ? x_f16 : xn_f16, M, K, probs);
+  if (st != DMQ_OK) return st;
+  if (decode) {
+    for (int i = 0; i < count; ++i) {
       probs[i].g = g;
       probs[i].eps = eps;
       probs[i].xn = i == 0 ? xn_f16 : nullptr;
@@ -247,10 +294,48 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   if (!decode) {
-    int st = hip_status(dmq::launch_rmsnorm(x_f16, g, eps, xn_f16, M, K, (hipStream_t)stream));
+    st = hip_status(dmq::launch_rmsnorm(x_f16, g, eps, xn_f16, M, K, (hipStream_t)stream));
     if (st != DMQ_OK) return st;
   }
-  return run_gemm(probs, count, decode, (hipStream_t)stream);
+  return run_projs(probs, count, decode, (hipStream_t)stream);
+}
+
+int dmq_residual_rmsnorm_gemm(const float* h_in, const float* y_add, const float* g, float eps, float* h_out,
+                              void* xn_f16, int64_t M, int64_t K, const dmq_proj_desc* projs, int32_t count,
+                              void* stream) {
+  if (!h_in || !y_add || !g || !h_out || !(eps >= 0.0f) || eps > 3.0e38f) return DMQ_ERR_INVALID_ARG;
+  if (!dim_ok(M) || check_quant_k(K) != DMQ_OK || K > kMaxK || M * K > (int64_t(1) << 40))
+    return DMQ_ERR_INVALID_ARG;
+  if (!aligned(h_in, 16) || !aligned(y_add, 16) || !aligned(g, 16) || !aligned(h_out, 16)) return DMQ_ERR_ALIGNMENT;
+  const int64_t hb = M * K * 4;
+  if (overlap(h_out, h_in, hb) || overlap(h_out, y_add, hb)) return DMQ_ERR_INVALID_ARG;
+  const bool decode = (M == 1 && K <= kGemvMaxK);
+  if (!decode && !xn_f16) return DMQ_ERR_INVALID_ARG;
+  if (xn_f16) {
+    if (!aligned(xn_f16, 16)) return DMQ_ERR_ALIGNMENT;
+    const int64_t xb = M * K * 2;
+    for (const void* p : {(const void*)h_in, (const void*)y_add, (const void*)h_out})
+      if ((uintptr_t)xn_f16 < (uintptr_t)p + (uintptr_t)hb && (uintptr_t)p < (uintptr_t)xn_f16 + (uintptr_t)xb)
+        return DMQ_ERR_INVALID_ARG;
+  }
+  dmq::GemmProblem probs[kMaxGroup];
+  // decode: the kernel reads h_in and y_add, not x; h_in stands in for the
+  // validation of the activation pointer
+  int st = proj_problems(projs, count, decode ? (const void*)h_in : xn_f16, M, K, probs);
+  if (st != DMQ_OK) return st;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  if (decode) {
+    for (int i = 0; i < count; ++i) {
+      probs[i].g = g;
+      probs[i].eps = eps;
+      probs[i].xn = i == 0 ? xn_f16 : nullptr;
+    }
+    return hip_status(dmq::launch_gemv_residual(probs, count, h_in, y_add, h_out, (hipStream_t)stream));
+  }
+  st = hip_status(dmq::launch_residual_rmsnorm(h_in, y_add, g, eps, h_out, xn_f16, M, K, (hipStream_t)stream));
+  if (st != DMQ_OK) return st;
+  return run_projs(probs, count, false, (hipStream_t)stream);
 }
 
 static bool heads_ok(int32_t hq, int32_t hkv) {

@@ -31,6 +31,7 @@
 // (low nibbles) and 2p+1 (high nibbles).  Q6_K part p owns half h = p >> 1
 // and weights with l in [16(p&1), 16(p&1)+16) of its four 32-weight quarters.
 #include "dmq_common.h"
+#include "gemv.h"
 
 #include <utility>
 
@@ -45,6 +46,9 @@ struct GemvDesc {
   const float* g;     // RMSNorm weights (K floats), or NULL: x is used as it is
   float eps;
   half_t* xn;         // with g: workgroup 0 writes the normalized x here (if set)
+  const float* hin;   // residual mode (with g): x = h_in + hadd in fp32, x is unused ...
+  const float* hadd;
+  float* hout;        // ... and workgroup 0 writes that sum here (if set)
   int32_t fmt, swiglu, N, K;
   int32_t wg_begin;   // first workgroup of this problem
 };
@@ -198,6 +202,22 @@ __device__ __forceinline__ int part_x_offset(int b, int part) {
 // super-blocks of the same 16 rows.
 constexpr int GEMV_ROWS = 16;
 
+// 1 / sqrt(mean((a + b)^2) + eps) over a row of K fp32 values: the sum a + b
+// rounded to fp32 first, as the residual connection stores it.
+__device__ __forceinline__ float rms_inv_sum(const float* a, const float* b, int K, float eps, float* red4) {
+  float ss = 0.0f;
+  for (int i = (int)threadIdx.x; i < K / 4; i += 256) {
+    const float4 x = ((const float4*)a)[i], y = ((const float4*)b)[i];
+    const float4 h = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    ss += (h.x * h.x + h.y * h.y) + (h.z * h.z + h.w * h.w);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float t = (red4[0] + red4[1]) + (red4[2] + red4[3]);
+  return 1.0f / __builtin_sqrtf(t / (float)K + eps);
+}
+
 template <int FMT, bool PAIR>
 __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_t* xs, float* red, float* red4) {
   typedef typename PartOf<FMT>::T Part;
@@ -217,8 +237,9 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
   // x of this wave's slice: global loads first, so the weight loads issued
   // next stay in flight while the slice is written to LDS
   const int xchunks = (b1 - b0) * 32;                     // 16-byte chunks
+  const bool res = P.hin != nullptr;                      // residual mode: no fp16 x
   const uint4* xg = (const uint4*)P.x + b0 * 32;
-  const bool xa = lane < xchunks, xb = lane + 64 < xchunks;
+  const bool xa = !res && lane < xchunks, xb = !res && lane + 64 < xchunks;
   uint4 xra = {0, 0, 0, 0}, xrb = {0, 0, 0, 0};
   if (xa) xra = xg[lane];
   if (xb) xrb = xg[lane + 64];
@@ -230,7 +251,7 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
   }
   // RMSNorm (when P.g is set): the workgroup's sum of squares over the
   // whole row, then each wave scales its slice as it stages it
-  const float rn = P.g ? rms_inv(P.x, P.K, P.eps, red4) : 1.0f;
+  const float rn = !P.g ? 1.0f : res ? rms_inv_sum(P.hin, P.hadd, P.K, P.eps, red4) : rms_inv(P.x, P.K, P.eps, red4);
   auto xput = [&](int i, uint4 v) {
     if (P.g) {
       v = norm8(v, P.g + 8 * i, rn);
@@ -238,10 +259,33 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
     }
     *(uint4*)((uint8_t*)xs + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v;
   };
-  if (xa) xput(b0 * 32 + lane, xra);
-  if (xb) xput(b0 * 32 + lane + 64, xrb);
-  for (int i = b0 * 32 + lane + 128; i < b1 * 32; i += 64)   // slices of more than 4 blocks
-    xput(i, ((const uint4*)P.x)[i]);
+  if (!res) {
+    if (xa) xput(b0 * 32 + lane, xra);
+    if (xb) xput(b0 * 32 + lane + 64, xrb);
+    for (int i = b0 * 32 + lane + 128; i < b1 * 32; i += 64)   // slices of more than 4 blocks
+      xput(i, ((const uint4*)P.x)[i]);
+  } else {
+    // residual mode: h = h_in + hadd (fp32, the residual stream; workgroup 0
+    // stores it), staged as fp16(h * g * r) like the residual kernel's xn
+    for (int i = b0 * 32 + lane; i < b1 * 32; i += 64) {
+      const float4 a0 = ((const float4*)P.hin)[2 * i], a1 = ((const float4*)P.hin)[2 * i + 1];
+      const float4 c0 = ((const float4*)P.hadd)[2 * i], c1 = ((const float4*)P.hadd)[2 * i + 1];
+      const float4 h0 = make_float4(a0.x + c0.x, a0.y + c0.y, a0.z + c0.z, a0.w + c0.w);
+      const float4 h1 = make_float4(a1.x + c1.x, a1.y + c1.y, a1.z + c1.z, a1.w + c1.w);
+      if (P.hout && wg_local == 0) {
+        ((float4*)P.hout)[2 * i] = h0;
+        ((float4*)P.hout)[2 * i + 1] = h1;
+      }
+      const float4 g0 = ((const float4*)P.g)[2 * i], g1 = ((const float4*)P.g)[2 * i + 1];
+      const h2 p0 = {(half_t)((h0.x * g0.x) * rn), (half_t)((h0.y * g0.y) * rn)};
+      const h2 p1 = {(half_t)((h0.z * g0.z) * rn), (half_t)((h0.w * g0.w) * rn)};
+      const h2 p2 = {(half_t)((h1.x * g1.x) * rn), (half_t)((h1.y * g1.y) * rn)};
+      const h2 p3 = {(half_t)((h1.z * g1.z) * rn), (half_t)((h1.w * g1.w) * rn)};
+      const uint4 v = make_uint4(as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3));
+      if (P.xn && wg_local == 0) ((uint4*)P.xn)[i] = v;
+      *(uint4*)((uint8_t*)xs + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v;
+    }
+  }
   // only this wave reads its slice: wait for its own LDS writes, no barrier
   // (the asm is also a compiler barrier for the LDS accesses around it)
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -320,7 +364,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs args) {
 
 // One workgroup per 16 rows; problems with the most bytes per workgroup
 // (the deepest K) are dispatched first so they do not trail.
-hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s) {
+static hipError_t launch_gemv_impl(const GemmProblem* probs, int count, const float* h_in, const float* h_add,
+                                   float* h_out, hipStream_t s) {
   for (int base = 0; base < count; base += GEMV_MAX_GROUP) {
     const int n = count - base < GEMV_MAX_GROUP ? count - base : GEMV_MAX_GROUP;
     int order[GEMV_MAX_GROUP];
@@ -341,6 +386,9 @@ hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s) {
       d.g = p.g;
       d.eps = p.eps;
       d.xn = (half_t*)p.xn;
+      d.hin = h_in;
+      d.hadd = h_add;
+      d.hout = order[i] == 0 ? h_out : nullptr;   // one writer of the residual stream
       d.fmt = p.fmt;
       d.swiglu = p.swiglu;
       d.N = p.N;
@@ -361,6 +409,15 @@ hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s) {
+  return launch_gemv_impl(probs, count, nullptr, nullptr, nullptr, s);
+}
+
+hipError_t launch_gemv_residual(const GemmProblem* probs, int count, const float* h_in, const float* h_add,
+                                float* h_out, hipStream_t s) {
+  return launch_gemv_impl(probs, count, h_in, h_add, h_out, s);
 }
 
 }  // namespace dmq

@@ -151,14 +151,19 @@ typedef struct {
 int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream);
 
 /*
- * One weight matrix of dmq_rmsnorm_gemm: y = RMSNorm(x) * W^T with W in the
- * given format (N rows of K/256 blocks) and y [M, N] fp32.
+ * One weight matrix of dmq_rmsnorm_gemm / dmq_residual_rmsnorm_gemm:
+ * y = RMSNorm(x) * W^T with W in the given format (N rows of K/256 blocks)
+ * and y [M, N] fp32.  With flags = DMQ_PROJ_SWIGLU, W is a Q4_K gate|up pair
+ * as in dmq_ffn_swiglu_q4k (rows 0..N/2-1 gate, N/2..N-1 up; N/2 a multiple
+ * of 256) and y points to the fp16 output h [M, N/2], h = silu(gate) * up
+ * (the SwiGLU of the FFN, article "Building DAMASCUS", layer description).
  */
+#define DMQ_PROJ_SWIGLU 1
 typedef struct {
   int32_t format;      /* DMQ_FMT_Q4K or DMQ_FMT_Q6K */
-  int32_t reserved;    /* must be 0 */
+  int32_t flags;       /* 0 or DMQ_PROJ_SWIGLU */
   const void* wq;
-  float* y;
+  float* y;            /* fp32 y, or fp16 h with DMQ_PROJ_SWIGLU (16-byte aligned) */
   int64_t N;
 } dmq_proj_desc;
 
@@ -187,6 +192,32 @@ typedef struct {
 int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
                      int64_t M, int64_t K, const dmq_proj_desc* projs, int32_t count,
                      void* stream);
+
+/*
+ * The residual connection, the next RMSNorm and the projections that read it,
+ * as one call: a decoder layer adds the attention output (then the FFN
+ * output) to the residual stream and normalizes the sum before the gate|up
+ * (then the next layer's Q|K|V) projections (overview page, "[04] one decode
+ * step"; article "Building DAMASCUS", layer description).
+ *   h_in, y_add : [M, K] fp32, 16-byte aligned (the residual stream and the
+ *                 output added to it).
+ *   h_out       : [M, K] fp32, 16-byte aligned: h_out = h_in + y_add (IEEE
+ *                 fp32 adds, exact to the bit).  It must not overlap h_in or
+ *                 y_add (other workgroups still read them): keep two residual
+ *                 buffers and alternate.
+ *   g, eps      : as in dmq_rmsnorm_gemm, applied to h_out.
+ *   xn_f16      : [M, K] fp16, 16-byte aligned, overlapping none of the
+ *                 above: fp16(h_out * g / sqrt(mean(h_out^2) + eps)) within
+ *                 one fp16 step of the exact value.  Optional (NULL) when
+ *                 M = 1 and K <= 32768: the decode kernel then forms the sum,
+ *                 the norm and the staged activations in one launch, every
+ *                 workgroup from h_in and y_add, one of them writing h_out.
+ *                 Otherwise a residual + RMSNorm kernel runs first.
+ *   projs       : as in dmq_rmsnorm_gemm, with xn as the activations.
+ */
+int dmq_residual_rmsnorm_gemm(const float* h_in, const float* y_add, const float* g, float eps,
+                              float* h_out, void* xn_f16, int64_t M, int64_t K,
+                              const dmq_proj_desc* projs, int32_t count, void* stream);
 
 /*
  * The attention side of a decoder layer (overview page, "[04] one decode step":

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(dmq.EXPORTS)
     raw = ctypes.CDLL(dmq.LIB_PATH)
     for n in names:
@@ -127,9 +127,9 @@ def test_gemm_k_limit():
     assert L.dmq_gemm_q6k(A16, A16, A16, 1, 4, (1 << 20) + 256, None) == dmq.DMQ_ERR_INVALID_ARG
 
 
-def _proj(fmt=0, N=4, wq=A16, y=A16, reserved=0):
+def _proj(fmt=0, N=4, wq=A16, y=A16, flags=0):
     d = dmq.ProjDesc()
-    d.format, d.reserved, d.wq, d.y, d.N = fmt, reserved, wq, y, N
+    d.format, d.flags, d.wq, d.y, d.N = fmt, flags, wq, y, N
     return d
 
 
@@ -152,7 +152,11 @@ def test_rmsnorm_gemm_validation():
     assert f(MIS, G, 1e-5, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
     assert f(X, G + 8, 1e-5, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
     assert f(X, G, 1e-5, XN + 8, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
-    bad = (dmq.ProjDesc * 1)(_proj(reserved=1))
+    bad = (dmq.ProjDesc * 1)(_proj(flags=2))                   # unknown flag
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.ProjDesc * 1)(_proj(flags=1))                   # SwiGLU pair: N/2 not a multiple of 256
+    assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.ProjDesc * 1)(_proj(fmt=1, N=512, flags=1))     # SwiGLU pair in Q6_K
     assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
     bad = (dmq.ProjDesc * 1)(_proj(fmt=5))
     assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
@@ -162,6 +166,33 @@ def test_rmsnorm_gemm_validation():
     assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_ALIGNMENT
     bad = (dmq.ProjDesc * 1)(_proj(wq=A16 + 2))                # Q4_K weights need 16 bytes
     assert f(X, G, 1e-5, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_ALIGNMENT
+
+
+def test_residual_rmsnorm_gemm_validation():
+    f = L.dmq_residual_rmsnorm_gemm
+    p = (dmq.ProjDesc * 2)(_proj(), _proj(fmt=1))
+    H, Y, G, HO, XN = (A16 + 0x1000 * i for i in range(5))
+    # M = 4, K = 256: 4 KiB of fp32 per residual buffer, 2 KiB of xn
+    assert f(H, Y, G, 1e-5, HO, XN, 4, 256, p, 0, None) == dmq.DMQ_ERR_INVALID_ARG      # count
+    assert f(H, Y, G, 1e-5, HO, XN, 4, 256, None, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(None, Y, G, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(H, None, G, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(H, Y, None, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(H, Y, G, 1e-5, None, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(H, Y, G, float("nan"), HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(H, Y, G, 1e-5, HO, XN, 4, 300, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG       # K % 256
+    assert f(H, Y, G, 1e-5, HO, None, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG     # xn needed for M > 1
+    assert f(H, Y, G, 1e-5, H, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG        # h_out is h_in
+    assert f(H, Y, G, 1e-5, H + 0x800, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG  # overlaps h_in
+    assert f(H, Y, G, 1e-5, Y, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG        # h_out is y_add
+    assert f(H, Y, G, 1e-5, HO, HO + 0x400, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG  # xn inside h_out
+    assert f(MIS, Y, G, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    assert f(H, Y, G, 1e-5, HO + 8, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    assert f(H, Y, G, 1e-5, HO, XN + 8, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
+    bad = (dmq.ProjDesc * 1)(_proj(flags=1))                   # SwiGLU pair: N/2 not a multiple of 256
+    assert f(H, Y, G, 1e-5, HO, XN, 4, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG
+    bad = (dmq.ProjDesc * 1)(_proj(N=0))
+    assert f(H, Y, G, 1e-5, HO, None, 1, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG  # decode path too
 
 
 def test_rope_kv_cache_validation():

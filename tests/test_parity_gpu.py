@@ -802,6 +802,52 @@ def test_residual_rmsnorm(dmq):
         assert ok.all(), f"residual+rmsnorm M={M}: {int((~ok).sum())} normalized values outside the interval"
 
 
+@pytest.mark.parametrize("M,K", [(1, 768), (1, 3072), (5, 768)])
+def test_residual_rmsnorm_gemm(dmq, M, K):
+    """Residual add + RMSNorm + projections in one call: at M = 1 the decode
+    kernel forms the sum and the norm while staging x (one launch), above it
+    the residual kernel runs first.  Plain Q4_K and Q6_K projections and a
+    SwiGLU gate|up pair (h = silu(gate) * up in fp16)."""
+    rng = np.random.default_rng(M * 31 + K)
+    h = rng.standard_normal((M, K)).astype(np.float32)
+    ya = (rng.standard_normal((M, K)) * 2.0).astype(np.float32)
+    g = _norm_weights(K, seed=K + 7)
+    wq4 = synthetic.q4k_blocks(96, K, seed=K + 1)
+    wq6 = synthetic.q6k_blocks(64, K, seed=K + 2)
+    wgu = synthetic.q4k_blocks(1024, K, seed=K + 3)
+
+    def run(with_xn):
+        ho = torch.empty((M, K), dtype=torch.float32, device=DEV)
+        xn = torch.empty((M, K), dtype=torch.float16, device=DEV) if with_xn else None
+        y4 = torch.empty((M, 96), dtype=torch.float32, device=DEV)
+        y6 = torch.empty((M, 64), dtype=torch.float32, device=DEV)
+        hh = torch.empty((M, 512), dtype=torch.float16, device=DEV)
+        projs = [("q4k", dev(wq4), y4, 96), ("q6k", dev(wq6), y6, 64), ("q4k", dev(wgu), hh, 1024, "swiglu")]
+        dmq.dmq_residual_rmsnorm_gemm(dev(h), dev(ya), dev(g), 1e-5, ho, xn, projs, M, K)
+        torch.cuda.synchronize()
+        return ho.cpu().numpy(), (None if xn is None else xn.cpu().numpy()), y4.cpu().numpy(), \
+            y6.cpu().numpy(), hh.cpu().numpy()
+
+    ho, xnh, y4, y6, hh = run(True)
+    assert np.array_equal(ho, h + ya), "h_out is not the fp32 sum"
+    lo, hi = oracle.rmsnorm_f16_interval(attn.rmsnorm_f64(ho, g, 1e-5))
+    xg = xnh.astype(np.float64)
+    assert np.all((xg >= lo) & (xg <= hi)), "xn outside the RMSNorm interval"
+    for fmt, wq, N, y in (("q4k", wq4, 96, y4), ("q6k", wq6, 64, y6)):
+        ref, sc = oracle.gemm_quant(fmt, xnh, wq, N, K)
+        err = np.abs(y.astype(np.float64) - ref)
+        assert (err <= oracle.gemm_tolerance(sc)).all(), f"{fmt} projection out of bound"
+    gu, sc = oracle.gemm_quant("q4k", xnh, wgu, 1024, K)
+    eg = oracle.gemm_tolerance(sc)
+    hlo, hhi = oracle.swiglu_interval(gu[:, :512], gu[:, 512:], eg[:, :512], eg[:, 512:])
+    assert oracle.swiglu_accepts(hh.astype(np.float64), hlo, hhi).all(), "SwiGLU h outside the interval"
+    if M == 1:
+        # without xn the decode launch computes the same staged activations
+        ho2, _, y42, y62, hh2 = run(False)
+        assert np.array_equal(ho2, ho) and np.array_equal(y42, y4) and np.array_equal(y62, y6)
+        assert np.array_equal(hh2, hh)
+
+
 @pytest.mark.parametrize("M,pos0", [(1, 37), (16, 0), (5, 200)])
 def test_decoder_layer_chain(dmq, M, pos0):
     """One decoder layer through the library on a small Llama-shaped layer
