@@ -262,10 +262,10 @@ int run_projs(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t
   return DMQ_OK;
 }
 
-// [p, p + n) and [q, q + n) share a byte
-bool overlap(const void* p, const void* q, int64_t n) {
+// [p, p + pn) and [q, q + qn) share a byte
+bool overlap(const void* p, int64_t pn, const void* q, int64_t qn) {
   const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
-  return a < b + (uintptr_t)n && b < a + (uintptr_t)n;
+  return a < b + (uintptr_t)qn && b < a + (uintptr_t)pn;
 }
 
 }  // namespace
@@ -308,15 +308,16 @@ int dmq_residual_rmsnorm_gemm(const float* h_in, const float* y_add, const float
     return DMQ_ERR_INVALID_ARG;
   if (!aligned(h_in, 16) || !aligned(y_add, 16) || !aligned(g, 16) || !aligned(h_out, 16)) return DMQ_ERR_ALIGNMENT;
   const int64_t hb = M * K * 4;
-  if (overlap(h_out, h_in, hb) || overlap(h_out, y_add, hb)) return DMQ_ERR_INVALID_ARG;
+  if (overlap(h_out, hb, h_in, hb) || overlap(h_out, hb, y_add, hb) || overlap(h_out, hb, g, K * 4))
+    return DMQ_ERR_INVALID_ARG;
   const bool decode = (M == 1 && K <= kGemvMaxK);
   if (!decode && !xn_f16) return DMQ_ERR_INVALID_ARG;
   if (xn_f16) {
     if (!aligned(xn_f16, 16)) return DMQ_ERR_ALIGNMENT;
     const int64_t xb = M * K * 2;
-    for (const void* p : {(const void*)h_in, (const void*)y_add, (const void*)h_out})
-      if ((uintptr_t)xn_f16 < (uintptr_t)p + (uintptr_t)hb && (uintptr_t)p < (uintptr_t)xn_f16 + (uintptr_t)xb)
-        return DMQ_ERR_INVALID_ARG;
+    if (overlap(xn_f16, xb, h_in, hb) || overlap(xn_f16, xb, y_add, hb) || overlap(xn_f16, xb, h_out, hb) ||
+        overlap(xn_f16, xb, g, K * 4))
+      return DMQ_ERR_INVALID_ARG;
   }
   dmq::GemmProblem probs[kMaxGroup];
   // decode: the kernel reads h_in and y_add, not x; h_in stands in for the

@@ -202,9 +202,10 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
  *   h_in, y_add : [M, K] fp32, 16-byte aligned (the residual stream and the
  *                 output added to it).
  *   h_out       : [M, K] fp32, 16-byte aligned: h_out = h_in + y_add (IEEE
- *                 fp32 adds, exact to the bit).  It must not overlap h_in or
- *                 y_add (other workgroups still read them): keep two residual
- *                 buffers and alternate.
+ *                 fp32 adds, exact to the bit).  It must not overlap h_in,
+ *                 y_add or g (other workgroups still read them): keep two
+ *                 residual buffers and alternate.  Overlaps are rejected
+ *                 (DMQ_ERR_INVALID_ARG).
  *   g, eps      : as in dmq_rmsnorm_gemm, applied to h_out.
  *   xn_f16      : [M, K] fp16, 16-byte aligned, overlapping none of the
  *                 above: fp16(h_out * g / sqrt(mean(h_out^2) + eps)) within

@@ -186,6 +186,8 @@ def test_residual_rmsnorm_gemm_validation():
     assert f(H, Y, G, 1e-5, H + 0x800, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG  # overlaps h_in
     assert f(H, Y, G, 1e-5, Y, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG        # h_out is y_add
     assert f(H, Y, G, 1e-5, HO, HO + 0x400, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG  # xn inside h_out
+    assert f(H, Y, HO + 0x200, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG  # g inside h_out
+    assert f(H, Y, XN + 0x100, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_INVALID_ARG  # g inside xn
     assert f(MIS, Y, G, 1e-5, HO, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
     assert f(H, Y, G, 1e-5, HO + 8, XN, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
     assert f(H, Y, G, 1e-5, HO, XN + 8, 4, 256, p, 2, None) == dmq.DMQ_ERR_ALIGNMENT
