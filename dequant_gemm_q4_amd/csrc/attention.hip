@@ -461,9 +461,10 @@ static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) 
 // whole key loop.  Keys go in blocks of 32, staged in LDS by each half (K
 // row-major with 16-byte chunks XOR-swizzled by the key; V transposed to
 // [dim][key pair], packed 32-bit words on conflict-free banks), double-
-// buffered, the next block's global loads in flight during the current
-// block's compute.  Per key block and wave, with v_mfma_f32_32x32x16_f16
-// (D = A B^T):
+// buffered, with the global loads of later blocks in flight during the
+// current block's compute.  A half's iteration forms the scores of its next
+// block while the current block's softmax runs (software pipeline).  Per key
+// block and wave, with v_mfma_f32_32x32x16_f16 (D = A B^T):
 //  * S^T = K Q^T (A = K rows, B = Q rows, 8 MFMAs over the 128 dims): an
 //    accumulator lane holds one query (its lane % 32) and 16 of the 32 keys,
 //    the lane 32 away the other 16, so a query's maximum and sum need one
@@ -540,10 +541,10 @@ __global__ __launch_bounds__(512) void attention_mfma_kernel(AttnArgs a, int M, 
   // ..+7).  V: thread t holds keys 2 jp, 2 jp + 1 at dims 8 cv .. +7 and
   // writes them as 8 key pairs (one 32-bit word per dim) of V^T; a wave's
   // lanes take 8 key pairs x 8 dim chunks, which the row stride of 18 words and
-  // the swizzle keep on 64 distinct banks.  The loads of block kb+1 are issued
-  // before block kb's compute and written to LDS after it; they are
-  // unconditional (rows past the last key re-read the last one and are zeroed
-  // when stored), so no branch makes the compiler wait for them early.
+  // the swizzle keep on 64 distinct banks.  A block's loads are issued before
+  // an iteration's compute and written to LDS after it (K two blocks ahead of
+  // the softmax, V one); rows past the last key re-read the last one and are
+  // zeroed when stored, so the load addresses need no branch.
   uint4 kr0, kr1, va, vb;
   const int ck0 = tid >> 4, ck1 = (tid + 256) >> 4, cch = tid & 15;
   const int jp = (tid & 7) + 8 * ((tid >> 6) & 1), cv = ((tid >> 3) & 7) + 8 * (tid >> 7);
