@@ -251,7 +251,35 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
   }
   // RMSNorm (when P.g is set): the workgroup's sum of squares over the
   // whole row, then each wave scales its slice as it stages it
-  const float rn = !P.g ? 1.0f : res ? rms_inv_sum(P.hin, P.hadd, P.K, P.eps, red4) : rms_inv(P.x, P.K, P.eps, red4);
+  // residual mode with slices of at most 4 blocks (K <= 4096, the same test in
+  // every wave): one pass, each lane keeps the sums of its own (at most two)
+  // chunks in registers while the row's sum of squares is reduced
+  const bool res1 = res && nb <= 16;
+  float4 hk[2][2];
+  float ss1 = 0.0f;
+  if (res1) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = b0 * 32 + lane + 64 * j;
+      if (lane + 64 * j < xchunks) {
+        const float4 a0 = ((const float4*)P.hin)[2 * i], a1 = ((const float4*)P.hin)[2 * i + 1];
+        const float4 c0 = ((const float4*)P.hadd)[2 * i], c1 = ((const float4*)P.hadd)[2 * i + 1];
+        hk[j][0] = make_float4(a0.x + c0.x, a0.y + c0.y, a0.z + c0.z, a0.w + c0.w);
+        hk[j][1] = make_float4(a1.x + c1.x, a1.y + c1.y, a1.z + c1.z, a1.w + c1.w);
+        ss1 += ((hk[j][0].x * hk[j][0].x + hk[j][0].y * hk[j][0].y) +
+                (hk[j][0].z * hk[j][0].z + hk[j][0].w * hk[j][0].w)) +
+               ((hk[j][1].x * hk[j][1].x + hk[j][1].y * hk[j][1].y) +
+                (hk[j][1].z * hk[j][1].z + hk[j][1].w * hk[j][1].w));
+      }
+    }
+    ss1 = wave_sum(ss1);
+    if (lane == 0) red4[wave] = ss1;
+    __syncthreads();
+  }
+  const float rn = !P.g ? 1.0f
+                 : res1 ? 1.0f / __builtin_sqrtf(((red4[0] + red4[1]) + (red4[2] + red4[3])) / (float)P.K + P.eps)
+                 : res  ? rms_inv_sum(P.hin, P.hadd, P.K, P.eps, red4)
+                        : rms_inv(P.x, P.K, P.eps, red4);
   auto xput = [&](int i, uint4 v) {
     if (P.g) {
       v = norm8(v, P.g + 8 * i, rn);
@@ -267,11 +295,17 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
   } else {
     // residual mode: h = h_in + hadd (fp32, the residual stream; workgroup 0
     // stores it), staged as fp16(h * g * r) like the residual kernel's xn
-    for (int i = b0 * 32 + lane; i < b1 * 32; i += 64) {
-      const float4 a0 = ((const float4*)P.hin)[2 * i], a1 = ((const float4*)P.hin)[2 * i + 1];
-      const float4 c0 = ((const float4*)P.hadd)[2 * i], c1 = ((const float4*)P.hadd)[2 * i + 1];
-      const float4 h0 = make_float4(a0.x + c0.x, a0.y + c0.y, a0.z + c0.z, a0.w + c0.w);
-      const float4 h1 = make_float4(a1.x + c1.x, a1.y + c1.y, a1.z + c1.z, a1.w + c1.w);
+    for (int i = b0 * 32 + lane, j = 0; i < b1 * 32; i += 64, ++j) {
+      float4 h0, h1;
+      if (res1) {   // j < 2 here: the slice has at most 128 chunks
+        h0 = j == 0 ? hk[0][0] : hk[1][0];
+        h1 = j == 0 ? hk[0][1] : hk[1][1];
+      } else {
+        const float4 a0 = ((const float4*)P.hin)[2 * i], a1 = ((const float4*)P.hin)[2 * i + 1];
+        const float4 c0 = ((const float4*)P.hadd)[2 * i], c1 = ((const float4*)P.hadd)[2 * i + 1];
+        h0 = make_float4(a0.x + c0.x, a0.y + c0.y, a0.z + c0.z, a0.w + c0.w);
+        h1 = make_float4(a1.x + c1.x, a1.y + c1.y, a1.z + c1.z, a1.w + c1.w);
+      }
       if (P.hout && wg_local == 0) {
         ((float4*)P.hout)[2 * i] = h0;
         ((float4*)P.hout)[2 * i + 1] = h1;

@@ -802,7 +802,7 @@ def test_residual_rmsnorm(dmq):
         assert ok.all(), f"residual+rmsnorm M={M}: {int((~ok).sum())} normalized values outside the interval"
 
 
-@pytest.mark.parametrize("M,K", [(1, 768), (1, 3072), (5, 768)])
+@pytest.mark.parametrize("M,K", [(1, 768), (1, 3072), (1, 8192), (5, 768)])
 def test_residual_rmsnorm_gemm(dmq, M, K):
     """Residual add + RMSNorm + projections in one call: at M = 1 the decode
     kernel forms the sum and the norm while staging x (one launch), above it
