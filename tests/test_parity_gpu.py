@@ -738,17 +738,18 @@ def test_attention_gqa_prefill_mfma(dmq, M, pos0, hq, hkv):
     _check_attention(q, kc, vc, out, M, pos0, hq, f"attention prefill M={M} pos0={pos0} hq={hq} hkv={hkv}")
 
 
-def test_attention_gqa_prefill_full_size_sampled(dmq):
-    """The Llama-3.2-3B prefill shape (1024 queries from position 0, 24 query
-    heads over 8 KV heads), every output of a sample of query rows that
-    covers every 128-query block and both ends."""
-    M, hq, hkv = 1024, 24, 8
-    q, kc, vc, out = _attention_case(dmq, M, 0, hq, hkv, M, seed=77)
-    rows = synthetic.row_sample(M, 24, seed=3, tile=128)
+@pytest.mark.parametrize("M", [1024, 2048])
+def test_attention_gqa_prefill_full_size_sampled(dmq, M):
+    """The Llama-3.2-3B prefill shape (1024 or 2048 queries from position 0,
+    24 query heads over 8 KV heads), every output of a sample of query rows
+    that covers every 128-query block and both ends."""
+    hq, hkv = 24, 8
+    q, kc, vc, out = _attention_case(dmq, M, 0, hq, hkv, M, seed=77 + M)
+    rows = synthetic.row_sample(M, 24 * M // 1024, seed=3, tile=128)
     # the oracle on the sampled rows: each row's attention depends only on its
     # own query and the cache
     for r in rows:
-        _check_attention(q[r:r + 1], kc, vc, out[r:r + 1], 1, int(r), hq, f"attention prefill 1024 row {r}")
+        _check_attention(q[r:r + 1], kc, vc, out[r:r + 1], 1, int(r), hq, f"attention prefill {M} row {r}")
 
 
 def test_attention_gqa_peaked_scores(dmq):
