@@ -689,3 +689,91 @@ def test_generators_deterministic_and_in_range():
     assert np.allclose(rms, 1.0, atol=2e-3)
     s = synthetic.row_sample(1024, 40, seed=1)
     assert s[0] == 0 and s[-1] == 1023 and len(set(s // 256)) == 4
+
+
+# ------------------------------------------------- acceptance intervals -----
+# oracle.f16_interval is the acceptance interval of every check whose GPU
+# result is one fp16 rounding of a value known within an absolute slack (the
+# RoPE outputs).  Pinned here against an exhaustive search of the fp16 grid:
+# every finite fp16 value, sorted, extended by -inf and +inf.
+
+def _fp16_grid():
+    v = np.arange(0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    v = v[np.isfinite(v)]
+    return np.unique(np.concatenate([v, [-np.inf, np.inf]]))     # -0 and +0 merge
+
+
+def test_f16_interval_closed_forms():
+    cases = [
+        # (exact, slack, lo, hi)
+        (1.0, 0.0, 1.0, 1.0),                                  # on the grid, no slack: degenerate
+        (-3.5, 0.0, -3.5, -3.5),
+        (0.0, 0.0, 0.0, 0.0),
+        (1.0, 1e-6, 1.0 - 2.0 ** -11, 1.0 + 2.0 ** -10),       # binade edge: the step below 1 is half
+        (2.0, 1e-6, 2.0 - 2.0 ** -10, 2.0 + 2.0 ** -9),
+        (-1.0, 1e-6, -(1.0 + 2.0 ** -10), -(1.0 - 2.0 ** -11)),  # negative: mirrored
+        (0.0, 1e-9, -2.0 ** -24, 2.0 ** -24),                  # smallest subnormals
+        (1.5 * 2.0 ** -24, 0.0, 2.0 ** -24, 2.0 ** -23),
+        (65504.0, 1.0, 65472.0, np.inf),                       # past the largest finite value: inf
+        (-65504.0, 1.0, -np.inf, -65472.0),
+        (1e6, 0.0, 65504.0, np.inf),                           # RNE(1e6) = inf lies inside
+    ]
+    ex = np.array([c[0] for c in cases])
+    sl = np.array([c[1] for c in cases])
+    lo, hi = oracle.f16_interval(ex, sl)
+    for i, (e, s, l, h) in enumerate(cases):
+        assert lo[i] == l and hi[i] == h, f"f16_interval({e}, {s}) = [{lo[i]}, {hi[i]}], want [{l}, {h}]"
+
+
+def test_f16_interval_matches_exhaustive_grid_search():
+    grid = _fp16_grid()
+    rng = np.random.default_rng(21)
+    n = 20000
+    scale = 2.0 ** rng.integers(-30, 18, n)                       # subnormal range to past overflow
+    exact = rng.standard_normal(n) * scale
+    exact[:2000] = rng.choice(grid[1:-1], 2000)                   # exact grid points
+    slack = np.abs(exact) * rng.choice([0.0, 2.0 ** -30, 2.0 ** -12, 2.0 ** -9, 2.0 ** -6], n)
+    slack[2000:2500] = 0.0
+    lo, hi = oracle.f16_interval(exact, slack)
+    a, b = exact - slack, exact + slack
+    lo_ref = grid[np.searchsorted(grid, a, side="right") - 1]     # largest grid value <= a
+    hi_ref = grid[np.searchsorted(grid, b, side="left")]          # smallest grid value >= b
+    assert np.array_equal(lo, lo_ref) and np.array_equal(hi, hi_ref)
+
+
+def test_f16_interval_accepts_rne_rejects_two_ulps():
+    """With zero slack the interval holds RNE(exact) (and the other grid
+    neighbour), and nothing two fp16 steps away."""
+    rng = np.random.default_rng(22)
+    exact = rng.standard_normal(5000) * 2.0 ** rng.integers(-12, 12, 5000)
+    lo, hi = oracle.f16_interval(exact, np.zeros_like(exact))
+    h = exact.astype(np.float16)
+    assert np.all((h.astype(np.float64) >= lo) & (h.astype(np.float64) <= hi))
+    for direction in (np.float16(np.inf), np.float16(-np.inf)):
+        far = np.nextafter(np.nextafter(h, direction), direction).astype(np.float64)
+        assert not np.any((far >= lo) & (far <= hi))
+
+
+def test_p13_attention_mass():
+    """mass = sum_t p_t |v_t|, the scale of each attention output: one
+    visible key gives |v_0|; equal keys give the mean of |v| over the visible
+    positions; with nonnegative values it equals the output; against the
+    explicit loops (with |v|) on a small prefill."""
+    rng = np.random.default_rng(23)
+    d = 16
+    q = rng.standard_normal((1, 6, d))
+    kc = rng.standard_normal((2, 7, d))
+    vc = rng.standard_normal((2, 7, d))
+    _, mass = attn.attention_gqa(q, kc, vc, 0)
+    for h in range(6):
+        assert np.array_equal(mass[0, h], np.abs(vc[h // 3, 0]))
+    kc_eq = np.repeat(kc[:, :1, :], 7, axis=1)
+    _, mass = attn.attention_gqa(q, kc_eq, vc, 4)                 # positions 0..4 visible
+    for h in range(6):
+        assert np.allclose(mass[0, h], np.abs(vc[h // 3, :5]).mean(axis=0), rtol=1e-14, atol=0)
+    qp = rng.standard_normal((3, 6, d))
+    out, mass = attn.attention_gqa(qp, kc, np.abs(vc), 2)
+    assert np.allclose(mass, out, rtol=1e-14, atol=0)
+    _, mass = attn.attention_gqa(qp, kc, vc, 2)
+    assert np.allclose(mass, _attention_loops(qp, kc, np.abs(vc), 2), rtol=1e-12, atol=1e-13)
+    assert np.all(mass >= np.abs(attn.attention_gqa(qp, kc, vc, 2)[0]) - 1e-12)
