@@ -222,11 +222,26 @@ int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream) {
 
 namespace {
 
+// [p, p + pn) and [q, q + qn) share a byte
+bool overlap(const void* p, int64_t pn, const void* q, int64_t qn) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qn && b < a + (uintptr_t)pn;
+}
+
+// A byte range the launch reads (or another output writes) while the
+// projections' outputs are being written.
+struct Range {
+  const void* p;
+  int64_t n;
+};
+
 // The projections of dmq_rmsnorm_gemm / dmq_residual_rmsnorm_gemm as problems
 // with activations x; with DMQ_PROJ_SWIGLU a Q4_K gate|up pair (N/2 a
 // multiple of 256) whose output is h = silu(gate) * up in fp16 [M, N/2].
+// No output may overlap another output or any of the `busy` ranges: in one
+// launch some workgroups write an output while others still read its inputs.
 int proj_problems(const dmq_proj_desc* projs, int32_t count, const void* x, int64_t M, int64_t K,
-                  dmq::GemmProblem* probs) {
+                  const Range* busy, int nbusy, dmq::GemmProblem* probs) {
   if (!projs || count < 1 || count > kMaxGroup) return DMQ_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
     const dmq_proj_desc& d = projs[i];
@@ -237,6 +252,13 @@ int proj_problems(const dmq_proj_desc* projs, int32_t count, const void* x, int6
     int st = check_gemm(d.format, x, d.wq, d.y, M, d.N, K);
     if (st != DMQ_OK) return st;
     probs[i] = make_problem(d.format, x, d.wq, d.y, M, d.N, K, swiglu);
+  }
+  auto out_bytes = [&](int i) { return projs[i].flags & DMQ_PROJ_SWIGLU ? M * (projs[i].N / 2) * 2 : M * projs[i].N * 4; };
+  for (int i = 0; i < count; ++i) {
+    for (int b = 0; b < nbusy; ++b)
+      if (busy[b].p && overlap(projs[i].y, out_bytes(i), busy[b].p, busy[b].n)) return DMQ_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlap(projs[i].y, out_bytes(i), projs[j].y, out_bytes(j))) return DMQ_ERR_INVALID_ARG;
   }
   return DMQ_OK;
 }
@@ -262,12 +284,6 @@ int run_projs(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t
   return DMQ_OK;
 }
 
-// [p, p + pn) and [q, q + qn) share a byte
-bool overlap(const void* p, int64_t pn, const void* q, int64_t qn) {
-  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
-  return a < b + (uintptr_t)qn && b < a + (uintptr_t)pn;
-}
-
 }  // namespace
 
 int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16, int64_t M, int64_t K,
@@ -282,7 +298,8 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
     if (!aligned(xn_f16, 16)) return DMQ_ERR_ALIGNMENT;
   }
   dmq::GemmProblem probs[kMaxGroup];
-  int st = proj_problems(projs, count, decode ? x_f16 : xn_f16, M, K, probs);
+  const Range busy[3] = {{x_f16, M * K * 2}, {g, K * 4}, {xn_f16, M * K * 2}};
+  int st = proj_problems(projs, count, decode ? x_f16 : xn_f16, M, K, busy, 3, probs);
   if (st != DMQ_OK) return st;
   if (decode) {
     for (int i = 0; i < count; ++i) {
@@ -322,7 +339,8 @@ int dmq_residual_rmsnorm_gemm(const float* h_in, const float* y_add, const float
   dmq::GemmProblem probs[kMaxGroup];
   // decode: the kernel reads h_in and y_add, not x; h_in stands in for the
   // validation of the activation pointer
-  int st = proj_problems(projs, count, decode ? (const void*)h_in : xn_f16, M, K, probs);
+  const Range busy[5] = {{h_in, hb}, {y_add, hb}, {h_out, hb}, {g, K * 4}, {xn_f16, M * K * 2}};
+  int st = proj_problems(projs, count, decode ? (const void*)h_in : xn_f16, M, K, busy, 5, probs);
   if (st != DMQ_OK) return st;
   int dc = check_device();
   if (dc != DMQ_OK) return dc;

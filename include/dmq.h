@@ -182,7 +182,9 @@ typedef struct {
  *            M = 1 (and K <= 32768) the decode kernel normalizes x while it
  *            stages it; xn is then optional (NULL: not written).
  *   projs  : 1..64 projections (host array, read before the call returns), all
- *            with reduction length K.
+ *            with reduction length K.  No projection output may overlap x, g,
+ *            xn or another projection's output (DMQ_ERR_INVALID_ARG): within
+ *            the launch, workgroups write outputs while others still read.
  * y_i = xn * W_i^T for each projection with xn as the activations, under the
  * rules and the per-output bound of dmq_gemm_q4k / dmq_gemm_q6k (one grouped
  * launch after the normalization).  The fp16 rounding of xn is part of the
@@ -214,7 +216,9 @@ int dmq_rmsnorm_gemm(const void* x_f16, const float* g, float eps, void* xn_f16,
  *                 the norm and the staged activations in one launch, every
  *                 workgroup from h_in and y_add, one of them writing h_out.
  *                 Otherwise a residual + RMSNorm kernel runs first.
- *   projs       : as in dmq_rmsnorm_gemm, with xn as the activations.
+ *   projs       : as in dmq_rmsnorm_gemm, with xn as the activations; no
+ *                 projection output may overlap h_in, y_add, h_out, g, xn or
+ *                 another output (DMQ_ERR_INVALID_ARG).
  */
 int dmq_residual_rmsnorm_gemm(const float* h_in, const float* y_add, const float* g, float eps,
                               float* h_out, void* xn_f16, int64_t M, int64_t K,

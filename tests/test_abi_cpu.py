@@ -197,6 +197,38 @@ def test_residual_rmsnorm_gemm_validation():
     assert f(H, Y, G, 1e-5, HO, None, 1, 256, bad, 1, None) == dmq.DMQ_ERR_INVALID_ARG  # decode path too
 
 
+def test_projection_outputs_must_not_overlap_inputs_or_each_other():
+    """In one launch some workgroups write a projection's output while others
+    still read the activations, the norm weights and the residual buffers
+    (and write the other outputs): every such overlap is rejected.  Each
+    case below is valid except for the one overlap it names (M = 4, K = 256:
+    2 KiB of fp16 x / xn, 4 KiB of fp32 residual rows, 1 KiB of g; a plain
+    projection with N = 4 writes 64 bytes, a SwiGLU pair with N = 512
+    writes 4 * 256 fp16 = 2 KiB)."""
+    X, G, XN = A16, A16 + 0x1000, A16 + 0x2000
+    Y0, Y1 = A16 + 0x8000, A16 + 0x9000
+
+    def rms(*projs):
+        arr = (dmq.ProjDesc * len(projs))(*projs)
+        return L.dmq_rmsnorm_gemm(X, G, 1e-5, XN, 4, 256, arr, len(projs), None)
+    for y in (X + 0x7c0, G + 0x20, XN, XN + 0x7f0):
+        assert rms(_proj(y=y)) == dmq.DMQ_ERR_INVALID_ARG, hex(y)
+    assert rms(_proj(y=Y0), _proj(y=Y0 + 0x30)) == dmq.DMQ_ERR_INVALID_ARG           # outputs overlap
+    assert rms(_proj(y=Y0), _proj(N=512, flags=1, y=Y0 - 0x7f0)) == dmq.DMQ_ERR_INVALID_ARG  # into h's 2 KiB
+    assert rms(_proj(y=Y0), _proj(y=Y1)) != dmq.DMQ_ERR_INVALID_ARG                  # disjoint: passes the checks
+
+    H, Yad, HO = A16 + 0x3000, A16 + 0x4000, A16 + 0x5000
+
+    def res(*projs, xn=XN, M=4):
+        arr = (dmq.ProjDesc * len(projs))(*projs)
+        return L.dmq_residual_rmsnorm_gemm(H, Yad, G, 1e-5, HO, xn, M, 256, arr, len(projs), None)
+    for y in (H + 0xff0, Yad, HO + 0x800, G, XN + 0x10):
+        assert res(_proj(y=y)) == dmq.DMQ_ERR_INVALID_ARG, hex(y)
+    assert res(_proj(y=Yad + 0x10), xn=None, M=1) == dmq.DMQ_ERR_INVALID_ARG          # the decode path too
+    assert res(_proj(y=Y0), _proj(y=Y0)) == dmq.DMQ_ERR_INVALID_ARG
+    assert res(_proj(y=Y0), _proj(y=Y1)) != dmq.DMQ_ERR_INVALID_ARG
+
+
 def test_rope_kv_cache_validation():
     f = L.dmq_rope_kv_cache
     Q, K, V, QO, KC, VC = (A16 + 0x1000 * i for i in range(6))

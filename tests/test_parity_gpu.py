@@ -233,6 +233,29 @@ def test_gemm_adversarial_cancellation(dmq):
         assert_within(y, ref, s, f"cancellation M={m_rows}")
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_gemv_max_k_every_output(dmq, fmt):
+    """M = 1 at K = 32768, the largest K of the decode kernel (its x slice
+    fills 73.7 KB of LDS): every output."""
+    K, N = 32768, 80
+    x = synthetic.activations(1, K, seed=41)
+    wq = synthetic.weight_blocks(fmt, N, K, seed=42)
+    y = gpu_gemm(dmq, fmt, x, wq, 1, N, K)
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y, ref, s, f"gemv {fmt} K={K}")
+
+
+def test_ffn_decode_max_k(dmq):
+    """The SwiGLU pair decode path (gate and up rows in one lane) at D = K =
+    32768, then the Q6_K down projection back to 32768 outputs."""
+    D, F = 32768, 256
+    wgu = synthetic.q4k_blocks(2 * F, D, seed=43)
+    wd = synthetic.q6k_blocks(D, F, seed=44)
+    x = synthetic.activations(1, D, seed=45, sigma=1.0 / 16)
+    h, y = run_ffn(dmq, x, wgu, wd, 1, D, F)
+    check_ffn(x, wgu, wd, h, y, D, F, np.array([0]), f"ffn decode D={D}")
+
+
 def test_gemm_large_k_m1(dmq):
     # K beyond the decode kernel's LDS staging: M = 1 runs the MFMA kernel
     M, N, K = 1, 24, 33024
@@ -253,22 +276,54 @@ def _layer_group(dmq, config, layer, M, unit_rms=True):
     return items
 
 
-def test_gemm_config2_group_sampled(dmq):
-    M = 1024
-    items = _layer_group(dmq, 2, 0, M)
-    # Q, K, V, gate, up share their input in a real layer; here each has its
-    # own seeded input as in the benchmark
-    probs, host = [], []
+def _run_layer_group(dmq, items, M):
+    """One grouped launch of a layer's projections; returns the host copies of y."""
+    probs = []
     for name, fmt, N, K, wq, x in items:
         y = torch.empty((M, N), dtype=torch.float32, device=DEV)
         probs.append((fmt, dev(x), dev(wq.reshape(-1)), y, M, N, K))
-        host.append((name, fmt, N, K, wq, x, y))
     dmq.dmq_gemm_group(probs)
     torch.cuda.synchronize()
-    rows = synthetic.row_sample(M, 24, seed=3)
-    for name, fmt, N, K, wq, x, y in host:
+    return [p[3].cpu().numpy() for p in probs]
+
+
+def test_gemm_config2_group_every_output(dmq):
+    """The benchmark's step: one layer's seven projections at M = 1024 in one
+    grouped launch (Q, K, V, O, gate, up in Q4_K, down in Q6_K; each with its
+    own seeded unit-RMS input), every output against the oracle."""
+    M = 1024
+    items = _layer_group(dmq, 2, 0, M)
+    ys = _run_layer_group(dmq, items, M)
+    for (name, fmt, N, K, wq, x), y in zip(items, ys):
+        ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+        assert_within(y, ref, s, f"config2 {name} M={M} (every output)")
+
+
+@pytest.mark.parametrize("layer", range(synthetic.N_LAYERS))
+def test_gemm_config4_m1024_layer_every_output(dmq, layer):
+    """Config 4 at M = 1024: each of the 28 independently seeded layers in
+    the grouped launch, every output of all seven projections."""
+    M = 1024
+    items = _layer_group(dmq, 4, layer, M)
+    ys = _run_layer_group(dmq, items, M)
+    for (name, fmt, N, K, wq, x), y in zip(items, ys):
+        ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+        assert_within(y, ref, s, f"config4 layer {layer} {name} M={M} (every output)")
+
+
+@pytest.mark.parametrize("M", [2048, 4096])
+def test_gemm_config4_large_m_group_sampled(dmq, M):
+    """Config 4 at M = 2048 / 4096 in the grouped launch the sweep times: one
+    row in every 32-row group (so every M tile of every height the launch
+    plan may pick), all columns of all seven projections (every N tile and
+    every split-K piece)."""
+    items = _layer_group(dmq, 4, 0, M)
+    ys = _run_layer_group(dmq, items, M)
+    rows = synthetic.row_sample(M, M // 32, seed=M + 1, tile=32)
+    assert len(np.unique(rows // 32)) == M // 32
+    for (name, fmt, N, K, wq, x), y in zip(items, ys):
         ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
-        assert_within(y.cpu().numpy()[rows], ref, s, f"config2 {name} M={M} (rows {len(rows)})")
+        assert_within(y[rows], ref, s, f"config4 {name} M={M} ({len(rows)} rows, all columns)")
 
 
 def test_gemm_group_matches_single_calls(dmq):
@@ -290,12 +345,11 @@ def test_gemm_group_matches_single_calls(dmq):
     first = [p[3].clone() for p in probs]
     dmq.dmq_gemm_group(probs)
     torch.cuda.synchronize()
-    rows = synthetic.row_sample(M, 12, seed=5)
     for p, s_, f, (name, fmt, N, K, wq, x) in zip(probs, singles, first, host):
         assert torch.equal(p[3], f), f"{name}: repeated grouped launch changed bits"
-        ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
-        assert_within(p[3].cpu().numpy()[rows], ref, s, f"group {name} M={M}")
-        assert_within(s_[3].cpu().numpy()[rows], ref, s, f"single {name} M={M}")
+        ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+        assert_within(p[3].cpu().numpy(), ref, s, f"group {name} M={M}")
+        assert_within(s_[3].cpu().numpy(), ref, s, f"single {name} M={M}")
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
@@ -316,9 +370,8 @@ def test_gemm_split_k(dmq, fmt, M, N, K):
     fn(xd, wd, y2, M, N, K)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2), "split-K result is not reproducible"
-    rows = np.arange(M) if M <= 64 else synthetic.row_sample(M, 24, seed=K)
-    ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
-    assert_within(y1.cpu().numpy()[rows], ref, s, f"split-K {fmt} {M}x{N}x{K}")
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y1.cpu().numpy(), ref, s, f"split-K {fmt} {M}x{N}x{K} (every output)")
 
 
 def test_gemm_split_k_interleaved_shapes(dmq):
@@ -352,9 +405,8 @@ def test_gemm_split_k_interleaved_shapes(dmq):
     assert torch.equal(first[2], other), "split-K bits differ on a second stream"
     for r, y in zip(runs, first):
         fmt, M, N, K, x, wq = r[:6]
-        rows = np.arange(M) if M <= 64 else synthetic.row_sample(M, 8, seed=K)
-        ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
-        assert_within(y.cpu().numpy()[rows], ref, s, f"interleaved split-K {fmt} {M}x{N}x{K}")
+        ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+        assert_within(y.cpu().numpy(), ref, s, f"interleaved split-K {fmt} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
@@ -397,38 +449,16 @@ def test_gemm_small_m_layer_group(dmq):
         assert_within(y.cpu().numpy(), ref, s, f"small-M group {name} M={M}")
 
 
-@pytest.mark.parametrize("M", [2048, 4096])
-def test_gemm_config4_large_m_sampled(dmq, M):
-    name, fmt, N, K = synthetic.LAYER_PROJECTIONS[0]
-    wq = synthetic.weight_blocks(fmt, N, K, seed=synthetic.weight_seed(4, 27, 0))
-    x = synthetic.activations(M, K, seed=synthetic.act_seed(4, 27, 0), unit_rms=True)
-    y = gpu_gemm(dmq, fmt, x, wq, M, N, K)
-    rows = synthetic.row_sample(M, 40, seed=M)
-    ref, s = oracle.gemm_quant(fmt, x[rows], wq, N, K)
-    assert_within(y[rows], ref, s, f"config4 q M={M}")
-    down = synthetic.LAYER_PROJECTIONS[6]
-    wq6 = synthetic.weight_blocks("q6k", down[2], down[3], seed=synthetic.weight_seed(4, 27, 6))
-    x6 = synthetic.activations(M, down[3], seed=synthetic.act_seed(4, 27, 6), unit_rms=True)
-    y6 = gpu_gemm(dmq, "q6k", x6, wq6, M, down[2], down[3])
-    ref6, s6 = oracle.gemm_quant("q6k", x6[rows], wq6, down[2], down[3])
-    assert_within(y6[rows], ref6, s6, f"config4 down M={M}")
-
-
-def test_lm_head_sampled(dmq):
+def test_lm_head_every_output(dmq):
+    """Config 4's tied LM head: Q6_K 3072 -> 128256 on 1024 rows, every
+    output (807 GFLOP in the oracle)."""
     name, fmt, N, K = synthetic.LM_HEAD
     M = 1024
     wq = synthetic.lm_head_weights(4)
     x = synthetic.activations(M, K, seed=synthetic.act_seed(4, 0, synthetic.LM_HEAD_INDEX), unit_rms=True)
     y = gpu_gemm(dmq, fmt, x, wq, M, N, K)
-    rows = synthetic.row_sample(M, 8, seed=4)
-    # one weight row per 256-row N tile plus the ragged end, dequantised alone
-    rng = np.random.default_rng(8)
-    ncols = np.unique(np.concatenate([np.arange(0, N, 256) + rng.integers(0, 256, (N + 255) // 256),
-                                      [N - 1]]))
-    ncols = ncols[ncols < N]
-    wrow = wq.reshape(N, -1)[ncols]
-    ref, s = oracle.gemm_quant(fmt, x[rows], wrow, len(ncols), K)
-    assert_within(y[np.ix_(rows, ncols)], ref, s, f"lm_head M={M} ({len(rows)}x{len(ncols)} outputs)")
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y, ref, s, f"lm_head M={M} (every output)")
 
 
 # ------------------------------------------------------------------- FFN ---
@@ -473,13 +503,13 @@ def _ffn_weights(config):
 
 
 @pytest.mark.parametrize("sigma", [1.0, 1.0 / 16])
-def test_ffn_config3_sampled(dmq, sigma):
+def test_ffn_config3_every_output(dmq, sigma):
+    """Config 3 at both input scales, every h value and every y output."""
     D, F, wgu, wd = _ffn_weights(3)
     M = 1024
     x = synthetic.activations(M, D, seed=synthetic.act_seed(3, 0, 0), sigma=sigma)
     h, y = run_ffn(dmq, x, wgu, wd, M, D, F)
-    rows = synthetic.row_sample(M, 12, seed=5)
-    ov = check_ffn(x, wgu, wd, h, y, D, F, rows, f"config3 sigma={sigma}")
+    ov = check_ffn(x, wgu, wd, h, y, D, F, np.arange(M), f"config3 sigma={sigma} (every output)")
     if sigma < 1:
         assert ov == 0.0
 
@@ -559,7 +589,7 @@ def test_rmsnorm_gemm_every_output(dmq, M, K):
     _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, f"rmsnorm+gemm M={M} K={K}")
 
 
-@pytest.mark.parametrize("K", [256, 3072, 8192])
+@pytest.mark.parametrize("K", [256, 3072, 8192, 32768])
 def test_rmsnorm_gemv_decode_every_output(dmq, K):
     # M = 1: the decode kernel normalizes x while staging it
     x = synthetic.activations(1, K, seed=K + 5, sigma=3.0)
@@ -595,7 +625,7 @@ def test_rmsnorm_edge_rows(dmq):
             _check_rmsnorm_outputs(x[m:m + 1], g, eps, projs, K, xn1, ys1, f"rmsnorm edge row {m} decode")
 
 
-def test_rmsnorm_qkv_layer_shapes_sampled(dmq):
+def test_rmsnorm_qkv_layer_shapes_every_output(dmq):
     # the Q|K|V projections of one Llama-3.2-3B-shaped layer behind their
     # RMSNorm, at M = 1024 (tiled kernel, grouped) and M = 1 (decode kernel)
     K = 3072
@@ -605,11 +635,7 @@ def test_rmsnorm_qkv_layer_shapes_sampled(dmq):
     M = 1024
     x = synthetic.activations(M, K, seed=synthetic.act_seed(2, 0, 0), sigma=1.5)
     xn, ys = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, M, K)
-    # xn on every row, y on sampled rows that hit every 256-row tile
-    lo, hi = oracle.rmsnorm_f16_interval(oracle.rmsnorm(x, g, 1e-5))
-    assert np.all((xn.astype(np.float64) >= lo) & (xn.astype(np.float64) <= hi))
-    rows = synthetic.row_sample(M, 24, seed=5)
-    _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, "rmsnorm QKV M=1024", rows=rows)
+    _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, "rmsnorm QKV M=1024 (every output)")
     xn1, ys1 = _rmsnorm_gemm(dmq, x[:1], g, 1e-5, projs, 1, K)
     _check_rmsnorm_outputs(x[:1], g, 1e-5, projs, K, xn1, ys1, "rmsnorm QKV M=1")
 
@@ -803,12 +829,16 @@ def test_residual_rmsnorm(dmq):
         assert ok.all(), f"residual+rmsnorm M={M}: {int((~ok).sum())} normalized values outside the interval"
 
 
-@pytest.mark.parametrize("M,K", [(1, 768), (1, 3072), (1, 8192), (5, 768)])
+@pytest.mark.parametrize("M,K", [(1, 768), (1, 3072), (1, 3328), (1, 4096), (1, 8192), (1, 32768), (5, 768)])
 def test_residual_rmsnorm_gemm(dmq, M, K):
     """Residual add + RMSNorm + projections in one call: at M = 1 the decode
     kernel forms the sum and the norm while staging x (one launch), above it
     the residual kernel runs first.  Plain Q4_K and Q6_K projections and a
-    SwiGLU gate|up pair (h = silu(gate) * up in fp16)."""
+    SwiGLU gate|up pair (h = silu(gate) * up in fp16).  K = 3328 gives uneven
+    wave slices (13 blocks), K = 4096 is the largest one-pass staging (every
+    lane's second chunk live), K = 8192 and 32768 take the two-pass staging,
+    the last with the largest x slice the decode kernel takes (73.7 KB of
+    LDS)."""
     rng = np.random.default_rng(M * 31 + K)
     h = rng.standard_normal((M, K)).astype(np.float32)
     ya = (rng.standard_normal((M, K)) * 2.0).astype(np.float32)
