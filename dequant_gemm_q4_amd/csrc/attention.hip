@@ -12,8 +12,7 @@
 
 #include <math.h>
 
-#include <mutex>
-#include <vector>
+#include <algorithm>
 
 namespace dmq {
 
@@ -418,41 +417,6 @@ __global__ __launch_bounds__(128) void attention_merge_kernel(AttnArgs a, const 
   a.out[((int64_t)m * a.hq + h) * HEAD_DIM + d] = (half_t)(o / sum);
 }
 
-// Workspace of the split path: one buffer per (device, stream), grown on
-// demand and kept until the process ends (as the GEMMs' split-K workspace).
-static hipError_t attention_workspace(hipStream_t s, size_t bytes, float** out) {
-  static std::mutex mu;
-  struct Ws {
-    int dev;
-    hipStream_t stream;
-    void* ptr;
-    size_t bytes;
-  };
-  static std::vector<Ws> pool;
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  std::lock_guard<std::mutex> lock(mu);
-  for (auto& w : pool) {
-    if (w.dev != dev || w.stream != s) continue;
-    if (w.bytes < bytes) {
-      if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;   // earlier launches may still use it
-      if ((err = hipFree(w.ptr)) != hipSuccess) return err;
-      w.ptr = nullptr;
-      w.bytes = 0;
-      if ((err = hipMalloc(&w.ptr, bytes)) != hipSuccess) return err;
-      w.bytes = bytes;
-    }
-    *out = (float*)w.ptr;
-    return hipSuccess;
-  }
-  void* p = nullptr;
-  if ((err = hipMalloc(&p, bytes)) != hipSuccess) return err;
-  pool.push_back(Ws{dev, s, p, bytes});
-  *out = (float*)p;
-  return hipSuccess;
-}
-
 // Many queries (prefill): MFMA flash attention.  One workgroup = 8 waves =
 // 128 consecutive queries of one query head, in two halves of 4 waves that
 // take the even and the odd key blocks and merge their softmax states in LDS
@@ -786,9 +750,17 @@ hipError_t launch_attention(const void* q, const void* k_cache, const void* v_ca
   const int64_t nsplit64 = (pos0 + M + SPLIT_S - 1) / SPLIT_S;
   if (M <= ATT_SPLIT_MAX_M && nsplit64 <= MERGE_MAX_PIECES) {
     const int nsplit = (int)nsplit64;
-    float* ws = nullptr;
-    hipError_t e = attention_workspace(s, (size_t)M * hq * nsplit * SPLIT_REC * sizeof(float), &ws);
+    // sized for the whole cache when that is at most 64 MiB (every position a
+    // later call on this stream can reach), so a decode loop over one cache
+    // does not grow it
+    const size_t rec_bytes = (size_t)M * hq * SPLIT_REC * sizeof(float);
+    const int64_t cap = std::min<int64_t>((cache_len + SPLIT_S - 1) / SPLIT_S, MERGE_MAX_PIECES);
+    size_t want = rec_bytes * (size_t)nsplit;
+    if (cap > nsplit && rec_bytes * (size_t)cap <= (size_t(64) << 20)) want = rec_bytes * (size_t)cap;
+    void* wp = nullptr;
+    hipError_t e = stream_workspace(WorkspaceUse::AttentionPieces, s, want, &wp);
     if (e != hipSuccess) return e;
+    float* ws = (float*)wp;
     const dim3 grid((unsigned)nsplit, (unsigned)hkv, (unsigned)M);
     switch (hq / hkv) {
       case 1: hipLaunchKernelGGL(attention_split_kernel<1>, grid, dim3(256), 0, s, a, ws, nsplit); break;

@@ -185,4 +185,9 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s);
 
 int device_cu_count();
 
+// Device workspace of one use, per (device, stream), kept by the library
+// (workspace.cpp): grown with stream-ordered allocations, never freed.
+enum class WorkspaceUse { SplitK = 0, AttentionPieces = 1 };
+hipError_t stream_workspace(WorkspaceUse use, hipStream_t s, size_t bytes, void** out);
+
 }  // namespace dmq

@@ -959,43 +959,6 @@ static hipError_t launch_pair(const Plan& pl, int tiles, const GemmArgs& a, hipS
   }
 }
 
-// Split-K workspace: one buffer per (device, stream), grown on demand and
-// kept until the process ends.  Calls on one stream are ordered, so they
-// may share it; calls on different streams get different buffers.
-static float* splitk_workspace(hipStream_t s, size_t bytes, hipError_t& err) {
-  static std::mutex mu;
-  struct Ws {
-    int dev;
-    hipStream_t stream;
-    void* ptr;
-    size_t bytes;
-  };
-  static std::vector<Ws> pool;
-  int dev = 0;
-  err = hipGetDevice(&dev);
-  if (err != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  for (auto& w : pool) {
-    if (w.dev != dev || w.stream != s) continue;
-    if (w.bytes >= bytes) return (float*)w.ptr;
-    // earlier launches on this stream may still read the old buffer
-    err = hipStreamSynchronize(s);
-    if (err == hipSuccess) err = hipFree(w.ptr);
-    if (err != hipSuccess) return nullptr;
-    w.ptr = nullptr;
-    w.bytes = 0;
-    err = hipMalloc(&w.ptr, bytes);
-    if (err != hipSuccess) return nullptr;
-    w.bytes = bytes;
-    return (float*)w.ptr;
-  }
-  void* p = nullptr;
-  err = hipMalloc(&p, bytes);
-  if (err != hipSuccess) return nullptr;
-  pool.push_back(Ws{dev, s, p, bytes});
-  return (float*)p;
-}
-
 static hipError_t launch_chunk(const GemmProblem* probs, int count, hipStream_t s) {
   const Plan pl = get_plan(probs, count);
   // workspace slices of the split problems (slice stride rounded to 4 floats)
@@ -1008,9 +971,10 @@ static hipError_t launch_chunk(const GemmProblem* probs, int count, hipStream_t 
   }
   float* ws = nullptr;
   if (ws_floats > 0) {
-    hipError_t e;
-    ws = splitk_workspace(s, (size_t)ws_floats * 4, e);
-    if (!ws) return e;
+    void* p = nullptr;
+    const hipError_t e = stream_workspace(WorkspaceUse::SplitK, s, (size_t)ws_floats * 4, &p);
+    if (e != hipSuccess) return e;
+    ws = (float*)p;
   }
   GemmArgs a{};
   ReduceArgs r{};

@@ -28,13 +28,19 @@
  *  - Every pointer except the stream is DEVICE memory owned by the caller
  *    (for example a torch tensor's data_ptr()).  Passing host memory is
  *    undefined behaviour.  The library keeps cached device properties,
- *    cached launch plans and, for GEMMs whose plan splits the reduction (see
- *    dmq_gemm_q4k), one workspace per (device, stream): allocated with
- *    hipMalloc by the first such call on that stream, grown when a later
- *    call needs more (after synchronising that stream), kept until the
+ *    cached launch plans and two kinds of device workspace, one buffer of
+ *    each per (device, stream): the partial sums of GEMMs whose plan splits
+ *    the reduction (see dmq_gemm_q4k) and the partial softmax states of the
+ *    decode attention (see dmq_attention_gqa).  A call that needs a larger
+ *    buffer than its stream has allocates one with hipMallocAsync on that
+ *    stream (stream-ordered: the call does not wait for queued work and does
+ *    not synchronise), at least twice the old size; the old buffer is kept,
+ *    never freed, because work queued earlier and HIP graphs captured
+ *    earlier on that stream may still use it.  Workspaces live until the
  *    process ends.  Nothing else is allocated.  A call made while its stream
  *    is being captured into a HIP graph must not need a new or larger
- *    workspace: make the same call once on that stream before capturing.
+ *    workspace (it then returns DMQ_ERR_HIP and enqueues nothing): make the
+ *    same call once on that stream before capturing.
  *  - stream is a hipStream_t passed as void*; NULL means the null stream.  The
  *    call only enqueues work: results are ready once the stream is
  *    synchronised.  The device is the caller's current HIP device.
@@ -268,9 +274,10 @@ int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M,
  * rounded to fp16 for the P V product).
  * With M <= 16 (decode) the positions are split into pieces of 64 over many
  * workgroups whose partial softmax states a second kernel merges in piece
- * order; the states go to a workspace the library keeps per (device, stream),
- * allocated and grown like the GEMMs' split-K workspace (same rule under
- * graph capture).  Every path gives the same bits on every run.
+ * order; the states go to a workspace the library keeps per (device, stream)
+ * (see the conventions above), sized on its first use for every position of
+ * the cache when that takes at most 64 MiB, so that a decode loop over one
+ * cache does not grow it.  Every path gives the same bits on every run.
  */
 int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16, int64_t M,
                       int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, void* stream);

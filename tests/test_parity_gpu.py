@@ -974,3 +974,116 @@ def test_decoder_layer_chain(dmq, M, pos0):
     rel = np.linalg.norm(cpu(out) - OUT) / np.linalg.norm(OUT)
     print(f"layer M={M} pos0={pos0}: end-to-end relative error {rel:.3g}")
     assert rel < 1e-2, f"layer output differs from the fp64 oracle layer by {rel:.3g} of its norm"
+
+
+# ------------------------------------------------------------ workspaces ---
+# The split-K partial sums and the decode attention's partial states live in
+# per-(device, stream) workspaces that grow with stream-ordered allocations:
+# a growing call must neither wait for work queued before it nor free a
+# buffer that work queued earlier (or a graph captured earlier) still uses.
+
+def _sleeping(stream, cycles=200_000_000):
+    """Queue a bounded spin kernel on `stream` and an event after it."""
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(cycles)
+        done = torch.cuda.Event()
+        done.record()
+    return done
+
+
+def test_workspace_growth_does_not_block(dmq):
+    """On a fresh stream, behind a long spin kernel: a split-K GEMM (new
+    workspace), a larger split-K GEMM (grown workspace) and two decode
+    attention calls (new, then larger) each return while the spin kernel is
+    still running, and give the bits of the same calls on the current
+    stream."""
+    import time
+    gemms = []
+    for fmt, M, N, K in (("q6k", 40, 37, 8192), ("q6k", 1024, 3072, 8192)):
+        x = synthetic.activations(M, K, seed=M + K)
+        wq = synthetic.weight_blocks(fmt, N, K, seed=N + K)
+        gemms.append((fmt, M, N, K, dev(x), dev(wq.reshape(-1))))
+    hq, hkv, L = 24, 8, 1024
+    rng = np.random.default_rng(9)
+    kc = dev(rng.standard_normal((hkv, L, D_HEAD)).astype(np.float16))
+    vc = dev(rng.standard_normal((hkv, L, D_HEAD)).astype(np.float16))
+    atts = [(M, L - M, dev(rng.standard_normal((M, hq * D_HEAD)).astype(np.float16))) for M in (1, 16)]
+
+    def gemm(i, stream=None):
+        fmt, M, N, K, xd, wd = gemms[i]
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        (dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k)(xd, wd, y, M, N, K, stream=stream)
+        return y
+
+    def att(i, stream=None):
+        M, pos0, q = atts[i]
+        out = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+        dmq.dmq_attention_gqa(q, kc, vc, out, M, pos0, hq, hkv, L, stream=stream)
+        return out
+
+    ref = [gemm(0), gemm(1), att(0), att(1)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    got, waits = [], []
+    for call in (lambda s: gemm(0, s), lambda s: gemm(1, s), lambda s: att(0, s), lambda s: att(1, s)):
+        done = _sleeping(side)
+        t0 = time.perf_counter()
+        with torch.cuda.stream(side):
+            got.append(call(side))
+        waits.append((time.perf_counter() - t0, done.query()))
+        side.synchronize()
+    for i, (dt, finished) in enumerate(waits):
+        assert not finished, f"call {i} returned only after the work queued before it ({dt * 1e3:.1f} ms)"
+    for i, (a, b) in enumerate(zip(ref, got)):
+        assert torch.equal(a, b), f"call {i}: bits differ from the same call on another stream"
+    print("host time of the growing calls (ms):", [round(dt * 1e3, 2) for dt, _ in waits])
+
+
+def test_graph_captured_before_growth_still_replays(dmq):
+    """A graph captured with the stream's workspace at one size keeps
+    working after a later call on that stream grew (replaced) it: replays,
+    with eager work and synchronisations between them, give the eager
+    result every time."""
+    hq, hkv, L = 24, 8, 2048
+    rng = np.random.default_rng(10)
+    kc = dev(rng.standard_normal((hkv, L, D_HEAD)).astype(np.float16))
+    vc = dev(rng.standard_normal((hkv, L, D_HEAD)).astype(np.float16))
+    q1 = dev(rng.standard_normal((1, hq * D_HEAD)).astype(np.float16))
+    q16 = dev(rng.standard_normal((16, hq * D_HEAD)).astype(np.float16))
+    fmt, M, N, K = "q6k", 40, 37, 8192
+    x = dev(synthetic.activations(M, K, seed=5))
+    wq = dev(synthetic.weight_blocks(fmt, N, K, seed=6).reshape(-1))
+    side = torch.cuda.Stream()
+    o1 = torch.empty((1, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    o16 = torch.empty((16, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(side):
+        dmq.dmq_attention_gqa(q1, kc, vc, o1, 1, 1000, hq, hkv, L, stream=side)
+        dmq.dmq_gemm_q6k(x, wq, y, M, N, K, stream=side)
+    side.synchronize()
+    want1, wanty = o1.clone(), y.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        dmq.dmq_attention_gqa(q1, kc, vc, o1, 1, 1000, hq, hkv, L, stream=side)
+        dmq.dmq_gemm_q6k(x, wq, y, M, N, K, stream=side)
+    # grow both workspaces of the stream: 16 queries, and a larger split-K GEMM
+    Mb, Nb = 1024, 3072
+    xb = dev(synthetic.activations(Mb, K, seed=7))
+    wb = dev(synthetic.weight_blocks(fmt, Nb, K, seed=8).reshape(-1))
+    yb = torch.empty((Mb, Nb), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(side):
+        dmq.dmq_attention_gqa(q16, kc, vc, o16, 16, L - 16, hq, hkv, L, stream=side)
+        dmq.dmq_gemm_q6k(xb, wb, yb, Mb, Nb, K, stream=side)
+    side.synchronize()
+    want16 = o16.clone()
+    for r in range(4):
+        o1.zero_()
+        y.zero_()
+        with torch.cuda.stream(side):
+            graph.replay()
+        side.synchronize()
+        assert torch.equal(o1, want1) and torch.equal(y, wanty), f"replay {r} differs from the eager result"
+        with torch.cuda.stream(side):   # eager work between replays
+            dmq.dmq_attention_gqa(q16, kc, vc, o16, 16, L - 16, hq, hkv, L, stream=side)
+        side.synchronize()
+        assert torch.equal(o16, want16)
