@@ -8,9 +8,12 @@
 // across the prompt rows; overview page, compartment 09 of "[02] the
 // pipeline": the dequant is fused and fp16 weights are never written):
 //
-//  * a workgroup owns 16 consecutive weight rows; its 4 waves split the
-//    rows' super-blocks into 4 contiguous slices, and a lane works on row
-//    l%16 and part l/16 of every super-block of its wave's slice;
+//  * a workgroup owns 16 consecutive weight rows; its waves (one per
+//    super-block of the row, at most 16) split the row's super-blocks into
+//    contiguous slices, and a lane works on row l%16 and part l/16 of every
+//    super-block of its wave's slice.  With a block or two per wave, every
+//    load of the workgroup is issued before the first multiply: the matrix
+//    streams in about one memory round trip instead of one per block;
 //  * v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16 and k-slots
 //    8*(l/16) .. +7; B: column l%16, the same k-slots; D: column l%16, rows
 //    4*(l/16) .. +3) takes 8 dequantised weights per lane as the A operand
@@ -23,8 +26,8 @@
 //    8(s%4) .. +7; Q6_K part p is half p/2, 16-weight column p%2 of each
 //    32-weight quarter, and step s covers quarter s/2, weights 8(s%2) .. +7;
 //  * the next block's quant bytes and x fragments are loaded while the
-//    current block is computed; the 4 waves' partial sums are added in
-//    wave order through LDS (the same result every run).
+//    current block is computed; the waves' partial sums are added in wave
+//    order through LDS (the same result every run).
 //
 // Dequant is exact as in the other kernels: Q4_K nibbles reach fp32 as fp8
 // E4M3 patterns (q * 2^-9, scale carrying 2^9), Q6_K quants through
@@ -37,6 +40,7 @@ namespace dmq {
 
 constexpr int SKINNY_MAX_GROUP = 8;
 constexpr int SKINNY_ROWS = 16;
+constexpr int SKINNY_MAX_WAVES = 16;
 
 struct SkinnyDesc {
   const half_t* x;
@@ -105,45 +109,39 @@ __device__ __forceinline__ h2 sk_pack(float a, float b) {
   return __builtin_convertvector(v, h2);
 }
 
-// Per-block scale values of a lane.  Q4_K: d*sc_j*2^9 and -dmin*m_j for the
-// 8 sub-blocks; Q6_K: d*sc of the lane's scale in each of the 8 steps.
+// Per-block scale fields of a lane, decoded once per block; the two scale
+// values of an MFMA step come from them on the fly (few live registers).
+//  Q4_K: the unpacked 6-bit scales and mins, d * 2^9 and dmin; step s is
+//        sub-block s: d*sc_s*2^9 and -dmin*m_s.
+//  Q6_K: d; step s uses int8 scale byte 2s + (p >= 2) of the 16 scales.
 struct SkScales {
-  float a[16];
+  Q4kScales q4;
+  float d, dmin;
 };
 __device__ __forceinline__ SkScales sk_scales(const SkQ4& r, int p) {
   (void)p;
-  Q4kScales s = unpack_q4k_scales(r.hdr.y, r.hdr.z, r.hdr.w);
-  const float d = half_bits_to_float(r.hdr.x) * 512.0f;
-  const float dmin = half_bits_to_float(r.hdr.x >> 16);
   SkScales o;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    o.a[2 * j] = d * (float)q4k_sc(s, j);
-    o.a[2 * j + 1] = -(dmin * (float)q4k_m(s, j));
-  }
+  o.q4 = unpack_q4k_scales(r.hdr.y, r.hdr.z, r.hdr.w);
+  o.d = half_bits_to_float(r.hdr.x) * 512.0f;
+  o.dmin = half_bits_to_float(r.hdr.x >> 16);
   return o;
 }
 __device__ __forceinline__ SkScales sk_scales(const SkQ6& r, int p) {
-  const float d = half_bits_to_float(r.s206 >> 16);
-  const uint32_t sw[4] = {r.sc.x, r.sc.y, r.sc.z, r.sc.w};
-  const uint32_t hi = p >= 2 ? 1u : 0u;
+  (void)p;
   SkScales o;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    // scale index 8h + 2t + (p >= 2), h = s/4, t = s%4: byte 2s + (p >= 2)
-    const uint32_t w = sw[s >> 1];
-    const int sc = (int)(int8_t)((w >> (16 * (s & 1) + 8 * hi)) & 0xffu);
-    o.a[s] = d * (float)sc;
-  }
+  o.q4 = Q4kScales{0, 0, 0, 0};
+  o.d = half_bits_to_float(r.s206 >> 16);
+  o.dmin = 0.0f;
   return o;
 }
 
 // The 8 fp16 weights of MFMA step s (exact dequant, one rounding to fp32,
 // RNE to fp16).
-__device__ __forceinline__ h8 sk_frag(const SkQ4& r, const SkScales& sc, int s) {
+__device__ __forceinline__ h8 sk_frag(const SkQ4& r, const SkScales& sc, int s, int p) {
+  (void)p;
   const uint2 qv = r.q[s >> 1];
   const bool hi = s & 1;
-  const float m = sc.a[2 * s], c = sc.a[2 * s + 1];
+  const float m = sc.d * (float)q4k_sc(sc.q4, s), c = -(sc.dmin * (float)q4k_m(sc.q4, s));
   const int b0 = (int)((hi ? qv.x >> 4 : qv.x) & 0x0f0f0f0fu);
   const int b1 = (int)((hi ? qv.y >> 4 : qv.y) & 0x0f0f0f0fu);
   const f2 q0 = __builtin_amdgcn_cvt_pk_f32_fp8(b0, false), q1 = __builtin_amdgcn_cvt_pk_f32_fp8(b0, true);
@@ -154,12 +152,15 @@ __device__ __forceinline__ h8 sk_frag(const SkQ4& r, const SkScales& sc, int s) 
   const h2 w67 = sk_pack(__builtin_fmaf(q3.x, m, c), __builtin_fmaf(q3.y, m, c));
   return (h8){w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
 }
-__device__ __forceinline__ h8 sk_frag(const SkQ6& r, const SkScales& sc, int s) {
+__device__ __forceinline__ h8 sk_frag(const SkQ6& r, const SkScales& sc, int s, int p) {
   const int h = s >> 2, t = s & 3;
   const uint2 l = r.ql[2 * h + (t & 1)];
   const uint2 hb = r.qh[h];
   const uint32_t nsh = t >= 2 ? 4u : 0u;
-  const float dsc = sc.a[s], off = dsc * -32.0f;
+  // scale index 8h + 2t + (p >= 2) = byte 2s + (p >= 2) of the 16 scales
+  const uint32_t sw = s < 2 ? r.sc.x : s < 4 ? r.sc.y : s < 6 ? r.sc.z : r.sc.w;
+  const int scb = (int)(int8_t)((sw >> (16 * (s & 1) + (p >= 2 ? 8 : 0))) & 0xffu);
+  const float dsc = sc.d * (float)scb, off = dsc * -32.0f;
   uint32_t q0 = ((l.x >> nsh) & 0x0f0f0f0fu) | (((hb.x >> (2 * t)) & 0x03030303u) << 4);
   uint32_t q1 = ((l.y >> nsh) & 0x0f0f0f0fu) | (((hb.y >> (2 * t)) & 0x03030303u) << 4);
   asm("" : "+v"(q0));   // keep v_cvt_f32_ubyteN on the packed bytes
@@ -171,7 +172,8 @@ __device__ __forceinline__ h8 sk_frag(const SkQ6& r, const SkScales& sc, int s) 
   return (h8){w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
 }
 
-template <int FMT, int NT>
+// D: blocks in flight per wave (a ring of D register sets).
+template <int FMT, int NT, int D>
 __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, float* red) {
   typedef typename SkPart<FMT>::T Part;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
@@ -183,7 +185,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   const int64_t row_bytes = (int64_t)nb * BLOCK_BYTES;
   const int n0 = wg_local * SKINNY_ROWS;
   const int row = n0 + rl < N ? n0 + rl : N - 1;        // ragged tail: clamp, result dropped
-  const int b0 = wave * nb / 4, b1 = (wave + 1) * nb / 4;
+  const int nw = (int)(blockDim.x >> 6);                 // waves of the workgroup
+  const int b0 = wave * nb / nw, b1 = (wave + 1) * nb / nw;
   const uint8_t* wrow = P.wq + (int64_t)row * row_bytes;
   // x rows of this lane's B operand: rl (group 0) and rl + 16 (group 1)
   const half_t* xr[NT];
@@ -215,31 +218,33 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
     const SkScales sc = sk_scales(w, p);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const h8 a = sk_frag(w, sc, s);
+      const h8 a = sk_frag(w, sc, s, p);
 #pragma unroll
       for (int g = 0; g < NT; ++g)
         acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, xf[g][s]), acc[g], 0, 0, 0);
     }
   };
 
-  Part w0, w1;
-  uint4 x0[NT][8], x1[NT][8];
-  if (b0 < b1) {
-    sk_load(wrow + (int64_t)b0 * BLOCK_BYTES, p, w0);
-    load_x(b0, x0);
-  }
-  for (int b = b0; b < b1; b += 2) {
-    if (b + 1 < b1) {
-      sk_load(wrow + (int64_t)(b + 1) * BLOCK_BYTES, p, w1);
-      load_x(b + 1, x1);
+  // the first D blocks' loads are all issued before the first multiply; each
+  // computed block's registers then take the block D further on
+  Part w[D];
+  uint4 xb[D][NT][8];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (b0 + i < b1) {
+      sk_load(wrow + (int64_t)(b0 + i) * BLOCK_BYTES, p, w[i]);
+      load_x(b0 + i, xb[i]);
     }
-    compute(w0, x0);
-    if (b + 1 < b1) {
-      if (b + 2 < b1) {
-        sk_load(wrow + (int64_t)(b + 2) * BLOCK_BYTES, p, w0);
-        load_x(b + 2, x0);
+  for (int b = b0; b < b1; b += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (b + i < b1) {
+        compute(w[i], xb[i]);
+        if (b + i + D < b1) {
+          sk_load(wrow + (int64_t)(b + i + D) * BLOCK_BYTES, p, w[i]);
+          load_x(b + i + D, xb[i]);
+        }
       }
-      compute(w1, x1);
     }
   }
 
@@ -250,22 +255,26 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[((wave * NT + g) * 16 + rl) * 16 + 4 * p + r] = acc[g][r];
   __syncthreads();
-  // thread (activation row m, weight row n): consecutive threads write
-  // consecutive n; the 4 waves' sums in wave order
+  // output t = (activation row m, weight row n) of the 16 x 16 tile:
+  // consecutive t write consecutive n; the waves' sums in wave order.  A
+  // workgroup may have fewer than 256 threads (one wave per block).
+  for (int t = (int)threadIdx.x; t < 256; t += (int)blockDim.x) {
 #pragma unroll
-  for (int g = 0; g < NT; ++g) {
-    const int ml = threadIdx.x >> 4, nl = threadIdx.x & 15;
-    const int m = ml + 16 * g, n = n0 + nl;
-    float v = red[((0 * NT + g) * 16 + ml) * 16 + nl];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + nl];
-    if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
+    for (int g = 0; g < NT; ++g) {
+      const int ml = t >> 4, nl = t & 15;
+      const int m = ml + 16 * g, n = n0 + nl;
+      float v = red[((0 * NT + g) * 16 + ml) * 16 + nl];
+      for (int w = 1; w < nw; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + nl];
+      if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
+    }
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs args) {
-  __shared__ float red[4 * NT * 16 * 16];
+// D = 1: up to 16 waves (one block each); D = 4: 8 waves with up to four
+// blocks each in flight (256 registers per lane).
+template <int NT, int D>
+__global__ __launch_bounds__(D == 1 ? 1024 : 512) void skinny_kernel(SkinnyArgs args) {
+  extern __shared__ float red[];   // [waves][NT][16][16]
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < SKINNY_MAX_GROUP; ++i)
@@ -273,21 +282,23 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs args) {
   const SkinnyDesc& P = args.d[pi];
   const int wg_local = (int)blockIdx.x - P.wg_begin;
   if (P.fmt == 0)
-    skinny_tile<0, NT>(P, wg_local, red);
+    skinny_tile<0, NT, D>(P, wg_local, red);
   else
-    skinny_tile<1, NT>(P, wg_local, red);
+    skinny_tile<1, NT, D>(P, wg_local, red);
 }
 
-// One workgroup per 16 weight rows; problems with the most bytes per
-// workgroup (the deepest K) are dispatched first so they do not trail.
+// One workgroup per 16 weight rows, one wave per super-block of the deepest
+// row (at most 16); problems with the most bytes per workgroup (the deepest
+// K) are dispatched first so they do not trail.
 hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
   for (int base = 0; base < count; base += SKINNY_MAX_GROUP) {
     const int n = count - base < SKINNY_MAX_GROUP ? count - base : SKINNY_MAX_GROUP;
     int order[SKINNY_MAX_GROUP];
-    int mmax = 0;
+    int mmax = 0, nbmax = 0;
     for (int i = 0; i < n; ++i) {
       order[i] = base + i;
       mmax = probs[base + i].M > mmax ? probs[base + i].M : mmax;
+      nbmax = probs[base + i].K / QK > nbmax ? probs[base + i].K / QK : nbmax;
     }
     auto wg_bytes = [&](int i) { return (int64_t)(probs[i].K / QK) * (probs[i].fmt == 0 ? Q4K_BYTES : Q6K_BYTES); };
     for (int i = 1; i < n; ++i)
@@ -309,7 +320,14 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
     }
     a.count = n;
     if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
-    hipLaunchKernelGGL(skinny_kernel<1>, dim3(wgs), dim3(256), 0, s, a);
+    // one wave per block up to 16 blocks per row (K <= 4096); deeper rows:
+    // 8 waves with four blocks each in flight (K <= 8192: all of them)
+    if (nbmax <= SKINNY_MAX_WAVES) {
+      hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(64 * nbmax), (size_t)nbmax * 256 * sizeof(float), s,
+                         a);
+    } else {
+      hipLaunchKernelGGL((skinny_kernel<1, 4>), dim3(wgs), dim3(64 * 8), (size_t)8 * 256 * sizeof(float), s, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -410,12 +410,14 @@ def test_gemm_split_k_interleaved_shapes(dmq):
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
-@pytest.mark.parametrize("M,N,K", [(2, 16, 256), (5, 37, 4864), (9, 33, 512), (16, 3072, 3072), (16, 48, 8192),
-                                   (17, 100, 1280), (32, 257, 768)])
+@pytest.mark.parametrize("M,N,K", [(2, 16, 256), (16, 40, 256), (12, 20, 768), (5, 37, 4864), (9, 33, 512),
+                                   (16, 3072, 3072), (16, 48, 8192), (7, 50, 9984), (17, 100, 1280), (32, 257, 768)])
 def test_gemm_small_m_every_output(dmq, fmt, M, N, K):
-    """M <= 16 runs the small-M kernel (16 weight rows per workgroup, K split
-    over its 4 waves, the rows' products on 16x16x32 MFMAs): every output,
-    ragged N, K blocks not a multiple of 4 (uneven wave slices), and the
+    """M <= 16 runs the small-M kernel (16 weight rows per workgroup, one wave
+    per K block up to 16, else 8 waves with several blocks each, the rows'
+    products on 16x16x32 MFMAs): every output, ragged N, workgroups of 1, 2
+    and 3 waves with all 16 activation rows live (fewer threads than
+    outputs), uneven wave slices (19 and 39 blocks over 8 waves), and the
     same bits on a second call.  M = 17 and 32, just past it, run the tiled
     kernel."""
     x = synthetic.activations(M, K, seed=M * 11 + N)
