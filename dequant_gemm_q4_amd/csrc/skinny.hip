@@ -270,10 +270,11 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   }
 }
 
-// D = 1: up to 16 waves (one block each); D = 4: 8 waves with up to four
-// blocks each in flight (256 registers per lane).
+// D = 1: up to 16 waves (one block each); D = 2: 4 waves, two blocks in
+// flight each (few registers: several workgroups per CU); D = 4: 8 waves
+// with up to four blocks each in flight (256 registers per lane).
 template <int NT, int D>
-__global__ __launch_bounds__(D == 1 ? 1024 : 512) void skinny_kernel(SkinnyArgs args) {
+__global__ __launch_bounds__(D == 1 ? 1024 : D == 2 ? 256 : 512) void skinny_kernel(SkinnyArgs args) {
   extern __shared__ float red[];   // [waves][NT][16][16]
   int pi = 0;
 #pragma unroll
@@ -320,9 +321,14 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
     }
     a.count = n;
     if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
-    // one wave per block up to 16 blocks per row (K <= 4096); deeper rows:
-    // 8 waves with four blocks each in flight (K <= 8192: all of them)
-    if (nbmax <= SKINNY_MAX_WAVES) {
+    // A grid of at least two workgroups per CU keeps every CU busy with
+    // several small workgroups (4 waves, two blocks in flight each).  A
+    // smaller grid (one projection) issues as many loads as it can at once:
+    // one wave per block up to 16 blocks per row (K <= 4096); deeper rows 8
+    // waves with four blocks each in flight (K <= 8192: all of them).
+    if (wgs >= 2 * device_cu_count()) {
+      hipLaunchKernelGGL((skinny_kernel<1, 2>), dim3(wgs), dim3(256), (size_t)4 * 256 * sizeof(float), s, a);
+    } else if (nbmax <= SKINNY_MAX_WAVES) {
       hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(64 * nbmax), (size_t)nbmax * 256 * sizeof(float), s,
                          a);
     } else {
