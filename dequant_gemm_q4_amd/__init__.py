@@ -22,6 +22,8 @@ DMQ_ERR_INVALID_ARG = -1
 DMQ_ERR_ALIGNMENT = -2
 DMQ_ERR_UNSUPPORTED = -3
 DMQ_ERR_HIP = -4
+DMQ_ERR_SCRATCH = -5
+DMQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 DMQ_FMT_Q4K = 0
 DMQ_FMT_Q6K = 1
 
@@ -32,8 +34,8 @@ FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
 # Every entry point declared in include/dmq.h.
 EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
            "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
-           "dmq_attention_gqa", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm", "dmq_status_string",
-           "dmq_version")
+           "dmq_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm",
+           "dmq_status_string", "dmq_version")
 HEAD_DIM = 128
 
 
@@ -77,12 +79,14 @@ def _load() -> ctypes.CDLL:
     L.dmq_rmsnorm_gemm.argtypes = [P, P, ctypes.c_float, P, I64, I64, ctypes.POINTER(ProjDesc), I32, P]
     L.dmq_rope_kv_cache.argtypes = [P, P, P, I64, I64, I32, I32, ctypes.c_double, P, P, P, P, I64, P]
     L.dmq_attention_gqa.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
+    L.dmq_attention_gqa_noalloc.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
     L.dmq_residual_rmsnorm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, P]
     L.dmq_residual_rmsnorm_gemm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, ctypes.POINTER(ProjDesc),
                                             I32, P]
     for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
                  "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
-                 "dmq_attention_gqa", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm"):
+                 "dmq_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm",
+                 "dmq_residual_rmsnorm_gemm"):
         getattr(L, name).restype = ctypes.c_int
     L.dmq_status_string.argtypes = [ctypes.c_int]
     L.dmq_status_string.restype = ctypes.c_char_p
@@ -301,6 +305,21 @@ def dmq_attention_gqa(q, k_cache, v_cache, out, M: int, pos0: int, n_q_heads: in
     po = _dev_tensor(out, torch.float16, "out", M * n_q_heads * D)
     _check(lib.dmq_attention_gqa(pq, pkc, pvc, po, M, pos0, n_q_heads, n_kv_heads, cache_len, _stream(stream)),
            "dmq_attention_gqa")
+
+
+def dmq_attention_gqa_noalloc(q, k_cache, v_cache, out, M: int, pos0: int, n_q_heads: int, n_kv_heads: int,
+                              cache_len: int, stream=None) -> None:
+    """dmq_attention_gqa without any device allocation: the decode path's
+    partial states go to the library's fixed per-GPU scratch (calls that
+    overlap on one GPU race)."""
+    import torch
+    D = HEAD_DIM
+    pq = _dev_tensor(q, torch.float16, "q", M * n_q_heads * D)
+    pkc = _dev_tensor(k_cache, torch.float16, "k_cache", n_kv_heads * cache_len * D)
+    pvc = _dev_tensor(v_cache, torch.float16, "v_cache", n_kv_heads * cache_len * D)
+    po = _dev_tensor(out, torch.float16, "out", M * n_q_heads * D)
+    _check(lib.dmq_attention_gqa_noalloc(pq, pkc, pvc, po, M, pos0, n_q_heads, n_kv_heads, cache_len,
+                                         _stream(stream)), "dmq_attention_gqa_noalloc")
 
 
 def dmq_residual_rmsnorm(h_in, y, g, eps: float, h_out, xn, M: int, K: int, stream=None) -> None:

@@ -8,11 +8,13 @@
 // MB per layer against the GEMMs' tens; they are bound by memory latency and
 // bandwidth, not by the matrix units.
 #include "attention.h"
+#include "dmq.h"
 #include "dmq_common.h"
 
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace dmq {
 
@@ -743,8 +745,43 @@ __global__ __launch_bounds__(512) void attention_mfma_kernel(AttnArgs a, int M, 
   }
 }
 
+// Scratch for callers that cannot allocate (dmq_attention_gqa_noalloc): the
+// partial softmax states of the decode path in a fixed array of every GPU's
+// code object, allocated when the library is loaded on that GPU and held
+// until the process ends.  Every record the merge kernel reads is written by
+// the piece kernel of the same call, so nothing needs clearing; calls that
+// overlap on one GPU share it and race.
+constexpr size_t NOALLOC_SCRATCH_BYTES = DMQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t noalloc_scratch(float** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static float* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // host code never uses `scratch` itself: its host-side name is not the
+    // device address, which differs per GPU
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    addr[dev] = (float*)p;
+  }
+  *ptr = addr[dev];
+  *bytes = NOALLOC_SCRATCH_BYTES;
+  return hipSuccess;
+}
+
+size_t attention_scratch_bytes(int64_t M, int64_t pos0, int hq) {
+  const int64_t nsplit = (pos0 + M + SPLIT_S - 1) / SPLIT_S;
+  if (M > ATT_SPLIT_MAX_M || nsplit > MERGE_MAX_PIECES) return 0;
+  return (size_t)M * hq * nsplit * SPLIT_REC * sizeof(float);
+}
+
 hipError_t launch_attention(const void* q, const void* k_cache, const void* v_cache, void* out, int64_t cache_len,
-                            int64_t M, int64_t pos0, int hq, int hkv, hipStream_t s) {
+                            int64_t M, int64_t pos0, int hq, int hkv, hipStream_t s, float* ws_given) {
   AttnArgs a{(const half_t*)q, (const half_t*)k_cache, (const half_t*)v_cache, (half_t*)out, cache_len,
              (int32_t)pos0, hq, hkv};
   const int64_t nsplit64 = (pos0 + M + SPLIT_S - 1) / SPLIT_S;
@@ -757,8 +794,8 @@ hipError_t launch_attention(const void* q, const void* k_cache, const void* v_ca
     const int64_t cap = std::min<int64_t>((cache_len + SPLIT_S - 1) / SPLIT_S, MERGE_MAX_PIECES);
     size_t want = rec_bytes * (size_t)nsplit;
     if (cap > nsplit && rec_bytes * (size_t)cap <= (size_t(64) << 20)) want = rec_bytes * (size_t)cap;
-    void* wp = nullptr;
-    hipError_t e = stream_workspace(WorkspaceUse::AttentionPieces, s, want, &wp);
+    void* wp = ws_given;
+    hipError_t e = ws_given ? hipSuccess : stream_workspace(WorkspaceUse::AttentionPieces, s, want, &wp);
     if (e != hipSuccess) return e;
     float* ws = (float*)wp;
     const dim3 grid((unsigned)nsplit, (unsigned)hkv, (unsigned)M);

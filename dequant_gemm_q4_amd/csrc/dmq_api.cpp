@@ -151,6 +151,7 @@ const char* dmq_status_string(int status) {
     case DMQ_ERR_ALIGNMENT: return "misaligned pointer (x, y, h, w_f16 and Q4_K weights need 16 bytes, Q6_K weights 2)";
     case DMQ_ERR_UNSUPPORTED: return "unsupported device (needs a gfx950 GPU)";
     case DMQ_ERR_HIP: return "HIP runtime error on launch";
+    case DMQ_ERR_SCRATCH: return "the call needs more than the fixed no-allocation scratch (DMQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -392,6 +393,28 @@ int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_
   if (dc != DMQ_OK) return dc;
   return hip_status(dmq::launch_attention(q_f16, k_cache_f16, v_cache_f16, out_f16, cache_len, M, pos0, n_q_heads,
                                           n_kv_heads, (hipStream_t)stream));
+}
+
+int dmq_attention_gqa_noalloc(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16,
+                              int64_t M, int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len,
+                              void* stream) {
+  if (!q_f16 || !k_cache_f16 || !v_cache_f16 || !out_f16 || out_f16 == q_f16) return DMQ_ERR_INVALID_ARG;
+  if (!heads_ok(n_q_heads, n_kv_heads) || !cache_ok(M, pos0, n_kv_heads, cache_len)) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(q_f16, 16) || !aligned(k_cache_f16, 16) || !aligned(v_cache_f16, 16) || !aligned(out_f16, 16))
+    return DMQ_ERR_ALIGNMENT;
+  const size_t need = dmq::attention_scratch_bytes(M, pos0, n_q_heads);
+  if (need > DMQ_NOALLOC_SCRATCH_BYTES) return DMQ_ERR_SCRATCH;
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  float* scratch = nullptr;
+  size_t have = 0;
+  if (need > 0) {
+    if (dmq::noalloc_scratch(&scratch, &have) != hipSuccess) return DMQ_ERR_HIP;
+    if (need > have) return DMQ_ERR_SCRATCH;
+  }
+  // the decode path uses the scratch; the other paths take no workspace at all
+  return hip_status(dmq::launch_attention(q_f16, k_cache_f16, v_cache_f16, out_f16, cache_len, M, pos0, n_q_heads,
+                                          n_kv_heads, (hipStream_t)stream, need > 0 ? scratch : nullptr));
 }
 
 int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, float eps, float* h_out, void* xn_f16,

@@ -40,7 +40,8 @@
  *    process ends.  Nothing else is allocated.  A call made while its stream
  *    is being captured into a HIP graph must not need a new or larger
  *    workspace (it then returns DMQ_ERR_HIP and enqueues nothing): make the
- *    same call once on that stream before capturing.
+ *    same call once on that stream before capturing, or use
+ *    dmq_attention_gqa_noalloc.
  *  - stream is a hipStream_t passed as void*; NULL means the null stream.  The
  *    call only enqueues work: results are ready once the stream is
  *    synchronised.  The device is the caller's current HIP device.
@@ -65,7 +66,9 @@ typedef enum {
   DMQ_ERR_INVALID_ARG = -1,   /* NULL pointer, size out of range, bad format */
   DMQ_ERR_ALIGNMENT = -2,     /* a pointer breaks the alignment rule above   */
   DMQ_ERR_UNSUPPORTED = -3,   /* no HIP device / not a gfx950 device         */
-  DMQ_ERR_HIP = -4            /* the HIP runtime reported a launch error     */
+  DMQ_ERR_HIP = -4,           /* the HIP runtime reported a launch error     */
+  DMQ_ERR_SCRATCH = -5        /* a *_noalloc call needs more than its fixed
+                                 scratch (DMQ_NOALLOC_SCRATCH_BYTES)         */
 } dmq_status;
 
 /* Weight formats for dmq_gemm_desc.format. */
@@ -281,6 +284,26 @@ int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M,
  */
 int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16, int64_t M,
                       int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, void* stream);
+
+/*
+ * dmq_attention_gqa for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and bits as dmq_attention_gqa; it
+ * calls no hipMalloc, hipFree or other allocating routine.  The decode path
+ * (M <= 16) keeps its partial softmax states, M * n_q_heads *
+ * ceil((pos0 + M) / 64) records of 520 bytes, in a fixed scratch array of
+ * DMQ_NOALLOC_SCRATCH_BYTES that each GPU holds from the first call on it
+ * until the process ends; a call that needs more returns DMQ_ERR_SCRATCH and
+ * enqueues nothing (e.g. 24 query heads: M = 1 up to 172,032 cached
+ * positions, M = 16 up to 10,752).  All calls on one GPU share that array,
+ * so calls that can overlap on one GPU (different streams, or graphs
+ * replayed concurrently) race: order them on one stream.  Nothing in it has
+ * to start at zero.  The prefill path (M > 16) takes no scratch.
+ */
+#define DMQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int dmq_attention_gqa_noalloc(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16,
+                              int64_t M, int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len,
+                              void* stream);
 
 /*
  * The residual connection, fused with the RMSNorm that follows it:

@@ -24,11 +24,29 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(dmq.EXPORTS)
     raw = ctypes.CDLL(dmq.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
+
+
+def test_noalloc_attention_validation():
+    """The no-allocation attention call checks like dmq_attention_gqa, and a
+    decode call whose partial states exceed the fixed scratch is rejected
+    with DMQ_ERR_SCRATCH before anything touches a device."""
+    f = L.dmq_attention_gqa_noalloc
+    Q, KC, VC, O = (A16 + 0x100000 * i for i in range(4))
+    assert f(None, KC, VC, O, 1, 0, 24, 8, 16, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert f(Q, KC, VC, Q, 1, 0, 24, 8, 16, None) == dmq.DMQ_ERR_INVALID_ARG          # out is q
+    assert f(Q, KC, VC, O, 1, 16, 24, 8, 16, None) == dmq.DMQ_ERR_INVALID_ARG         # past the cache
+    assert f(Q, KC, VC, O, 1, 0, 24, 7, 16, None) == dmq.DMQ_ERR_INVALID_ARG          # heads not grouped
+    assert f(Q + 8, KC, VC, O, 1, 0, 24, 8, 16, None) == dmq.DMQ_ERR_ALIGNMENT
+    rec = 520                                                   # bytes per (query, head, piece)
+    cap_pieces = dmq.DMQ_NOALLOC_SCRATCH_BYTES // (16 * 24 * rec)
+    L_big = 64 * (cap_pieces + 1)
+    assert f(Q, KC, VC, O, 16, L_big - 16, 24, 8, L_big, None) == dmq.DMQ_ERR_SCRATCH
+    assert "scratch" in dmq.status_string(dmq.DMQ_ERR_SCRATCH)
 
 
 def test_version_and_status_strings():
