@@ -137,12 +137,30 @@ def _timed(torch, fn, reps=20, warm=5):
     return e0.elapsed_time(e1) / reps
 
 
-def sweep(torch, dmq):
+SWEEP_PARTS = ("config0", "ffn", "layers", "rmsnorm", "lmhead", "chain")
+
+
+def sweep(torch, dmq, parts=SWEEP_PARTS):
     """The other configurations of the scope table, one JSON line each:
     config 0 (one Q projection at M=16), config 3 (fused SwiGLU FFN at
     M=1024, x ~ N(0,1) and the sigma=1/16 companion), config 4 (one layer's
     seven GEMMs at M = 1024 / 2048 / 4096, weights rotated over 5 layers,
-    and the Q6_K LM head on 1024 rows)."""
+    and the Q6_K LM head on 1024 rows).  `parts` selects which."""
+    if "config0" in parts:
+        sweep_config0(torch, dmq)
+    if "ffn" in parts:
+        sweep_ffn(torch, dmq)
+    if "layers" in parts:
+        sweep_layers(torch, dmq)
+    if "rmsnorm" in parts:
+        sweep_rmsnorm(torch, dmq)
+    if "lmhead" in parts:
+        sweep_lmhead(torch, dmq)
+    if "chain" in parts:
+        layer_chain_sweep(torch, dmq)
+
+
+def sweep_config0(torch, dmq):
     dev = "cuda"
     # config 0: one Q projection, M = 16, weights rotated (64 copies > 256 MB cache)
     M, N, K = 16, 3072, 3072
@@ -164,7 +182,25 @@ def sweep(torch, dmq):
                       "weight_GB/s": round(wbytes / ms / 1e6, 1),
                       "graph_us": round(gms * 1e3, 2), "graph_weight_GB/s": round(wbytes / gms / 1e6, 1)}), flush=True)
     del ws
+    # one layer's seven projections at M = 16 in one grouped launch (the
+    # small-M kernel), 8 rotating layers, graph replay
+    M = 16
+    xs, ys = {}, {}
+    for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
+        xs[name] = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(0, 0, idx))).to(dev)
+        ys[name] = torch.empty((M, N), dtype=torch.float32, device=dev)
+    layers = [layer_problems(torch, dmq, 0, layer, M, xs, ys) for layer in range(8)]
+    per = time_graph(torch, dmq.dmq_gemm_group, [g for g, _ in layers], 20, per_replay=True)
+    us = float(np.median(per)) * 1e3
+    print(json.dumps({"sweep": "layer GEMMs M=16 (grouped small-M launch, 8 rotating layers, graph replay)",
+                      "us_per_layer": round(us, 2), "weight_GB/s": round(weight_bytes() / us / 1e3, 1),
+                      "TFLOP/s": round(flops_of(M) / us / 1e6, 2), "ms_per_layer": stats(per)}), flush=True)
+    del layers
 
+
+
+def sweep_ffn(torch, dmq):
+    dev = "cuda"
     # config 3: fused FFN, M = 1024, D = 3072, F = 8192
     M, D, F = 1024, 3072, 8192
     wgu = torch.from_numpy(synthetic.q4k_blocks(2 * F, D, seed=synthetic.weight_seed(3, 0, 4)).reshape(-1)).to(dev)
@@ -181,6 +217,10 @@ def sweep(torch, dmq):
                           "h_overflow_fraction": round(float((~torch.isfinite(hf)).float().mean()), 4)}), flush=True)
     del wgu, wd, h, yf
 
+
+
+def sweep_layers(torch, dmq):
+    dev = "cuda"
     # config 4: one layer's seven GEMMs at M = 1024, 2048, 4096 (grouped launch)
     for M in (1024, 2048, 4096):
         xs, ys = {}, {}
@@ -200,6 +240,10 @@ def sweep(torch, dmq):
                           "pct_fp16_peak": round(100 * flops_of(M) / ms / 1e9 / PEAK_FP16_TFLOPS, 2)}), flush=True)
         del layers, xs, ys
 
+
+
+def sweep_rmsnorm(torch, dmq):
+    dev = "cuda"
     # RMSNorm ahead of the Q|K|V projections (K = 3072): the normalize-then-
     # GEMM call against the same three GEMMs on already normalized input, at
     # M = 1024 (norm kernel + grouped GEMM) and M = 1 (norm fused into the
@@ -237,6 +281,10 @@ def sweep(torch, dmq):
                           "TFLOP/s_with_norm": round(fl / t_norm / 1e9, 1)}), flush=True)
         del ws, projs, groups
 
+
+
+def sweep_lmhead(torch, dmq):
+    dev = "cuda"
     # config 4: tied LM head, Q6_K 3072 -> 128256 on 1024 rows
     name, fmt, N, K = synthetic.LM_HEAD
     M = 1024
@@ -408,6 +456,99 @@ def settle(torch, fn, min_launches, min_ms=SETTLE_MS, chunk=25, cap=20000):
     return n, ms, first
 
 
+def stats(ms_list):
+    """Median, 95th percentile, min, max and coefficient of variation of a
+    list of per-run times (ms)."""
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"n": int(a.size), "median": round(float(np.median(a)), 5), "p95": round(float(np.percentile(a, 95)), 5),
+            "min": round(float(a.min()), 5), "max": round(float(a.max()), 5),
+            "cv": round(float(a.std() / a.mean()), 4) if a.size > 1 else 0.0}
+
+
+def device_record(torch):
+    """What the run ran on: device name and architecture, compute units,
+    memory, ROCm / HIP / torch versions."""
+    p = torch.cuda.get_device_properties(0)
+    rec = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "memory_GiB": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rec["rocm"] = f.read().strip()
+    except OSError:
+        rec["rocm"] = None
+    return rec
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz) with amdsmi from a thread while
+    the caller keeps the GPU busy; median of the samples.  Reports None (and
+    why) where amdsmi is missing or cannot see the device."""
+
+    def __init__(self, torch):
+        self.samples, self.error, self.handle = [], None, None
+        try:
+            import amdsmi
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            p = torch.cuda.get_device_properties(0)
+            bus = getattr(p, "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if bus is None or int(bdf.split(":")[1], 16) == int(bus):
+                    self.handle = h
+                    break
+            if self.handle is None:
+                self.error = "device not found among amdsmi handles"
+        except Exception as e:   # noqa: BLE001
+            self.error = f"amdsmi unavailable: {type(e).__name__}: {e}"
+
+    def _read(self):
+        """Mean of the per-XCD current graphics clocks (MHz)."""
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        v = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if v:
+            return float(np.mean(v))
+        return float(m["current_gfxclk"])
+
+    def run_while(self, busy_fn, seconds=1.0):
+        """Call busy_fn() repeatedly (it enqueues GPU work) for `seconds`,
+        sampling the clock from a second thread; the samples of the first
+        quarter (while the clock may still be ramping) are dropped."""
+        import threading
+        if self.handle is None:
+            return None
+        stop = threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    v = self._read()
+                    if time.perf_counter() - t0 > seconds / 4:
+                        self.samples.append(v)
+                except Exception as e:   # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                time.sleep(0.01)
+        t = threading.Thread(target=sample)
+        t0 = time.perf_counter()
+        t.start()
+        import torch
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                busy_fn()
+            torch.cuda.synchronize()
+        stop.set()
+        t.join()
+        return self.result()
+
+    def result(self):
+        if not self.samples:
+            return {"median_MHz": None, "samples": 0, "error": self.error}
+        return {"median_MHz": round(float(np.median(self.samples)), 1), "min_MHz": round(min(self.samples), 1),
+                "max_MHz": round(max(self.samples), 1), "samples": len(self.samples), "source": "amdsmi"}
+
+
 def time_launches(torch, launch, groups, steps, warmup):
     """Run `launch(group)` over the rotating groups; events bracket every
     launch on the current (launch) stream.  Returns (total_ms, [per-launch
@@ -434,10 +575,11 @@ def time_launches(torch, launch, groups, steps, warmup):
     return t0.elapsed_time(t1), per, {"launches": nw, "gpu_ms": round(wms, 1), "first_ms_per_step": round(cold, 4)}
 
 
-def time_graph(torch, launch, groups, replays):
+def time_graph(torch, launch, groups, replays, per_replay=False):
     """Capture one launch per group into a HIP graph and time `replays`
-    replays (kernels back to back, no host launch gaps).  Returns ms per
-    launch."""
+    replays (kernels back to back, no host launch gaps), each between its own
+    pair of events.  Returns ms per launch (mean over the replays), or with
+    per_replay the list of per-replay ms per launch."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -452,14 +594,15 @@ def time_graph(torch, launch, groups, replays):
         for g in groups:
             launch(g)
     settle(torch, graph.replay, 2, chunk=5)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(replays):
-        graph.replay()
-    t1.record()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / (replays * len(groups))
+    for a, b in ev:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) / len(groups) for a, b in ev]
+    return per if per_replay else float(np.mean(per))
 
 
 def cpu_baseline(rows_sample: int):
@@ -491,7 +634,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of known size (counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
-                    help="only measure the other configurations (M=16, FFN, M sweep, LM head) and exit")
+                    help="only measure the other configurations (M=16, FFN, M sweep, LM head, layer chain) and exit")
+    ap.add_argument("--sweep-part", choices=SWEEP_PARTS, action="append",
+                    help="with --sweep: only these parts (repeatable)")
     ap.add_argument("--layer", action="store_true",
                     help="only time whole decoder layers (decode step and prefill) through the library and exit")
     ap.add_argument("--vendor-gemm-probe", action="store_true",
@@ -513,9 +658,7 @@ def main():
         vendor_gemm_probe(torch)
         return
     if args.sweep:
-        import dequant_gemm_q4_amd as dmq
-        sweep(torch, dmq)
-        layer_chain_sweep(torch, dmq)
+        sweep(torch, dmq, tuple(args.sweep_part) if args.sweep_part else SWEEP_PARTS)
         return
     if args.layer:
         layer_chain_sweep(torch, dmq)
@@ -563,7 +706,21 @@ def main():
                      "kernel": "dmq::gemm_kernel<3,8,2,false> (grouped Q4_K/Q6_K prefill launch) + "
                                "dmq::splitk_reduce_kernel (piece-order sum of the split down projection)",
                      "launch_ms": round(kern_ms, 4)},
+        # per-step times (events around each of the K timed steps): the pages'
+        # protocol reports medians and 95th percentiles over repeated runs
+        "step_ms": stats(per),
+        "device": device_record(torch),
+        "seeds": {"weights": "1000003*config + 1009*layer + projection (0..6 = q,k,v,o,gate,up,down)",
+                  "activations": "weight seed + 500000000", "config": 2, "layers": list(range(ROTATE_LAYERS)),
+                  "generator": "numpy PCG64"},
     }
+    # achieved graphics clock, sampled while the same step runs again (untimed)
+    it = [0]
+
+    def again():
+        dmq.dmq_gemm_group(groups[it[0] % len(groups)])
+        it[0] += 1
+    out["sclk_during_step"] = ClockSampler(torch).run_while(again)
 
     if not args.no_decode:
         dxs, dys = {}, {}
@@ -577,15 +734,20 @@ def main():
         d_total, d_per, _ = time_launches(torch, dmq.dmq_gemm_group, dgroups, dsteps, args.warmup)
         wb = weight_bytes()
         d_ms = float(np.mean(d_per))
-        # a decode loop replays its launches from a graph: time that too
-        g_ms = time_graph(torch, dmq.dmq_gemm_group, dgroups, 8)
+        # a decode loop replays its launches from a graph: time that too, 20
+        # replays of the 8 rotating layers, each replay between its own events
+        g_per = time_graph(torch, dmq.dmq_gemm_group, dgroups, 20, per_replay=True)
+        g_ms = float(np.median(g_per))
         out["decode"] = {"workload": "M=1, one layer's 7 projections in one grouped launch, 8 rotating layers",
                          "us_per_layer": round(1e3 * d_total / dsteps, 2),
                          "GB/s": round(wb / (d_total / dsteps / 1e3) / 1e9, 1),
                          "kernel_GB/s": round(wb / (d_ms / 1e3) / 1e9, 1),
+                         "kernel_ms": stats(d_per),
                          "graph_us_per_layer": round(1e3 * g_ms, 2),
                          "graph_GB/s": round(wb / (g_ms / 1e3) / 1e9, 1),
-                         "frac_hbm": round(wb / (g_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         "graph_ms_per_layer": stats(g_per),
+                         "frac_hbm": round(wb / (g_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "seeds": {"config": 1, "layers": list(range(DECODE_ROTATE))}}
 
     if args.cpu_rows > 0:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
