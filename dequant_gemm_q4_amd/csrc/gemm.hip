@@ -69,10 +69,10 @@ struct GemmArgs {
 
 typedef float f16x __attribute__((ext_vector_type(16)));
 
-template <int JB, int IB>
+template <int JB, int IB, int NW = 4>
 struct TileCfg {
   static constexpr int BM = 32 * JB;                 // activation rows per tile
-  static constexpr int BN = 128 * IB;                // weight rows per tile
+  static constexpr int BN = 32 * IB * NW;            // weight rows per tile (NW waves of 32*IB rows)
   static constexpr int XBUF = BM * 128;              // bytes per x buffer (64 fp16 per row)
   static constexpr int TSTRIDE = 20;                 // floats per table row (16 + 4 pad)
   static constexpr int TBUF = BN * TSTRIDE * 4;      // bytes of the scale table
@@ -298,13 +298,14 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // and 16 rows m: for a fixed accumulator register the 64 lanes hold 32
 // consecutive columns of two rows, and the epilogue's dword stores write
 // whole 128-byte lines of y straight from the accumulators.
-template <int FMT, int JB, int IB, bool SWIGLU>
+template <int FMT, int JB, int IB, int NW, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_tile, int kb0, int nbk, void* out,
                                           uint8_t* x0, uint8_t* x1, uint8_t* x2, uint8_t* x3, float* tab) {
-  typedef TileCfg<JB, IB> C;
+  typedef TileCfg<JB, IB, NW> C;
   typedef typename RawOf<FMT>::T Raw;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
-  constexpr int XQ = JB;                             // x load instructions per wave per chunk (BM/8 row groups / 4 waves)
+  constexpr int XQ = 4 * JB / NW;                    // x load instructions per wave per chunk (BM/8 row groups / NW waves)
+  static_assert(XQ * NW == 4 * JB, "the tile's 8-row groups must split evenly over the waves");
   constexpr int NRAW = FMT == 0 ? IB : 3 * IB;       // VMEM instructions of one raw load round
   constexpr int NSC = FMT == 0 ? 16 : 8;             // scale floats per row a lane keeps
   const int tid = threadIdx.x, lane = tid & 63;
@@ -343,14 +344,14 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   uint32_t xoff[XQ];
 #pragma unroll
   for (int i = 0; i < XQ; ++i) {
-    const int r = 8 * (4 * i + wave) + (lane >> 3);
+    const int r = 8 * (NW * i + wave) + (lane >> 3);
     xoff[i] = (uint32_t)r * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
   uint8_t* const xb[4] = {x0, x1, x2, x3};
   auto load_x = [&](int ck, uint8_t* xd) {
 #pragma unroll
     for (int i = 0; i < XQ; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xd + (4 * i + wave) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xd + (NW * i + wave) * 1024),
                                                16, xoff[i], (uint32_t)(128 * ck), 0, 0);
   };
   // B-fragment offsets of row li (j-block 0) in an x buffer for the 4 K
@@ -429,6 +430,22 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       for (int k = 0; k < va; ++k) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
   };
+  // NW = 8 (one i-block per wave): each B fragment feeds exactly one MFMA, so
+  // its next-step read follows that MFMA into the same registers (no second
+  // set of fragments); the order per MFMA: the MFMA, its fragment's read,
+  // the step's share of VMEM loads, va VALU instructions.
+  auto interleave_rd = [&](int nv, int va) {
+#pragma unroll
+    for (int i = 0; i < JB * IB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int v = (i + 1) * nv / (JB * IB) - i * nv / (JB * IB);
+#pragma unroll
+      for (int k = 0; k < v; ++k) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+      for (int k = 0; k < va; ++k) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
+  };
   // The VMEM loads chunk j of a block issues for later chunks, spread over its
   // K steps 0..2 (a burst of them at the chunk start would fill the
   // texture-address FIFO and stall the wave's MFMA issue behind it):
@@ -450,7 +467,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         }
       } else if (t < nr + XQ) {
         const int i = t - nr;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xb[(j + 3) & 3] + (4 * i + wave) * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xb[(j + 3) & 3] + (NW * i + wave) * 1024),
                                                  16, xoff[i], (uint32_t)(128 * ck3), 0, 0);
       } else if constexpr (FMT == 0) {
         raw_load_q4(wr[t - nr - XQ], roff, ck3, rs[(j + 3) & 3][t - nr - XQ]);
@@ -505,6 +522,68 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       const int nxt = FMT == 0 ? ((j + 1) & 3) : (((j + 1) & 3) >> 1);
       // x (and raw bytes) of chunk ck+3 go into the buffers chunk ck-1 used
       const int ck3 = ck + 3 < 4 * nb ? ck + 3 : 4 * nb - 1;
+
+      if constexpr (NW == 8) {
+        // K steps 0..2
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          h8 afn[IB];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
+          if (j == 3 && s == 0 && more && tab_thread)
+            tab_store<FMT>(my_tab, hdr, hdr4);
+          const int nv = issue_loads(j, s, ck3, b, bnext);
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+            for (int c = 0; c < IB; ++c)
+              acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[jb], af[c], acc[jb][c], 0, 0, 0);
+            bf[jb] = *(const h8*)(xc + boff[s + 1] + jb * 32 * 128);
+          }
+          interleave_rd(nv, j == 3 && s == 0 ? 6 : 3);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < IB; ++c) af[c] = afn[c];
+        }
+        // K step 3: as below; the next chunk's fragments are read from its
+        // buffer after the barrier, each after the MFMA that frees it
+        if constexpr (FMT == 0) {
+          wait_vm_barrier<2 * (XQ + NRAW)>();
+        } else {
+          if (j == 0 || j == 2) wait_vm_barrier<2 * XQ + NRAW>();
+          else wait_vm_barrier<2 * XQ>();
+        }
+        h8 afn[IB];
+        float svn[IB][4];
+        if (pf1) {
+          if (j == 3) read_scales();
+          chunk_scales((j + 1) & 3, svn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (pf1) {
+#pragma unroll
+          for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
+        }
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+          for (int c = 0; c < IB; ++c)
+            acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[jb], af[c], acc[jb][c], 0, 0, 0);
+          if (pf1) bf[jb] = *(const h8*)(xn + boff[0] + jb * 32 * 128);
+        }
+        interleave_rd(0, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (pf1) {
+#pragma unroll
+          for (int c = 0; c < IB; ++c) {
+            af[c] = afn[c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
+          }
+        }
+        continue;
+      }
 
       // K steps 0..2
 #pragma unroll
@@ -640,20 +719,21 @@ __device__ __forceinline__ const GemmDesc& tile_of(const GemmArgs& args, int& m_
   return P;
 }
 
-template <int FMT, int JBA, int JBB, bool SWIGLU>
+template <int FMT, int JBA, int JBB, bool SWIGLU, int NW>
 __device__ __forceinline__ void run_tile(const GemmDesc& P, int m_tile, int n_tile, int piece, uint8_t* x0,
                                          uint8_t* x1, uint8_t* x2, uint8_t* x3, float* tab) {
+  constexpr int IB = 8 / NW;   // weight i-blocks per wave: 256 weight rows per tile
   const int kb0 = piece * P.kbs;
   const int left = P.K / QK - kb0;
   const int nbk = left < P.kbs ? left : P.kbs;
   void* out = SWIGLU ? P.out : (void*)((float*)P.out + piece * P.out_stride);
   if constexpr (JBA == JBB) {
-    gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+    gemm_tile<FMT, JBA, IB, NW, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
   } else {
     if (P.alt)
-      gemm_tile<FMT, JBB, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+      gemm_tile<FMT, JBB, IB, NW, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
     else
-      gemm_tile<FMT, JBA, 2, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
+      gemm_tile<FMT, JBA, IB, NW, SWIGLU>(P, m_tile, n_tile, kb0, nbk, out, x0, x1, x2, x3, tab);
   }
 }
 
@@ -662,9 +742,10 @@ __device__ __forceinline__ void run_tile(const GemmDesc& P, int m_tile, int n_ti
 // the kernel branches per workgroup (uniformly) on the segment's format, so
 // a group of mixed-format problems is one launch rather than one per format
 // serialised on the stream.
-template <int FMT_MASK, int JBA, int JBB, bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
-  typedef TileCfg<JBA, 2> C;   // LDS sized for the taller tile
+template <int FMT_MASK, int JBA, int JBB, bool SWIGLU, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs args) {
+  static_assert(!SWIGLU || NW == 4, "the SwiGLU epilogue pairs a wave's two i-blocks");
+  typedef TileCfg<JBA, 8 / NW, NW> C;   // LDS sized for the taller tile
   __shared__ __attribute__((aligned(16))) uint8_t x0[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x1[C::XBUF];
   __shared__ __attribute__((aligned(16))) uint8_t x2[C::XBUF];
@@ -674,14 +755,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs args) {
   int m_tile, n_tile, piece;
   const GemmDesc& P = tile_of(args, m_tile, n_tile, piece);
   if constexpr (FMT_MASK == 1) {
-    run_tile<0, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+    run_tile<0, JBA, JBB, SWIGLU, NW>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
   } else if constexpr (FMT_MASK == 2) {
-    run_tile<1, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+    run_tile<1, JBA, JBB, SWIGLU, NW>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
   } else {
     if (P.fmt == 0)
-      run_tile<0, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+      run_tile<0, JBA, JBB, SWIGLU, NW>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
     else
-      run_tile<1, JBA, JBB, SWIGLU>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
+      run_tile<1, JBA, JBB, SWIGLU, NW>(P, m_tile, n_tile, piece, x0, x1, x2, x3, tab);
   }
 #else
   (void)args, (void)x0, (void)x1, (void)x2, (void)x3, (void)tab;
@@ -943,23 +1024,44 @@ static Plan get_plan(const GemmProblem* probs, int count) {
   return pl;
 }
 
-template <int FMT_MASK, int JBA, int JBB, bool SWIGLU>
+template <int FMT_MASK, int JBA, int JBB, bool SWIGLU, int NW>
 static hipError_t launch_k(int tiles, const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<FMT_MASK, JBA, JBB, SWIGLU>), dim3(tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT_MASK, JBA, JBB, SWIGLU, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
+// nw: waves per workgroup, 4 (two i-blocks each) or 8 (one each, two waves
+// per SIMD); 8 needs tiles of at least 64 rows and no SwiGLU epilogue.
 template <int JBA, int JBB>
-static hipError_t launch_pair(const Plan& pl, int tiles, const GemmArgs& a, hipStream_t s) {
-  if (pl.swiglu) return launch_k<1, JBA, JBB, true>(tiles, a, s);
+static hipError_t launch_pair(const Plan& pl, int tiles, const GemmArgs& a, hipStream_t s, int nw) {
+  if (pl.swiglu) return launch_k<1, JBA, JBB, true, 4>(tiles, a, s);
+  if constexpr (JBB >= 2) {
+    if (nw == 8) {
+      switch (pl.fmt_mask) {
+        case 1: return launch_k<1, JBA, JBB, false, 8>(tiles, a, s);
+        case 2: return launch_k<2, JBA, JBB, false, 8>(tiles, a, s);
+        default: return launch_k<3, JBA, JBB, false, 8>(tiles, a, s);
+      }
+    }
+  }
   switch (pl.fmt_mask) {
-    case 1: return launch_k<1, JBA, JBB, false>(tiles, a, s);
-    case 2: return launch_k<2, JBA, JBB, false>(tiles, a, s);
-    default: return launch_k<3, JBA, JBB, false>(tiles, a, s);
+    case 1: return launch_k<1, JBA, JBB, false, 4>(tiles, a, s);
+    case 2: return launch_k<2, JBA, JBB, false, 4>(tiles, a, s);
+    default: return launch_k<3, JBA, JBB, false, 4>(tiles, a, s);
   }
 }
 
+// Waves per workgroup for a plan: 8 where the kernel has them (tiles of at
+// least 64 rows, no SwiGLU epilogue), else 4.
+static int plan_waves(const Plan& pl) { return !pl.swiglu && pl.jbb >= 2 ? 8 : 4; }
+
+static hipError_t launch_chunk_nw(const GemmProblem* probs, int count, hipStream_t s, int nw);
+
 static hipError_t launch_chunk(const GemmProblem* probs, int count, hipStream_t s) {
+  return launch_chunk_nw(probs, count, s, plan_waves(get_plan(probs, count)));
+}
+
+static hipError_t launch_chunk_nw(const GemmProblem* probs, int count, hipStream_t s, int nw) {
   const Plan pl = get_plan(probs, count);
   // workspace slices of the split problems (slice stride rounded to 4 floats)
   int64_t ws_floats = 0;
@@ -1018,10 +1120,10 @@ static hipError_t launch_chunk(const GemmProblem* probs, int count, hipStream_t 
   a.count = pl.nseg;
   hipError_t e;
   switch (pl.jba) {
-    case 8: e = pl.jbb == 2 ? launch_pair<8, 2>(pl, tiles, a, s) : launch_pair<8, 4>(pl, tiles, a, s); break;
-    case 4: e = launch_pair<4, 2>(pl, tiles, a, s); break;
-    case 2: e = launch_pair<2, 1>(pl, tiles, a, s); break;
-    default: e = launch_pair<1, 1>(pl, tiles, a, s); break;
+    case 8: e = pl.jbb == 2 ? launch_pair<8, 2>(pl, tiles, a, s, nw) : launch_pair<8, 4>(pl, tiles, a, s, nw); break;
+    case 4: e = launch_pair<4, 2>(pl, tiles, a, s, nw); break;
+    case 2: e = launch_pair<2, 1>(pl, tiles, a, s, nw); break;
+    default: e = launch_pair<1, 1>(pl, tiles, a, s, nw); break;
   }
   if (e != hipSuccess || r.count == 0) return e;
   const int64_t groups = r.begin[r.count];
