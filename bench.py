@@ -137,7 +137,7 @@ def _timed(torch, fn, reps=20, warm=5):
     return e0.elapsed_time(e1) / reps
 
 
-SWEEP_PARTS = ("config0", "ffn", "layers", "rmsnorm", "lmhead", "chain")
+SWEEP_PARTS = ("config0", "ffn", "layers", "rmsnorm", "lmhead", "chain", "overlap")
 
 
 def sweep(torch, dmq, parts=SWEEP_PARTS):
@@ -158,6 +158,8 @@ def sweep(torch, dmq, parts=SWEEP_PARTS):
         sweep_lmhead(torch, dmq)
     if "chain" in parts:
         layer_chain_sweep(torch, dmq)
+    if "overlap" in parts:
+        layer_overlap_sweep(torch, dmq)
 
 
 def sweep_config0(torch, dmq):
@@ -417,6 +419,63 @@ def layer_chain_sweep(torch, dmq):
                       "layer_TFLOP/s": round((gemm_flop + att_flop) / ms / 1e9, 1)}), flush=True)
 
 
+def layer_overlap_sweep(torch, dmq):
+    """dmq_layer_prefill on Llama-3.2-3B shapes (weights rotated over 3 seeded
+    layers): the attention side of chunk c+1 overlapped with the FFN of chunk
+    c on two streams, against the same chunked schedule on one stream and
+    against one pass over all rows."""
+    dev = "cuda"
+    D, F, HQ, HKV, HD = synthetic.HIDDEN, synthetic.FFN, synthetic.N_HEADS, synthetic.N_KV_HEADS, synthetic.HEAD_DIM
+    rng = np.random.default_rng(4321)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    g = [t((s_ * rng.uniform(0.5, 1.5, D)).astype(np.float32)) for s_ in (0.02, 0.05, 0.02)]
+    for M in (1024, 4096):
+        L = M
+        e = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+        x = t(rng.standard_normal((M, D)).astype(np.float32))
+        xn = e(M, D, dt=torch.float16)
+        dmq.dmq_residual_rmsnorm(x, torch.zeros_like(x), g[0], 1e-5, e(M, D), xn, M, D)
+        B = {"h_in": x, "xn_in": xn, "yq": e(M, HQ * HD), "yk": e(M, HKV * HD), "yv": e(M, HKV * HD),
+             "q_rot": e(M, HQ * HD, dt=torch.float16), "attn": e(M, HQ * HD, dt=torch.float16), "yo": e(M, D),
+             "h_mid": e(M, D), "xn_ffn": e(M, D, dt=torch.float16), "h_ffn": e(M, F, dt=torch.float16),
+             "y_down": e(M, D), "h_out": e(M, D), "xn_out": e(M, D, dt=torch.float16)}
+        layers = []
+        for layer in range(3):
+            w = {name: wq for name, fmt, N, K, wq in synthetic.layer_weights(4, layer)}
+            W = {"q": t(w["q"].reshape(-1)), "k": t(w["k"].reshape(-1)), "v": t(w["v"].reshape(-1)),
+                 "o": t(w["o"].reshape(-1)), "gate_up": t(np.concatenate([w["gate"], w["up"]]).reshape(-1)),
+                 "down": t(w["down"].reshape(-1)), "g_ffn": g[1], "g_next": g[2],
+                 "k_cache": torch.zeros((HKV, L, HD), dtype=torch.float16, device=dev),
+                 "v_cache": torch.zeros((HKV, L, HD), dtype=torch.float16, device=dev)}
+            layers.append((W, dmq.make_layer(W, B, M, D, F, HQ, HKV, L)))
+        side = torch.cuda.Stream()
+        res = {}
+        plan = [("one_pass", M, False)]
+        for ch in (M // 2, M // 4, 256):
+            plan += [(f"chunk{ch}_one_stream", ch, False), (f"chunk{ch}_two_streams", ch, True)]
+        for label, chunk, two in plan:
+            it = [0]
+
+            def one():
+                dmq.dmq_layer_prefill(layers[it[0] % 3][1], M, 0, D, F, HQ, HKV, L, 1e-5, chunk,
+                                      stream_attn=torch.cuda.current_stream(),
+                                      stream_ffn=side if two else None)
+                it[0] += 1
+            res[label] = _timed(torch, one, reps=10, warm=3)
+        att_flop = 4.0 * HQ * HD * (M * (M + 1) / 2)
+        fl = flops_of(M) + att_flop
+        best = min((k for k in res if k.endswith("two_streams")), key=lambda k: res[k])
+        gains = {k.replace("_two_streams", ""): round(res[k.replace("two_streams", "one_stream")] / res[k], 3)
+                 for k in res if k.endswith("two_streams")}
+        print(json.dumps({"sweep": f"prefill layer, attention || FFN on two streams (dmq_layer_prefill), M={M}",
+                          **{f"{k}_ms": round(v, 4) for k, v in res.items()},
+                          "two_stream_gain_over_one_stream": gains,
+                          "best_two_streams": best, "best_vs_one_pass": round(res["one_pass"] / res[best], 3),
+                          "TFLOP/s_one_pass": round(fl / res["one_pass"] / 1e9, 1),
+                          "TFLOP/s_best_two_streams": round(fl / res[best] / 1e9, 1)}), flush=True)
+        del layers, B
+
+
 def layer_problems(torch, dmq, config, layer, M, xs, ys):
     probs = []
     for name, fmt, N, K, wq in synthetic.layer_weights(config, layer):
@@ -624,6 +683,41 @@ def cpu_baseline(rows_sample: int):
                       f"(exact dequant + fp64 matmul; {fl / 1e9:.1f} GFLOP in {dt:.1f} s)"}
 
 
+def counters_workload(torch, dmq, reps=5):
+    """A short run for counter collection (rocprofv3 --pmc): `reps` launches
+    each of the M = 1024 prefill layer (one grouped GEMM call), the M = 1
+    decode layer (one grouped GEMV launch), config 0 (M = 16 small-M kernel)
+    and a plain device copy of COPY_PROBE_BYTES (the reference that scales
+    FETCH_SIZE / WRITE_SIZE to bytes), with no warm-up loops."""
+    xs, ys, dxs, dys = {}, {}, {}, {}
+    for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
+        xs[name] = torch.from_numpy(synthetic.activations(M_PREFILL, K, seed=synthetic.act_seed(2, 0, idx),
+                                                          unit_rms=True)).cuda()
+        ys[name] = torch.empty((M_PREFILL, N), dtype=torch.float32, device="cuda")
+        dxs[name] = torch.from_numpy(synthetic.activations(1, K, seed=synthetic.act_seed(1, 0, idx))).cuda()
+        dys[name] = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    pre = [layer_problems(torch, dmq, 2, layer, M_PREFILL, xs, ys) for layer in range(ROTATE_LAYERS)]
+    dec = [layer_problems(torch, dmq, 1, layer, 1, dxs, dys) for layer in range(DECODE_ROTATE)]
+    M, N, K = 16, 3072, 3072
+    x0 = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(0, 0, 0))).cuda()
+    w0 = [torch.from_numpy(synthetic.q4k_blocks(N, K, seed=synthetic.weight_seed(0, layer, 0)).reshape(-1)).cuda()
+          for layer in range(8)]
+    y0 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for i in range(reps):
+        dmq.dmq_gemm_group(pre[i % len(pre)][0])
+    for i in range(reps):
+        dmq.dmq_gemm_group(dec[i % len(dec)][0])
+    for i in range(reps):
+        dmq.dmq_gemm_q4k(x0, w0[i % len(w0)], y0, M, N, K)
+    torch.cuda.synchronize()
+    src = torch.randint(0, 255, (COPY_PROBE_BYTES,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_workload": {"reps": reps, "copy_bytes": COPY_PROBE_BYTES}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -639,6 +733,8 @@ def main():
                     help="with --sweep: only these parts (repeatable)")
     ap.add_argument("--layer", action="store_true",
                     help="only time whole decoder layers (decode step and prefill) through the library and exit")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run a few launches of each hot kernel and a calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--vendor-gemm-probe", action="store_true",
                     help="only time dense fp16 torch.matmul on the layer shapes (reference) and exit")
     args = ap.parse_args()
@@ -657,11 +753,15 @@ def main():
     if args.vendor_gemm_probe:
         vendor_gemm_probe(torch)
         return
+    if args.counters:
+        counters_workload(torch, dmq)
+        return
     if args.sweep:
         sweep(torch, dmq, tuple(args.sweep_part) if args.sweep_part else SWEEP_PARTS)
         return
     if args.layer:
         layer_chain_sweep(torch, dmq)
+        layer_overlap_sweep(torch, dmq)
         return
     M = M_PREFILL
 

@@ -35,7 +35,7 @@ FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
 EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
            "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
            "dmq_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm",
-           "dmq_status_string", "dmq_version")
+           "dmq_layer_prefill", "dmq_status_string", "dmq_version")
 HEAD_DIM = 128
 
 
@@ -56,6 +56,21 @@ class ProjDesc(ctypes.Structure):
     """Mirror of dmq_proj_desc."""
     _fields_ = [("format", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("wq", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
+class LayerWeights(ctypes.Structure):
+    """Mirror of dmq_layer_weights."""
+    _fields_ = [("fmt_q", ctypes.c_int32), ("fmt_k", ctypes.c_int32), ("fmt_v", ctypes.c_int32),
+                ("fmt_o", ctypes.c_int32), ("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("wv", ctypes.c_void_p),
+                ("wo", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("g_ffn", ctypes.c_void_p), ("g_next", ctypes.c_void_p), ("freq_factors", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+
+
+class LayerBuffers(ctypes.Structure):
+    """Mirror of dmq_layer_buffers."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("h_in", "xn_in", "yq", "yk", "yv", "q_rot", "attn", "yo", "h_mid",
+                                                "xn_ffn", "h_ffn", "y_down", "h_out", "xn_out")]
 
 
 def _load() -> ctypes.CDLL:
@@ -80,13 +95,15 @@ def _load() -> ctypes.CDLL:
     L.dmq_rope_kv_cache.argtypes = [P, P, P, I64, I64, I32, I32, ctypes.c_double, P, P, P, P, I64, P]
     L.dmq_attention_gqa.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
     L.dmq_attention_gqa_noalloc.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
+    L.dmq_layer_prefill.argtypes = [ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerBuffers), I64, I64, I32, I32,
+                                    I32, I32, I64, ctypes.c_double, ctypes.c_float, I64, P, P]
     L.dmq_residual_rmsnorm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, P]
     L.dmq_residual_rmsnorm_gemm.argtypes = [P, P, P, ctypes.c_float, P, P, I64, I64, ctypes.POINTER(ProjDesc),
                                             I32, P]
     for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
                  "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
                  "dmq_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm",
-                 "dmq_residual_rmsnorm_gemm"):
+                 "dmq_residual_rmsnorm_gemm", "dmq_layer_prefill"):
         getattr(L, name).restype = ctypes.c_int
     L.dmq_status_string.argtypes = [ctypes.c_int]
     L.dmq_status_string.restype = ctypes.c_char_p
@@ -332,6 +349,57 @@ def dmq_residual_rmsnorm(h_in, y, g, eps: float, h_out, xn, M: int, K: int, stre
     pg = None if g is None else _dev_tensor(g, torch.float32, "g", K)
     pn = None if g is None else _dev_tensor(xn, torch.float16, "xn", M * K)
     _check(lib.dmq_residual_rmsnorm(ph, py, pg, float(eps), po, pn, M, K, _stream(stream)), "dmq_residual_rmsnorm")
+
+
+def make_layer(weights: dict, buffers: dict, M: int, D: int, F: int, n_q_heads: int, n_kv_heads: int,
+               cache_len: int):
+    """(LayerWeights, LayerBuffers) for dmq_layer_prefill from dicts of torch
+    tensors, each checked for device, dtype, contiguity and size.  weights:
+    q, k, v, o (uint8 blocks; formats fmt_q .. fmt_o, default "q4k"),
+    gate_up (Q4_K, 2F rows), down (Q6_K), g_ffn, optional g_next and
+    freq_factors (float32), k_cache, v_cache (float16 [Hkv, cache_len, 128]).
+    buffers: h_in, xn_in, yq, yk, yv, q_rot, attn, yo, h_mid, xn_ffn, h_ffn,
+    y_down, h_out and (with g_next) xn_out.  Keep the tensors alive while the
+    structures are in use."""
+    import torch
+    QD, KD = n_q_heads * HEAD_DIM, n_kv_heads * HEAD_DIM
+    fm = {k: FORMATS[weights.get("fmt_" + k, "q4k")] for k in ("q", "k", "v", "o")}
+    wt = lambda name, fmt, rows, k: _dev_tensor(weights[name], torch.uint8, name, _wq_bytes(fmt, rows, k))  # noqa: E731
+    lw = LayerWeights()
+    lw.fmt_q, lw.fmt_k, lw.fmt_v, lw.fmt_o = fm["q"], fm["k"], fm["v"], fm["o"]
+    lw.wq = wt("q", fm["q"], QD, D)
+    lw.wk = wt("k", fm["k"], KD, D)
+    lw.wv = wt("v", fm["v"], KD, D)
+    lw.wo = wt("o", fm["o"], D, QD)
+    lw.w_gate_up = wt("gate_up", DMQ_FMT_Q4K, 2 * F, D)
+    lw.w_down = wt("down", DMQ_FMT_Q6K, D, F)
+    lw.g_ffn = _dev_tensor(weights["g_ffn"], torch.float32, "g_ffn", D)
+    lw.g_next = None if weights.get("g_next") is None else _dev_tensor(weights["g_next"], torch.float32, "g_next", D)
+    ff = weights.get("freq_factors")
+    lw.freq_factors = None if ff is None else _dev_tensor(ff, torch.float32, "freq_factors", HEAD_DIM // 2)
+    lw.k_cache = _dev_tensor(weights["k_cache"], torch.float16, "k_cache", KD * cache_len)
+    lw.v_cache = _dev_tensor(weights["v_cache"], torch.float16, "v_cache", KD * cache_len)
+    shapes = {"h_in": (torch.float32, D), "xn_in": (torch.float16, D), "yq": (torch.float32, QD),
+              "yk": (torch.float32, KD), "yv": (torch.float32, KD), "q_rot": (torch.float16, QD),
+              "attn": (torch.float16, QD), "yo": (torch.float32, D), "h_mid": (torch.float32, D),
+              "xn_ffn": (torch.float16, D), "h_ffn": (torch.float16, F), "y_down": (torch.float32, D),
+              "h_out": (torch.float32, D), "xn_out": (torch.float16, D)}
+    lb = LayerBuffers()
+    for name, (dt, width) in shapes.items():
+        t = buffers.get(name)
+        setattr(lb, name, None if t is None else _dev_tensor(t, dt, name, M * width))
+    return lw, lb
+
+
+def dmq_layer_prefill(layer, M: int, pos0: int, D: int, F: int, n_q_heads: int, n_kv_heads: int, cache_len: int,
+                      eps: float, chunk: int, stream_attn=None, stream_ffn=None, theta: float = 500000.0) -> None:
+    """One decoder layer's prefill with attention and FFN chunks overlapped
+    on two streams (the same stream twice: serial); layer = make_layer(...)."""
+    lw, lb = layer
+    _check(lib.dmq_layer_prefill(ctypes.byref(lw), ctypes.byref(lb), M, pos0, D, F, n_q_heads, n_kv_heads, cache_len,
+                                 float(theta), float(eps), chunk, _stream(stream_attn),
+                                 _stream(stream_ffn if stream_ffn is not None else stream_attn)),
+           "dmq_layer_prefill")
 
 
 def dmq_version() -> int:

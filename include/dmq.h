@@ -317,6 +317,83 @@ int dmq_attention_gqa_noalloc(const void* q_f16, const void* k_cache_f16, const 
 int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, float eps, float* h_out, void* xn_f16,
                          int64_t M, int64_t K, void* stream);
 
+/*
+ * One decoder layer's prefill with its attention side and its feed-forward
+ * side running concurrently on two streams over shared device buffers: the
+ * one-GPU form of the overview page's "[03] zero-copy / unified memory"
+ * split (attention on one engine, the FFN on another, one shared buffer).
+ *
+ * For M tokens at positions pos0 .. pos0+M-1 (D hidden, F FFN width, head
+ * dimension 128):
+ *   yq|yk|yv = xn_in * Wq|Wk|Wv^T; RoPE + cache append (dmq_rope_kv_cache);
+ *   attn = attention over the cache (dmq_attention_gqa); yo = attn * Wo^T;
+ *   h_mid = h_in + yo, xn_ffn = RMSNorm(h_mid; g_ffn);
+ *   h_ffn = silu(xn_ffn * Wg^T) * (xn_ffn * Wu^T); y_down = h_ffn * Wd^T;
+ *   h_out = h_mid + y_down, xn_out = RMSNorm(h_out; g_next)
+ * (the layer description of the article "Building DAMASCUS" and the overview
+ * page's "[04] one decode step"), each step exactly as the single calls
+ * named.  The rows are cut into chunks of `chunk`: the attention side of
+ * chunk c+1 runs on stream_attn while the feed-forward side of chunk c runs
+ * on stream_ffn; events hand each chunk over, stream_ffn first waits for the
+ * work already queued on stream_attn, and stream_attn finally waits for
+ * stream_ffn, so the layer's results are ordered before later work on
+ * stream_attn.  stream_ffn == stream_attn runs the same chunked schedule on
+ * one stream, with the same bits.  Chunking changes the launch plans of the
+ * GEMMs (and so may change fp32 summation orders) against one call for all M
+ * rows; a chunk of at least M is one pass.
+ *   w : weights (formats of Q, K, V, O: DMQ_FMT_Q4K or DMQ_FMT_Q6K; gate|up
+ *       Q4_K, 2F rows, gate first; down Q6_K), the two RMSNorm weight vectors
+ *       (g_next may be NULL: then xn_out is not written), optional RoPE
+ *       frequency factors, and the layer's KV cache (fp16 [n_kv_heads,
+ *       cache_len, 128]; rows pos0 .. pos0+M-1 are written).
+ *   b : device buffers of M rows, 16-byte aligned, none overlapping another:
+ *       inputs h_in (fp32 [M, D]) and xn_in (fp16 [M, D], this layer's input
+ *       RMSNorm of h_in); outputs h_mid, h_out (fp32 [M, D]) and xn_out
+ *       (fp16 [M, D]); scratch yq (fp32 [M, n_q_heads*128]), yk, yv (fp32 [M,
+ *       n_kv_heads*128]), q_rot, attn (fp16 [M, n_q_heads*128]), yo, y_down
+ *       (fp32 [M, D]), xn_ffn (fp16 [M, D]), h_ffn (fp16 [M, F]).
+ * Requirements: D, F and n_q_heads*128 multiples of 256, chunk >= 1, at most
+ * 4096 chunks, and those of the single calls.  The library keeps a pool of
+ * HIP events per device (created on first use, kept until the process ends);
+ * calls from several host threads are serialised on it.  A failing step
+ * returns its status; steps before it stay enqueued.
+ */
+typedef struct {
+  int32_t fmt_q, fmt_k, fmt_v, fmt_o;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* w_gate_up;
+  const void* w_down;
+  const float* g_ffn;
+  const float* g_next;
+  const float* freq_factors;
+  void* k_cache;
+  void* v_cache;
+} dmq_layer_weights;
+
+typedef struct {
+  const float* h_in;
+  const void* xn_in;
+  float* yq;
+  float* yk;
+  float* yv;
+  void* q_rot;
+  void* attn;
+  float* yo;
+  float* h_mid;
+  void* xn_ffn;
+  void* h_ffn;
+  float* y_down;
+  float* h_out;
+  void* xn_out;
+} dmq_layer_buffers;
+
+int dmq_layer_prefill(const dmq_layer_weights* w, const dmq_layer_buffers* b, int64_t M, int64_t pos0, int32_t D,
+                      int32_t F, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, double theta, float eps,
+                      int64_t chunk, void* stream_attn, void* stream_ffn);
+
 /* Human-readable text of a status code (static storage). */
 const char* dmq_status_string(int status);
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(dmq.EXPORTS)
     raw = ctypes.CDLL(dmq.LIB_PATH)
     for n in names:
@@ -47,6 +47,42 @@ def test_noalloc_attention_validation():
     L_big = 64 * (cap_pieces + 1)
     assert f(Q, KC, VC, O, 16, L_big - 16, 24, 8, L_big, None) == dmq.DMQ_ERR_SCRATCH
     assert "scratch" in dmq.status_string(dmq.DMQ_ERR_SCRATCH)
+
+
+def test_layer_prefill_validation():
+    """dmq_layer_prefill checks its sizes, formats and pointers on the host
+    before it records an event or enqueues a kernel."""
+    f = L.dmq_layer_prefill
+    w = dmq.LayerWeights()
+    for i, n in enumerate(("wq", "wk", "wv", "wo", "w_gate_up", "w_down", "g_ffn", "k_cache", "v_cache")):
+        setattr(w, n, A16 + 0x100000 * (i + 1))
+    b = dmq.LayerBuffers()
+    for i, n in enumerate(("h_in", "xn_in", "yq", "yk", "yv", "q_rot", "attn", "yo", "h_mid", "xn_ffn", "h_ffn",
+                           "y_down", "h_out", "xn_out")):
+        setattr(b, n, A16 + 0x1000000 * (i + 1))
+    args = lambda **k: dict(dict(M=8, pos0=0, D=768, F=1024, hq=6, hkv=2, L=64, chunk=4), **k)  # noqa: E731
+
+    def call(wp, bp, a):
+        return f(wp, bp, a["M"], a["pos0"], a["D"], a["F"], a["hq"], a["hkv"], a["L"], 500000.0, 1e-5, a["chunk"],
+                 None, None)
+    assert call(None, ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    assert call(ctypes.byref(w), None, args()) == dmq.DMQ_ERR_INVALID_ARG
+    assert call(ctypes.byref(w), ctypes.byref(b), args(D=700)) == dmq.DMQ_ERR_INVALID_ARG     # D % 256
+    assert call(ctypes.byref(w), ctypes.byref(b), args(F=0)) == dmq.DMQ_ERR_INVALID_ARG
+    assert call(ctypes.byref(w), ctypes.byref(b), args(hq=3)) == dmq.DMQ_ERR_INVALID_ARG      # 3*128 % 256
+    assert call(ctypes.byref(w), ctypes.byref(b), args(chunk=0)) == dmq.DMQ_ERR_INVALID_ARG
+    assert call(ctypes.byref(w), ctypes.byref(b), args(M=0)) == dmq.DMQ_ERR_INVALID_ARG
+    w.fmt_v = 7
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    w.fmt_v = 0
+    b.h_mid = A16 + 8
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_ALIGNMENT
+    b.h_mid = None
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    b.h_mid = A16 + 0x20000000
+    w.g_next = A16 + 0x30000000
+    b.xn_out = None                                          # g_next without xn_out
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
 
 
 def test_version_and_status_strings():

@@ -1089,3 +1089,114 @@ def test_graph_captured_before_growth_still_replays(dmq):
             dmq.dmq_attention_gqa(q16, kc, vc, o16, 16, L - 16, hq, hkv, L, stream=side)
         side.synchronize()
         assert torch.equal(o16, want16)
+
+
+# ------------------------------------------- attention || FFN (layer) ---
+
+def _layer_setup(M, pos0, cache_len, seed=5):
+    """A small Llama-shaped layer (hidden 768 = 6 query heads x 128, 2 KV
+    heads, FFN 1024) with its inputs, as in the decoder-layer chain test."""
+    Dm, hq, hkv, F = 768, 6, 2, 1024
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, Dm)).astype(np.float32)
+    g1 = (0.02 * _norm_weights(Dm, 1)).astype(np.float32)
+    g2 = (0.05 * _norm_weights(Dm, 2)).astype(np.float32)
+    g3 = (0.03 * _norm_weights(Dm, 3)).astype(np.float32)
+    host = {"q": synthetic.q4k_blocks(hq * D_HEAD, Dm, seed=11), "k": synthetic.q4k_blocks(hkv * D_HEAD, Dm, seed=12),
+            "v": synthetic.q6k_blocks(hkv * D_HEAD, Dm, seed=13), "o": synthetic.q4k_blocks(Dm, hq * D_HEAD, seed=14),
+            "gate_up": synthetic.q4k_blocks(2 * F, Dm, seed=15), "down": synthetic.q6k_blocks(Dm, F, seed=16)}
+    kc0 = np.zeros((hkv, cache_len, D_HEAD), np.float16)
+    vc0 = np.zeros((hkv, cache_len, D_HEAD), np.float16)
+    kc0[:, :pos0] = (rng.standard_normal((hkv, pos0, D_HEAD)) * 2).astype(np.float16)
+    vc0[:, :pos0] = rng.standard_normal((hkv, pos0, D_HEAD)).astype(np.float16)
+    return dict(Dm=Dm, hq=hq, hkv=hkv, F=F, x=x, g1=g1, g2=g2, g3=g3, host=host, kc0=kc0, vc0=vc0)
+
+
+def _layer_run(dmq, S, M, pos0, cache_len, chunk, two_streams):
+    Dm, hq, hkv, F = S["Dm"], S["hq"], S["hkv"], S["F"]
+    e = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device=DEV)  # noqa: E731
+    xd = dev(S["x"])
+    xn = e(M, Dm, dt=torch.float16)
+    dmq.dmq_residual_rmsnorm(xd, torch.zeros_like(xd), dev(S["g1"]), 1e-5, e(M, Dm), xn, M, Dm)
+    W = {k: dev(v.reshape(-1)) for k, v in S["host"].items()}
+    W.update(fmt_v="q6k", g_ffn=dev(S["g2"]), g_next=dev(S["g3"]), k_cache=dev(S["kc0"]), v_cache=dev(S["vc0"]))
+    B = {"h_in": xd, "xn_in": xn, "yq": e(M, hq * D_HEAD), "yk": e(M, hkv * D_HEAD), "yv": e(M, hkv * D_HEAD),
+         "q_rot": e(M, hq * D_HEAD, dt=torch.float16), "attn": e(M, hq * D_HEAD, dt=torch.float16),
+         "yo": e(M, Dm), "h_mid": e(M, Dm), "xn_ffn": e(M, Dm, dt=torch.float16), "h_ffn": e(M, F, dt=torch.float16),
+         "y_down": e(M, Dm), "h_out": e(M, Dm), "xn_out": e(M, Dm, dt=torch.float16)}
+    layer = dmq.make_layer(W, B, M, Dm, F, hq, hkv, cache_len)
+    torch.cuda.synchronize()
+    sa = torch.cuda.current_stream()
+    sf = torch.cuda.Stream() if two_streams else sa
+    dmq.dmq_layer_prefill(layer, M, pos0, Dm, F, hq, hkv, cache_len, 1e-5, chunk, stream_attn=sa, stream_ffn=sf)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in B.items()}
+    out["k_cache"], out["v_cache"] = W["k_cache"].cpu().numpy(), W["v_cache"].cpu().numpy()
+    return out, W, B
+
+
+@pytest.mark.parametrize("M,pos0,chunk", [(300, 50, 64), (256, 0, 128), (40, 7, 16)])
+def test_layer_prefill_two_streams_same_bits(dmq, M, pos0, chunk):
+    """The attention side of chunk c+1 and the FFN of chunk c on two streams
+    give exactly the bits of the same chunked schedule on one stream, in every
+    output, scratch and cache buffer, and on a repeat."""
+    cache_len = pos0 + M + 5
+    S = _layer_setup(M, pos0, cache_len)
+    serial, _, _ = _layer_run(dmq, S, M, pos0, cache_len, chunk, two_streams=False)
+    for rep in range(2):
+        conc, _, _ = _layer_run(dmq, S, M, pos0, cache_len, chunk, two_streams=True)
+        for k in serial:
+            assert np.array_equal(serial[k].view(np.uint8), conc[k].view(np.uint8)), f"{k} differs (repeat {rep})"
+    assert np.isfinite(serial["h_ffn"].astype(np.float32)).all()
+
+
+def test_layer_prefill_matches_single_calls_and_oracle(dmq):
+    """One pass (chunk >= M) equals the layer composed of the single calls
+    bit for bit; the two-stream chunked layer matches the fp64 oracle layer
+    end to end (1% of the output norm, as the decoder-layer chain test)."""
+    M, pos0 = 96, 30
+    cache_len = pos0 + M + 2
+    S = _layer_setup(M, pos0, cache_len, seed=6)
+    Dm, hq, hkv, F = S["Dm"], S["hq"], S["hkv"], S["F"]
+    one, W, B = _layer_run(dmq, S, M, pos0, cache_len, M, two_streams=False)
+    # the same layer from the single calls
+    e = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device=DEV)  # noqa: E731
+    kc, vc = dev(S["kc0"]), dev(S["vc0"])
+    yq, yk, yv = e(M, hq * D_HEAD), e(M, hkv * D_HEAD), e(M, hkv * D_HEAD)
+    dmq.dmq_gemm_group([("q4k", B["xn_in"], W["q"], yq, M, hq * D_HEAD, Dm), ("q4k", B["xn_in"], W["k"], yk, M, hkv * D_HEAD, Dm),
+                        ("q6k", B["xn_in"], W["v"], yv, M, hkv * D_HEAD, Dm)])
+    qr, att = e(M, hq * D_HEAD, dt=torch.float16), e(M, hq * D_HEAD, dt=torch.float16)
+    dmq.dmq_rope_kv_cache(yq, yk, yv, M, pos0, hq, hkv, qr, kc, vc, cache_len)
+    dmq.dmq_attention_gqa(qr, kc, vc, att, M, pos0, hq, hkv, cache_len)
+    yo = e(M, Dm)
+    dmq.dmq_gemm_group([("q4k", att, W["o"], yo, M, Dm, hq * D_HEAD)])
+    h1, xn2 = e(M, Dm), e(M, Dm, dt=torch.float16)
+    dmq.dmq_residual_rmsnorm(B["h_in"], yo, W["g_ffn"], 1e-5, h1, xn2, M, Dm)
+    hf, yd = e(M, F, dt=torch.float16), e(M, Dm)
+    dmq.dmq_ffn_swiglu_q4k(xn2, W["gate_up"], W["down"], hf, yd, M, Dm, F)
+    ho, xo = e(M, Dm), e(M, Dm, dt=torch.float16)
+    dmq.dmq_residual_rmsnorm(h1, yd, W["g_next"], 1e-5, ho, xo, M, Dm)
+    torch.cuda.synchronize()
+    for name, t in (("h_mid", h1), ("h_out", ho), ("xn_out", xo), ("h_ffn", hf), ("attn", att)):
+        assert np.array_equal(one[name].view(np.uint8), t.cpu().numpy().view(np.uint8)), f"{name} differs from the single calls"
+    assert np.array_equal(one["k_cache"].view(np.uint16), kc.cpu().numpy().view(np.uint16))
+    # end to end against the fp64 oracle layer, for the two-stream chunked run
+    conc, _, _ = _layer_run(dmq, S, M, pos0, cache_len, 32, two_streams=True)
+    x = S["x"]
+    pos = np.arange(pos0, pos0 + M)
+    Wd = lambda fmt, wq, n, k: oracle.f16_bits_to_f64(oracle.dequant(fmt, wq, n, k))  # noqa: E731
+    H = S["host"]
+    xh1 = attn.rmsnorm_f64(x, S["g1"], 1e-5)
+    Q = attn.rope((xh1 @ Wd("q4k", H["q"], hq * D_HEAD, Dm).T).reshape(M, hq, D_HEAD), pos)
+    Kn = attn.rope((xh1 @ Wd("q4k", H["k"], hkv * D_HEAD, Dm).T).reshape(M, hkv, D_HEAD), pos)
+    Vn = (xh1 @ Wd("q6k", H["v"], hkv * D_HEAD, Dm).T).reshape(M, hkv, D_HEAD)
+    Kc = S["kc0"].astype(np.float64); Vc = S["vc0"].astype(np.float64)  # noqa: E702
+    Kc[:, pos0:pos0 + M] = Kn.transpose(1, 0, 2); Vc[:, pos0:pos0 + M] = Vn.transpose(1, 0, 2)  # noqa: E702
+    A, _ = attn.attention_gqa(Q, Kc, Vc, pos0)
+    H1 = attn.residual_add(x, A.reshape(M, -1) @ Wd("q4k", H["o"], Dm, hq * D_HEAD).T)
+    xh2 = attn.rmsnorm_f64(H1, S["g2"], 1e-5)
+    Wgu = Wd("q4k", H["gate_up"], 2 * F, Dm)
+    OUT = attn.residual_add(H1, (oracle.silu(xh2 @ Wgu[:F].T) * (xh2 @ Wgu[F:].T)) @ Wd("q6k", H["down"], Dm, F).T)
+    rel = np.linalg.norm(conc["h_out"] - OUT) / np.linalg.norm(OUT)
+    print(f"layer prefill (two streams, chunk 32): end-to-end relative error {rel:.3g}")
+    assert rel < 1e-2
