@@ -780,6 +780,21 @@ def test_attention_gqa_prefill_full_size_sampled(dmq, M):
         _check_attention(q[r:r + 1], kc, vc, out[r:r + 1], 1, int(r), hq, f"attention prefill {M} row {r}")
 
 
+def test_attention_gqa_long_context_fallback(dmq):
+    """Beyond 4096 pieces of 64 positions (262,144 cached positions) the
+    decode attention runs its one-workgroup-per-KV-head kernel instead of the
+    split pieces; the no-allocation call takes the same kernel (it needs no
+    scratch there) and gives the same bits."""
+    M, pos0, hq, hkv = 2, 262200, 4, 1
+    cache_len = pos0 + M + 6
+    q, kc, vc, out = _attention_case(dmq, M, pos0, hq, hkv, cache_len, seed=21)
+    _check_attention(q, kc, vc, out, M, pos0, hq, "attention fallback past 262144 positions")
+    o2 = torch.empty((M, hq * D_HEAD), dtype=torch.float16, device=DEV)
+    dmq.dmq_attention_gqa_noalloc(dev(q), dev(kc), dev(vc), o2, M, pos0, hq, hkv, cache_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(o2.cpu().numpy().view(np.uint16), out.view(np.uint16))
+
+
 def test_attention_gqa_peaked_scores(dmq):
     """Large score spread (one key dominates, many weights underflow) and a
     run of 3 decode steps appending to the same cache."""
