@@ -249,11 +249,14 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   }
 
   // D: lane l holds activation row l%16 (+16g) and weight rows 4(l/16) .. +3
-  // of the tile.  LDS: red[wave][g][activation row][weight row].
+  // of the tile.  LDS: red[wave][g][activation row m][weight row n], the
+  // four 4-float chunks of row m permuted by chunk ^ red_swz(m) so that the
+  // lanes' 16-byte stores (16 rows, one chunk each) and the 4-byte loads of
+  // 64 consecutive outputs both hit distinct banks.
+  const auto red_swz = [](int m) { return ((m >> 1) ^ (m >> 3)) & 3; };
 #pragma unroll
   for (int g = 0; g < NT; ++g)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[((wave * NT + g) * 16 + rl) * 16 + 4 * p + r] = acc[g][r];
+    ((f4*)red)[((wave * NT + g) * 16 + rl) * 4 + (p ^ red_swz(rl))] = acc[g];
   __syncthreads();
   // output t = (activation row m, weight row n) of the 16 x 16 tile:
   // consecutive t write consecutive n; the waves' sums in wave order.  A
@@ -263,8 +266,9 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
     for (int g = 0; g < NT; ++g) {
       const int ml = t >> 4, nl = t & 15;
       const int m = ml + 16 * g, n = n0 + nl;
-      float v = red[((0 * NT + g) * 16 + ml) * 16 + nl];
-      for (int w = 1; w < nw; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + nl];
+      const int col = ((((nl >> 2) ^ red_swz(ml)) << 2) | (nl & 3));
+      float v = red[((0 * NT + g) * 16 + ml) * 16 + col];
+      for (int w = 1; w < nw; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + col];
       if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
     }
   }
@@ -275,7 +279,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
 // with up to four blocks each in flight (256 registers per lane).
 template <int NT, int D>
 __global__ __launch_bounds__(D == 1 ? 1024 : D == 2 ? 256 : 512) void skinny_kernel(SkinnyArgs args) {
-  extern __shared__ float red[];   // [waves][NT][16][16]
+  extern __shared__ __align__(16) float red[];   // [waves][NT][16][16]
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < SKINNY_MAX_GROUP; ++i)
