@@ -46,7 +46,7 @@ SETTLE_MS = 150.0              # untimed GPU work before any timed region (clock
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": "1305205177e265fb316edb8a106ba9f6e02b8e76551184af473b45adf1d6f132", "bytes_per_launch": 619831867}
+TRAFFIC = {"sources_sha256": "5c2ff78ffa98168ae0fce7bc71c4e93ee8d4d2aa3f17c731d61125cd43a2e4c9", "bytes_per_launch": 621890125}
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -120,6 +120,8 @@ def vendor_gemm_probe(torch):
     e1.record()
     torch.cuda.synchronize()
     out["square_8192_fp16_out_TFLOPs"] = round(2 * 8192 ** 3 / (e0.elapsed_time(e1) / 10) / 1e9, 1)
+    # graphics clock and socket power while the square GEMM runs
+    out["square_8192_clock_power"] = ClockSampler(torch).run_while(lambda: torch.matmul(a, a))
     print(json.dumps({"vendor_gemm_probe": out}), flush=True)
 
 
@@ -539,12 +541,23 @@ def device_record(torch):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock (MHz) with amdsmi from a thread while
-    the caller keeps the GPU busy; median of the samples.  Reports None (and
-    why) where amdsmi is missing or cannot see the device."""
+    """Graphics clock and power while the caller keeps the GPU busy, two ways.
+
+    * Shader clock from the GPU itself: torch.cuda._sleep(n) spins one wave
+      for n cycles of the shader-clock counter (s_memtime); a long spin on a
+      side stream, timed with events while the load runs, gives n / t.
+    * amdsmi's metrics table (per-XCD current graphics clocks, socket power,
+      energy accumulator).  The table is refreshed only now and then, so a
+      sample counts only when its firmware timestamp differs from the one
+      before it; average power is the energy accumulator's growth between the
+      first and the last refresh seen, over the host time between them.
+    Reports None for a part (and why) where it cannot be measured."""
+
+    SPIN = 50_000_000   # cycles: 21-29 ms at 1.7-2.4 GHz
 
     def __init__(self, torch):
-        self.samples, self.error, self.handle = [], None, None
+        self.refreshes, self.error, self.handle = [], None, None
+        self.spin_mhz = None
         try:
             import amdsmi
             self.amdsmi = amdsmi
@@ -563,49 +576,102 @@ class ClockSampler:
             self.error = f"amdsmi unavailable: {type(e).__name__}: {e}"
 
     def _read(self):
-        """Mean of the per-XCD current graphics clocks (MHz)."""
+        """(firmware timestamp, mean per-XCD current graphics clock in MHz,
+        socket power in W or None, energy accumulator or None)."""
         m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
         v = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-        if v:
-            return float(np.mean(v))
-        return float(m["current_gfxclk"])
+        clk = float(np.mean(v)) if v else float(m["current_gfxclk"])
+        pw = m.get("current_socket_power")
+        en = m.get("energy_accumulator")
+        return (m.get("firmware_timestamp"), clk, float(pw) if isinstance(pw, (int, float)) else None,
+                int(en) if isinstance(en, int) else None)
 
-    def run_while(self, busy_fn, seconds=1.0):
-        """Call busy_fn() repeatedly (it enqueues GPU work) for `seconds`,
-        sampling the clock from a second thread; the samples of the first
-        quarter (while the clock may still be ramping) are dropped."""
+    def _spin_clock(self, torch, stream, busy_fn, reps=3):
+        """Shader clock in MHz from a timed clock-counter spin of SPIN cycles
+        on `stream` (median of `reps`).  Before each spin, enough calls of
+        the load are queued to outlast it even at 1 GHz; the spin's start
+        may wait for a workgroup of the load to finish (well under 1% of
+        the spin)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            busy_fn()
+        e1.record()
+        e1.synchronize()
+        per_call_ms = max(e0.elapsed_time(e1) / 20, 1e-3)
+        calls = int(1.5 * (self.SPIN / 1e6) / per_call_ms) + 1
+        est = []
+        for _ in range(reps):
+            for _ in range(calls):
+                busy_fn()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                s0.record()
+                torch.cuda._sleep(self.SPIN)
+                s1.record()
+            torch.cuda.synchronize()
+            est.append(self.SPIN / (s0.elapsed_time(s1) * 1e3))
+        return float(np.median(est))
+
+    def run_while(self, busy_fn, seconds=3.0):
+        """Call busy_fn() repeatedly (it enqueues GPU work) for `seconds`;
+        amdsmi is polled from a second thread, and the spins run on a side
+        stream once a quarter of the time has passed (clock settled)."""
         import threading
-        if self.handle is None:
-            return None
+        import torch
         stop = threading.Event()
+        t0 = time.perf_counter()
 
         def sample():
+            last = None
             while not stop.is_set():
                 try:
-                    v = self._read()
-                    if time.perf_counter() - t0 > seconds / 4:
-                        self.samples.append(v)
+                    ts, clk, pw, en = self._read()
                 except Exception as e:   # noqa: BLE001
                     self.error = f"{type(e).__name__}: {e}"
                     return
-                time.sleep(0.01)
-        t = threading.Thread(target=sample)
-        t0 = time.perf_counter()
-        t.start()
-        import torch
+                now = time.perf_counter()
+                if last is not None and ts != last and now - t0 > seconds / 4:
+                    self.refreshes.append((now, clk, pw, en))
+                last = ts
+                time.sleep(0.005)
+        t = None
+        if self.handle is not None:
+            t = threading.Thread(target=sample)
+            t.start()
+        side = torch.cuda.Stream()
+        spun = False
         while time.perf_counter() - t0 < seconds:
             for _ in range(20):
                 busy_fn()
+            if not spun and time.perf_counter() - t0 > seconds / 4:
+                self.spin_mhz = self._spin_clock(torch, side, busy_fn)
+                spun = True
             torch.cuda.synchronize()
         stop.set()
-        t.join()
+        if t is not None:
+            t.join()
         return self.result()
 
     def result(self):
-        if not self.samples:
-            return {"median_MHz": None, "samples": 0, "error": self.error}
-        return {"median_MHz": round(float(np.median(self.samples)), 1), "min_MHz": round(min(self.samples), 1),
-                "max_MHz": round(max(self.samples), 1), "samples": len(self.samples), "source": "amdsmi"}
+        out = {"spin_MHz": round(self.spin_mhz, 1) if self.spin_mhz else None,
+               "spin_source": "torch.cuda._sleep spin of 5e7 shader-clock cycles on a side stream under the load, event-timed"}
+        r = self.refreshes
+        if not r:
+            out.update({"amdsmi_MHz": None, "amdsmi_refreshes": 0,
+                        "amdsmi_error": self.error or "metrics table not refreshed during the window"})
+            return out
+        clk = [c for _, c, _, _ in r]
+        pw = [p for _, _, p, _ in r if p is not None]
+        out.update({"amdsmi_MHz": round(float(np.median(clk)), 1), "amdsmi_min_MHz": round(min(clk), 1),
+                    "amdsmi_max_MHz": round(max(clk), 1),
+                    "socket_power_W": round(float(np.median(pw)), 1) if pw else None,
+                    "amdsmi_refreshes": len(r)})
+        en = [(tt, e) for tt, _, _, e in r if e is not None]
+        if len(en) >= 2 and en[-1][0] > en[0][0]:
+            res_uj = self.amdsmi.amdsmi_get_energy_count(self.handle)["counter_resolution"]
+            out["energy_avg_power_W"] = round((en[-1][1] - en[0][1]) * res_uj * 1e-6 / (en[-1][0] - en[0][0]), 1)
+        return out
 
 
 def time_launches(torch, launch, groups, steps, warmup):
@@ -803,7 +869,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": (TRAFFIC["bytes_per_launch"] if TRAFFIC["sources_sha256"] == sources_sha256() else None),
-                     "kernel": "dmq::gemm_kernel<3,8,2,false> (grouped Q4_K/Q6_K prefill launch) + "
+                     "kernel": "dmq::gemm_kernel<3,8,2,false,8> (grouped Q4_K/Q6_K prefill launch) + "
                                "dmq::splitk_reduce_kernel (piece-order sum of the split down projection)",
                      "launch_ms": round(kern_ms, 4)},
         # per-step times (events around each of the K timed steps): the pages'
@@ -814,7 +880,8 @@ def main():
                   "activations": "weight seed + 500000000", "config": 2, "layers": list(range(ROTATE_LAYERS)),
                   "generator": "numpy PCG64"},
     }
-    # achieved graphics clock, sampled while the same step runs again (untimed)
+    # achieved graphics clock and socket power, sampled while the same step
+    # runs again (untimed)
     it = [0]
 
     def again():

@@ -6,8 +6,10 @@
 // the fused dequant never writes fp16 weights to memory (overview page, same
 // section, and compartment 09 of "[02] the pipeline").
 //
-// One workgroup = 4 waves = one BM x BN output tile, BM = 32*JB activation
-// rows, BN = 4 * 32*IB weight rows.
+// One workgroup = NW waves = one BM x BN output tile, BM = 32*JB activation
+// rows, BN = NW * 32*IB = 256 weight rows: 4 waves of two 32-row i-blocks, or
+// (tiles of at least 64 activation rows, no SwiGLU) 8 waves of one, two per
+// SIMD, so that one wave's dequantisation runs beside the other's MFMAs.
 //  * Each wave owns 32*IB weight rows and all BM activation rows.  It decodes
 //    its raw blocks straight into MFMA A-operand registers: every weight is
 //    dequantised once per workgroup and no dequantised tile touches LDS or
