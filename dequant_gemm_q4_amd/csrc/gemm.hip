@@ -333,6 +333,10 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   const uint32_t roff = (uint32_t)(li * row_bytes) + (FMT == 0 ? 16u * (uint32_t)g : 0u);
   // table thread tt decodes local row tt = 32*IB*w + 32*c + i (clamped to a valid row)
   const bool tab_thread = tid < C::BN;
+  // the same test per wave (BN is a multiple of 64): a scalar branch, so
+  // waves without table rows skip the decode instead of issuing it masked
+  static_assert(C::BN % 64 == 0 && 64 * NW >= C::BN, "table rows fill whole waves");
+  const bool tab_wave = wave < C::BN / 64;
   const int tt = tab_thread ? tid : 0;
   int trow_i = iblock_row0<IB, SWIGLU>(tt / (32 * IB), (tt / 32) % IB, n0, hb, F) + (tt & 31);
   trow_i = trow_i < N ? trow_i : N - 1;
@@ -362,6 +366,23 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   uint32_t boff[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) boff[s] = (uint32_t)(li * 128 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ ((li >> 1) & 7)));
+  // The same offsets plus 64 KiB, opaque to the compiler: buffers x2 and x3
+  // lie above 64 KiB of LDS, beyond a ds_read's 16-bit immediate offset, and
+  // from boff the compiler re-forms their addresses with one v_or per read.
+  // Addressed as x2/x3 + (boffh - 64 KiB), they take these registers plus an
+  // immediate offset, and the pointer still derives from the buffer (the
+  // compiler's LDS-DMA alias tracking sees which buffer a read touches).
+  uint32_t boffh[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    boffh[s] = boff[s] + 65536u;
+    asm volatile("" : "+v"(boffh[s]));
+  }
+  // B fragment of K step s, j-block jb, from x buffer j
+  auto bread = [&](int j, int s, int jb) -> h8 {
+    const uint8_t* const p = j >= 2 ? xb[j] + (boffh[s] - 65536u) : xb[j] + boff[s];
+    return *(const h8*)(p + jb * 32 * 128);
+  };
 
   f16x acc[JB][IB];
 #pragma unroll
@@ -504,7 +525,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
 #pragma unroll
   for (int c = 0; c < IB; ++c) af[c] = frag(rs[0][c], 0, 0, sv[c]);
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) bf[jb] = *(const h8*)(x0 + boff[0] + jb * 32 * 128);
+  for (int jb = 0; jb < JB; ++jb) bf[jb] = bread(0, 0, jb);
 
   for (int b = 0; b < nb; ++b) {
     const bool more = b + 1 < nb;
@@ -517,9 +538,6 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ck = 4 * b + j;
-      const uint8_t* const xc = xb[j];
-      const uint8_t* const xn = xb[(j + 1) & 3];
-      const bool pf1 = j < 3 || more;     // chunk ck + 1 exists
       const int cur = FMT == 0 ? j : (j >> 1);                    // raw set of chunk ck
       const int nxt = FMT == 0 ? ((j + 1) & 3) : (((j + 1) & 3) >> 1);
       // x (and raw bytes) of chunk ck+3 go into the buffers chunk ck-1 used
@@ -533,7 +551,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
-          if (j == 3 && s == 0 && more && tab_thread)
+          if (j == 3 && s == 0 && more && tab_wave)
             tab_store<FMT>(my_tab, hdr, hdr4);
           const int nv = issue_loads(j, s, ck3, b, bnext);
 #pragma unroll
@@ -541,7 +559,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
 #pragma unroll
             for (int c = 0; c < IB; ++c)
               acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[jb], af[c], acc[jb][c], 0, 0, 0);
-            bf[jb] = *(const h8*)(xc + boff[s + 1] + jb * 32 * 128);
+            bf[jb] = bread(j, s + 1, jb);
           }
           interleave_rd(nv, j == 3 && s == 0 ? 6 : 3);
           __builtin_amdgcn_sched_barrier(0);
@@ -558,31 +576,25 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         }
         h8 afn[IB];
         float svn[IB][4];
-        if (pf1) {
-          if (j == 3) read_scales();
-          chunk_scales((j + 1) & 3, svn);
-        }
+        if (j == 3) read_scales();
+        chunk_scales((j + 1) & 3, svn);
         __builtin_amdgcn_sched_barrier(0);
-        if (pf1) {
 #pragma unroll
-          for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
-        }
+        for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
           for (int c = 0; c < IB; ++c)
             acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[jb], af[c], acc[jb][c], 0, 0, 0);
-          if (pf1) bf[jb] = *(const h8*)(xn + boff[0] + jb * 32 * 128);
+          bf[jb] = bread((j + 1) & 3, 0, jb);
         }
         interleave_rd(0, 3);
         __builtin_amdgcn_sched_barrier(0);
-        if (pf1) {
 #pragma unroll
-          for (int c = 0; c < IB; ++c) {
-            af[c] = afn[c];
+        for (int c = 0; c < IB; ++c) {
+          af[c] = afn[c];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
-          }
+          for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
         }
         continue;
       }
@@ -592,11 +604,11 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       for (int s = 0; s < 3; ++s) {
         h8 afn[IB], bfn[JB];
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(xc + boff[s + 1] + jb * 32 * 128);
+        for (int jb = 0; jb < JB; ++jb) bfn[jb] = bread(j, s + 1, jb);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
-        if (j == 3 && s == 0 && more && tab_thread)
+        if (j == 3 && s == 0 && more && tab_wave)
           tab_store<FMT>(my_tab, hdr, hdr4);
         const int nv = issue_loads(j, s, ck3, b, bnext);
         mfma_step(af, bf);
@@ -612,7 +624,11 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
 
       // K step 3: wait for chunk ck+1's x and raw bytes and, at a block
       // boundary, the new table; the loads of later chunks stay in flight
-      // (counts: VMEM instructions issued after the last one needed here)
+      // (counts: VMEM instructions issued after the last one needed here).
+      // After the tile's last chunk there is no chunk ck+1: its fragments
+      // are still read and decoded (from LDS and registers the tile owns,
+      // results unused), so no step carries a branch that would keep the
+      // scheduler from interleaving the decode with the MFMAs.
       if constexpr (FMT == 0) {
         wait_vm_barrier<2 * (XQ + NRAW)>();
       } else {
@@ -621,30 +637,24 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       }
       h8 afn[IB], bfn[JB];
       float svn[IB][4];
-      if (pf1) {
-        if (j == 3) read_scales();
-        chunk_scales((j + 1) & 3, svn);
+      if (j == 3) read_scales();
+      chunk_scales((j + 1) & 3, svn);
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bfn[jb] = *(const h8*)(xn + boff[0] + jb * 32 * 128);
-      }
+      for (int jb = 0; jb < JB; ++jb) bfn[jb] = bread((j + 1) & 3, 0, jb);
       __builtin_amdgcn_sched_barrier(0);
-      if (pf1) {
 #pragma unroll
-        for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
-      }
+      for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
       mfma_step(af, bf);
       interleave(0, 3);
       __builtin_amdgcn_sched_barrier(0);
-      if (pf1) {
 #pragma unroll
-        for (int c = 0; c < IB; ++c) {
-          af[c] = afn[c];
+      for (int c = 0; c < IB; ++c) {
+        af[c] = afn[c];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
-        }
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
+        for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
       }
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
     }
   }
   // no direct-to-LDS load may still be in flight when the workgroup ends
