@@ -431,3 +431,52 @@ int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, floa
 }
 
 }  // extern "C"
+
+namespace dmq {
+// The requirements of every single call dmq_layer_prefill makes, checked for
+// all M rows at once (each chunk's arguments are row ranges of these), and no
+// written buffer overlapping another buffer, cache or weight array: run
+// before the layer records an event or enqueues a kernel.
+int check_layer(const dmq_layer_weights* w, const dmq_layer_buffers* b, int64_t M, int64_t pos0, int32_t D,
+                int32_t F, int32_t hq, int32_t hkv, int64_t cache_len, double theta, float eps) {
+  if (!w || !b) return DMQ_ERR_INVALID_ARG;
+  if (!heads_ok(hq, hkv) || (int64_t)hq * 128 % 256 || !cache_ok(M, pos0, hkv, cache_len)) return DMQ_ERR_INVALID_ARG;
+  if (!(theta > 1.0) || theta > 1e30 || !(eps >= 0.0f) || eps > 3.0e38f) return DMQ_ERR_INVALID_ARG;
+  if (!dim_ok(D) || !dim_ok(F)) return DMQ_ERR_INVALID_ARG;
+  const int64_t QD = (int64_t)hq * 128, KD = (int64_t)hkv * 128;
+  int st;
+  if ((st = check_gemm(w->fmt_q, b->xn_in, w->wq, b->yq, M, QD, D)) != DMQ_OK) return st;
+  if ((st = check_gemm(w->fmt_k, b->xn_in, w->wk, b->yk, M, KD, D)) != DMQ_OK) return st;
+  if ((st = check_gemm(w->fmt_v, b->xn_in, w->wv, b->yv, M, KD, D)) != DMQ_OK) return st;
+  if ((st = check_gemm(w->fmt_o, b->attn, w->wo, b->yo, M, D, QD)) != DMQ_OK) return st;
+  if ((st = check_gemm(DMQ_FMT_Q4K, b->xn_ffn, w->w_gate_up, b->h_ffn, M, 2 * (int64_t)F, D)) != DMQ_OK) return st;
+  if ((st = check_gemm(DMQ_FMT_Q6K, b->h_ffn, w->w_down, b->y_down, M, D, F)) != DMQ_OK) return st;
+  if (!b->h_in || !b->q_rot || !b->h_mid || !b->h_out || !w->g_ffn || !w->k_cache || !w->v_cache)
+    return DMQ_ERR_INVALID_ARG;
+  if (w->g_next && !b->xn_out) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(w->g_ffn, 16) || (w->g_next && !aligned(w->g_next, 16)) || !aligned(w->k_cache, 16) ||
+      !aligned(w->v_cache, 16) || (w->freq_factors && !aligned(w->freq_factors, 4)))
+    return DMQ_ERR_ALIGNMENT;
+  auto wbytes = [](int fmt, int64_t n, int64_t k) { return n * (k / 256) * (fmt == DMQ_FMT_Q4K ? 144 : 210); };
+  const int64_t cache_bytes = (int64_t)hkv * cache_len * 128 * 2;
+  const Range written[] = {{b->yq, M * QD * 4}, {b->yk, M * KD * 4}, {b->yv, M * KD * 4},
+                           {b->q_rot, M * QD * 2}, {b->attn, M * QD * 2}, {b->yo, M * D * 4},
+                           {b->h_mid, M * D * 4}, {b->xn_ffn, M * D * 2}, {b->h_ffn, M * (int64_t)F * 2},
+                           {b->y_down, M * D * 4}, {b->h_out, M * D * 4}, {w->g_next ? b->xn_out : nullptr, M * D * 2},
+                           {w->k_cache, cache_bytes}, {w->v_cache, cache_bytes}};
+  const Range read[] = {{b->h_in, M * D * 4}, {b->xn_in, M * D * 2},
+                        {w->wq, wbytes(w->fmt_q, QD, D)}, {w->wk, wbytes(w->fmt_k, KD, D)},
+                        {w->wv, wbytes(w->fmt_v, KD, D)}, {w->wo, wbytes(w->fmt_o, D, QD)},
+                        {w->w_gate_up, wbytes(DMQ_FMT_Q4K, 2 * (int64_t)F, D)}, {w->w_down, wbytes(DMQ_FMT_Q6K, D, F)},
+                        {w->g_ffn, (int64_t)D * 4}, {w->g_next, (int64_t)D * 4}, {w->freq_factors, 64 * 4}};
+  const int nw = (int)(sizeof(written) / sizeof(written[0])), nr = (int)(sizeof(read) / sizeof(read[0]));
+  for (int i = 0; i < nw; ++i) {
+    if (!written[i].p) continue;
+    for (int j = i + 1; j < nw; ++j)
+      if (written[j].p && overlap(written[i].p, written[i].n, written[j].p, written[j].n)) return DMQ_ERR_INVALID_ARG;
+    for (int j = 0; j < nr; ++j)
+      if (read[j].p && overlap(written[i].p, written[i].n, read[j].p, read[j].n)) return DMQ_ERR_INVALID_ARG;
+  }
+  return DMQ_OK;
+}
+}  // namespace dmq

@@ -16,6 +16,7 @@
 // With one stream for both sides the same kernels run in the same order per
 // stream, which gives the same bits.
 #include "../../include/dmq.h"
+#include "layer.h"
 
 #include <hip/hip_runtime.h>
 
@@ -77,6 +78,9 @@ extern "C" int dmq_layer_prefill(const dmq_layer_weights* w, const dmq_layer_buf
   const bool two = sa != sf;
   const int64_t nchunks = (M + chunk - 1) / chunk;
   if (nchunks > 4096) return DMQ_ERR_INVALID_ARG;
+  // everything the single calls below would reject, before any is made
+  const int chk = dmq::check_layer(w, b, M, pos0, D, F, n_q_heads, n_kv_heads, cache_len, theta, eps);
+  if (chk != DMQ_OK) return chk;
   std::lock_guard<std::mutex> lock(g_ev_mu);
   std::vector<hipEvent_t> ev;
   if (two) {

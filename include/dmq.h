@@ -353,10 +353,13 @@ int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, floa
  *       n_kv_heads*128]), q_rot, attn (fp16 [M, n_q_heads*128]), yo, y_down
  *       (fp32 [M, D]), xn_ffn (fp16 [M, D]), h_ffn (fp16 [M, F]).
  * Requirements: D, F and n_q_heads*128 multiples of 256, chunk >= 1, at most
- * 4096 chunks, and those of the single calls.  The library keeps a pool of
- * HIP events per device (created on first use, kept until the process ends);
- * calls from several host threads are serialised on it.  A failing step
- * returns its status; steps before it stay enqueued.
+ * 4096 chunks, those of the single calls (checked for all M rows), and no
+ * written buffer or cache overlapping another buffer, cache, weight array or
+ * norm vector.  They are checked on the host before any event is recorded or
+ * kernel enqueued: a rejected call enqueues nothing.  The library keeps a
+ * pool of HIP events per device (created on first use, kept until the process
+ * ends); calls from several host threads are serialised on it.  A HIP error
+ * in a later step returns its status with the steps before it enqueued.
  */
 typedef struct {
   int32_t fmt_q, fmt_k, fmt_v, fmt_o;

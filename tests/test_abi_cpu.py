@@ -62,8 +62,8 @@ def test_layer_prefill_validation():
         setattr(b, n, A16 + 0x1000000 * (i + 1))
     args = lambda **k: dict(dict(M=8, pos0=0, D=768, F=1024, hq=6, hkv=2, L=64, chunk=4), **k)  # noqa: E731
 
-    def call(wp, bp, a):
-        return f(wp, bp, a["M"], a["pos0"], a["D"], a["F"], a["hq"], a["hkv"], a["L"], 500000.0, 1e-5, a["chunk"],
+    def call(wp, bp, a, theta=500000.0):
+        return f(wp, bp, a["M"], a["pos0"], a["D"], a["F"], a["hq"], a["hkv"], a["L"], theta, 1e-5, a["chunk"],
                  None, None)
     assert call(None, ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
     assert call(ctypes.byref(w), None, args()) == dmq.DMQ_ERR_INVALID_ARG
@@ -83,6 +83,29 @@ def test_layer_prefill_validation():
     w.g_next = A16 + 0x30000000
     b.xn_out = None                                          # g_next without xn_out
     assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    b.xn_out = A16 + 0x40000000
+    # the single calls' requirements, checked before anything is enqueued
+    assert call(ctypes.byref(w), ctypes.byref(b), args(hkv=4)) == dmq.DMQ_ERR_INVALID_ARG   # 6 % 4 heads
+    assert call(ctypes.byref(w), ctypes.byref(b), args(pos0=60)) == dmq.DMQ_ERR_INVALID_ARG  # past the cache
+    assert call(ctypes.byref(w), ctypes.byref(b), args(), theta=1.0) == dmq.DMQ_ERR_INVALID_ARG
+    w.k_cache = A16 + 0x800008
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_ALIGNMENT
+    w.k_cache = A16 + 0x800000
+    # written buffers overlapping each other, a cache or a weight array
+    yk = b.yk
+    b.yk = b.yq
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    b.yk = yk
+    yo = b.yo
+    b.yo = w.wq
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    b.yo = w.v_cache
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    b.yo = yo
+    h_out = b.h_out
+    b.h_out = b.h_in
+    assert call(ctypes.byref(w), ctypes.byref(b), args()) == dmq.DMQ_ERR_INVALID_ARG
+    b.h_out = h_out
 
 
 def test_version_and_status_strings():
