@@ -28,6 +28,33 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 bool dim_ok(int64_t v) { return v >= 1 && v <= kMaxDim; }
 
+// [p, p + pn) and [q, q + qn) share a byte
+bool overlap(const void* p, int64_t pn, const void* q, int64_t qn) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qn && b < a + (uintptr_t)pn;
+}
+
+// A byte range a launch reads or writes (NULL: none).
+struct Range {
+  const void* p;
+  int64_t n;
+};
+
+// True when one of the written ranges shares a byte with another written
+// range or with a range the same launches read: kernels would race on it.
+bool races(const Range* out, int nout, const Range* in, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    if (!out[i].p) continue;
+    for (int j = i + 1; j < nout; ++j)
+      if (out[j].p && overlap(out[i].p, out[i].n, out[j].p, out[j].n)) return true;
+    for (int j = 0; j < nin; ++j)
+      if (in[j].p && overlap(out[i].p, out[i].n, in[j].p, in[j].n)) return true;
+  }
+  return false;
+}
+
+int64_t weight_bytes(int fmt, int64_t n, int64_t k) { return n * (k / 256) * (fmt == DMQ_FMT_Q4K ? 144 : 210); }
+
 int check_quant_k(int64_t k) { return (dim_ok(k) && k % 256 == 0) ? DMQ_OK : DMQ_ERR_INVALID_ARG; }
 
 int check_weights(int fmt, const void* wq) {
@@ -123,6 +150,8 @@ dmq::GemmProblem make_problem(int fmt, const void* x, const void* wq, void* out,
 int gemm_one(int fmt, const void* x, const void* wq, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
   int st = check_gemm(fmt, x, wq, y, M, N, K);
   if (st != DMQ_OK) return st;
+  const Range out[1] = {{y, M * N * 4}}, in[2] = {{x, M * K * 2}, {wq, weight_bytes(fmt, N, K)}};
+  if (races(out, 1, in, 2)) return DMQ_ERR_INVALID_ARG;
   dmq::GemmProblem p = make_problem(fmt, x, wq, y, M, N, K, 0);
   bool decode = (M == 1 && K <= kGemvMaxK);
   return run_gemm(&p, 1, decode, (hipStream_t)stream);
@@ -162,6 +191,7 @@ int dmq_dequant_q4k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* 
   if (w != DMQ_OK) return w;
   if (!weight_bytes_ok(DMQ_FMT_Q4K, rows, k)) return DMQ_ERR_INVALID_ARG;
   if (!aligned(w_f16, 16)) return DMQ_ERR_ALIGNMENT;
+  if (overlap(w_f16, rows * k * 2, wq, weight_bytes(DMQ_FMT_Q4K, rows, k))) return DMQ_ERR_INVALID_ARG;
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   return hip_status(dmq::launch_dequant_q4k(wq, w_f16, rows, k, (hipStream_t)stream));
@@ -173,6 +203,7 @@ int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* 
   if (w != DMQ_OK) return w;
   if (!weight_bytes_ok(DMQ_FMT_Q6K, rows, k)) return DMQ_ERR_INVALID_ARG;
   if (!aligned(w_f16, 16)) return DMQ_ERR_ALIGNMENT;
+  if (overlap(w_f16, rows * k * 2, wq, weight_bytes(DMQ_FMT_Q6K, rows, k))) return DMQ_ERR_INVALID_ARG;
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   return hip_status(dmq::launch_dequant_q6k(wq, w_f16, rows, k, (hipStream_t)stream));
@@ -193,6 +224,10 @@ int dmq_ffn_swiglu_q4k(const void* x_f16, const void* w_gate_up_q4k, const void*
   if (st != DMQ_OK) return st;
   st = check_gemm(DMQ_FMT_Q6K, h_f16, w_down_q6k, y, M, D, F);
   if (st != DMQ_OK) return st;
+  const Range out[2] = {{h_f16, M * F * 2}, {y, M * D * 4}};
+  const Range in[3] = {{x_f16, M * D * 2}, {w_gate_up_q4k, weight_bytes(DMQ_FMT_Q4K, 2 * F, D)},
+                       {w_down_q6k, weight_bytes(DMQ_FMT_Q6K, D, F)}};
+  if (races(out, 2, in, 3)) return DMQ_ERR_INVALID_ARG;
   bool decode = (M == 1 && D <= kGemvMaxK && F <= kGemvMaxK);
   dmq::GemmProblem up = make_problem(DMQ_FMT_Q4K, x_f16, w_gate_up_q4k, h_f16, M, 2 * F, D, 1);
   st = run_gemm(&up, 1, decode, (hipStream_t)stream);
@@ -214,6 +249,16 @@ int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream) {
     probs[i] = make_problem(d.format, d.x_f16, d.wq, d.y, d.M, d.N, d.K, 0);
   }
   if (n_decode != 0 && n_decode != count) return DMQ_ERR_INVALID_ARG;   // one kernel kind per call
+  {
+    Range out[kMaxGroup], in[2 * kMaxGroup];
+    for (int i = 0; i < count; ++i) {
+      const dmq_gemm_desc& d = descs[i];
+      out[i] = Range{d.y, d.M * d.N * 4};
+      in[2 * i] = Range{d.x_f16, d.M * d.K * 2};
+      in[2 * i + 1] = Range{d.wq, weight_bytes(d.format, d.N, d.K)};
+    }
+    if (races(out, count, in, 2 * count)) return DMQ_ERR_INVALID_ARG;
+  }
   // Longest reduction first: tiles of the deepest K are dispatched first so
   // they do not trail at the end of the launch.
   std::stable_sort(probs, probs + count,
@@ -222,19 +267,6 @@ int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream) {
 }
 
 namespace {
-
-// [p, p + pn) and [q, q + qn) share a byte
-bool overlap(const void* p, int64_t pn, const void* q, int64_t qn) {
-  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
-  return a < b + (uintptr_t)qn && b < a + (uintptr_t)pn;
-}
-
-// A byte range the launch reads (or another output writes) while the
-// projections' outputs are being written.
-struct Range {
-  const void* p;
-  int64_t n;
-};
 
 // The projections of dmq_rmsnorm_gemm / dmq_residual_rmsnorm_gemm as problems
 // with activations x; with DMQ_PROJ_SWIGLU a Q4_K gate|up pair (N/2 a
@@ -457,7 +489,7 @@ int check_layer(const dmq_layer_weights* w, const dmq_layer_buffers* b, int64_t 
   if (!aligned(w->g_ffn, 16) || (w->g_next && !aligned(w->g_next, 16)) || !aligned(w->k_cache, 16) ||
       !aligned(w->v_cache, 16) || (w->freq_factors && !aligned(w->freq_factors, 4)))
     return DMQ_ERR_ALIGNMENT;
-  auto wbytes = [](int fmt, int64_t n, int64_t k) { return n * (k / 256) * (fmt == DMQ_FMT_Q4K ? 144 : 210); };
+  auto wbytes = weight_bytes;
   const int64_t cache_bytes = (int64_t)hkv * cache_len * 128 * 2;
   const Range written[] = {{b->yq, M * QD * 4}, {b->yk, M * KD * 4}, {b->yv, M * KD * 4},
                            {b->q_rot, M * QD * 2}, {b->attn, M * QD * 2}, {b->yo, M * D * 4},
@@ -470,13 +502,6 @@ int check_layer(const dmq_layer_weights* w, const dmq_layer_buffers* b, int64_t 
                         {w->w_gate_up, wbytes(DMQ_FMT_Q4K, 2 * (int64_t)F, D)}, {w->w_down, wbytes(DMQ_FMT_Q6K, D, F)},
                         {w->g_ffn, (int64_t)D * 4}, {w->g_next, (int64_t)D * 4}, {w->freq_factors, 64 * 4}};
   const int nw = (int)(sizeof(written) / sizeof(written[0])), nr = (int)(sizeof(read) / sizeof(read[0]));
-  for (int i = 0; i < nw; ++i) {
-    if (!written[i].p) continue;
-    for (int j = i + 1; j < nw; ++j)
-      if (written[j].p && overlap(written[i].p, written[i].n, written[j].p, written[j].n)) return DMQ_ERR_INVALID_ARG;
-    for (int j = 0; j < nr; ++j)
-      if (read[j].p && overlap(written[i].p, written[i].n, read[j].p, read[j].n)) return DMQ_ERR_INVALID_ARG;
-  }
-  return DMQ_OK;
+  return races(written, nw, read, nr) ? DMQ_ERR_INVALID_ARG : DMQ_OK;
 }
 }  // namespace dmq

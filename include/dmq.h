@@ -50,7 +50,10 @@
  *    K (and D, F) a multiple of 256 and, for the GEMM calls, at most 2^20,
  *    x / y / h / w_f16 16-byte aligned, Q4_K weights 16-byte aligned, Q6_K
  *    weights 2-byte aligned.
- *  - Output buffers must not overlap inputs.
+ *  - An output may not share a byte with an input of the same call or with
+ *    another output (workgroups would write it while others still read it):
+ *    such calls are rejected with DMQ_ERR_INVALID_ARG.  Inputs may share
+ *    memory (several projections of one x, one weight array twice).
  */
 #ifndef DMQ_H
 #define DMQ_H

@@ -118,6 +118,14 @@ def test_version_and_status_strings():
 L = dmq.lib
 
 
+def _no_gpu():
+    """True when no HIP device is visible (counting devices does not
+    initialise one).  Only then may a test make a call whose arguments pass
+    the host checks: with a device it would launch on these fake pointers."""
+    import torch
+    return torch.cuda.device_count() == 0
+
+
 @pytest.mark.parametrize("fn", ["dmq_gemm_q4k", "dmq_gemm_q6k"])
 def test_gemm_validation(fn):
     f = getattr(L, fn)
@@ -292,7 +300,8 @@ def test_projection_outputs_must_not_overlap_inputs_or_each_other():
         assert rms(_proj(y=y)) == dmq.DMQ_ERR_INVALID_ARG, hex(y)
     assert rms(_proj(y=Y0), _proj(y=Y0 + 0x30)) == dmq.DMQ_ERR_INVALID_ARG           # outputs overlap
     assert rms(_proj(y=Y0), _proj(N=512, flags=1, y=Y0 - 0x7f0)) == dmq.DMQ_ERR_INVALID_ARG  # into h's 2 KiB
-    assert rms(_proj(y=Y0), _proj(y=Y1)) != dmq.DMQ_ERR_INVALID_ARG                  # disjoint: passes the checks
+    if _no_gpu():   # disjoint: passes the host checks (and then finds no device)
+        assert rms(_proj(y=Y0), _proj(y=Y1)) == dmq.DMQ_ERR_UNSUPPORTED
 
     H, Yad, HO = A16 + 0x3000, A16 + 0x4000, A16 + 0x5000
 
@@ -303,7 +312,8 @@ def test_projection_outputs_must_not_overlap_inputs_or_each_other():
         assert res(_proj(y=y)) == dmq.DMQ_ERR_INVALID_ARG, hex(y)
     assert res(_proj(y=Yad + 0x10), xn=None, M=1) == dmq.DMQ_ERR_INVALID_ARG          # the decode path too
     assert res(_proj(y=Y0), _proj(y=Y0)) == dmq.DMQ_ERR_INVALID_ARG
-    assert res(_proj(y=Y0), _proj(y=Y1)) != dmq.DMQ_ERR_INVALID_ARG
+    if _no_gpu():
+        assert res(_proj(y=Y0), _proj(y=Y1)) == dmq.DMQ_ERR_UNSUPPORTED
 
 
 def test_rope_kv_cache_validation():
@@ -357,3 +367,45 @@ def test_residual_rmsnorm_validation():
     # another argument's error, so no call ever reaches the device
     assert f(H, Y, None, float("nan"), HO, None, 2, 300, None) == dmq.DMQ_ERR_INVALID_ARG
     assert f(MIS, Y, None, float("nan"), HO, None, 2, 256, None) == dmq.DMQ_ERR_ALIGNMENT
+
+
+def test_outputs_overlapping_inputs_are_rejected():
+    """The GEMM, grouped GEMM, FFN and dequant calls reject an output that
+    shares a byte with an input of the same launch or with another output
+    (some workgroups would write it while others still read it).  M = 4,
+    N = 4, K = 256: x is 2 KiB, y 64 bytes, a Q4_K weight array 4 blocks of
+    144 bytes, a Q6_K one 4 blocks of 210 bytes."""
+    X, W, Y = A16, A16 + 0x1000, A16 + 0x2000
+    g = L.dmq_gemm_q4k
+    for y in (X, X + 0x7f0, W, W + 0x230):
+        assert g(X, W, y, 4, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG, hex(y)
+    assert L.dmq_gemm_q6k(X, W, W + 0x340, 4, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG   # Q6_K: 840 bytes
+    if _no_gpu():
+        assert g(X, W, Y, 4, 4, 256, None) == dmq.DMQ_ERR_UNSUPPORTED
+        assert L.dmq_gemm_q6k(X, W, W + 0x350, 4, 4, 256, None) == dmq.DMQ_ERR_UNSUPPORTED
+
+    def group(*ps):
+        arr = (dmq.GemmDesc * len(ps))()
+        for i, (x, w, y) in enumerate(ps):
+            arr[i].format, arr[i].x_f16, arr[i].wq, arr[i].y = 0, x, w, y
+            arr[i].M, arr[i].N, arr[i].K = 4, 4, 256
+        return L.dmq_gemm_group(arr, len(ps), None)
+    assert group((X, W, Y), (X, W, Y + 0x30)) == dmq.DMQ_ERR_INVALID_ARG     # two outputs share bytes
+    assert group((X, W, Y), (Y, W, Y + 0x100)) == dmq.DMQ_ERR_INVALID_ARG    # one's output is another's x
+    assert group((X, W, Y), (X, Y - 0x10, Y + 0x100)) == dmq.DMQ_ERR_INVALID_ARG   # ... or its weights
+    if _no_gpu():
+        assert group((X, W, Y), (X, W, Y + 0x40)) == dmq.DMQ_ERR_UNSUPPORTED   # shared inputs are fine
+
+    # FFN, M = 4, D = 256, F = 256: h is 2 KiB of fp16, y 4 KiB of fp32
+    WGU, WD, H, YF = A16 + 0x10000, A16 + 0x20000, A16 + 0x30000, A16 + 0x40000
+    ffn = lambda x=X, h=H, y=YF: L.dmq_ffn_swiglu_q4k(x, WGU, WD, h, y, 4, 256, 256, None)  # noqa: E731
+    assert ffn(h=X + 0x10) == dmq.DMQ_ERR_INVALID_ARG
+    assert ffn(y=H + 0x7f0) == dmq.DMQ_ERR_INVALID_ARG
+    assert ffn(y=WD) == dmq.DMQ_ERR_INVALID_ARG
+    assert ffn(h=WGU + 0x400) == dmq.DMQ_ERR_INVALID_ARG
+    if _no_gpu():
+        assert ffn() == dmq.DMQ_ERR_UNSUPPORTED
+
+    # dequant: 4 rows of 256 weights, 2 KiB of fp16 out
+    assert L.dmq_dequant_q4k(W, W + 0x200, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+    assert L.dmq_dequant_q6k(W, W - 0x7f0, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
