@@ -400,6 +400,14 @@ static bool cache_ok(int64_t M, int64_t pos0, int32_t hkv, int64_t cache_len) {
          (int64_t)hkv * cache_len * 128 <= (int64_t(1) << 40) && M * 1024 * 128 <= (int64_t(1) << 40);
 }
 
+// The attention output sharing a byte with the queries or the caches it reads.
+static bool attention_races(const void* q, const void* kc, const void* vc, const void* out, int64_t M, int32_t hq,
+                            int32_t hkv, int64_t cache_len) {
+  const int64_t qd = (int64_t)hq * 128, cb = (int64_t)hkv * 128 * cache_len * 2;
+  const Range o[1] = {{out, M * qd * 2}}, in[3] = {{q, M * qd * 2}, {kc, cb}, {vc, cb}};
+  return races(o, 1, in, 3);
+}
+
 int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M, int64_t pos0, int32_t n_q_heads,
                       int32_t n_kv_heads, double theta, const float* freq_factors, void* q_f16, void* k_cache_f16,
                       void* v_cache_f16, int64_t cache_len, void* stream) {
@@ -409,6 +417,12 @@ int dmq_rope_kv_cache(const float* q, const float* k, const float* v, int64_t M,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_f16, 16) || !aligned(k_cache_f16, 16) ||
       !aligned(v_cache_f16, 16) || (freq_factors && !aligned(freq_factors, 4)))
     return DMQ_ERR_ALIGNMENT;
+  {
+    const int64_t qd = (int64_t)n_q_heads * 128, kd = (int64_t)n_kv_heads * 128, cb = kd * cache_len * 2;
+    const Range out[3] = {{q_f16, M * qd * 2}, {k_cache_f16, cb}, {v_cache_f16, cb}};
+    const Range in[4] = {{q, M * qd * 4}, {k, M * kd * 4}, {v, M * kd * 4}, {freq_factors, 64 * 4}};
+    if (races(out, 3, in, 4)) return DMQ_ERR_INVALID_ARG;
+  }
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   return hip_status(dmq::launch_rope_kv(q, k, v, freq_factors, q_f16, k_cache_f16, v_cache_f16, theta, cache_len, M,
@@ -421,6 +435,8 @@ int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_
   if (!heads_ok(n_q_heads, n_kv_heads) || !cache_ok(M, pos0, n_kv_heads, cache_len)) return DMQ_ERR_INVALID_ARG;
   if (!aligned(q_f16, 16) || !aligned(k_cache_f16, 16) || !aligned(v_cache_f16, 16) || !aligned(out_f16, 16))
     return DMQ_ERR_ALIGNMENT;
+  if (attention_races(q_f16, k_cache_f16, v_cache_f16, out_f16, M, n_q_heads, n_kv_heads, cache_len))
+    return DMQ_ERR_INVALID_ARG;
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   return hip_status(dmq::launch_attention(q_f16, k_cache_f16, v_cache_f16, out_f16, cache_len, M, pos0, n_q_heads,
@@ -434,6 +450,8 @@ int dmq_attention_gqa_noalloc(const void* q_f16, const void* k_cache_f16, const 
   if (!heads_ok(n_q_heads, n_kv_heads) || !cache_ok(M, pos0, n_kv_heads, cache_len)) return DMQ_ERR_INVALID_ARG;
   if (!aligned(q_f16, 16) || !aligned(k_cache_f16, 16) || !aligned(v_cache_f16, 16) || !aligned(out_f16, 16))
     return DMQ_ERR_ALIGNMENT;
+  if (attention_races(q_f16, k_cache_f16, v_cache_f16, out_f16, M, n_q_heads, n_kv_heads, cache_len))
+    return DMQ_ERR_INVALID_ARG;
   const size_t need = dmq::attention_scratch_bytes(M, pos0, n_q_heads);
   if (need > DMQ_NOALLOC_SCRATCH_BYTES) return DMQ_ERR_SCRATCH;
   int dc = check_device();
@@ -456,6 +474,20 @@ int dmq_residual_rmsnorm(const float* h_in, const float* y, const float* g, floa
   if (!dim_ok(M) || check_quant_k(K) != DMQ_OK || K > kMaxK || M * K > (int64_t(1) << 40)) return DMQ_ERR_INVALID_ARG;
   if (!aligned(h_in, 16) || !aligned(y, 16) || !aligned(h_out, 16) || (g && (!aligned(g, 16) || !aligned(xn_f16, 16))))
     return DMQ_ERR_ALIGNMENT;
+  {
+    // h_out may be h_in or y exactly (each element is read before it is
+    // written, by the same thread), but not overlap them otherwise; xn and g
+    // overlap nothing written
+    const int64_t hb = M * K * 4;
+    if ((h_out != h_in && overlap(h_out, hb, h_in, hb)) || (h_out != y && overlap(h_out, hb, y, hb)))
+      return DMQ_ERR_INVALID_ARG;
+    if (g) {
+      const Range out[2] = {{h_out, hb}, {xn_f16, M * K * 2}};
+      const Range in[3] = {{h_in, hb}, {y, hb}, {g, K * 4}};
+      if (races(out + 1, 1, in, 3) || races(out, 2, in + 2, 1) || overlap(xn_f16, M * K * 2, h_out, hb))
+        return DMQ_ERR_INVALID_ARG;
+    }
+  }
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   return hip_status(dmq::launch_residual_rmsnorm(h_in, y, g, eps, h_out, g ? xn_f16 : nullptr, M, K,

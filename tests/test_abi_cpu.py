@@ -36,7 +36,7 @@ def test_noalloc_attention_validation():
     decode call whose partial states exceed the fixed scratch is rejected
     with DMQ_ERR_SCRATCH before anything touches a device."""
     f = L.dmq_attention_gqa_noalloc
-    Q, KC, VC, O = (A16 + 0x100000 * i for i in range(4))
+    Q, KC, VC, O = (A16 + 0x10000000 * i for i in range(4))   # 256 MiB apart: no overlaps
     assert f(None, KC, VC, O, 1, 0, 24, 8, 16, None) == dmq.DMQ_ERR_INVALID_ARG
     assert f(Q, KC, VC, Q, 1, 0, 24, 8, 16, None) == dmq.DMQ_ERR_INVALID_ARG          # out is q
     assert f(Q, KC, VC, O, 1, 16, 24, 8, 16, None) == dmq.DMQ_ERR_INVALID_ARG         # past the cache
@@ -409,3 +409,31 @@ def test_outputs_overlapping_inputs_are_rejected():
     # dequant: 4 rows of 256 weights, 2 KiB of fp16 out
     assert L.dmq_dequant_q4k(W, W + 0x200, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
     assert L.dmq_dequant_q6k(W, W - 0x7f0, 4, 256, None) == dmq.DMQ_ERR_INVALID_ARG
+
+
+def test_layer_step_overlaps_are_rejected():
+    """RoPE + cache append, attention and residual + RMSNorm reject outputs
+    that share bytes with what they read.  M = 2, 6 query heads and 2 KV
+    heads of 128, cache of 16 positions: q fp32 6 KiB, q_f16 3 KiB, each
+    cache 8 KiB, attention output 3 KiB; residual rows K = 256."""
+    Q, K_, V, QH, KC, VC, O = (A16 + 0x10000 * i for i in range(7))
+    rope = lambda qh=QH, kc=KC, vc=VC, q=Q: L.dmq_rope_kv_cache(  # noqa: E731
+        q, K_, V, 2, 0, 6, 2, 500000.0, None, qh, kc, vc, 16, None)
+    assert rope(qh=Q + 0x1000) == dmq.DMQ_ERR_INVALID_ARG          # q_f16 over q
+    assert rope(kc=V + 0x100) == dmq.DMQ_ERR_INVALID_ARG           # cache over v
+    assert rope(vc=KC + 0x1ff0) == dmq.DMQ_ERR_INVALID_ARG         # the two caches
+    att = lambda out=O, q=QH: L.dmq_attention_gqa(q, KC, VC, out, 2, 14, 6, 2, 16, None)  # noqa: E731
+    assert att(out=QH + 0x100) == dmq.DMQ_ERR_INVALID_ARG
+    assert att(out=VC + 0x1ff0) == dmq.DMQ_ERR_INVALID_ARG
+    assert L.dmq_attention_gqa_noalloc(QH, KC, VC, KC, 2, 14, 6, 2, 16, None) == dmq.DMQ_ERR_INVALID_ARG
+    H, Yr, G, XN, HO = (A16 + 0x100000 + 0x10000 * i for i in range(5))
+    res = lambda ho=HO, xn=XN, g=G: L.dmq_residual_rmsnorm(H, Yr, g, 1e-5, ho, xn, 4, 256, None)  # noqa: E731
+    assert res(ho=H + 0x10) == dmq.DMQ_ERR_INVALID_ARG              # partly over h_in
+    assert res(xn=Yr + 0x3f0) == dmq.DMQ_ERR_INVALID_ARG            # xn over y
+    assert res(xn=HO + 0x200) == dmq.DMQ_ERR_INVALID_ARG            # xn over h_out
+    assert res(ho=G - 0x10) == dmq.DMQ_ERR_INVALID_ARG              # h_out over g
+    if _no_gpu():
+        assert res(ho=H) == dmq.DMQ_ERR_UNSUPPORTED                # in place: allowed
+        assert res(ho=Yr) == dmq.DMQ_ERR_UNSUPPORTED
+        assert rope() == dmq.DMQ_ERR_UNSUPPORTED
+        assert att() == dmq.DMQ_ERR_UNSUPPORTED
