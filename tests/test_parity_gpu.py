@@ -463,6 +463,17 @@ def test_lm_head_every_output(dmq):
     assert_within(y, ref, s, f"lm_head M={M} (every output)")
 
 
+def test_lm_head_decode_every_output(dmq):
+    """The tied LM head at M = 1 (one decode token): the decode kernel over
+    128,256 Q6_K rows in 8,016 workgroups, every output."""
+    name, fmt, N, K = synthetic.LM_HEAD
+    wq = synthetic.lm_head_weights(4)
+    x = synthetic.activations(1, K, seed=synthetic.act_seed(4, 0, synthetic.LM_HEAD_INDEX) + 1, unit_rms=True)
+    y = gpu_gemm(dmq, fmt, x, wq, 1, N, K)
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y, ref, s, "lm_head M=1 (every output)")
+
+
 # ------------------------------------------------------------------- FFN ---
 
 def run_ffn(dmq, x, wgu, wd, M, D, F):
@@ -589,6 +600,18 @@ def test_rmsnorm_gemm_every_output(dmq, M, K):
              ("q6k", synthetic.q6k_blocks(64, K, seed=M + 3), 64)]
     xn, ys = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, M, K)
     _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, f"rmsnorm+gemm M={M} K={K}")
+
+
+def test_rmsnorm_lm_head_decode_every_output(dmq):
+    """The end of a decode step: the final RMSNorm fused into the tied LM
+    head (Q6_K 3072 -> 128256) at M = 1, 8,016 workgroups each normalizing
+    x while staging it; xn from workgroup 0, every logit."""
+    name, fmt, N, K = synthetic.LM_HEAD
+    x = synthetic.activations(1, K, seed=77, sigma=3.0)
+    g = _norm_weights(K, seed=78)
+    projs = [(fmt, synthetic.lm_head_weights(4), N)]
+    xn, ys = _rmsnorm_gemm(dmq, x, g, 1e-5, projs, 1, K)
+    _check_rmsnorm_outputs(x, g, 1e-5, projs, K, xn, ys, "final rmsnorm + lm_head M=1")
 
 
 @pytest.mark.parametrize("K", [256, 3072, 8192, 32768])
