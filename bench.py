@@ -346,10 +346,13 @@ def layer_chain_sweep(torch, dmq):
     # forms h = h_in + y and its RMSNorm while it stages x.  The residual
     # stream alternates between x and h1; this layer's first call adds the
     # previous layer's FFN output.
-    def step_fused(W, B, kc, vc, M, pos0, L):
+    def step_fused(W, B, kc, vc, M, pos0, L, rope_in_attention=False):
         dmq.dmq_residual_rmsnorm_gemm(B["h1"], B["yd"], g1, 1e-5, B["x"], None, W["qkv_p"], M, D)
-        dmq.dmq_rope_kv_cache(B["yq"], B["yk"], B["yv"], M, pos0, HQ, HKV, B["qr"], kc, vc, L)
-        dmq.dmq_attention_gqa(B["qr"], kc, vc, B["att"], M, pos0, HQ, HKV, L)
+        if rope_in_attention:   # RoPE + cache append inside the attention call (one launch fewer at M = 1)
+            dmq.dmq_rope_attention_gqa(B["yq"], B["yk"], B["yv"], M, pos0, HQ, HKV, B["qr"], kc, vc, L, B["att"])
+        else:
+            dmq.dmq_rope_kv_cache(B["yq"], B["yk"], B["yv"], M, pos0, HQ, HKV, B["qr"], kc, vc, L)
+            dmq.dmq_attention_gqa(B["qr"], kc, vc, B["att"], M, pos0, HQ, HKV, L)
         dmq.dmq_gemm_q4k(B["att"], W["o"], B["yo"], M, D, HQ * HD)
         dmq.dmq_residual_rmsnorm_gemm(B["x"], B["yo"], g2, 1e-5, B["h1"], None, W["gu_p"], M, D)
         dmq.dmq_gemm_q6k(B["hf"], W["down"], B["yd"], M, D, F)
@@ -381,6 +384,7 @@ def layer_chain_sweep(torch, dmq):
         B["h1"].copy_(B["x"])
         B["yd"].zero_()
         uf = time_graph(torch, lambda it: step_fused(it[0], B, it[1][0], it[1][1], 1, pos0, L), items, 8) * 1e3
+        ur = time_graph(torch, lambda it: step_fused(it[0], B, it[1][0], it[1][1], 1, pos0, L, True), items, 8) * 1e3
         # the attention kernel alone at this context
         ua = time_graph(torch, lambda it: dmq.dmq_attention_gqa(B["qr"], it[1][0], it[1][1], B["att"], 1, pos0,
                                                                 HQ, HKV, L), items, 8) * 1e3
@@ -388,6 +392,7 @@ def layer_chain_sweep(torch, dmq):
         print(json.dumps({"sweep": f"decode step, one Llama-3.2-3B layer, all kernels (graph replay, 8 rotating layers), "
                                    f"context {L}", "us_per_layer": round(us, 2),
                           "fused_residual_us_per_layer": round(uf, 2),
+                          "fused_residual_and_rope_us_per_layer": round(ur, 2),
                           "attention_us": round(ua, 2), "attention_kv_GB/s": round(kv_bytes / ua / 1e3, 1)}),
               flush=True)
         del Ws, B, caches, items

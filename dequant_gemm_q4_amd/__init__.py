@@ -34,8 +34,8 @@ FORMATS = {"q4k": DMQ_FMT_Q4K, "q6k": DMQ_FMT_Q6K}
 # Every entry point declared in include/dmq.h.
 EXPORTS = ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
            "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
-           "dmq_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm",
-           "dmq_layer_prefill", "dmq_status_string", "dmq_version")
+           "dmq_attention_gqa", "dmq_rope_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm",
+           "dmq_residual_rmsnorm_gemm", "dmq_layer_prefill", "dmq_status_string", "dmq_version")
 HEAD_DIM = 128
 
 
@@ -94,6 +94,7 @@ def _load() -> ctypes.CDLL:
     L.dmq_rmsnorm_gemm.argtypes = [P, P, ctypes.c_float, P, I64, I64, ctypes.POINTER(ProjDesc), I32, P]
     L.dmq_rope_kv_cache.argtypes = [P, P, P, I64, I64, I32, I32, ctypes.c_double, P, P, P, P, I64, P]
     L.dmq_attention_gqa.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
+    L.dmq_rope_attention_gqa.argtypes = [P, P, P, I64, I64, I32, I32, ctypes.c_double, P, P, P, P, I64, P, P]
     L.dmq_attention_gqa_noalloc.argtypes = [P, P, P, P, I64, I64, I32, I32, I64, P]
     L.dmq_layer_prefill.argtypes = [ctypes.POINTER(LayerWeights), ctypes.POINTER(LayerBuffers), I64, I64, I32, I32,
                                     I32, I32, I64, ctypes.c_double, ctypes.c_float, I64, P, P]
@@ -102,8 +103,8 @@ def _load() -> ctypes.CDLL:
                                             I32, P]
     for name in ("dmq_dequant_q4k", "dmq_dequant_q6k", "dmq_gemm_q4k", "dmq_gemm_q6k",
                  "dmq_ffn_swiglu_q4k", "dmq_gemm_group", "dmq_rmsnorm_gemm", "dmq_rope_kv_cache",
-                 "dmq_attention_gqa", "dmq_attention_gqa_noalloc", "dmq_residual_rmsnorm",
-                 "dmq_residual_rmsnorm_gemm", "dmq_layer_prefill"):
+                 "dmq_attention_gqa", "dmq_rope_attention_gqa", "dmq_attention_gqa_noalloc",
+                 "dmq_residual_rmsnorm", "dmq_residual_rmsnorm_gemm", "dmq_layer_prefill"):
         getattr(L, name).restype = ctypes.c_int
     L.dmq_status_string.argtypes = [ctypes.c_int]
     L.dmq_status_string.restype = ctypes.c_char_p
@@ -308,6 +309,26 @@ def dmq_rope_kv_cache(q, k, v, M: int, pos0: int, n_q_heads: int, n_kv_heads: in
     pvc = _dev_tensor(v_cache, torch.float16, "v_cache", n_kv_heads * cache_len * D)
     _check(lib.dmq_rope_kv_cache(pq, pk, pv, M, pos0, n_q_heads, n_kv_heads, float(theta), pf, po, pkc, pvc,
                                  cache_len, _stream(stream)), "dmq_rope_kv_cache")
+
+
+def dmq_rope_attention_gqa(q, k, v, M: int, pos0: int, n_q_heads: int, n_kv_heads: int, q_out, k_cache, v_cache,
+                           cache_len: int, out, theta: float = 500000.0, freq_factors=None, stream=None) -> None:
+    """dmq_rope_kv_cache then dmq_attention_gqa in one call (one kernel fewer at
+    M = 1): q_out float16 [M, Hq*128] receives the rotated queries, rows
+    pos0..pos0+M-1 of the caches the rotated k and the v, out float16
+    [M, Hq*128] the attention output."""
+    import torch
+    D = HEAD_DIM
+    pq = _dev_tensor(q, torch.float32, "q", M * n_q_heads * D)
+    pk = _dev_tensor(k, torch.float32, "k", M * n_kv_heads * D)
+    pv = _dev_tensor(v, torch.float32, "v", M * n_kv_heads * D)
+    pf = None if freq_factors is None else _dev_tensor(freq_factors, torch.float32, "freq_factors", D // 2)
+    pqo = _dev_tensor(q_out, torch.float16, "q_out", M * n_q_heads * D)
+    pkc = _dev_tensor(k_cache, torch.float16, "k_cache", n_kv_heads * cache_len * D)
+    pvc = _dev_tensor(v_cache, torch.float16, "v_cache", n_kv_heads * cache_len * D)
+    po = _dev_tensor(out, torch.float16, "out", M * n_q_heads * D)
+    _check(lib.dmq_rope_attention_gqa(pq, pk, pv, M, pos0, n_q_heads, n_kv_heads, float(theta), pf, pqo, pkc, pvc,
+                                      cache_len, po, _stream(stream)), "dmq_rope_attention_gqa")
 
 
 def dmq_attention_gqa(q, k_cache, v_cache, out, M: int, pos0: int, n_q_heads: int, n_kv_heads: int,

@@ -12,6 +12,12 @@ namespace dmq {
 hipError_t launch_rope_kv(const float* q, const float* k, const float* v, const float* ff, void* q_out, void* k_cache,
                           void* v_cache, double theta, int64_t cache_len, int64_t M, int64_t pos0, int hq, int hkv,
                           hipStream_t s);
+// RoPE + cache append (launch_rope_kv) followed by attention
+// (launch_attention), with the same results bit for bit; at M = 1 on the
+// split path both run in the pieces' kernel (no RoPE launch).
+hipError_t launch_rope_attention(const float* q, const float* k, const float* v, const float* ff, void* q_out,
+                                 void* k_cache, void* v_cache, void* out, double theta, int64_t cache_len, int64_t M,
+                                 int64_t pos0, int hq, int hkv, hipStream_t s);
 // ws: NULL, or a device buffer of at least attention_scratch_bytes(M, pos0,
 // hq) bytes for the decode path's partial softmax states; NULL takes the
 // stream's workspace (workspace.cpp).

@@ -39,6 +39,25 @@ struct RopeArgs {
   int32_t pos0, hq, hkv;
 };
 
+// cos and sin of pair i's angle at position pos (fp64 angle, reduced modulo
+// 2 pi, each rounded to fp32).  The RoPE kernel and the fused decode
+// attention kernel both take their angles from here, so they agree bit for bit.
+__device__ __forceinline__ void rope_angle(double theta, const float* ff, int64_t pos, int i, float& c, float& s) {
+  double inv = pow(theta, -2.0 * i / HEAD_DIM);
+  if (ff) inv /= (double)ff[i];
+  const double ang = remainder((double)pos * inv, 2.0 * M_PI);
+  c = (float)cos(ang);
+  s = (float)sin(ang);
+}
+
+// (a, b) -> (a cos - b sin, a sin + b cos) in fp32, each rounded once to
+// fp16; the fused multiply-adds are written out so that every kernel using
+// this rounds the same way.
+__device__ __forceinline__ h2 rope_pair(float2 x, float c, float s) {
+  const h2 o = {(half_t)__builtin_fmaf(x.x, c, -(x.y * s)), (half_t)__builtin_fmaf(x.x, s, x.y * c)};
+  return o;
+}
+
 // grid: (token, unit): units 0 .. ceil(Hq/8)-1 take 8 query heads each, the
 // following ones 8 KV heads (K and V) each.
 constexpr int ROPE_UNIT = 8;
@@ -47,21 +66,12 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   const int m = blockIdx.x, unit = blockIdx.y, tid = threadIdx.x;
   const int uq = (a.hq + ROPE_UNIT - 1) / ROPE_UNIT;
   const int64_t pos = (int64_t)a.pos0 + m;
-  if (tid < HEAD_DIM / 2) {
-    double inv = pow(a.theta, -2.0 * tid / HEAD_DIM);
-    if (a.ff) inv /= (double)a.ff[tid];
-    const double ang = remainder((double)pos * inv, 2.0 * M_PI);
-    cs[tid] = (float)cos(ang);
-    sn[tid] = (float)sin(ang);
-  }
+  if (tid < HEAD_DIM / 2) rope_angle(a.theta, a.ff, pos, tid, cs[tid], sn[tid]);
   __syncthreads();
   auto rot = [&](const float* src, half_t* dst, int pairs) {
     for (int p = tid; p < pairs; p += 256) {
       const int i = p & (HEAD_DIM / 2 - 1);
-      const float2 x = ((const float2*)src)[p];
-      const float c = cs[i], s = sn[i];
-      const h2 o = {(half_t)(x.x * c - x.y * s), (half_t)(x.x * s + x.y * c)};
-      ((h2*)dst)[p] = o;
+      ((h2*)dst)[p] = rope_pair(((const float2*)src)[p], cs[i], sn[i]);
     }
   };
   if (unit < uq) {
@@ -76,10 +86,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
     const int h = k0 + p / (HEAD_DIM / 2), i = p % (HEAD_DIM / 2);
     const int64_t src = ((int64_t)m * a.hkv + h) * HEAD_DIM + 2 * i;
     const int64_t row = ((int64_t)h * a.cache_len + pos) * HEAD_DIM + 2 * i;
-    const float2 x = *(const float2*)(a.k + src);
-    const float c = cs[i], sv = sn[i];
-    const h2 ko = {(half_t)(x.x * c - x.y * sv), (half_t)(x.x * sv + x.y * c)};
-    *(h2*)(a.k_cache + row) = ko;
+    *(h2*)(a.k_cache + row) = rope_pair(*(const float2*)(a.k + src), cs[i], sn[i]);
     const float2 v = *(const float2*)(a.v + src);
     const h2 vo = {(half_t)v.x, (half_t)v.y};
     *(h2*)(a.v_cache + row) = vo;
@@ -252,22 +259,69 @@ constexpr int SPLIT_S = 64;
 constexpr int MERGE_MAX_PIECES = 4096;    // pieces the merge stages in LDS (262144 positions)
 constexpr int SPLIT_REC = HEAD_DIM + 2;   // floats per (query head, piece): o[128], max, sum
 
-template <int G>
-__global__ __launch_bounds__(256) void attention_split_kernel(AttnArgs a, float* ws, int nsplit) {
+// The RoPE inputs of the fused decode variant (ROPE): the Q, K and V
+// projections' fp32 rows, and where the rotated queries and the new cache
+// rows go.
+struct RopeIn {
+  const float* q;          // [1, Hq*128]
+  const float* k;          // [1, Hkv*128]
+  const float* v;          // [1, Hkv*128]
+  const float* ff;         // 64 frequency factors, or NULL
+  half_t* q_out;           // [1, Hq*128] fp16: the rotated queries
+  half_t* k_cache;         // the caches of AttnArgs, written at row pos0
+  half_t* v_cache;
+  double theta;
+};
+
+// ROPE (one query, M = 1): the workgroup rotates the queries of its KV group
+// itself, with the angles of position pos0 (the RoPE kernel's arithmetic),
+// instead of reading them rotated; piece 0 also stores them to q_out.  The
+// piece that holds position pos0 (the last one) rotates K and rounds V of
+// that position, writes them to the cache row pos0 and reads them back from
+// there after the barrier that follows, like every other row; no other piece
+// reads that row.  So the results are those of the RoPE kernel followed by
+// this kernel, bit for bit, without the RoPE launch in between.
+template <int G, bool ROPE>
+__global__ __launch_bounds__(256) void attention_split_kernel(AttnArgs a, RopeIn r, float* ws, int nsplit) {
   __shared__ __attribute__((aligned(16))) float qs[G][HEAD_DIM];
   __shared__ float ps[G][SPLIT_S];
   __shared__ float st[G][2];
   __shared__ float vsl[8][G][HEAD_DIM];
+  __shared__ float rcs[ROPE ? HEAD_DIM / 2 : 1], rsn[ROPE ? HEAD_DIM / 2 : 1];
   const int sp = blockIdx.x, kv = blockIdx.y, m = blockIdx.z, tid = threadIdx.x;
   const int n = a.pos0 + m + 1;
   const int c0 = sp * SPLIT_S;
   if (c0 >= n) return;   // no positions: the merge reads pieces < ceil(n / SPLIT_S) only
   const int cn = n - c0 < SPLIT_S ? n - c0 : SPLIT_S;
   const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
-  for (int i = tid; i < G * HEAD_DIM; i += 256)
-    qs[i / HEAD_DIM][i % HEAD_DIM] = (float)a.q[((int64_t)m * a.hq + kv * G) * HEAD_DIM + i] * scale;
+  if constexpr (ROPE) {
+    const int64_t pos = (int64_t)a.pos0 + m;
+    if (tid < HEAD_DIM / 2) rope_angle(r.theta, r.ff, pos, tid, rcs[tid], rsn[tid]);
+    __syncthreads();
+    for (int p = tid; p < G * HEAD_DIM / 2; p += 256) {
+      const int g = p / (HEAD_DIM / 2), i = p % (HEAD_DIM / 2);
+      const int64_t off = ((int64_t)m * a.hq + kv * G + g) * HEAD_DIM + 2 * i;
+      const h2 o = rope_pair(*(const float2*)(r.q + off), rcs[i], rsn[i]);
+      if (sp == 0) *(h2*)(r.q_out + off) = o;
+      qs[g][2 * i] = (float)o.x * scale;
+      qs[g][2 * i + 1] = (float)o.y * scale;
+    }
+    if (pos >= c0 && pos < c0 + cn && tid < HEAD_DIM / 2) {
+      const int64_t src = ((int64_t)m * a.hkv + kv) * HEAD_DIM + 2 * tid;
+      const int64_t row = ((int64_t)kv * a.cache_len + pos) * HEAD_DIM + 2 * tid;
+      *(h2*)(r.k_cache + row) = rope_pair(*(const float2*)(r.k + src), rcs[tid], rsn[tid]);
+      const float2 vv = *(const float2*)(r.v + src);
+      const h2 vo = {(half_t)vv.x, (half_t)vv.y};
+      *(h2*)(r.v_cache + row) = vo;
+    }
+  } else {
+    for (int i = tid; i < G * HEAD_DIM; i += 256)
+      qs[i / HEAD_DIM][i % HEAD_DIM] = (float)a.q[((int64_t)m * a.hq + kv * G) * HEAD_DIM + i] * scale;
+  }
   const half_t* kc = a.k_cache + (int64_t)kv * a.cache_len * HEAD_DIM;
   const half_t* vc = a.v_cache + (int64_t)kv * a.cache_len * HEAD_DIM;
+  // (with ROPE, also orders the new cache row's stores before its loads
+  // below: a workgroup barrier carries a workgroup-scope release and acquire)
   __syncthreads();
   // scores: 4 threads per position, 32 dimensions each, summed across the quad
   {
@@ -774,45 +828,56 @@ hipError_t noalloc_scratch(float** ptr, size_t* bytes) {
   return hipSuccess;
 }
 
+// Whether M queries from position pos0 take the split (decode) path.
+static bool split_path(int64_t M, int64_t pos0) {
+  return M <= ATT_SPLIT_MAX_M && (pos0 + M + SPLIT_S - 1) / SPLIT_S <= MERGE_MAX_PIECES;
+}
+
 size_t attention_scratch_bytes(int64_t M, int64_t pos0, int hq) {
+  if (!split_path(M, pos0)) return 0;
   const int64_t nsplit = (pos0 + M + SPLIT_S - 1) / SPLIT_S;
-  if (M > ATT_SPLIT_MAX_M || nsplit > MERGE_MAX_PIECES) return 0;
   return (size_t)M * hq * nsplit * SPLIT_REC * sizeof(float);
+}
+
+// The split path: the pieces' kernel (with ROPE, the fused RoPE variant at
+// M = 1), then the merge.  ws_given: a buffer for the partial states, or NULL
+// for the stream's workspace.
+template <bool ROPE>
+static hipError_t launch_split(const AttnArgs& a, const RopeIn& r, int64_t M, int64_t pos0, hipStream_t s,
+                               float* ws_given) {
+  const int nsplit = (int)((pos0 + M + SPLIT_S - 1) / SPLIT_S);
+  // sized for the whole cache when that is at most 64 MiB (every position a
+  // later call on this stream can reach), so a decode loop over one cache
+  // does not grow it
+  const size_t rec_bytes = (size_t)M * a.hq * SPLIT_REC * sizeof(float);
+  const int64_t cap = std::min<int64_t>((a.cache_len + SPLIT_S - 1) / SPLIT_S, MERGE_MAX_PIECES);
+  size_t want = rec_bytes * (size_t)nsplit;
+  if (cap > nsplit && rec_bytes * (size_t)cap <= (size_t(64) << 20)) want = rec_bytes * (size_t)cap;
+  void* wp = ws_given;
+  hipError_t e = ws_given ? hipSuccess : stream_workspace(WorkspaceUse::AttentionPieces, s, want, &wp);
+  if (e != hipSuccess) return e;
+  float* ws = (float*)wp;
+  const dim3 grid((unsigned)nsplit, (unsigned)a.hkv, (unsigned)M);
+  switch (a.hq / a.hkv) {
+    case 1: hipLaunchKernelGGL((attention_split_kernel<1, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    case 2: hipLaunchKernelGGL((attention_split_kernel<2, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    case 3: hipLaunchKernelGGL((attention_split_kernel<3, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    case 4: hipLaunchKernelGGL((attention_split_kernel<4, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    case 5: hipLaunchKernelGGL((attention_split_kernel<5, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    case 6: hipLaunchKernelGGL((attention_split_kernel<6, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    case 7: hipLaunchKernelGGL((attention_split_kernel<7, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+    default: hipLaunchKernelGGL((attention_split_kernel<8, ROPE>), grid, dim3(256), 0, s, a, r, ws, nsplit); break;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)a.hq, (unsigned)M), dim3(HEAD_DIM), 0, s, a, ws, nsplit);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const void* q, const void* k_cache, const void* v_cache, void* out, int64_t cache_len,
                             int64_t M, int64_t pos0, int hq, int hkv, hipStream_t s, float* ws_given) {
   AttnArgs a{(const half_t*)q, (const half_t*)k_cache, (const half_t*)v_cache, (half_t*)out, cache_len,
              (int32_t)pos0, hq, hkv};
-  const int64_t nsplit64 = (pos0 + M + SPLIT_S - 1) / SPLIT_S;
-  if (M <= ATT_SPLIT_MAX_M && nsplit64 <= MERGE_MAX_PIECES) {
-    const int nsplit = (int)nsplit64;
-    // sized for the whole cache when that is at most 64 MiB (every position a
-    // later call on this stream can reach), so a decode loop over one cache
-    // does not grow it
-    const size_t rec_bytes = (size_t)M * hq * SPLIT_REC * sizeof(float);
-    const int64_t cap = std::min<int64_t>((cache_len + SPLIT_S - 1) / SPLIT_S, MERGE_MAX_PIECES);
-    size_t want = rec_bytes * (size_t)nsplit;
-    if (cap > nsplit && rec_bytes * (size_t)cap <= (size_t(64) << 20)) want = rec_bytes * (size_t)cap;
-    void* wp = ws_given;
-    hipError_t e = ws_given ? hipSuccess : stream_workspace(WorkspaceUse::AttentionPieces, s, want, &wp);
-    if (e != hipSuccess) return e;
-    float* ws = (float*)wp;
-    const dim3 grid((unsigned)nsplit, (unsigned)hkv, (unsigned)M);
-    switch (hq / hkv) {
-      case 1: hipLaunchKernelGGL(attention_split_kernel<1>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      case 2: hipLaunchKernelGGL(attention_split_kernel<2>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      case 3: hipLaunchKernelGGL(attention_split_kernel<3>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      case 4: hipLaunchKernelGGL(attention_split_kernel<4>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      case 5: hipLaunchKernelGGL(attention_split_kernel<5>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      case 6: hipLaunchKernelGGL(attention_split_kernel<6>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      case 7: hipLaunchKernelGGL(attention_split_kernel<7>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-      default: hipLaunchKernelGGL(attention_split_kernel<8>, grid, dim3(256), 0, s, a, ws, nsplit); break;
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)hq, (unsigned)M), dim3(HEAD_DIM), 0, s, a, ws, nsplit);
-    return hipGetLastError();
-  }
+  if (split_path(M, pos0)) return launch_split<false>(a, RopeIn{}, M, pos0, s, ws_given);
   if (M > ATT_SPLIT_MAX_M) {
     const int nqb = (int)((M + FA_QB - 1) / FA_QB);
     const int per = (nqb * hq + 7) / 8;   // work items per XCD
@@ -831,6 +896,20 @@ hipError_t launch_attention(const void* q, const void* k_cache, const void* v_ca
     default: hipLaunchKernelGGL(attention_kernel<8>, grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rope_attention(const float* q, const float* k, const float* v, const float* ff, void* q_out,
+                                 void* k_cache, void* v_cache, void* out, double theta, int64_t cache_len, int64_t M,
+                                 int64_t pos0, int hq, int hkv, hipStream_t s) {
+  if (M == 1 && split_path(M, pos0)) {
+    const AttnArgs a{(const half_t*)q_out, (const half_t*)k_cache, (const half_t*)v_cache, (half_t*)out, cache_len,
+                     (int32_t)pos0, hq, hkv};
+    const RopeIn r{q, k, v, ff, (half_t*)q_out, (half_t*)k_cache, (half_t*)v_cache, theta};
+    return launch_split<true>(a, r, M, pos0, s, nullptr);
+  }
+  hipError_t e = launch_rope_kv(q, k, v, ff, q_out, k_cache, v_cache, theta, cache_len, M, pos0, hq, hkv, s);
+  if (e != hipSuccess) return e;
+  return launch_attention(q_out, k_cache, v_cache, out, cache_len, M, pos0, hq, hkv, s);
 }
 
 // ----------------------------------------------------- residual + RMSNorm --

@@ -443,6 +443,31 @@ int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_
                                           n_kv_heads, (hipStream_t)stream));
 }
 
+int dmq_rope_attention_gqa(const float* q, const float* k, const float* v, int64_t M, int64_t pos0,
+                           int32_t n_q_heads, int32_t n_kv_heads, double theta, const float* freq_factors,
+                           void* q_f16, void* k_cache_f16, void* v_cache_f16, int64_t cache_len, void* out_f16,
+                           void* stream) {
+  if (!q || !k || !v || !q_f16 || !k_cache_f16 || !v_cache_f16 || !out_f16) return DMQ_ERR_INVALID_ARG;
+  if (!heads_ok(n_q_heads, n_kv_heads) || !cache_ok(M, pos0, n_kv_heads, cache_len)) return DMQ_ERR_INVALID_ARG;
+  if (!(theta > 1.0) || theta > 1e30) return DMQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_f16, 16) || !aligned(k_cache_f16, 16) ||
+      !aligned(v_cache_f16, 16) || !aligned(out_f16, 16) || (freq_factors && !aligned(freq_factors, 4)))
+    return DMQ_ERR_ALIGNMENT;
+  {
+    // written: the rotated queries, both caches (rows pos0 .. pos0+M-1) and
+    // the output; read: the projections, the frequency factors, and (by the
+    // attention) the rotated queries and the caches
+    const int64_t qd = (int64_t)n_q_heads * 128, kd = (int64_t)n_kv_heads * 128, cb = kd * cache_len * 2;
+    const Range out[4] = {{q_f16, M * qd * 2}, {k_cache_f16, cb}, {v_cache_f16, cb}, {out_f16, M * qd * 2}};
+    const Range in[4] = {{q, M * qd * 4}, {k, M * kd * 4}, {v, M * kd * 4}, {freq_factors, 64 * 4}};
+    if (races(out, 4, in, 4)) return DMQ_ERR_INVALID_ARG;
+  }
+  int dc = check_device();
+  if (dc != DMQ_OK) return dc;
+  return hip_status(dmq::launch_rope_attention(q, k, v, freq_factors, q_f16, k_cache_f16, v_cache_f16, out_f16, theta,
+                                               cache_len, M, pos0, n_q_heads, n_kv_heads, (hipStream_t)stream));
+}
+
 int dmq_attention_gqa_noalloc(const void* q_f16, const void* k_cache_f16, const void* v_cache_f16, void* out_f16,
                               int64_t M, int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len,
                               void* stream) {

@@ -289,6 +289,24 @@ int dmq_attention_gqa(const void* q_f16, const void* k_cache_f16, const void* v_
                       int64_t pos0, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_len, void* stream);
 
 /*
+ * dmq_rope_kv_cache followed by dmq_attention_gqa on the same arguments, in
+ * one call: the RoPE and cache-append step of the overview's "[04] one decode
+ * step" joined to the attention that reads its results.  Arguments as in
+ * those two calls (q, k, v: the projections' fp32 rows; q_f16: receives the
+ * rotated queries; k_cache_f16, v_cache_f16: rows pos0 .. pos0+M-1 written;
+ * out_f16: the attention output), with the checks of both; additionally
+ * out_f16 overlapping any other buffer is rejected.  Every output has the
+ * bits the two calls give.  At M = 1 (one decode token) the rotation, the
+ * cache append and the attention's per-piece pass run in one kernel, saving
+ * the RoPE launch; other M run the two calls' kernels in turn.  Uses the
+ * attention's per-stream workspace like dmq_attention_gqa.
+ */
+int dmq_rope_attention_gqa(const float* q, const float* k, const float* v, int64_t M, int64_t pos0,
+                           int32_t n_q_heads, int32_t n_kv_heads, double theta, const float* freq_factors,
+                           void* q_f16, void* k_cache_f16, void* v_cache_f16, int64_t cache_len, void* out_f16,
+                           void* stream);
+
+/*
  * dmq_attention_gqa for callers that cannot allocate device memory: code
  * being captured into a HIP graph, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, results and bits as dmq_attention_gqa; it

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(dmq.EXPORTS)
     raw = ctypes.CDLL(dmq.LIB_PATH)
     for n in names:
@@ -332,6 +332,34 @@ def test_rope_kv_cache_validation():
     for bad in (dict(q=MIS), dict(k=MIS), dict(v=MIS), dict(qo=MIS), dict(kc=MIS), dict(vc=MIS),
                 dict(ff=A16 + 2)):
         assert call(**bad) == dmq.DMQ_ERR_ALIGNMENT, bad
+
+
+def test_rope_attention_gqa_validation():
+    """The fused RoPE + cache append + attention call makes the checks of
+    both calls, and rejects an output over any other buffer.  M = 2, 24
+    query and 8 KV heads of 128, cache of 16 positions: q fp32 24 KiB, k and
+    v fp32 8 KiB each, q_f16 and the output 12 KiB each, each cache 32 KiB."""
+    f = L.dmq_rope_attention_gqa
+    Q, K, V, QO, KC, VC, O = (A16 + 0x100000 * i for i in range(7))   # 1 MiB apart: no overlaps
+    ok = dict(q=Q, k=K, v=V, M=2, pos0=0, hq=24, hkv=8, theta=500000.0, ff=None, qo=QO, kc=KC, vc=VC, L=16, o=O)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["M"], a["pos0"], a["hq"], a["hkv"], a["theta"], a["ff"], a["qo"],
+                 a["kc"], a["vc"], a["L"], a["o"], None)
+    for bad in (dict(q=None), dict(k=None), dict(v=None), dict(qo=None), dict(kc=None), dict(vc=None), dict(o=None),
+                dict(M=0), dict(pos0=-1), dict(pos0=15), dict(L=0), dict(hq=25), dict(hkv=0), dict(hq=72),
+                dict(theta=1.0), dict(theta=float("nan"))):
+        assert call(**bad) == dmq.DMQ_ERR_INVALID_ARG, bad
+    for bad in (dict(q=MIS), dict(k=MIS), dict(v=MIS), dict(qo=MIS), dict(kc=MIS), dict(vc=MIS), dict(o=MIS),
+                dict(ff=A16 + 2)):
+        assert call(**bad) == dmq.DMQ_ERR_ALIGNMENT, bad
+    for bad in (dict(o=QO), dict(o=QO + 0x2ff0), dict(o=KC + 0x7ff0), dict(o=VC), dict(o=Q + 0x10),
+                dict(qo=K), dict(kc=V + 0x1ff0), dict(vc=KC + 0x10), dict(kc=O - 0x7ff0)):
+        assert call(**bad) == dmq.DMQ_ERR_INVALID_ARG, bad
+    if _no_gpu():
+        assert call() == dmq.DMQ_ERR_UNSUPPORTED
+        assert call(M=1, pos0=15) == dmq.DMQ_ERR_UNSUPPORTED
 
 
 def test_attention_gqa_validation():

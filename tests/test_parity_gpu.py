@@ -722,6 +722,40 @@ def test_rope_kv_cache(dmq, M, pos0, hq, hkv, cache_len):
     _check_rope(q, k, v, qo, kc, vc, sent, M, pos0, hq, hkv, f"rope M={M} pos0={pos0} hq={hq} hkv={hkv}")
 
 
+@pytest.mark.parametrize("M,pos0,hq,hkv,cache_len,ff", [(1, 0, 24, 8, 16, False), (1, 63, 24, 8, 128, False),
+                                                         (1, 64, 24, 8, 128, True), (1, 1023, 24, 8, 1024, False),
+                                                         (1, 4095, 8, 1, 5000, True), (1, 300, 6, 2, 512, False),
+                                                         (1, 131071, 24, 8, 131072, False),
+                                                         (5, 100, 24, 8, 200, False), (40, 7, 24, 8, 64, True)])
+def test_rope_attention_fused_equals_two_calls(dmq, M, pos0, hq, hkv, cache_len, ff):
+    """dmq_rope_attention_gqa gives the bits of dmq_rope_kv_cache followed by
+    dmq_attention_gqa on every output: the rotated queries, both caches
+    whole (the appended rows and every row it must not touch) and the
+    attention output.  M = 1 runs the fused decode kernel; M = 5 (split
+    path) and M = 40 (MFMA path) run the two launches."""
+    rng = np.random.default_rng(M * 7919 + pos0)
+    qd, kd = hq * D_HEAD, hkv * D_HEAD
+    q = dev(rng.standard_normal((M, qd)).astype(np.float32))
+    k = dev(rng.standard_normal((M, kd)).astype(np.float32))
+    v = dev(rng.standard_normal((M, kd)).astype(np.float32))
+    f = dev(rng.uniform(1.0, 32.0, D_HEAD // 2).astype(np.float32)) if ff else None
+    cache0 = [rng.standard_normal((hkv, cache_len, D_HEAD), dtype=np.float32).astype(np.float16) for _ in range(2)]
+    outs = []
+    for fused in (False, True):
+        kc, vc = dev(cache0[0]), dev(cache0[1])
+        qo = torch.empty((M, qd), dtype=torch.float16, device=DEV)
+        out = torch.empty((M, qd), dtype=torch.float16, device=DEV)
+        if fused:
+            dmq.dmq_rope_attention_gqa(q, k, v, M, pos0, hq, hkv, qo, kc, vc, cache_len, out, freq_factors=f)
+        else:
+            dmq.dmq_rope_kv_cache(q, k, v, M, pos0, hq, hkv, qo, kc, vc, cache_len, freq_factors=f)
+            dmq.dmq_attention_gqa(qo, kc, vc, out, M, pos0, hq, hkv, cache_len)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().view(np.uint16) for t in (qo, kc, vc, out)])
+    for name, a, b in zip(("q_f16", "k_cache", "v_cache", "out"), outs[0], outs[1]):
+        assert np.array_equal(a, b), f"{name}: {int((a != b).sum())} of {a.size} values differ"
+
+
 def test_rope_kv_cache_freq_factors(dmq):
     # the factors as the kernel receives them (fp32); the oracle takes the same values
     f = np.random.default_rng(9).uniform(1.0, 32.0, D_HEAD // 2).astype(np.float32)
