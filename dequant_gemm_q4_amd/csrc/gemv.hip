@@ -59,8 +59,11 @@ struct GemvArgs {
 };
 
 // x in LDS: each group of 64 values (128 bytes) is followed by 16 bytes of
-// padding, so the x reads of the 16 blocks of a step (512 bytes apart
-// unpadded, i.e. the same banks) spread over all 64 banks.
+// padding.  A wave's lanes read the x of the four parts of one block at a
+// time; Q4_K parts are one group apart, which unpadded would put parts 0 and
+// 2 (and 1 and 3) on the same banks, and padded puts all four on distinct
+// ones.  (Q6_K parts 1 and 2 still share banks; a layout without that
+// conflict measured no faster.)
 constexpr int X_GROUP_BYTES = 144;
 
 typedef float f2 __attribute__((ext_vector_type(2)));
