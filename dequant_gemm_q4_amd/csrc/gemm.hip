@@ -11,13 +11,15 @@
 // (tiles of at least 64 activation rows, no SwiGLU) 8 waves of one, two per
 // SIMD, so that one wave's dequantisation runs beside the other's MFMAs.
 //  * Each wave owns 32*IB weight rows and all BM activation rows.  It decodes
-//    its raw blocks straight into MFMA A-operand registers: every weight is
-//    dequantised once per workgroup and no dequantised tile touches LDS or
-//    HBM.
+//    its raw blocks straight into the registers of the MFMA's B operand (the
+//    weights; x fragments read from LDS are the A operand, so an accumulator
+//    lane holds one output column): every weight is dequantised once per
+//    workgroup and no dequantised tile touches LDS or HBM.  (In the code,
+//    `af` names the weight fragments and `bf` the x fragments.)
 //  * x is staged in LDS per 64-wide K chunk by direct global->LDS loads
 //    (buffer_load ... lds, no VGPR staging) into four buffers, three chunks
 //    ahead, with the 16-byte chunks of each 128-byte row XOR-swizzled by the
-//    row so that B-fragment reads are free of bank conflicts.
+//    row so that the x-fragment reads are free of bank conflicts.
 //  * Sub-block scales / mins are decoded once per super-block and weight row
 //    into an LDS table.  Per weight the lanes then do: isolate the quant in
 //    a byte, convert it to fp32 exactly (Q4_K: the nibble read as an fp8
