@@ -8,12 +8,15 @@
 // across the prompt rows; overview page, compartment 09 of "[02] the
 // pipeline": the dequant is fused and fp16 weights are never written):
 //
-//  * a workgroup owns 16 consecutive weight rows; its waves (one per
-//    super-block of the row, at most 16) split the row's super-blocks into
-//    contiguous slices, and a lane works on row l%16 and part l/16 of every
-//    super-block of its wave's slice.  With a block or two per wave, every
-//    load of the workgroup is issued before the first multiply: the matrix
-//    streams in about one memory round trip instead of one per block;
+//  * a workgroup owns 16 consecutive weight rows; its waves split the row's
+//    super-blocks into contiguous slices, and a lane works on row l%16 and
+//    part l/16 of every super-block of its wave's slice.  A single
+//    projection takes one wave per super-block (up to 16; deeper rows 8
+//    waves with four blocks each in flight), so every load of the
+//    workgroup is issued before the first multiply and the matrix streams
+//    in about one memory round trip instead of one per block; a grid of at
+//    least two workgroups per CU (several projections in one launch) keeps
+//    4-wave workgroups with two blocks in flight;
 //  * v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16 and k-slots
 //    8*(l/16) .. +7; B: column l%16, the same k-slots; D: column l%16, rows
 //    4*(l/16) .. +3) takes 8 dequantised weights per lane as the A operand
