@@ -409,6 +409,87 @@ def test_gemm_split_k_interleaved_shapes(dmq):
         assert_within(y.cpu().numpy(), ref, s, f"interleaved split-K {fmt} {M}x{N}x{K}")
 
 
+def test_concurrent_host_threads_same_bits(dmq):
+    """Four host threads call the library at once, each on a stream of its
+    own: split-K GEMMs (the plan cache and the per-stream workspaces), a
+    decode GEMV, the SwiGLU FFN and RoPE + attention in one call (the
+    attention workspace).  Every output has the bits of the same call made
+    alone on the default stream."""
+    import threading
+    rng = np.random.default_rng(77)
+
+    def gemm_case(fmt, M, N, K, seed):
+        x = dev(synthetic.activations(M, K, seed=seed))
+        wq = dev(synthetic.weight_blocks(fmt, N, K, seed=seed + 1).reshape(-1))
+        fn = dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k
+
+        def run(stream):
+            y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            fn(x, wq, y, M, N, K, stream=stream)
+            return [y]
+        return run
+
+    def ffn_case(M, D, F, seed):
+        x = dev(synthetic.activations(M, D, seed=seed))
+        wgu = dev(synthetic.q4k_blocks(2 * F, D, seed=seed + 1).reshape(-1))
+        wd = dev(synthetic.q6k_blocks(D, F, seed=seed + 2).reshape(-1))
+
+        def run(stream):
+            h = torch.empty((M, F), dtype=torch.float16, device=DEV)
+            y = torch.empty((M, D), dtype=torch.float32, device=DEV)
+            dmq.dmq_ffn_swiglu_q4k(x, wgu, wd, h, y, M, D, F, stream=stream)
+            return [h, y]
+        return run
+
+    def attn_case(pos0, hq, hkv, L):
+        q, k, v = (dev(rng.standard_normal((1, n * D_HEAD)).astype(np.float32)) for n in (hq, hkv, hkv))
+        base = [rng.standard_normal((hkv, L, D_HEAD)).astype(np.float16) for _ in range(2)]
+
+        def run(stream):
+            kc, vc = dev(base[0]), dev(base[1])
+            qo = torch.empty((1, hq * D_HEAD), dtype=torch.float16, device=DEV)
+            out = torch.empty((1, hq * D_HEAD), dtype=torch.float16, device=DEV)
+            # the cache copies above are on the current stream, which is the call's
+            dmq.dmq_rope_attention_gqa(q, k, v, 1, pos0, hq, hkv, qo, kc, vc, L, out, stream=stream)
+            return [qo, kc, vc, out]
+        return run
+
+    jobs = [[gemm_case("q6k", 1024, 3072, 8192, 5), gemm_case("q4k", 1, 3072, 3072, 6)],
+            [gemm_case("q4k", 33, 250, 4864, 7), ffn_case(300, 768, 1024, 8)],
+            [attn_case(1000, 24, 8, 1024), gemm_case("q6k", 40, 37, 8192, 9)],
+            [gemm_case("q4k", 700, 1000, 3072, 10), attn_case(63, 6, 2, 128)]]
+    ref = [[[t.clone() for t in run(None)] for run in job] for job in jobs]
+    torch.cuda.synchronize()
+    got = [None] * len(jobs)
+    errors = []
+
+    def worker(j):
+        try:
+            stream = torch.cuda.Stream()
+            res = []
+            with torch.cuda.stream(stream):
+                for _ in range(5):
+                    res.append([run(stream.cuda_stream) for run in jobs[j]])
+            stream.synchronize()
+            got[j] = res
+        except Exception as e:   # reported below, in the main thread
+            errors.append(e)
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    def bits(t):   # NaNs (the FFN's overflowed h feeds inf - inf into y) compare by their bits
+        return t.view(torch.int16 if t.dtype == torch.float16 else torch.int32)
+    for j, job_ref in enumerate(ref):
+        for it, outs in enumerate(got[j]):
+            for c, (a, b) in enumerate(zip(job_ref, outs)):
+                for ta, tb in zip(a, b):
+                    assert torch.equal(bits(ta), bits(tb)), f"thread {j} call {c} round {it}: bits differ from the lone call"
+
+
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 @pytest.mark.parametrize("M,N,K", [(2, 16, 256), (16, 40, 256), (12, 20, 768), (5, 37, 4864), (9, 33, 512),
                                    (16, 3072, 3072), (16, 48, 8192), (7, 50, 9984), (17, 100, 1280), (32, 257, 768)])
