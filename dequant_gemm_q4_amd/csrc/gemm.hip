@@ -15,7 +15,7 @@
 //    weights; x fragments read from LDS are the A operand, so an accumulator
 //    lane holds one output column): every weight is dequantised once per
 //    workgroup and no dequantised tile touches LDS or HBM.  (In the code,
-//    `af` names the weight fragments and `bf` the x fragments.)
+//    `wf` names the weight fragments and `xf` the x fragments.)
 //  * x is staged in LDS per 64-wide K chunk by direct global->LDS loads
 //    (buffer_load ... lds, no VGPR staging) into four buffers, three chunks
 //    ahead, with the 16-byte chunks of each 128-byte row XOR-swizzled by the
@@ -398,7 +398,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   Raw rs[NSET][IB];          // raw quant sets: Q4_K chunk mod 4, Q6_K block half
   float scl[IB][NSC];        // this block's scale-table entries of the lane's rows
   float sv[IB][4];           // scales of the current chunk
-  h8 af[IB], bf[JB];
+  h8 wf[IB], xf[JB];
 
   auto read_scales = [&]() {
 #pragma unroll
@@ -525,9 +525,9 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
   read_scales();
   chunk_scales(0, sv);
 #pragma unroll
-  for (int c = 0; c < IB; ++c) af[c] = frag(rs[0][c], 0, 0, sv[c]);
+  for (int c = 0; c < IB; ++c) wf[c] = frag(rs[0][c], 0, 0, sv[c]);
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) bf[jb] = bread(0, 0, jb);
+  for (int jb = 0; jb < JB; ++jb) xf[jb] = bread(0, 0, jb);
 
   for (int b = 0; b < nb; ++b) {
     const bool more = b + 1 < nb;
@@ -549,10 +549,10 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         // K steps 0..2
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
-          h8 afn[IB];
+          h8 wfn[IB];
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
+          for (int c = 0; c < IB; ++c) wfn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
           if (j == 3 && s == 0 && more && tab_wave)
             tab_store<FMT>(my_tab, hdr, hdr4);
           const int nv = issue_loads(j, s, ck3, b, bnext);
@@ -560,13 +560,13 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
           for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
             for (int c = 0; c < IB; ++c)
-              acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[jb], af[c], acc[jb][c], 0, 0, 0);
-            bf[jb] = bread(j, s + 1, jb);
+              acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf[jb], wf[c], acc[jb][c], 0, 0, 0);
+            xf[jb] = bread(j, s + 1, jb);
           }
           interleave_rd(nv, j == 3 && s == 0 ? 6 : 3);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int c = 0; c < IB; ++c) af[c] = afn[c];
+          for (int c = 0; c < IB; ++c) wf[c] = wfn[c];
         }
         // K step 3: as below; the next chunk's fragments are read from its
         // buffer after the barrier, each after the MFMA that frees it
@@ -576,25 +576,25 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
           if (j == 0 || j == 2) wait_vm_barrier<2 * XQ + NRAW>();
           else wait_vm_barrier<2 * XQ>();
         }
-        h8 afn[IB];
+        h8 wfn[IB];
         float svn[IB][4];
         if (j == 3) read_scales();
         chunk_scales((j + 1) & 3, svn);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
+        for (int c = 0; c < IB; ++c) wfn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll
           for (int c = 0; c < IB; ++c)
-            acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[jb], af[c], acc[jb][c], 0, 0, 0);
-          bf[jb] = bread((j + 1) & 3, 0, jb);
+            acc[jb][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf[jb], wf[c], acc[jb][c], 0, 0, 0);
+          xf[jb] = bread((j + 1) & 3, 0, jb);
         }
         interleave_rd(0, 3);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < IB; ++c) {
-          af[c] = afn[c];
+          wf[c] = wfn[c];
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
         }
@@ -604,24 +604,24 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       // K steps 0..2
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
-        h8 afn[IB], bfn[JB];
+        h8 wfn[IB], xfn[JB];
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bfn[jb] = bread(j, s + 1, jb);
+        for (int jb = 0; jb < JB; ++jb) xfn[jb] = bread(j, s + 1, jb);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < IB; ++c) afn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
+        for (int c = 0; c < IB; ++c) wfn[c] = frag(rs[cur][c], s + 1, j, sv[c]);
         if (j == 3 && s == 0 && more && tab_wave)
           tab_store<FMT>(my_tab, hdr, hdr4);
         const int nv = issue_loads(j, s, ck3, b, bnext);
-        mfma_step(af, bf);
+        mfma_step(wf, xf);
         // the step that also decodes the next block's scale table has more
         // VALU work to place
         interleave(nv, j == 3 && s == 0 ? 6 : 3);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < IB; ++c) af[c] = afn[c];
+        for (int c = 0; c < IB; ++c) wf[c] = wfn[c];
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
+        for (int jb = 0; jb < JB; ++jb) xf[jb] = xfn[jb];
       }
 
       // K step 3: wait for chunk ck+1's x and raw bytes and, at a block
@@ -637,26 +637,26 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
         if (j == 0 || j == 2) wait_vm_barrier<2 * XQ + NRAW>();
         else wait_vm_barrier<2 * XQ>();
       }
-      h8 afn[IB], bfn[JB];
+      h8 wfn[IB], xfn[JB];
       float svn[IB][4];
       if (j == 3) read_scales();
       chunk_scales((j + 1) & 3, svn);
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) bfn[jb] = bread((j + 1) & 3, 0, jb);
+      for (int jb = 0; jb < JB; ++jb) xfn[jb] = bread((j + 1) & 3, 0, jb);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < IB; ++c) afn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
-      mfma_step(af, bf);
+      for (int c = 0; c < IB; ++c) wfn[c] = frag(rs[nxt][c], 0, (j + 1) & 3, svn[c]);
+      mfma_step(wf, xf);
       interleave(0, 3);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < IB; ++c) {
-        af[c] = afn[c];
+        wf[c] = wfn[c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[c][e] = svn[c][e];
       }
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) bf[jb] = bfn[jb];
+      for (int jb = 0; jb < JB; ++jb) xf[jb] = xfn[jb];
     }
   }
   // no direct-to-LDS load may still be in flight when the workgroup ends
