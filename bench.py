@@ -46,7 +46,7 @@ SETTLE_MS = 150.0              # untimed GPU work before any timed region (clock
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": "412b27affb235b14809e05d2a482e52ac39af2c6e947c26861d95066a235a35f", "bytes_per_launch": 622238126}
+TRAFFIC = {"sources_sha256": "5bc32ebaf9c2ef5ea6b1624483a1ecdb1bc78bb7891f12423917b312392e2230", "bytes_per_launch": 622238126}
 COPY_PROBE_BYTES = 256 << 20
 
 

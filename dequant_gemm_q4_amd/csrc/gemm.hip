@@ -117,7 +117,7 @@ __device__ __forceinline__ void nibbles_fma_pairs(uint32_t b, float s512, float 
   p1 = as_u32(__builtin_convertvector(v1, h2));
 }
 
-// 8 Q4_K weights (one A fragment) from two quant dwords: their low (hi =
+// 8 Q4_K weights (one weight fragment) from two quant dwords: their low (hi =
 // false) or high nibbles; dsc512 = d*sc*2^9, ndm = -dmin*m.
 __device__ __forceinline__ h8 q4k_frag(uint32_t w0, uint32_t w1, bool hi, float dsc512, float ndm) {
   const uint32_t b0 = (hi ? w0 >> 4 : w0) & 0x0f0f0f0fu;
@@ -240,7 +240,7 @@ __device__ __forceinline__ void raw_load_q6(rsrc_t wr, uint32_t roff, int bi, in
 }
 __device__ __forceinline__ const Q6Fields& q6_fields(const RawQ6& r) { return r; }
 
-// A fragment of K step s (0..3) of chunk cc (0..3 within the block).
+// Weight fragment of K step s (0..3) of chunk cc (0..3 within the block).
 // sv: Q4_K (d*sc*2^9 and -dmin*m of the chunk's even and odd sub-block);
 // Q6_K (d*sc of the lane's two sub-blocks of the chunk).
 __device__ __forceinline__ h8 a_frag_q4(const RawQ4& r, int s, const float (&sv)[4]) {
@@ -287,9 +287,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 //  * every chunk has one barrier, before its last K step, after which the
 //    next chunk's x buffer and (at a block boundary) the next scale table are
 //    visible; the last step's MFMAs then overlap the next chunk's first
-//    dequant and B-fragment reads, so no chunk starts with an exposed
+//    dequant and x-fragment reads, so no chunk starts with an exposed
 //    prologue;
-//  * within a step, the B fragments of the next step are requested first and
+//  * within a step, the x fragments of the next step are requested first and
 //    the next step's dequant (VALU) is interleaved with this step's MFMAs.
 // The scale table holds one super-block: per weight row, decoded by one
 // thread, from a header loaded a block ahead; each lane copies its rows'
@@ -362,7 +362,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xd + (NW * i + wave) * 1024),
                                                16, xoff[i], (uint32_t)(128 * ck), 0, 0);
   };
-  // B-fragment offsets of row li (j-block 0) in an x buffer for the 4 K
+  // x-fragment offsets of row li (j-block 0) in an x buffer for the 4 K
   // steps: 16-byte chunk 4*(s/2) + 2*g + (s%2), swizzled by the row (rows of
   // other j-blocks differ by multiples of 32: same swizzle).
   uint32_t boff[4];
@@ -380,7 +380,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
     boffh[s] = boff[s] + 65536u;
     asm volatile("" : "+v"(boffh[s]));
   }
-  // B fragment of K step s, j-block jb, from x buffer j
+  // x fragment of K step s, j-block jb, from x buffer j
   auto bread = [&](int j, int s, int jb) -> h8 {
     const uint8_t* const p = j >= 2 ? xb[j] + (boffh[s] - 65536u) : xb[j] + boff[s];
     return *(const h8*)(p + jb * 32 * 128);
@@ -455,7 +455,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& P, int m_tile, int n_t
       for (int k = 0; k < va; ++k) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
   };
-  // NW = 8 (one i-block per wave): each B fragment feeds exactly one MFMA, so
+  // NW = 8 (one i-block per wave): each x fragment feeds exactly one MFMA, so
   // its next-step read follows that MFMA into the same registers (no second
   // set of fragments); the order per MFMA: the MFMA, its fragment's read,
   // the step's share of VMEM loads, va VALU instructions.
