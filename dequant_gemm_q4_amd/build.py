@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdmq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["dequant.hip", "gemv.hip", "gemm.hip", "skinny.hip", "rmsnorm.hip", "attention.hip", "workspace.cpp", "layer.cpp", "dmq_api.cpp"]
+SOURCES = ["dequant.hip", "gemv.hip", "gemm.hip", "plan.cpp", "skinny.hip", "rmsnorm.hip", "attention.hip", "workspace.cpp", "layer.cpp", "dmq_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting v_pk_{add,mul,fma}_f32.
