@@ -333,16 +333,22 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
     acc += part_dot(g, part, xp);
     if (PAIR) accu += part_dot(up, part, xp);
   };
+  // the next block's loads go out at raised wave priority, so that the other
+  // waves' dequant on this SIMD does not hold back the memory requests
   for (int b = b0; b < b1; b += 2) {
     if (b + 1 < b1) {
+      __builtin_amdgcn_s_setprio(2);
       load_part(wg_ + (int64_t)(b + 1) * BLOCK_BYTES, part, g1);
       if (PAIR) load_part(wu_ + (int64_t)(b + 1) * BLOCK_BYTES, part, u1p);
+      __builtin_amdgcn_s_setprio(0);
     }
     step(b, g0, u0p);
     if (b + 1 < b1) {
       if (b + 2 < b1) {
+        __builtin_amdgcn_s_setprio(2);
         load_part(wg_ + (int64_t)(b + 2) * BLOCK_BYTES, part, g0);
         if (PAIR) load_part(wu_ + (int64_t)(b + 2) * BLOCK_BYTES, part, u0p);
+        __builtin_amdgcn_s_setprio(0);
       }
       step(b + 1, g1, u1p);
     }
