@@ -14,16 +14,18 @@
 //    through LDS in wave order (no atomics, the same result every run);
 //  * every byte of W is read exactly once; Q6_K blocks (210 bytes, so a
 //    field may start 2 mod 4) are read with 2-byte-aligned 16-byte loads;
-//  * each weight is dequantised exactly: the quant goes to fp32 exactly
-//    (Q4_K: a nibble read as an fp8 E4M3 pattern is q * 2^-9, converted two
-//    per v_cvt_pk_f32_fp8; Q6_K: fp16 magic numbers), one fp32 FMA of exact
-//    operands gives q*d*sc - dmin*m rounded once to fp32, and
-//    v_cvt_pk_f16_f32 rounds pairs to fp16; the
-//    fp16 pairs meet x in v_dot2_f32_f16 with fp32 accumulation.  Factoring
-//    the sub-block scale and min out of the sum would be cheaper, but when
-//    d*sc*q and dmin*m nearly cancel its fp32 rounding error is not bounded
-//    by sum |x*w|.  Q6_K has no min, so there the scale is factored out of
-//    each 16-weight dot;
+//  * the sub-block scale and min are factored out of the dot products, so a
+//    weight costs a byte permute, a mask, a packed fp16 subtract and half a
+//    v_dot2_f32_f16.  Q4_K: per 32-weight sub-block with a = d*sc and
+//    b = dmin*m, sum x (a q - b) = a * sum x (q - c) - (b - a c) * sum x,
+//    where c is the integer in [0, 15] nearest b / a.  q - c is exact in
+//    fp16, and centring on c keeps every term's size within a small multiple
+//    of |a q - b| (|b - a c| <= a / 2 unless c is clamped, and then no
+//    weight changes sign), so the fp32 rounding error stays a few units of
+//    2^-24 times sum |x*w| even where the weights cancel to exact zeros.
+//    The sums of x per sub-block are formed once, as x is staged.  Q6_K has
+//    no min: its scale is factored out of each 16-weight dot, with the
+//    quants as fp16 magic numbers minus 1056 (exact);
 //  * SwiGLU pairs (gate row r and up row r + N/2 in the same lane) live in
 //    their own kernel instance: they need twice the registers.
 //
@@ -56,6 +58,7 @@ struct GemvDesc {
 struct GemvArgs {
   GemvDesc d[GEMV_MAX_GROUP];
   int32_t count;
+  int32_t sx_offset;   // byte offset of the sums of x per 32 values in dynamic LDS
 };
 
 // x in LDS: each group of 64 values (128 bytes) is followed by 16 bytes of
@@ -63,7 +66,8 @@ struct GemvArgs {
 // time; Q4_K parts are one group apart, which unpadded would put parts 0 and
 // 2 (and 1 and 3) on the same banks, and padded puts all four on distinct
 // ones.  (Q6_K parts 1 and 2 still share banks; a layout without that
-// conflict measured no faster.)
+// conflict measured no faster.)  After the whole row's x come the fp32 sums
+// of x over each run of 32 values (Q4_K sub-blocks), K / 32 floats.
 constexpr int X_GROUP_BYTES = 144;
 
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -112,21 +116,31 @@ __device__ __forceinline__ void load_part(const uint8_t* blk, int p, PartQ6& r) 
 }
 
 // Dot product of one Q4_K part (64 weights) with x (LDS; xs = x of this part:
-// xs[0..31] for sub-block 2p, xs[32..63] for sub-block 2p+1).
-__device__ __forceinline__ float part_dot(const PartQ4& r, int p, const half_t* xs) {
+// xs[0..31] for sub-block 2p, xs[32..63] for sub-block 2p+1; sx = the sums of
+// those two runs of x), factored per sub-block around c = round(b / a).
+__device__ __forceinline__ float part_dot(const PartQ4& r, int p, const half_t* xs, const float* sx) {
   Q4kScales s = unpack_q4k_scales(r.hdr.y, r.hdr.z, r.hdr.w);
   const uint32_t scw = p < 2 ? s.sc_lo : s.sc_hi;
   const uint32_t mw = p < 2 ? s.m_lo : s.m_hi;
   const uint32_t sh = (uint32_t)(p & 1) * 16u;
   const float d = half_bits_to_float(r.hdr.x);
   const float dmin = half_bits_to_float(r.hdr.x >> 16);
-  // nibbles go to fp32 as q * 2^-9 (fp8 E4M3 patterns 0..15, two per
-  // instruction), so the scales carry 2^9: q*2^-9 * d*sc*2^9 is exactly
-  // q*d*sc and the FMA rounds once, as with an integer q
-  const float dsc0 = d * (float)((scw >> sh) & 0xffu) * 512.0f;
-  const float dsc1 = d * (float)((scw >> (sh + 8)) & 0xffu) * 512.0f;
-  const float ndm0 = -(dmin * (float)((mw >> sh) & 0xffu));
-  const float ndm1 = -(dmin * (float)((mw >> (sh + 8)) & 0xffu));
+  // a = d*sc and b = dmin*m are exact in fp32 (11-bit times 6-bit)
+  const float a0 = d * (float)((scw >> sh) & 0xffu);
+  const float a1 = d * (float)((scw >> (sh + 8)) & 0xffu);
+  const float b0 = dmin * (float)((mw >> sh) & 0xffu);
+  const float b1 = dmin * (float)((mw >> (sh + 8)) & 0xffu);
+  // c in [0, 15]; a = 0 gives b * inf (or NaN when b = 0 too), which the
+  // clamp turns into 15 (or 0): any c is correct, it only sizes the terms
+  const float c0 = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(b0 * __builtin_amdgcn_rcpf(a0)), 0.0f), 15.0f);
+  const float c1 = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(b1 * __builtin_amdgcn_rcpf(a1)), 0.0f), 15.0f);
+  const float e0 = __builtin_fmaf(-a0, c0, b0);   // b - a c (exact where it matters)
+  const float e1 = __builtin_fmaf(-a1, c1, b1);
+  // a quant byte B goes to fp16 as [0x64, B]: masked to the low nibble that
+  // is 1024 + q, to the high nibble 1024 + 16 q; subtracting 1024 + c (or
+  // 1024 + 16 c) leaves q - c (or 16 (q - c)) exactly
+  const half_t n0 = (half_t)(-1024.0f - c0), n1 = (half_t)(-1024.0f - 16.0f * c1);
+  const h2 bias0 = {n0, n0}, bias1 = {n1, n1};
   const uint32_t qw[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
   const uint4* xv = (const uint4*)xs;
   float acc0 = 0.0f, acc1 = 0.0f;
@@ -139,21 +153,24 @@ __device__ __forceinline__ float part_dot(const PartQ4& r, int p, const half_t* 
     const uint32_t xb_w[4] = {xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int lo = (int)(qw[i + u] & 0x0f0f0f0fu);
-      const int hi = (int)((qw[i + u] >> 4) & 0x0f0f0f0fu);
-      const f2 ql01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), ql23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-      const f2 qh01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), qh23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-      const h2 wl01 = pack_h2(__builtin_fmaf(ql01.x, dsc0, ndm0), __builtin_fmaf(ql01.y, dsc0, ndm0));
-      const h2 wl23 = pack_h2(__builtin_fmaf(ql23.x, dsc0, ndm0), __builtin_fmaf(ql23.y, dsc0, ndm0));
-      const h2 wh01 = pack_h2(__builtin_fmaf(qh01.x, dsc1, ndm1), __builtin_fmaf(qh01.y, dsc1, ndm1));
-      const h2 wh23 = pack_h2(__builtin_fmaf(qh23.x, dsc1, ndm1), __builtin_fmaf(qh23.y, dsc1, ndm1));
-      acc0 = __builtin_amdgcn_fdot2(wl01, as_h2(xa_w[2 * u]), acc0, false);
-      acc0 = __builtin_amdgcn_fdot2(wl23, as_h2(xa_w[2 * u + 1]), acc0, false);
-      acc1 = __builtin_amdgcn_fdot2(wh01, as_h2(xb_w[2 * u]), acc1, false);
-      acc1 = __builtin_amdgcn_fdot2(wh23, as_h2(xb_w[2 * u + 1]), acc1, false);
+      // bytes [0x64, B1, 0x64, B0] and [0x64, B3, 0x64, B2] of the quant word
+      const uint32_t p01 = __builtin_amdgcn_perm(0x64646464u, qw[i + u], 0x04010400u);
+      const uint32_t p23 = __builtin_amdgcn_perm(0x64646464u, qw[i + u], 0x04030402u);
+      const h2 l01 = as_h2(p01 & 0xff0fff0fu) + bias0;
+      const h2 l23 = as_h2(p23 & 0xff0fff0fu) + bias0;
+      const h2 h01 = as_h2(p01 & 0xfff0fff0u) + bias1;
+      const h2 h23 = as_h2(p23 & 0xfff0fff0u) + bias1;
+      acc0 = __builtin_amdgcn_fdot2(l01, as_h2(xa_w[2 * u]), acc0, false);
+      acc0 = __builtin_amdgcn_fdot2(l23, as_h2(xa_w[2 * u + 1]), acc0, false);
+      acc1 = __builtin_amdgcn_fdot2(h01, as_h2(xb_w[2 * u]), acc1, false);
+      acc1 = __builtin_amdgcn_fdot2(h23, as_h2(xb_w[2 * u + 1]), acc1, false);
     }
   }
-  return acc0 + acc1;
+  const float2 sxp = *(const float2*)sx;
+  float y = a0 * acc0;
+  y = __builtin_fmaf(-e0, sxp.x, y);
+  y = __builtin_fmaf(a1 * 0.0625f, acc1, y);
+  return __builtin_fmaf(-e1, sxp.y, y);
 }
 
 // Dot product of one Q6_K part (64 weights) with x (LDS, padded layout; xs =
@@ -205,6 +222,19 @@ __device__ __forceinline__ int part_x_offset(int b, int part) {
 // super-blocks of the same 16 rows.
 constexpr int GEMV_ROWS = 16;
 
+// Sum of x over 32 values (chunk i holds values 8i .. 8i+7 as staged): each
+// lane adds its chunk's 8 values in a fixed order, the 4 lanes of a quad
+// (chunks 4j .. 4j+3, which every caller keeps active together) add theirs,
+// and the quad's first lane stores the sum of run j.
+__device__ __forceinline__ void put_xsum(float* sxs, int i, uint4 v) {
+  const h2 v0 = as_h2(v.x), v1 = as_h2(v.y), v2 = as_h2(v.z), v3 = as_h2(v.w);
+  float t = (((float)v0.x + (float)v0.y) + ((float)v1.x + (float)v1.y)) +
+            (((float)v2.x + (float)v2.y) + ((float)v3.x + (float)v3.y));
+  t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0xb1, 0xf, 0xf, false));
+  t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x4e, 0xf, 0xf, false));
+  if ((threadIdx.x & 3) == 0) sxs[i >> 2] = t;
+}
+
 // 1 / sqrt(mean((a + b)^2) + eps) over a row of K fp32 values: the sum a + b
 // rounded to fp32 first, as the residual connection stores it.
 __device__ __forceinline__ float rms_inv_sum(const float* a, const float* b, int K, float eps, float* red4) {
@@ -222,7 +252,8 @@ __device__ __forceinline__ float rms_inv_sum(const float* a, const float* b, int
 }
 
 template <int FMT, bool PAIR>
-__device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_t* xs, float* red, float* red4) {
+__device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_t* xs, float* sxs, float* red,
+                                          float* red4) {
   typedef typename PartOf<FMT>::T Part;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
   const int lane = threadIdx.x & 63;
@@ -289,6 +320,7 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
       if (P.xn && wg_local == 0) ((uint4*)P.xn)[i] = v;
     }
     *(uint4*)((uint8_t*)xs + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v;
+    if (FMT == 0) put_xsum(sxs, i, v);
   };
   if (!res) {
     if (xa) xput(b0 * 32 + lane, xra);
@@ -321,6 +353,7 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
       const uint4 v = make_uint4(as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3));
       if (P.xn && wg_local == 0) ((uint4*)P.xn)[i] = v;
       *(uint4*)((uint8_t*)xs + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v;
+      if (FMT == 0) put_xsum(sxs, i, v);
     }
   }
   // only this wave reads its slice: wait for its own LDS writes, no barrier
@@ -330,8 +363,13 @@ __device__ __forceinline__ void gemv_tile(const GemvDesc& P, int wg_local, half_
   float acc = 0.0f, accu = 0.0f;
   auto step = [&](int b, const Part& g, const Part& up) {
     const half_t* xp = (const half_t*)((const uint8_t*)xs + part_x_offset<FMT>(b, part));
-    acc += part_dot(g, part, xp);
-    if (PAIR) accu += part_dot(up, part, xp);
+    if constexpr (FMT == 0) {
+      const float* sp = sxs + 8 * b + 2 * part;   // sub-blocks 2p, 2p+1 of block b
+      acc += part_dot(g, part, xp, sp);
+      if (PAIR) accu += part_dot(up, part, xp, sp);
+    } else {
+      acc += part_dot(g, part, xp);
+    }
   };
   // the next block's loads go out at raised wave priority, so that the other
   // waves' dequant on this SIMD does not hold back the memory requests
@@ -395,13 +433,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs args) {
     if (i < args.count && (int)blockIdx.x >= args.d[i].wg_begin) pi = i;
   const GemvDesc& P = args.d[pi];
   const int wg_local = (int)blockIdx.x - P.wg_begin;
+  float* sxs = (float*)((uint8_t*)xs + args.sx_offset);
   if (P.fmt == 0) {
     if (PAIRS && P.swiglu)
-      gemv_tile<0, PAIRS>(P, wg_local, xs, red, red4);
+      gemv_tile<0, PAIRS>(P, wg_local, xs, sxs, red, red4);
     else
-      gemv_tile<0, false>(P, wg_local, xs, red, red4);
+      gemv_tile<0, false>(P, wg_local, xs, sxs, red, red4);
   } else {
-    gemv_tile<1, false>(P, wg_local, xs, red, red4);
+    gemv_tile<1, false>(P, wg_local, xs, sxs, red, red4);
   }
 }
 
@@ -443,7 +482,8 @@ static hipError_t launch_gemv_impl(const GemmProblem* probs, int count, const fl
       kmax = p.K > kmax ? p.K : kmax;
     }
     a.count = n;
-    const size_t xbytes = (size_t)(kmax / 64) * X_GROUP_BYTES;
+    a.sx_offset = (kmax / 64) * X_GROUP_BYTES;   // a multiple of 16
+    const size_t xbytes = (size_t)a.sx_offset + (size_t)(kmax / 32) * sizeof(float);
     if (pairs)
       hipLaunchKernelGGL(gemv_kernel<true>, dim3(wgs), dim3(256), xbytes, s, a);
     else

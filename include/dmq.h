@@ -110,7 +110,11 @@ int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* 
  * into pieces whose fp32 partial sums a second kernel adds in piece order
  * (workspace: see above).  Every path gives the same bits on every run.
  * Per output, |y - y_exact| stays within 1e-3 * sum_k |x[m][k] * w[n][k]|
- * + 1e-5 (w the fp16-rounded weight).
+ * + 1e-5 (w the fp16-rounded weight).  The MFMA kernels multiply by the
+ * fp16-rounded weights themselves; the M = 1 kernel factors each 32-weight
+ * sub-block's scale and min out of the sum (centred so that cancelling
+ * weights stay within the bound), so its y can differ from theirs in the
+ * last bits.
  */
 int dmq_gemm_q4k(const void* x_f16, const void* wq, float* y,
                  int64_t M, int64_t N, int64_t K, void* stream);
