@@ -114,7 +114,9 @@ int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* 
  * fp16-rounded weights themselves; the M = 1 kernel factors each 32-weight
  * sub-block's scale and min out of the sum (centred so that cancelling
  * weights stay within the bound), so its y can differ from theirs in the
- * last bits.
+ * last bits.  With an infinite x the M = 1 result can be NaN where the
+ * product with the fp16 weights is +-inf (a zero scale or a zero centred
+ * min still multiplies the infinite sum of x).
  */
 int dmq_gemm_q4k(const void* x_f16, const void* wq, float* y,
                  int64_t M, int64_t N, int64_t K, void* stream);
