@@ -19,6 +19,7 @@ import pytest
 
 import oracle
 import synthetic
+from _centring import centring_blocks
 from _packing import f16_bits, pack_q4k, pack_q6k
 
 torch = pytest.importorskip("torch")
@@ -233,64 +234,15 @@ def test_gemm_adversarial_cancellation(dmq):
         assert_within(y, ref, s, f"cancellation M={m_rows}")
 
 
-def _centring_blocks(rng, n_blocks, all_zero_rows=()):
-    """Q4_K blocks whose sub-blocks hit every case of the decode kernel's
-    factored dot product, sum x (a q - b) = a sum x (q - c) - (b - a c) sum x
-    with a = d*sc, b = dmin*m and c = round(b / a) clamped to [0, 15]:
-    sc = 0 (with and without a min), m = 0, b / a on and next to half
-    integers, b / a above 15 (c clamped), weights cancelling to exact zeros,
-    and random fields.  Blocks listed in all_zero_rows hold only zeros."""
-    d_choices = [f16_bits(0.01), f16_bits(0.5), f16_bits(2.0 ** -20), f16_bits(3.0e-3)]
-    blocks = []
-    for bi in range(n_blocks):
-        d = int(rng.choice(d_choices))
-        dmin = d if rng.random() < 0.6 else int(rng.choice(d_choices))
-        sc, mn, q = [], [], []
-        for j in range(8):
-            case = (bi * 8 + j) % 9 if bi not in all_zero_rows else 5
-            qj = rng.integers(0, 16, 32)
-            if case == 0:      # a = 0, b > 0: every weight is -b
-                s, m = 0, int(rng.integers(1, 64))
-            elif case == 1:    # a = b = 0
-                s, m = 0, 0
-            elif case == 2:    # b = 0: c = 0
-                s, m = int(rng.integers(1, 64)), 0
-            elif case == 3:    # b / a = k + 1/2 when dmin = d (a tie for c)
-                s, m = 2, 2 * int(rng.integers(0, 15)) + 1
-            elif case == 4:    # b / a > 15: c clamped to 15
-                s, m = 1, int(rng.integers(16, 64))
-            elif case == 5:    # q = c and b = a c: exact zeros when dmin = d
-                q0 = int(rng.integers(0, 16))
-                s = int(rng.integers(1, 4))
-                m = s * q0
-                qj = np.full(32, q0)
-            elif case == 6:    # b / a just above 15 (15.25)
-                s, m = 4, 61
-            elif case == 7:    # half the quants on c, the rest random
-                q0 = int(rng.integers(0, 16))
-                s = int(rng.integers(1, 4))
-                m = s * q0
-                qj = np.where(rng.random(32) < 0.5, q0, qj)
-            else:              # random fields
-                s, m = int(rng.integers(0, 64)), int(rng.integers(0, 64))
-            sc.append(s)
-            mn.append(m)
-            q.extend(int(v) for v in qj)
-        if bi in all_zero_rows:
-            dmin = d
-        blocks.append(pack_q4k(d, dmin, sc, mn, q))
-    return np.stack(blocks)
-
-
 def test_gemv_q4k_centring_cases(dmq):
     """The decode kernel's factored Q4_K dot product on the sub-block cases
-    that size its terms (see _centring_blocks), at M = 1, every output, and
+    that size its terms (tests/_centring.py), at M = 1, every output, and
     as the SwiGLU gate|up pair of a decode FFN.  Row 0 holds only exact
     zeros: its bound is the 1e-5 floor, and the kernel gives exactly 0."""
     rng = np.random.default_rng(17)
     N, K = 96, 2048
     nb = K // 256
-    wq = _centring_blocks(rng, N * nb, all_zero_rows=set(range(nb))).reshape(-1)
+    wq = centring_blocks(rng, N * nb, all_zero_blocks=set(range(nb))).reshape(-1)
     for seed, sigma in ((18, 1.0), (19, 1.0 / 64)):
         x = synthetic.activations(1, K, seed=seed, sigma=sigma)
         y = gpu_gemm(dmq, "q4k", x, wq, 1, N, K)
@@ -300,7 +252,7 @@ def test_gemv_q4k_centring_cases(dmq):
     # such blocks as the gate|up pair of a decode FFN (gate row r and up row
     # r + F in one lane), D = K, F = 256, then a random Q6_K down projection
     D, F = K, 256
-    wgu = _centring_blocks(rng, 2 * F * nb)
+    wgu = centring_blocks(rng, 2 * F * nb)
     wd = synthetic.q6k_blocks(D, F, seed=21)
     x = synthetic.activations(1, D, seed=20, sigma=1.0 / 16)
     h, y = run_ffn(dmq, x, wgu, wd, 1, D, F)
