@@ -243,11 +243,15 @@ def test_gemv_q4k_centring_cases(dmq):
     N, K = 96, 2048
     nb = K // 256
     wq = centring_blocks(rng, N * nb, all_zero_blocks=set(range(nb))).reshape(-1)
-    for seed, sigma in ((18, 1.0), (19, 1.0 / 64)):
-        x = synthetic.activations(1, K, seed=seed, sigma=sigma)
+    spiky = np.random.default_rng(22).standard_normal(K)
+    spiky[::32] = np.sign(spiky[::32]) * 1800.0   # a large x opening every sub-block
+    xs = [("sigma=1", synthetic.activations(1, K, seed=18, sigma=1.0)),
+          ("sigma=1/64", synthetic.activations(1, K, seed=19, sigma=1.0 / 64)),
+          ("spiky", spiky.astype(np.float16).reshape(1, K))]
+    for what, x in xs:
         y = gpu_gemm(dmq, "q4k", x, wq, 1, N, K)
         ref, s = oracle.gemm_quant("q4k", x, wq, N, K)
-        assert_within(y, ref, s, f"centring cases sigma={sigma}")
+        assert_within(y, ref, s, f"centring cases, x {what}")
         assert y[0, 0] == 0.0
     # such blocks as the gate|up pair of a decode FFN (gate row r and up row
     # r + F in one lane), D = K, F = 256, then a random Q6_K down projection
