@@ -14,10 +14,11 @@
 //    through LDS in wave order (no atomics, the same result every run);
 //  * every byte of W is read exactly once; Q6_K blocks (210 bytes, so a
 //    field may start 2 mod 4) are read with 2-byte-aligned 16-byte loads;
-//  * the sub-block scale and min are factored out of the dot products, so a
-//    weight costs a byte permute, a mask, a packed fp16 subtract and half a
-//    v_dot2_f32_f16.  Q4_K: per 32-weight sub-block with a = d*sc and
-//    b = dmin*m, sum x (a q - b) = a * sum x (q - c) - (b - a c) * sum x,
+//  * the sub-block scale and min are factored out of the dot products, so
+//    four weights cost one byte permute, two masks, two packed fp16
+//    subtracts and two v_dot2_f32_f16.  Q4_K: per 32-weight sub-block with
+//    a = d*sc and b = dmin*m,
+//    sum x (a q - b) = a * sum x (q - c) - (b - a c) * sum x,
 //    where c is the integer in [0, 15] nearest b / a.  q - c is exact in
 //    fp16, and centring on c keeps every term's size within a small multiple
 //    of |a q - b| (|b - a c| <= a / 2 unless c is clamped, and then no
