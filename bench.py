@@ -916,8 +916,21 @@ def main():
         # replays of the 8 rotating layers, each replay between its own events
         g_per = time_graph(torch, dmq.dmq_gemm_group, dgroups, 20, per_replay=True)
         g_ms = float(np.median(g_per))
+        # the cost of a launch itself: a one-wave kernel (torch's spin kernel,
+        # one cycle) launched back to back on the same stream, no events
+        # between the launches; every decode launch carries this much
+        for _ in range(50):
+            torch.cuda._sleep(1)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(dsteps):
+            torch.cuda._sleep(1)
+        f1.record()
+        f1.synchronize()
+        floor_us = 1e3 * f0.elapsed_time(f1) / dsteps
         out["decode"] = {"workload": "M=1, one layer's 7 projections in one grouped launch, 8 rotating layers",
                          "us_per_layer": round(1e3 * d_total / dsteps, 2),
+                         "launch_floor_us": round(floor_us, 2),
                          "GB/s": round(wb / (d_total / dsteps / 1e3) / 1e9, 1),
                          "kernel_GB/s": round(wb / (d_ms / 1e3) / 1e9, 1),
                          "kernel_ms": stats(d_per),
