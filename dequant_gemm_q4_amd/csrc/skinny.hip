@@ -11,12 +11,18 @@
 //  * a workgroup owns 16 consecutive weight rows; its waves split the row's
 //    super-blocks into contiguous slices, and a lane works on row l%16 and
 //    part l/16 of every super-block of its wave's slice.  A single
-//    projection takes one wave per super-block (up to 16; deeper rows 8
-//    waves with four blocks each in flight), so every load of the
-//    workgroup is issued before the first multiply and the matrix streams
-//    in about one memory round trip instead of one per block; a grid of at
-//    least two workgroups per CU (several projections in one launch) keeps
-//    4-wave workgroups with two blocks in flight;
+//    projection takes one wave per super-block (up to 16), so every load of
+//    the workgroup is issued before the first multiply and the matrix
+//    streams in about one memory round trip instead of one per block; a
+//    grid of at least two workgroups per CU (several projections in one
+//    launch) takes 4-wave workgroups that walk their slices block by block,
+//    four workgroups per CU; deeper rows of a single projection take 8
+//    waves with four blocks each in flight;
+//  * x goes through LDS (the first two shapes): a wave copies a block's x,
+//    16 rows x 512 bytes, with 8 direct-to-LDS loads that each cover two
+//    whole rows, i.e. full 128-byte lines.  Loaded straight into the B
+//    operand, each load would instead touch half of 16 lines (16 rows x 64
+//    bytes), and the x loads would cost the L1 twice the lookups;
 //  * v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16 and k-slots
 //    8*(l/16) .. +7; B: column l%16, the same k-slots; D: column l%16, rows
 //    4*(l/16) .. +3) takes 8 dequantised weights per lane as the A operand
@@ -28,9 +34,8 @@
 //    and MFMA step s takes the low (s < 4) or high nibbles of its bytes
 //    8(s%4) .. +7; Q6_K part p is half p/2, 16-weight column p%2 of each
 //    32-weight quarter, and step s covers quarter s/2, weights 8(s%2) .. +7;
-//  * the next block's quant bytes and x fragments are loaded while the
-//    current block is computed; the waves' partial sums are added in wave
-//    order through LDS (the same result every run).
+//  * the waves' partial sums are added in wave order through LDS (the same
+//    result every run).
 //
 // Dequant is exact as in the other kernels: Q4_K nibbles reach fp32 as fp8
 // E4M3 patterns (q * 2^-9, scale carrying 2^9), Q6_K quants through
@@ -42,6 +47,13 @@
 namespace dmq {
 
 constexpr int SKINNY_MAX_GROUP = 8;
+
+// Buffer resource over [base, base + bytes): loads past the end read zeros.
+typedef __amdgpu_buffer_rsrc_t sk_rsrc_t;
+__device__ __forceinline__ sk_rsrc_t sk_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)n, 0x00020000);
+}
 constexpr int SKINNY_ROWS = 16;
 constexpr int SKINNY_MAX_WAVES = 16;
 
@@ -228,6 +240,33 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
     }
   };
 
+  if constexpr (D == 1 && NT == 1) {
+    // block by block: the block's quant bytes into registers and its x (16
+    // rows x 512 bytes) into the wave's LDS slot with 8 direct-to-LDS loads
+    // of 2 whole rows each; row r's 16-byte chunk c lands at slot c ^ r, so
+    // the 8 lanes of one fragment read (rows r .. r+7, one chunk) hit
+    // distinct banks.  Rows past M read as zero (the buffer's range).
+    uint8_t* const xsl = (uint8_t*)red + nw * 1024 + wave * 8192;
+    const sk_rsrc_t xrs = sk_rsrc(P.x, (int64_t)M * K * 2);
+    for (int b = b0; b < b1; ++b) {
+      Part w0;
+      asm volatile("" ::: "memory");   // the slot's previous reads stay above
+      sk_load(wrow + (int64_t)b * BLOCK_BYTES, p, w0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 2 * i + (lane >> 5), j = lane & 31;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(xsl + i * 1024), 16,
+                                                 (uint32_t)(r * K * 2 + b * 512 + 16 * (j ^ r)), 0, 0, 0);
+      }
+      // only this wave reads its slot: its own loads landing is enough
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint4 xf[1][8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        xf[0][s] = *(const uint4*)(xsl + (rl >> 1) * 1024 + (rl & 1) * 512 + 16 * ((4 * s + p) ^ rl));
+      compute(w0, xf);
+    }
+  } else {
   // the first D blocks' loads are all issued before the first multiply; each
   // computed block's registers then take the block D further on
   Part w[D];
@@ -249,6 +288,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
         }
       }
     }
+  }
   }
 
   // D: lane l holds activation row l%16 (+16g) and weight rows 4(l/16) .. +3
@@ -277,12 +317,14 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   }
 }
 
-// D = 1: up to 16 waves (one block each); D = 2: 4 waves, two blocks in
-// flight each (few registers: several workgroups per CU); D = 4: 8 waves
-// with up to four blocks each in flight (256 registers per lane).
+// D = 1: x through LDS, a block at a time (up to 16 waves of one block
+// each, or 4 waves walking their slices); D = 4: 8 waves with up to four
+// blocks each in flight, x straight into registers (256 registers per lane).
 template <int NT, int D>
-__global__ __launch_bounds__(D == 1 ? 1024 : D == 2 ? 256 : 512) void skinny_kernel(SkinnyArgs args) {
-  extern __shared__ __align__(16) float red[];   // [waves][NT][16][16]
+__global__ __launch_bounds__(D == 1 ? 1024 : 512) void skinny_kernel(SkinnyArgs args) {
+  // [waves][NT][16][16] floats for the partial sums, then (D = 1) one 8 KB
+  // x slot per wave
+  extern __shared__ __align__(16) float red[];
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < SKINNY_MAX_GROUP; ++i)
@@ -329,15 +371,16 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
     a.count = n;
     if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
     // A grid of at least two workgroups per CU keeps every CU busy with
-    // several small workgroups (4 waves, two blocks in flight each).  A
-    // smaller grid (one projection) issues as many loads as it can at once:
-    // one wave per block up to 16 blocks per row (K <= 4096); deeper rows 8
-    // waves with four blocks each in flight (K <= 8192: all of them).
+    // several small workgroups (4 waves walking their slices a block at a
+    // time, 36 KB of LDS: four per CU).  A smaller grid (one projection)
+    // issues as many loads as it can at once: one wave per block up to 16
+    // blocks per row (K <= 4096, up to 144 KB of LDS); deeper rows 8 waves
+    // with four blocks each in flight (K <= 8192: all of them).
+    constexpr size_t WAVE_LDS = 256 * sizeof(float) + 8192;   // partial sums + x slot
     if (wgs >= 2 * device_cu_count()) {
-      hipLaunchKernelGGL((skinny_kernel<1, 2>), dim3(wgs), dim3(256), (size_t)4 * 256 * sizeof(float), s, a);
+      hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(256), 4 * WAVE_LDS, s, a);
     } else if (nbmax <= SKINNY_MAX_WAVES) {
-      hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(64 * nbmax), (size_t)nbmax * 256 * sizeof(float), s,
-                         a);
+      hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(64 * nbmax), (size_t)nbmax * WAVE_LDS, s, a);
     } else {
       hipLaunchKernelGGL((skinny_kernel<1, 4>), dim3(wgs), dim3(64 * 8), (size_t)8 * 256 * sizeof(float), s, a);
     }

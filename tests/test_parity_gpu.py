@@ -522,15 +522,19 @@ def test_concurrent_host_threads_same_bits(dmq):
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 @pytest.mark.parametrize("M,N,K", [(2, 16, 256), (16, 40, 256), (12, 20, 768), (5, 37, 4864), (9, 33, 512),
-                                   (16, 3072, 3072), (16, 48, 8192), (7, 50, 9984), (17, 100, 1280), (32, 257, 768)])
+                                   (16, 3072, 3072), (16, 48, 8192), (7, 50, 9984), (17, 100, 1280), (32, 257, 768),
+                                   (5, 8195, 1280), (3, 8200, 256)])
 def test_gemm_small_m_every_output(dmq, fmt, M, N, K):
-    """M <= 16 runs the small-M kernel (16 weight rows per workgroup, one wave
-    per K block up to 16, else 8 waves with several blocks each, the rows'
-    products on 16x16x32 MFMAs): every output, ragged N, workgroups of 1, 2
-    and 3 waves with all 16 activation rows live (fewer threads than
-    outputs), uneven wave slices (19 and 39 blocks over 8 waves), and the
-    same bits on a second call.  M = 17 and 32, just past it, run the tiled
-    kernel."""
+    """M <= 16 runs the small-M kernel (16 weight rows per workgroup, the
+    rows' products on 16x16x32 MFMAs): every output and the same bits on a
+    second call.  Shapes: one wave per K block up to 16 (x through LDS),
+    workgroups of 1, 2 and 3 waves with all 16 activation rows live (fewer
+    threads than outputs); 8 waves with several blocks each in flight
+    (uneven slices: 19 and 39 blocks over 8 waves); grids of at least two
+    workgroups per CU (N = 8195, 8200: 4 waves walking their slices block by
+    block, x through LDS, with rows past M read as zero, a ragged last
+    workgroup, and waves without blocks at K = 256).  M = 17 and 32, just
+    past it, run the tiled kernel."""
     x = synthetic.activations(M, K, seed=M * 11 + N)
     wq = synthetic.weight_blocks(fmt, N, K, seed=N * 13 + K + M)
     xd, wd = dev(x), dev(wq.reshape(-1))
