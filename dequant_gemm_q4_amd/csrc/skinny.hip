@@ -15,14 +15,13 @@
 //    the workgroup is issued before the first multiply and the matrix
 //    streams in about one memory round trip instead of one per block; a
 //    grid of at least two workgroups per CU (several projections in one
-//    launch) takes 4-wave workgroups that walk their slices block by block,
-//    four workgroups per CU; deeper rows of a single projection take 8
-//    waves with four blocks each in flight;
-//  * x goes through LDS (the first two shapes): a wave copies a block's x,
-//    16 rows x 512 bytes, with 8 direct-to-LDS loads that each cover two
-//    whole rows, i.e. full 128-byte lines.  Loaded straight into the B
-//    operand, each load would instead touch half of 16 lines (16 rows x 64
-//    bytes), and the x loads would cost the L1 twice the lookups;
+//    launch) takes 4-wave workgroups, four per CU; deeper rows of a single
+//    projection take 16 waves.  Each wave walks its slice a block at a time;
+//  * x goes through LDS: a wave copies a block's x, 16 rows x 512 bytes,
+//    with 8 direct-to-LDS loads that each cover two whole rows, i.e. full
+//    128-byte lines.  Loaded straight into the B operand, each load would
+//    instead touch half of 16 lines (16 rows x 64 bytes), and the x loads
+//    would cost the L1 twice the lookups;
 //  * v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16 and k-slots
 //    8*(l/16) .. +7; B: column l%16, the same k-slots; D: column l%16, rows
 //    4*(l/16) .. +3) takes 8 dequantised weights per lane as the A operand
@@ -187,8 +186,9 @@ __device__ __forceinline__ h8 sk_frag(const SkQ6& r, const SkScales& sc, int s, 
   return (h8){w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
 }
 
-// D: blocks in flight per wave (a ring of D register sets).
-template <int FMT, int NT, int D>
+// One workgroup: 16 weight rows of one problem; wave w takes super-blocks
+// [w nb / nw, (w+1) nb / nw) of them, a block at a time.
+template <int FMT>
 __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, float* red) {
   typedef typename SkPart<FMT>::T Part;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
@@ -203,127 +203,66 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   const int nw = (int)(blockDim.x >> 6);                 // waves of the workgroup
   const int b0 = wave * nb / nw, b1 = (wave + 1) * nb / nw;
   const uint8_t* wrow = P.wq + (int64_t)row * row_bytes;
-  // x rows of this lane's B operand: rl (group 0) and rl + 16 (group 1)
-  const half_t* xr[NT];
-  bool xv[NT];
-#pragma unroll
-  for (int g = 0; g < NT; ++g) {
-    xv[g] = rl + 16 * g < M;
-    xr[g] = P.x + (int64_t)(xv[g] ? rl + 16 * g : 0) * K;
-  }
-  int kofs[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) kofs[s] = sk_kofs(p, s);
 
-  // x fragments of one super-block: activation row rl (+16g) if it exists,
-  // else zeros; the 8 x values of each MFMA step (16 bytes at k offset kofs)
-  auto load_x = [&](int b, uint4 (&xf)[NT][8]) {
-#pragma unroll
-    for (int g = 0; g < NT; ++g)
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        xf[g][s] = xv[g] ? *(const uint4*)(xr[g] + b * QK + kofs[s]) : make_uint4(0, 0, 0, 0);
-  };
-
-  f4 acc[NT];
-#pragma unroll
-  for (int g = 0; g < NT; ++g) acc[g] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto compute = [&](const Part& w, const uint4 (&xf)[NT][8]) {
+  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // 8 MFMA steps of one block: the lane's dequantised weights (A) against
+  // the 8 x values of activation row rl at the step's k-slots (B)
+  auto compute = [&](const Part& w, const uint4 (&xf)[8]) {
     const SkScales sc = sk_scales(w, p);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const h8 a = sk_frag(w, sc, s, p);
-#pragma unroll
-      for (int g = 0; g < NT; ++g)
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, xf[g][s]), acc[g], 0, 0, 0);
-    }
+    for (int s = 0; s < 8; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sk_frag(w, sc, s, p), __builtin_bit_cast(h8, xf[s]), acc, 0, 0, 0);
   };
 
-  if constexpr (D == 1 && NT == 1) {
-    // block by block: the block's quant bytes into registers and its x (16
-    // rows x 512 bytes) into the wave's LDS slot with 8 direct-to-LDS loads
-    // of 2 whole rows each; row r's 16-byte chunk c lands at slot c ^ r, so
-    // the 8 lanes of one fragment read (rows r .. r+7, one chunk) hit
-    // distinct banks.  Rows past M read as zero (the buffer's range).
-    uint8_t* const xsl = (uint8_t*)red + nw * 1024 + wave * 8192;
-    const sk_rsrc_t xrs = sk_rsrc(P.x, (int64_t)M * K * 2);
-    for (int b = b0; b < b1; ++b) {
-      Part w0;
-      asm volatile("" ::: "memory");   // the slot's previous reads stay above
-      sk_load(wrow + (int64_t)b * BLOCK_BYTES, p, w0);
+  // block by block: the block's quant bytes into registers and its x (16
+  // rows x 512 bytes) into the wave's LDS slot with 8 direct-to-LDS loads
+  // of 2 whole rows each; row r's 16-byte chunk c lands at slot c ^ r, so
+  // the 8 lanes of one fragment read (rows r .. r+7, one chunk) hit
+  // distinct banks.  Rows past M read as zero (the buffer's range).
+  uint8_t* const xsl = (uint8_t*)red + nw * 1024 + wave * 8192;
+  const sk_rsrc_t xrs = sk_rsrc(P.x, (int64_t)M * K * 2);
+  for (int b = b0; b < b1; ++b) {
+    Part w;
+    asm volatile("" ::: "memory");   // the slot's previous reads stay above
+    sk_load(wrow + (int64_t)b * BLOCK_BYTES, p, w);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 2 * i + (lane >> 5), j = lane & 31;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(xsl + i * 1024), 16,
-                                                 (uint32_t)(r * K * 2 + b * 512 + 16 * (j ^ r)), 0, 0, 0);
-      }
-      // only this wave reads its slot: its own loads landing is enough
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      uint4 xf[1][8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        xf[0][s] = *(const uint4*)(xsl + (rl >> 1) * 1024 + (rl & 1) * 512 + 16 * ((4 * s + p) ^ rl));
-      compute(w0, xf);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i + (lane >> 5), j = lane & 31;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(xsl + i * 1024), 16,
+                                               (uint32_t)(r * K * 2 + b * 512 + 16 * (j ^ r)), 0, 0, 0);
     }
-  } else {
-  // the first D blocks' loads are all issued before the first multiply; each
-  // computed block's registers then take the block D further on
-  Part w[D];
-  uint4 xb[D][NT][8];
+    // only this wave reads its slot: its own loads landing is enough
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint4 xf[8];
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (b0 + i < b1) {
-      sk_load(wrow + (int64_t)(b0 + i) * BLOCK_BYTES, p, w[i]);
-      load_x(b0 + i, xb[i]);
-    }
-  for (int b = b0; b < b1; b += D) {
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      if (b + i < b1) {
-        compute(w[i], xb[i]);
-        if (b + i + D < b1) {
-          sk_load(wrow + (int64_t)(b + i + D) * BLOCK_BYTES, p, w[i]);
-          load_x(b + i + D, xb[i]);
-        }
-      }
-    }
-  }
+    for (int s = 0; s < 8; ++s)
+      xf[s] = *(const uint4*)(xsl + (rl >> 1) * 1024 + (rl & 1) * 512 + 16 * ((sk_kofs(p, s) / 8) ^ rl));
+    compute(w, xf);
   }
 
-  // D: lane l holds activation row l%16 (+16g) and weight rows 4(l/16) .. +3
-  // of the tile.  LDS: red[wave][g][activation row m][weight row n], the
-  // four 4-float chunks of row m permuted by chunk ^ red_swz(m) so that the
+  // D: lane l holds activation row l%16 and weight rows 4(l/16) .. +3 of
+  // the tile.  LDS: red[wave][activation row m][weight row n], the four
+  // 4-float chunks of row m permuted by chunk ^ red_swz(m) so that the
   // lanes' 16-byte stores (16 rows, one chunk each) and the 4-byte loads of
   // 64 consecutive outputs both hit distinct banks.
   const auto red_swz = [](int m) { return ((m >> 1) ^ (m >> 3)) & 3; };
-#pragma unroll
-  for (int g = 0; g < NT; ++g)
-    ((f4*)red)[((wave * NT + g) * 16 + rl) * 4 + (p ^ red_swz(rl))] = acc[g];
+  ((f4*)red)[(wave * 16 + rl) * 4 + (p ^ red_swz(rl))] = acc;
   __syncthreads();
   // output t = (activation row m, weight row n) of the 16 x 16 tile:
   // consecutive t write consecutive n; the waves' sums in wave order.  A
   // workgroup may have fewer than 256 threads (one wave per block).
   for (int t = (int)threadIdx.x; t < 256; t += (int)blockDim.x) {
-#pragma unroll
-    for (int g = 0; g < NT; ++g) {
-      const int ml = t >> 4, nl = t & 15;
-      const int m = ml + 16 * g, n = n0 + nl;
-      const int col = ((((nl >> 2) ^ red_swz(ml)) << 2) | (nl & 3));
-      float v = red[((0 * NT + g) * 16 + ml) * 16 + col];
-      for (int w = 1; w < nw; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + col];
-      if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
-    }
+    const int m = t >> 4, nl = t & 15, n = n0 + nl;
+    const int col = ((((nl >> 2) ^ red_swz(m)) << 2) | (nl & 3));
+    float v = red[m * 16 + col];
+    for (int w = 1; w < nw; ++w) v += red[(w * 16 + m) * 16 + col];
+    if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
   }
 }
 
-// D = 1: x through LDS, a block at a time (up to 16 waves of one block
-// each, or 4 waves walking their slices); D = 4: 8 waves with up to four
-// blocks each in flight, x straight into registers (256 registers per lane).
-template <int NT, int D>
-__global__ __launch_bounds__(D == 1 ? 1024 : 512) void skinny_kernel(SkinnyArgs args) {
-  // [waves][NT][16][16] floats for the partial sums, then (D = 1) one 8 KB
-  // x slot per wave
+// Up to 16 waves; the dynamic LDS holds, per wave, 16 x 16 partial sums
+// (1 KB) and then an 8 KB x slot.
+__global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs args) {
   extern __shared__ __align__(16) float red[];
   int pi = 0;
 #pragma unroll
@@ -332,9 +271,9 @@ __global__ __launch_bounds__(D == 1 ? 1024 : 512) void skinny_kernel(SkinnyArgs 
   const SkinnyDesc& P = args.d[pi];
   const int wg_local = (int)blockIdx.x - P.wg_begin;
   if (P.fmt == 0)
-    skinny_tile<0, NT, D>(P, wg_local, red);
+    skinny_tile<0>(P, wg_local, red);
   else
-    skinny_tile<1, NT, D>(P, wg_local, red);
+    skinny_tile<1>(P, wg_local, red);
 }
 
 // One workgroup per 16 weight rows, one wave per super-block of the deepest
@@ -371,19 +310,13 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
     a.count = n;
     if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
     // A grid of at least two workgroups per CU keeps every CU busy with
-    // several small workgroups (4 waves walking their slices a block at a
-    // time, 36 KB of LDS: four per CU).  A smaller grid (one projection)
-    // issues as many loads as it can at once: one wave per block up to 16
-    // blocks per row (K <= 4096, up to 144 KB of LDS); deeper rows 8 waves
-    // with four blocks each in flight (K <= 8192: all of them).
+    // several small workgroups (4 waves, 36 KB of LDS: four per CU).  A
+    // smaller grid (one projection) takes one wave per block up to 16, so
+    // that all its loads are issued before the first multiply; deeper rows
+    // 16 waves, each walking its slice (up to 144 KB of LDS).
     constexpr size_t WAVE_LDS = 256 * sizeof(float) + 8192;   // partial sums + x slot
-    if (wgs >= 2 * device_cu_count()) {
-      hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(256), 4 * WAVE_LDS, s, a);
-    } else if (nbmax <= SKINNY_MAX_WAVES) {
-      hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(wgs), dim3(64 * nbmax), (size_t)nbmax * WAVE_LDS, s, a);
-    } else {
-      hipLaunchKernelGGL((skinny_kernel<1, 4>), dim3(wgs), dim3(64 * 8), (size_t)8 * 256 * sizeof(float), s, a);
-    }
+    const int waves = wgs >= 2 * device_cu_count() ? 4 : (nbmax < SKINNY_MAX_WAVES ? nbmax : SKINNY_MAX_WAVES);
+    hipLaunchKernelGGL(skinny_kernel, dim3(wgs), dim3(64 * waves), (size_t)waves * WAVE_LDS, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

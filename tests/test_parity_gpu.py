@@ -527,14 +527,14 @@ def test_concurrent_host_threads_same_bits(dmq):
 def test_gemm_small_m_every_output(dmq, fmt, M, N, K):
     """M <= 16 runs the small-M kernel (16 weight rows per workgroup, the
     rows' products on 16x16x32 MFMAs): every output and the same bits on a
-    second call.  Shapes: one wave per K block up to 16 (x through LDS),
-    workgroups of 1, 2 and 3 waves with all 16 activation rows live (fewer
-    threads than outputs); 8 waves with several blocks each in flight
-    (uneven slices: 19 and 39 blocks over 8 waves); grids of at least two
-    workgroups per CU (N = 8195, 8200: 4 waves walking their slices block by
-    block, x through LDS, with rows past M read as zero, a ragged last
-    workgroup, and waves without blocks at K = 256).  M = 17 and 32, just
-    past it, run the tiled kernel."""
+    second call.  Shapes: one wave per K block up to 16, workgroups of 1, 2
+    and 3 waves with all 16 activation rows live (fewer threads than
+    outputs); 16 waves walking several blocks each (uneven slices: 19, 32
+    and 39 blocks over 16 waves); grids of at least two
+    workgroups per CU (N = 8195, 8200: 4 waves, with rows past M read as
+    zero, a ragged last workgroup, and waves without blocks at K = 256).  x
+    goes through LDS in every shape.  M = 17 and 32, just past it, run the
+    tiled kernel."""
     x = synthetic.activations(M, K, seed=M * 11 + N)
     wq = synthetic.weight_blocks(fmt, N, K, seed=N * 13 + K + M)
     xd, wd = dev(x), dev(wq.reshape(-1))
