@@ -126,7 +126,7 @@ int run_gemm(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t 
   if (decode) return hip_status(dmq::launch_gemv(probs, count, s));
   bool skinny = true;
   for (int i = 0; i < count; ++i)
-    if (probs[i].swiglu || probs[i].M > kSkinnyMaxM) skinny = false;
+    if (probs[i].M > kSkinnyMaxM) skinny = false;
   return hip_status(skinny ? dmq::launch_skinny(probs, count, s) : dmq::launch_gemm(probs, count, s));
 }
 

@@ -34,7 +34,9 @@
 //    8(s%4) .. +7; Q6_K part p is half p/2, 16-weight column p%2 of each
 //    32-weight quarter, and step s covers quarter s/2, weights 8(s%2) .. +7;
 //  * the waves' partial sums are added in wave order through LDS (the same
-//    result every run).
+//    result every run);
+//  * SwiGLU gate|up pairs: a workgroup takes 8 gate rows and the matching 8
+//    up rows, and forms h = fp16(silu(g) * u) from the two sums.
 //
 // Dequant is exact as in the other kernels: Q4_K nibbles reach fp32 as fp8
 // E4M3 patterns (q * 2^-9, scale carrying 2^9), Q6_K quants through
@@ -59,8 +61,8 @@ constexpr int SKINNY_MAX_WAVES = 16;
 struct SkinnyDesc {
   const half_t* x;
   const uint8_t* wq;
-  float* y;
-  int32_t fmt, M, N, K;
+  void* out;             // y [M, N] fp32, or h [M, N/2] fp16 in SwiGLU mode
+  int32_t fmt, swiglu, M, N, K;
   int32_t wg_begin;
 };
 
@@ -186,8 +188,11 @@ __device__ __forceinline__ h8 sk_frag(const SkQ6& r, const SkScales& sc, int s, 
   return (h8){w01.x, w01.y, w23.x, w23.y, w45.x, w45.y, w67.x, w67.y};
 }
 
-// One workgroup: 16 weight rows of one problem; wave w takes super-blocks
-// [w nb / nw, (w+1) nb / nw) of them, a block at a time.
+__device__ __forceinline__ float sk_silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// One workgroup: 16 weight rows of one problem (SwiGLU: 8 gate rows and the
+// matching 8 up rows); wave w takes super-blocks [w nb / nw, (w+1) nb / nw)
+// of them, a block at a time.
 template <int FMT>
 __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, float* red) {
   typedef typename SkPart<FMT>::T Part;
@@ -198,8 +203,12 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   const int M = P.M, N = P.N, K = P.K;
   const int nb = K / QK;
   const int64_t row_bytes = (int64_t)nb * BLOCK_BYTES;
-  const int n0 = wg_local * SKINNY_ROWS;
-  const int row = n0 + rl < N ? n0 + rl : N - 1;        // ragged tail: clamp, result dropped
+  // local row rl: row n0 + rl; SwiGLU: gate row n0 + rl%8 for rl < 8, the
+  // up row F + n0 + rl%8 after it (ragged tails clamped, results dropped)
+  const int F = N / 2;
+  const int n0 = wg_local * (P.swiglu ? SKINNY_ROWS / 2 : SKINNY_ROWS);
+  const int row = P.swiglu ? (n0 + (rl & 7) < F ? n0 + (rl & 7) : F - 1) + (rl >> 3) * F
+                           : (n0 + rl < N ? n0 + rl : N - 1);
   const int nw = (int)(blockDim.x >> 6);                 // waves of the workgroup
   const int b0 = wave * nb / nw, b1 = (wave + 1) * nb / nw;
   const uint8_t* wrow = P.wq + (int64_t)row * row_bytes;
@@ -248,15 +257,28 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   const auto red_swz = [](int m) { return ((m >> 1) ^ (m >> 3)) & 3; };
   ((f4*)red)[(wave * 16 + rl) * 4 + (p ^ red_swz(rl))] = acc;
   __syncthreads();
-  // output t = (activation row m, weight row n) of the 16 x 16 tile:
-  // consecutive t write consecutive n; the waves' sums in wave order.  A
-  // workgroup may have fewer than 256 threads (one wave per block).
-  for (int t = (int)threadIdx.x; t < 256; t += (int)blockDim.x) {
-    const int m = t >> 4, nl = t & 15, n = n0 + nl;
+  // the waves' sums of local row nl for activation row m, in wave order
+  auto total = [&](int m, int nl) {
     const int col = ((((nl >> 2) ^ red_swz(m)) << 2) | (nl & 3));
     float v = red[m * 16 + col];
     for (int w = 1; w < nw; ++w) v += red[(w * 16 + m) * 16 + col];
-    if (m < M && n < N) P.y[(int64_t)m * N + n] = v;
+    return v;
+  };
+  // output t = (activation row m, weight row n) of the 16 x 16 tile:
+  // consecutive t write consecutive n.  A workgroup may have fewer than 256
+  // threads (one wave per block).  SwiGLU: h[m][n0 + j] = silu(g) * u from
+  // local rows j and j + 8, rounded once to fp16.
+  if (P.swiglu) {
+    for (int t = (int)threadIdx.x; t < 128; t += (int)blockDim.x) {
+      const int m = t >> 3, j = t & 7;
+      if (m < M && n0 + j < F)
+        ((half_t*)P.out)[(int64_t)m * F + n0 + j] = (half_t)(sk_silu(total(m, j)) * total(m, j + 8));
+    }
+  } else {
+    for (int t = (int)threadIdx.x; t < 256; t += (int)blockDim.x) {
+      const int m = t >> 4, nl = t & 15, n = n0 + nl;
+      if (m < M && n < N) ((float*)P.out)[(int64_t)m * N + n] = total(m, nl);
+    }
   }
 }
 
@@ -299,13 +321,14 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
       SkinnyDesc& d = a.d[i];
       d.x = (const half_t*)p.x;
       d.wq = p.wq;
-      d.y = (float*)p.out;
+      d.out = p.out;
       d.fmt = p.fmt;
+      d.swiglu = p.swiglu;
       d.M = p.M;
       d.N = p.N;
       d.K = p.K;
       d.wg_begin = wgs;
-      wgs += (p.N + SKINNY_ROWS - 1) / SKINNY_ROWS;
+      wgs += p.swiglu ? (p.N / 2 + SKINNY_ROWS / 2 - 1) / (SKINNY_ROWS / 2) : (p.N + SKINNY_ROWS - 1) / SKINNY_ROWS;
     }
     a.count = n;
     if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel

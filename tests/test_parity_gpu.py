@@ -649,8 +649,16 @@ def test_ffn_decode_m1(dmq):
     check_ffn(x, wgu, wd, h, y, D, F, np.array([0]), "ffn decode M=1")
 
 
-@pytest.mark.parametrize("M,D,F", [(2, 256, 512), (40, 512, 768), (300, 768, 256), (1, 512, 1024)])
+@pytest.mark.parametrize("M,D,F", [(2, 256, 512), (40, 512, 768), (300, 768, 256), (1, 512, 1024), (16, 3072, 8192),
+                                   (7, 1280, 768)])
 def test_ffn_small_every_output(dmq, M, D, F):
+    """The FFN chain on every output.  M = 2, 7 and 16 run the gate|up pair
+    in the small-M kernel's SwiGLU mode (8 gate and 8 up rows per
+    workgroup): at 3072 -> 2 x 8192 (the Llama-3.2-3B shape) a grid of 1024
+    4-wave workgroups, at 1280 -> 2 x 768 one wave per block; the down
+    projection then takes 16 waves walking 2 blocks each (K = 8192) or one
+    wave per block.  M = 1 runs the decode kernel's pairs, M = 40 and 300
+    the tiled kernel."""
     wgu = synthetic.q4k_blocks(2 * F, D, seed=M + D)
     wd = synthetic.q6k_blocks(D, F, seed=M + F)
     x = synthetic.activations(M, D, seed=M * 3, sigma=0.25)
