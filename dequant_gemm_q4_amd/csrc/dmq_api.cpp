@@ -114,19 +114,28 @@ int hip_status(hipError_t e) { return e == hipSuccess ? DMQ_OK : DMQ_ERR_HIP; }
 // The decode kernel stages x in LDS; it takes K up to this size.
 constexpr int64_t kGemvMaxK = 32768;
 
-// Largest M the small-M kernel takes (one 16-row MFMA column group).  At
-// M = 32 the tiled kernel with split-K measured faster (one layer: 45 vs
-// 63 us); at M = 16 the small-M kernel (40 vs 43 us; one 3072x3072 Q4_K
-// projection: 7.8 vs 14.5 us).
+// The small-M kernel takes M <= 16 always (one 16-row MFMA column group).
+// At M = 17 .. 32 (two groups) it takes launches with a SwiGLU gate|up pair
+// and launches of fewer than two of its workgroups per CU: the FFN 3072 ->
+// 8192 -> 3072 runs in 36 us there against 49-50 us on the tiled kernel,
+// while one layer's seven projections (1,728 workgroups) run faster tiled
+// (37.5-38.3 against 40.9-41.4 us).
 constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyWideMaxM = 32;
 
 int run_gemm(const dmq::GemmProblem* probs, int count, bool decode, hipStream_t s) {
   int dc = check_device();
   if (dc != DMQ_OK) return dc;
   if (decode) return hip_status(dmq::launch_gemv(probs, count, s));
-  bool skinny = true;
-  for (int i = 0; i < count; ++i)
-    if (probs[i].M > kSkinnyMaxM) skinny = false;
+  int64_t mmax = 0, wgs = 0;   // wgs: the small-M kernel's workgroups (16 weight rows each)
+  bool swiglu = false;
+  for (int i = 0; i < count; ++i) {
+    mmax = probs[i].M > mmax ? probs[i].M : mmax;
+    swiglu = swiglu || probs[i].swiglu;
+    wgs += (probs[i].N + 15) / 16;
+  }
+  const bool skinny = mmax <= kSkinnyMaxM ||
+                      (mmax <= kSkinnyWideMaxM && (swiglu || wgs < 2 * (int64_t)dmq::device_cu_count()));
   return hip_status(skinny ? dmq::launch_skinny(probs, count, s) : dmq::launch_gemm(probs, count, s));
 }
 

@@ -193,7 +193,8 @@ __device__ __forceinline__ float sk_silu(float g) { return g * __builtin_amdgcn_
 // One workgroup: 16 weight rows of one problem (SwiGLU: 8 gate rows and the
 // matching 8 up rows); wave w takes super-blocks [w nb / nw, (w+1) nb / nw)
 // of them, a block at a time.
-template <int FMT>
+// NT: 16-row groups of activation rows (M <= 16 NT).
+template <int FMT, int NT>
 __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, float* red) {
   typedef typename SkPart<FMT>::T Part;
   constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
@@ -213,39 +214,50 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   const int b0 = wave * nb / nw, b1 = (wave + 1) * nb / nw;
   const uint8_t* wrow = P.wq + (int64_t)row * row_bytes;
 
-  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  f4 acc[NT];
+#pragma unroll
+  for (int g = 0; g < NT; ++g) acc[g] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
   // 8 MFMA steps of one block: the lane's dequantised weights (A) against
-  // the 8 x values of activation row rl at the step's k-slots (B)
-  auto compute = [&](const Part& w, const uint4 (&xf)[8]) {
+  // the 8 x values of activation row rl + 16 g at the step's k-slots (B)
+  auto compute = [&](const Part& w, const uint4 (&xf)[NT][8]) {
     const SkScales sc = sk_scales(w, p);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sk_frag(w, sc, s, p), __builtin_bit_cast(h8, xf[s]), acc, 0, 0, 0);
+    for (int s = 0; s < 8; ++s) {
+      const h8 a = sk_frag(w, sc, s, p);
+#pragma unroll
+      for (int g = 0; g < NT; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, xf[g][s]), acc[g], 0, 0, 0);
+    }
   };
 
-  // block by block: the block's quant bytes into registers and its x (16
-  // rows x 512 bytes) into the wave's LDS slot with 8 direct-to-LDS loads
-  // of 2 whole rows each; row r's 16-byte chunk c lands at slot c ^ r, so
-  // the 8 lanes of one fragment read (rows r .. r+7, one chunk) hit
-  // distinct banks.  Rows past M read as zero (the buffer's range).
-  uint8_t* const xsl = (uint8_t*)red + nw * 1024 + wave * 8192;
+  // block by block: the block's quant bytes into registers and its x (16 NT
+  // rows x 512 bytes) into the wave's LDS slot with 8 NT direct-to-LDS
+  // loads of 2 whole rows each; row r's 16-byte chunk c lands at slot
+  // c ^ r, so the 8 lanes of one fragment read (rows r .. r+7 of one group,
+  // one chunk) hit distinct banks.  Rows past M read as zero (the buffer's
+  // range).
+  uint8_t* const xsl = (uint8_t*)red + nw * NT * 1024 + wave * NT * 8192;
   const sk_rsrc_t xrs = sk_rsrc(P.x, (int64_t)M * K * 2);
   for (int b = b0; b < b1; ++b) {
     Part w;
     asm volatile("" ::: "memory");   // the slot's previous reads stay above
     sk_load(wrow + (int64_t)b * BLOCK_BYTES, p, w);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 * NT; ++i) {
       const int r = 2 * i + (lane >> 5), j = lane & 31;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(xsl + i * 1024), 16,
                                                (uint32_t)(r * K * 2 + b * 512 + 16 * (j ^ r)), 0, 0, 0);
     }
     // only this wave reads its slot: its own loads landing is enough
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    uint4 xf[8];
+    uint4 xf[NT][8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      xf[s] = *(const uint4*)(xsl + (rl >> 1) * 1024 + (rl & 1) * 512 + 16 * ((sk_kofs(p, s) / 8) ^ rl));
+    for (int g = 0; g < NT; ++g) {
+      const int r = rl + 16 * g;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        xf[g][s] = *(const uint4*)(xsl + (r >> 1) * 1024 + (r & 1) * 512 + 16 * ((sk_kofs(p, s) / 8) ^ r));
+    }
     compute(w, xf);
   }
 
@@ -255,13 +267,15 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   // lanes' 16-byte stores (16 rows, one chunk each) and the 4-byte loads of
   // 64 consecutive outputs both hit distinct banks.
   const auto red_swz = [](int m) { return ((m >> 1) ^ (m >> 3)) & 3; };
-  ((f4*)red)[(wave * 16 + rl) * 4 + (p ^ red_swz(rl))] = acc;
+#pragma unroll
+  for (int g = 0; g < NT; ++g) ((f4*)red)[((wave * NT + g) * 16 + rl) * 4 + (p ^ red_swz(rl))] = acc[g];
   __syncthreads();
   // the waves' sums of local row nl for activation row m, in wave order
   auto total = [&](int m, int nl) {
-    const int col = ((((nl >> 2) ^ red_swz(m)) << 2) | (nl & 3));
-    float v = red[m * 16 + col];
-    for (int w = 1; w < nw; ++w) v += red[(w * 16 + m) * 16 + col];
+    const int g = m >> 4, ml = m & 15;
+    const int col = ((((nl >> 2) ^ red_swz(ml)) << 2) | (nl & 3));
+    float v = red[(g * 16 + ml) * 16 + col];
+    for (int w = 1; w < nw; ++w) v += red[((w * NT + g) * 16 + ml) * 16 + col];
     return v;
   };
   // output t = (activation row m, weight row n) of the 16 x 16 tile:
@@ -269,21 +283,22 @@ __device__ __forceinline__ void skinny_tile(const SkinnyDesc& P, int wg_local, f
   // threads (one wave per block).  SwiGLU: h[m][n0 + j] = silu(g) * u from
   // local rows j and j + 8, rounded once to fp16.
   if (P.swiglu) {
-    for (int t = (int)threadIdx.x; t < 128; t += (int)blockDim.x) {
+    for (int t = (int)threadIdx.x; t < 128 * NT; t += (int)blockDim.x) {
       const int m = t >> 3, j = t & 7;
       if (m < M && n0 + j < F)
         ((half_t*)P.out)[(int64_t)m * F + n0 + j] = (half_t)(sk_silu(total(m, j)) * total(m, j + 8));
     }
   } else {
-    for (int t = (int)threadIdx.x; t < 256; t += (int)blockDim.x) {
+    for (int t = (int)threadIdx.x; t < 256 * NT; t += (int)blockDim.x) {
       const int m = t >> 4, nl = t & 15, n = n0 + nl;
       if (m < M && n < N) ((float*)P.out)[(int64_t)m * N + n] = total(m, nl);
     }
   }
 }
 
-// Up to 16 waves; the dynamic LDS holds, per wave, 16 x 16 partial sums
-// (1 KB) and then an 8 KB x slot.
+// Up to 16 waves; the dynamic LDS holds, per wave, NT 16 x 16 partial sums
+// (NT KB) and then an 8 NT KB x slot.
+template <int NT>
 __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs args) {
   extern __shared__ __align__(16) float red[];
   int pi = 0;
@@ -293,9 +308,9 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs args) {
   const SkinnyDesc& P = args.d[pi];
   const int wg_local = (int)blockIdx.x - P.wg_begin;
   if (P.fmt == 0)
-    skinny_tile<0>(P, wg_local, red);
+    skinny_tile<0, NT>(P, wg_local, red);
   else
-    skinny_tile<1>(P, wg_local, red);
+    skinny_tile<1, NT>(P, wg_local, red);
 }
 
 // One workgroup per 16 weight rows, one wave per super-block of the deepest
@@ -331,15 +346,20 @@ hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s) {
       wgs += p.swiglu ? (p.N / 2 + SKINNY_ROWS / 2 - 1) / (SKINNY_ROWS / 2) : (p.N + SKINNY_ROWS - 1) / SKINNY_ROWS;
     }
     a.count = n;
-    if (mmax > 16) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
+    if (mmax > 32) return hipErrorInvalidValue;   // the caller routes larger M to the tiled kernel
     // A grid of at least two workgroups per CU keeps every CU busy with
     // several small workgroups (4 waves, 36 KB of LDS: four per CU).  A
     // smaller grid (one projection) takes one wave per block up to 16, so
     // that all its loads are issued before the first multiply; deeper rows
     // 16 waves, each walking its slice (up to 144 KB of LDS).
-    constexpr size_t WAVE_LDS = 256 * sizeof(float) + 8192;   // partial sums + x slot
-    const int waves = wgs >= 2 * device_cu_count() ? 4 : (nbmax < SKINNY_MAX_WAVES ? nbmax : SKINNY_MAX_WAVES);
-    hipLaunchKernelGGL(skinny_kernel, dim3(wgs), dim3(64 * waves), (size_t)waves * WAVE_LDS, s, a);
+    const int nt = mmax > 16 ? 2 : 1;   // 16-row groups of activation rows
+    const size_t wave_lds = (size_t)nt * (256 * sizeof(float) + 8192);   // partial sums + x slot
+    const int wmax = SKINNY_MAX_WAVES / nt;                            // at most 144 KB
+    const int waves = wgs >= 2 * device_cu_count() ? 4 : (nbmax < wmax ? nbmax : wmax);
+    if (nt == 1)
+      hipLaunchKernelGGL(skinny_kernel<1>, dim3(wgs), dim3(64 * waves), waves * wave_lds, s, a);
+    else
+      hipLaunchKernelGGL(skinny_kernel<2>, dim3(wgs), dim3(64 * waves), waves * wave_lds, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -533,8 +533,9 @@ def test_gemm_small_m_every_output(dmq, fmt, M, N, K):
     and 39 blocks over 16 waves); grids of at least two
     workgroups per CU (N = 8195, 8200: 4 waves, with rows past M read as
     zero, a ragged last workgroup, and waves without blocks at K = 256).  x
-    goes through LDS in every shape.  M = 17 and 32, just past it, run the
-    tiled kernel."""
+    goes through LDS in every shape.  M = 17 and 32 (single projections,
+    fewer than two workgroups per CU) run it with two 16-row groups of
+    activation rows."""
     x = synthetic.activations(M, K, seed=M * 11 + N)
     wq = synthetic.weight_blocks(fmt, N, K, seed=N * 13 + K + M)
     xd, wd = dev(x), dev(wq.reshape(-1))
@@ -650,15 +651,17 @@ def test_ffn_decode_m1(dmq):
 
 
 @pytest.mark.parametrize("M,D,F", [(2, 256, 512), (40, 512, 768), (300, 768, 256), (1, 512, 1024), (16, 3072, 8192),
-                                   (7, 1280, 768)])
+                                   (7, 1280, 768), (24, 3072, 8192)])
 def test_ffn_small_every_output(dmq, M, D, F):
     """The FFN chain on every output.  M = 2, 7 and 16 run the gate|up pair
     in the small-M kernel's SwiGLU mode (8 gate and 8 up rows per
     workgroup): at 3072 -> 2 x 8192 (the Llama-3.2-3B shape) a grid of 1024
     4-wave workgroups, at 1280 -> 2 x 768 one wave per block; the down
     projection then takes 16 waves walking 2 blocks each (K = 8192) or one
-    wave per block.  M = 1 runs the decode kernel's pairs, M = 40 and 300
-    the tiled kernel."""
+    wave per block.  M = 24 runs both stages on the small-M kernel with two
+    16-row groups of activation rows (4-wave workgroups for the pair, 8
+    waves for the down projection).  M = 1 runs the decode kernel's pairs,
+    M = 40 and 300 the tiled kernel."""
     wgu = synthetic.q4k_blocks(2 * F, D, seed=M + D)
     wd = synthetic.q6k_blocks(D, F, seed=M + F)
     x = synthetic.activations(M, D, seed=M * 3, sigma=0.25)
