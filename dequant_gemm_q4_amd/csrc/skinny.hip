@@ -1,4 +1,4 @@
-// Small-M kernel (2 <= M <= 16): y = x * W^T for a few activation rows.
+// Small-M kernel (2 <= M <= 32): y = x * W^T for a few activation rows.
 //
 // With a handful of rows the work is still a stream of the weights (each
 // weight is used M times, far below the MFMA ridge), so this kernel keeps
@@ -36,7 +36,9 @@
 //  * the waves' partial sums are added in wave order through LDS (the same
 //    result every run);
 //  * SwiGLU gate|up pairs: a workgroup takes 8 gate rows and the matching 8
-//    up rows, and forms h = fp16(silu(g) * u) from the two sums.
+//    up rows, and forms h = fp16(silu(g) * u) from the two sums;
+//  * 17 <= M <= 32: two 16-row groups of activation rows, each dequantised
+//    weight fragment feeding two MFMAs (16 KB x slots, at most 8 waves).
 //
 // Dequant is exact as in the other kernels: Q4_K nibbles reach fp32 as fp8
 // E4M3 patterns (q * 2^-9, scale carrying 2^9), Q6_K quants through
