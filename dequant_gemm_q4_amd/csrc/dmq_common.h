@@ -175,12 +175,16 @@ struct GemmProblem {
   void* xn;           // decode kernel, with g: if set, the normalized x (K fp16) is written here
 };
 
-// Decode kernel (M = 1): y[n] = sum_k x[k] w[n][k] for every problem.
+// Decode kernel: y[m][n] = sum_k x[m][k] w[n][k] for every problem, M = 1,
+// or M = 2 where gemv_rows_fit (then without the RMSNorm and residual
+// modes).
+constexpr int GEMV_MAX_ROWS = 2;
+bool gemv_rows_fit(int64_t m, int64_t kmax);
 hipError_t launch_gemv(const GemmProblem* probs, int count, hipStream_t s);
 // MFMA kernel (M >= 2).
 hipError_t launch_gemm(const GemmProblem* probs, int count, hipStream_t s);
-// Small-M MFMA kernel (M <= 16, no SwiGLU): the decode kernel's work split
-// with the rows' multiply-adds on v_mfma_f32_16x16x32_f16.
+// Small-M MFMA kernel (M <= 32): the decode kernel's work split with the
+// rows' multiply-adds on v_mfma_f32_16x16x32_f16.
 hipError_t launch_skinny(const GemmProblem* probs, int count, hipStream_t s);
 
 int device_cu_count();

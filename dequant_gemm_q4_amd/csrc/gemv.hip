@@ -42,6 +42,12 @@ namespace dmq {
 
 constexpr int GEMV_MAX_GROUP = 8;
 
+// Activation rows of one launch: 1, or 2 with both rows' x staged (at most
+// 96 KB of LDS, so K up to 20480 at two rows).
+bool gemv_rows_fit(int64_t m, int64_t kmax) {
+  return m >= 1 && m <= GEMV_MAX_ROWS && m * ((kmax / 64) * 144 + (kmax / 32) * 4) <= 96 * 1024;
+}
+
 struct GemvDesc {
   const half_t* x;
   const uint8_t* wq;
@@ -53,6 +59,7 @@ struct GemvDesc {
   const float* hadd;
   float* hout;        // ... and workgroup 0 writes that sum here (if set)
   int32_t fmt, swiglu, N, K;
+  int32_t m;          // activation rows (the few-rows kernel; 1 otherwise)
   int32_t wg_begin;   // first workgroup of this problem
 };
 
@@ -211,6 +218,112 @@ __device__ __forceinline__ float part_dot(const PartQ6& r, int p, const half_t* 
     acc = __builtin_fmaf(dsc, dt, acc);
   }
   return acc;
+}
+
+// The same dot products for NR activation rows at once: the quants are
+// converted once and meet each row's x (row r's staged x at xs + r * xrb
+// bytes, its sums of x at sx + r * srb floats).  Each row's arithmetic is
+// the single-row part_dot's, in the same order; the part's value is added
+// to tot[r].
+template <int NR>
+__device__ __forceinline__ void part_dot_nr(const PartQ4& r_, int p, const uint8_t* xs, int xrb, const float* sx, int srb,
+                                            float (&tot)[NR]) {
+  Q4kScales s = unpack_q4k_scales(r_.hdr.y, r_.hdr.z, r_.hdr.w);
+  const uint32_t scw = p < 2 ? s.sc_lo : s.sc_hi;
+  const uint32_t mw = p < 2 ? s.m_lo : s.m_hi;
+  const uint32_t sh = (uint32_t)(p & 1) * 16u;
+  const float d = half_bits_to_float(r_.hdr.x);
+  const float dmin = half_bits_to_float(r_.hdr.x >> 16);
+  const float a0 = d * (float)((scw >> sh) & 0xffu);
+  const float a1 = d * (float)((scw >> (sh + 8)) & 0xffu);
+  const float b0 = dmin * (float)((mw >> sh) & 0xffu);
+  const float b1 = dmin * (float)((mw >> (sh + 8)) & 0xffu);
+  const float c0 = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(b0 * __builtin_amdgcn_rcpf(a0)), 0.0f), 15.0f);
+  const float c1 = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(b1 * __builtin_amdgcn_rcpf(a1)), 0.0f), 15.0f);
+  const float e0 = __builtin_fmaf(-a0, c0, b0);
+  const float e1 = __builtin_fmaf(-a1, c1, b1);
+  const half_t n0 = (half_t)(-1024.0f - c0), n1 = (half_t)(-1024.0f - 16.0f * c1);
+  const h2 bias0 = {n0, n0}, bias1 = {n1, n1};
+  const uint32_t qw[8] = {r_.q0.x, r_.q0.y, r_.q0.z, r_.q0.w, r_.q1.x, r_.q1.y, r_.q1.z, r_.q1.w};
+  float acc0[NR], acc1[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc0[r] = acc1[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t p01 = __builtin_amdgcn_perm(0x64646464u, qw[i + u], 0x04010400u);
+      const uint32_t p23 = __builtin_amdgcn_perm(0x64646464u, qw[i + u], 0x04030402u);
+      const h2 l01 = as_h2(p01 & 0xff0fff0fu) + bias0;
+      const h2 l23 = as_h2(p23 & 0xff0fff0fu) + bias0;
+      const h2 h01 = as_h2(p01 & 0xfff0fff0u) + bias1;
+      const h2 h23 = as_h2(p23 & 0xfff0fff0u) + bias1;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint4* xv = (const uint4*)(xs + r * xrb);
+        const uint4 xa = xv[i >> 1];
+        const uint4 xb = xv[4 + (i >> 1)];
+        const uint32_t xa_w[4] = {xa.x, xa.y, xa.z, xa.w};
+        const uint32_t xb_w[4] = {xb.x, xb.y, xb.z, xb.w};
+        acc0[r] = __builtin_amdgcn_fdot2(l01, as_h2(xa_w[2 * u]), acc0[r], false);
+        acc0[r] = __builtin_amdgcn_fdot2(l23, as_h2(xa_w[2 * u + 1]), acc0[r], false);
+        acc1[r] = __builtin_amdgcn_fdot2(h01, as_h2(xb_w[2 * u]), acc1[r], false);
+        acc1[r] = __builtin_amdgcn_fdot2(h23, as_h2(xb_w[2 * u + 1]), acc1[r], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float2 sxp = *(const float2*)(sx + r * srb);
+    float y = a0 * acc0[r];
+    y = __builtin_fmaf(-e0, sxp.x, y);
+    y = __builtin_fmaf(a1 * 0.0625f, acc1[r], y);
+    tot[r] += __builtin_fmaf(-e1, sxp.y, y);
+  }
+}
+
+template <int NR>
+__device__ __forceinline__ void part_dot_nr(const PartQ6& r_, int p, const uint8_t* xs, int xrb, const float*, int,
+                                            float (&tot)[NR]) {
+  const int lh = p & 1;
+  const uint4 qa = r_.qa, qb = r_.qb, qh = r_.qh;
+  const float d = half_bits_to_float(r_.s206 >> 16);
+  const h2 k1056 = {(half_t)1056.0f, (half_t)1056.0f};
+  const uint32_t qaw[4] = {qa.x, qa.y, qa.z, qa.w};
+  const uint32_t qbw[4] = {qb.x, qb.y, qb.z, qb.w};
+  const uint32_t qhw[4] = {qh.x, qh.y, qh.z, qh.w};
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t sb = 2 * t + lh;
+    const int sc = (int)(int8_t)((((sb >> 2) ? r_.sc.y : r_.sc.x) >> (8 * (sb & 3))) & 0xffu);
+    const float dsc = d * (float)sc;
+    const uint32_t* ql = (t & 1) ? qbw : qaw;
+    const uint32_t nsh = (t >= 2) ? 4u : 0u;
+    const int xo = X_GROUP_BYTES * (t >> 1) + 64 * (t & 1);
+    float dt[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) dt[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t q = ((ql[i] >> nsh) & 0x0f0f0f0fu) | (((qhw[i] >> (2 * t)) & 0x03030303u) << 4);
+      const h2 q01 = as_h2(magic_pair_lo(q)) - k1056;
+      const h2 q23 = as_h2(magic_pair_hi(q)) - k1056;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint4 xq = *(const uint4*)(xs + r * xrb + xo + 16 * (i >> 1));
+        const uint32_t xw0 = (i & 1) ? xq.z : xq.x, xw1 = (i & 1) ? xq.w : xq.y;
+        dt[r] = __builtin_amdgcn_fdot2(q01, as_h2(xw0), dt[r], false);
+        dt[r] = __builtin_amdgcn_fdot2(q23, as_h2(xw1), dt[r], false);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = __builtin_fmaf(dsc, dt[r], acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) tot[r] += acc[r];
 }
 
 // byte offset of the x of a lane's part of block b
@@ -445,6 +558,131 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs args) {
   }
 }
 
+// Decode kernel for NR activation rows (M <= NR; launched with NR = 2 for
+// M = 2): the single-row kernel's shape and arithmetic, with the x of every
+// row staged (rows past M as zeros) and each part's quants converted once
+// for all rows.  Row r's result has the same bits as a single-row call on
+// row r.  No RMSNorm or residual modes.  LDS: NR rows of x (xrb bytes
+// each), then NR rows of sums (srb floats each).  A four-row form ran
+// slower than the small-M MFMA kernel at M = 3 and 4 (its SwiGLU pair
+// holds 230 VGPRs), so it is not built.
+template <int FMT, bool PAIR, int NR>
+__device__ __forceinline__ void gemv_tile_nr(const GemvDesc& P, int wg_local, int M, uint8_t* xl, int xrb, int srb,
+                                             float* red) {
+  typedef typename PartOf<FMT>::T Part;
+  constexpr int BLOCK_BYTES = FMT == 0 ? Q4K_BYTES : Q6K_BYTES;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int part = lane & 3, rq = lane >> 2;
+  const int nb = P.K / QK;
+  const int rows_out = PAIR ? P.N / 2 : P.N;
+  const int64_t row_bytes = (int64_t)nb * BLOCK_BYTES;
+  const int row = wg_local * GEMV_ROWS + rq;
+  const int rowc = row < rows_out ? row : rows_out - 1;   // ragged tail: clamp, result dropped
+  const int b0 = wave * nb / 4, b1 = (wave + 1) * nb / 4;
+  const uint8_t* wg_ = P.wq + (int64_t)rowc * row_bytes;
+  const uint8_t* wu_ = P.wq + (int64_t)(rowc + rows_out) * row_bytes;
+  float* const sxl = (float*)(xl + NR * xrb);
+
+  Part g0, u0p, g1, u1p;
+  if (b0 < b1) {
+    load_part(wg_ + (int64_t)b0 * BLOCK_BYTES, part, g0);
+    if (PAIR) load_part(wu_ + (int64_t)b0 * BLOCK_BYTES, part, u0p);
+  }
+  // this wave's slice of every row's x (each row's sums as in the
+  // single-row kernel); only this wave reads it
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    for (int i = b0 * 32 + lane; i < b1 * 32; i += 64) {
+      const uint4 v = r < M ? ((const uint4*)P.x)[(int64_t)r * (P.K / 8) + i] : make_uint4(0, 0, 0, 0);
+      *(uint4*)(xl + r * xrb + X_GROUP_BYTES * (i >> 3) + 16 * (i & 7)) = v;
+      if (FMT == 0) put_xsum(sxl + r * srb, i, v);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  float acc[NR], accu[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = accu[r] = 0.0f;
+  auto step = [&](int b, const Part& g, const Part& up) {
+    const uint8_t* xp = xl + part_x_offset<FMT>(b, part);
+    const float* sp = sxl + 8 * b + 2 * part;
+    part_dot_nr<NR>(g, part, xp, xrb, sp, srb, acc);
+    if (PAIR) part_dot_nr<NR>(up, part, xp, xrb, sp, srb, accu);
+  };
+  for (int b = b0; b < b1; b += 2) {
+    if (b + 1 < b1) {
+      __builtin_amdgcn_s_setprio(2);
+      load_part(wg_ + (int64_t)(b + 1) * BLOCK_BYTES, part, g1);
+      if (PAIR) load_part(wu_ + (int64_t)(b + 1) * BLOCK_BYTES, part, u1p);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    step(b, g0, u0p);
+    if (b + 1 < b1) {
+      if (b + 2 < b1) {
+        __builtin_amdgcn_s_setprio(2);
+        load_part(wg_ + (int64_t)(b + 2) * BLOCK_BYTES, part, g0);
+        if (PAIR) load_part(wu_ + (int64_t)(b + 2) * BLOCK_BYTES, part, u0p);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      step(b + 1, g1, u1p);
+    }
+  }
+
+  auto quad_sum = [](float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
+    return v;
+  };
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    acc[r] = quad_sum(acc[r]);
+    if (PAIR) accu[r] = quad_sum(accu[r]);
+    if (part == 0) {
+      red[(wave * NR + r) * 2 * GEMV_ROWS + rq] = acc[r];
+      if (PAIR) red[(wave * NR + r) * 2 * GEMV_ROWS + GEMV_ROWS + rq] = accu[r];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < GEMV_ROWS * NR) {
+    const int r = threadIdx.x / GEMV_ROWS, q = threadIdx.x % GEMV_ROWS;
+    const int orow = wg_local * GEMV_ROWS + q;
+    float gs = red[r * 2 * GEMV_ROWS + q], us = red[r * 2 * GEMV_ROWS + GEMV_ROWS + q];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      gs += red[(w * NR + r) * 2 * GEMV_ROWS + q];
+      if (PAIR) us += red[(w * NR + r) * 2 * GEMV_ROWS + GEMV_ROWS + q];
+    }
+    if (r < M && orow < rows_out) {
+      if (PAIR)
+        ((half_t*)P.out)[(int64_t)r * rows_out + orow] = (half_t)(silu_f32(gs) * us);
+      else
+        ((float*)P.out)[(int64_t)r * P.N + orow] = gs;
+    }
+  }
+}
+
+template <bool PAIRS, int NR>
+__global__ __launch_bounds__(256) void gemv_kernel_nr(GemvArgs args, int xrb, int srb) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+  __shared__ float red[4 * NR * 2 * GEMV_ROWS];
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < GEMV_MAX_GROUP; ++i)
+    if (i < args.count && (int)blockIdx.x >= args.d[i].wg_begin) pi = i;
+  const GemvDesc& P = args.d[pi];
+  const int wg_local = (int)blockIdx.x - P.wg_begin;
+  const int M = P.m;
+  if (P.fmt == 0) {
+    if (PAIRS && P.swiglu)
+      gemv_tile_nr<0, PAIRS, NR>(P, wg_local, M, xl, xrb, srb, red);
+    else
+      gemv_tile_nr<0, false, NR>(P, wg_local, M, xl, xrb, srb, red);
+  } else {
+    gemv_tile_nr<1, false, NR>(P, wg_local, M, xl, xrb, srb, red);
+  }
+}
+
 // One workgroup per 16 rows; problems with the most bytes per workgroup
 // (the deepest K) are dispatched first so they do not trail.
 static hipError_t launch_gemv_impl(const GemmProblem* probs, int count, const float* h_in, const float* h_add,
@@ -459,7 +697,7 @@ static hipError_t launch_gemv_impl(const GemmProblem* probs, int count, const fl
     for (int i = 1; i < n; ++i)   // insertion sort, stable, by bytes per workgroup (descending)
       for (int j = i; j > 0 && wg_bytes(order[j]) > wg_bytes(order[j - 1]); --j) std::swap(order[j], order[j - 1]);
     GemvArgs a{};
-    int wgs = 0, kmax = 0, pairs = 0;
+    int wgs = 0, kmax = 0, pairs = 0, mmax = 0;
     for (int i = 0; i < n; ++i) {
       const GemmProblem& p = probs[order[i]];
       GemvDesc& d = a.d[i];
@@ -476,6 +714,8 @@ static hipError_t launch_gemv_impl(const GemmProblem* probs, int count, const fl
       d.swiglu = p.swiglu;
       d.N = p.N;
       d.K = p.K;
+      d.m = p.M;
+      mmax = p.M > mmax ? p.M : mmax;
       const int rows = p.swiglu ? p.N / 2 : p.N;
       d.wg_begin = wgs;
       wgs += (rows + GEMV_ROWS - 1) / GEMV_ROWS;
@@ -484,11 +724,21 @@ static hipError_t launch_gemv_impl(const GemmProblem* probs, int count, const fl
     }
     a.count = n;
     a.sx_offset = (kmax / 64) * X_GROUP_BYTES;   // a multiple of 16
-    const size_t xbytes = (size_t)a.sx_offset + (size_t)(kmax / 32) * sizeof(float);
-    if (pairs)
-      hipLaunchKernelGGL(gemv_kernel<true>, dim3(wgs), dim3(256), xbytes, s, a);
-    else
-      hipLaunchKernelGGL(gemv_kernel<false>, dim3(wgs), dim3(256), xbytes, s, a);
+    if (mmax > 1) {   // a few rows: no residual or RMSNorm modes
+      if (mmax > GEMV_MAX_ROWS || h_in || !gemv_rows_fit(mmax, kmax)) return hipErrorInvalidValue;
+      const int xrb = a.sx_offset, srb = kmax / 32;
+      const size_t lds = 2 * ((size_t)xrb + (size_t)srb * sizeof(float));
+      if (pairs)
+        hipLaunchKernelGGL((gemv_kernel_nr<true, 2>), dim3(wgs), dim3(256), lds, s, a, xrb, srb);
+      else
+        hipLaunchKernelGGL((gemv_kernel_nr<false, 2>), dim3(wgs), dim3(256), lds, s, a, xrb, srb);
+    } else {
+      const size_t xbytes = (size_t)a.sx_offset + (size_t)(kmax / 32) * sizeof(float);
+      if (pairs)
+        hipLaunchKernelGGL(gemv_kernel<true>, dim3(wgs), dim3(256), xbytes, s, a);
+      else
+        hipLaunchKernelGGL(gemv_kernel<false>, dim3(wgs), dim3(256), xbytes, s, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -104,9 +104,11 @@ int dmq_dequant_q6k(const void* wq, void* w_f16, int64_t rows, int64_t k, void* 
  * y = x * W^T with W in Q4_K, dequantised inside the kernel (no fp16 weight
  * matrix is ever written to memory).
  *   x_f16 : [M, K] fp16;  wq : N rows of K/256 Q4_K blocks;  y : [M, N] fp32.
- * M = 1 runs the decode matrix-vector kernel; 2 <= M <= 16 a small-M MFMA
- * kernel (up to M = 32 too for launches with a SwiGLU pair or of a few
- * rows); larger M the tiled MFMA prefill kernel.  When a problem has too
+ * M = 1 runs the decode matrix-vector kernel, and so does M = 2 with
+ * K <= 20480 (both rows' x staged; each row then gets the bits of an M = 1
+ * call on it); other M up to 16 a small-M MFMA kernel (up to M = 32 too for
+ * launches with a SwiGLU pair or of a few rows); larger M the tiled MFMA
+ * prefill kernel.  When a problem has too
  * few output tiles to fill the GPU, the tiled kernel splits the K blocks
  * into pieces whose fp32 partial sums a second kernel adds in piece order
  * (workspace: see above).  Every path gives the same bits on every run.

@@ -190,6 +190,52 @@ def test_gemv_group_equals_single_calls(dmq):
         assert torch.equal(yg, ys)
 
 
+@pytest.mark.parametrize("M", [2])
+def test_gemv_few_rows_equal_single_row_calls(dmq, M):
+    """2 activation rows take the decode kernel with both rows' x staged:
+    each row's outputs have the bits of an M = 1 call on that row,
+    for a decode layer's seven projections in one group (Q4_K and Q6_K,
+    K = 3072 and 8192) and for the SwiGLU FFN 3072 -> 8192 -> 3072."""
+    x = synthetic.activations(M, 3072, seed=50 + M)
+    hx = synthetic.activations(M, 8192, seed=60 + M, sigma=1.0 / 16)
+    probs, ws = [], []
+    for name, fmt, N, K, wq in synthetic.layer_weights(1, 2):
+        w = dev(wq.reshape(-1))
+        xin = hx if K == 8192 else x
+        probs.append((fmt, dev(xin), w, torch.empty((M, N), dtype=torch.float32, device=DEV), M, N, K))
+        ws.append((name, fmt, w, xin, N, K))
+    dmq.dmq_gemm_group(probs)
+    torch.cuda.synchronize()
+    for (name, fmt, w, xin, N, K), (*_, yg, _, _, _) in zip(ws, probs):
+        for r in range(M):
+            yr = torch.empty((1, N), dtype=torch.float32, device=DEV)
+            (dmq.dmq_gemm_q4k if fmt == "q4k" else dmq.dmq_gemm_q6k)(dev(xin[r:r + 1]), w, yr, 1, N, K)
+            torch.cuda.synchronize()
+            assert torch.equal(yg[r:r + 1], yr), f"{name} M={M} row {r} differs from the M = 1 call"
+    D, F, wgu, wd = _ffn_weights(1)
+    xf = synthetic.activations(M, D, seed=70 + M, sigma=1.0 / 16)
+    h, y = run_ffn(dmq, xf, wgu, wd, M, D, F)
+    for r in range(M):
+        h1, y1 = run_ffn(dmq, xf[r:r + 1], wgu, wd, 1, D, F)
+        assert np.array_equal(h[r:r + 1].view(np.uint16), h1.view(np.uint16)), f"FFN h, M={M} row {r}"
+        assert np.array_equal(y[r:r + 1].view(np.uint32), y1.view(np.uint32)), f"FFN y, M={M} row {r}"
+    check_ffn(xf, wgu, wd, h, y, D, F, np.arange(M), f"few-rows FFN M={M}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,N,K", [(2, 37, 10240), (2, 24, 20480), (2, 100, 512), (2, 17, 4864), (2, 9, 20736),
+                                   (3, 20, 768)])
+def test_gemv_few_rows_every_output(dmq, fmt, M, N, K):
+    """The two-row decode kernel against the oracle, every output: ragged N
+    and the largest K whose two rows of x fit its LDS (20480); K = 20736
+    and M = 3 take the small-M MFMA kernel instead."""
+    x = synthetic.activations(M, K, seed=K + M)
+    wq = synthetic.weight_blocks(fmt, N, K, seed=K + 7)
+    y = gpu_gemm(dmq, fmt, x, wq, M, N, K)
+    ref, s = oracle.gemm_quant(fmt, x, wq, N, K)
+    assert_within(y, ref, s, f"few-rows gemv {fmt} M={M} N={N} K={K}")
+
+
 # ------------------------------------------------------------------ GEMM ---
 
 def test_gemm_config0_every_output(dmq):
