@@ -186,21 +186,21 @@ def sweep_config0(torch, dmq):
                       "weight_GB/s": round(wbytes / ms / 1e6, 1),
                       "graph_us": round(gms * 1e3, 2), "graph_weight_GB/s": round(wbytes / gms / 1e6, 1)}), flush=True)
     del ws
-    # one layer's seven projections at M = 16 in one grouped launch (the
-    # small-M kernel), 8 rotating layers, graph replay
-    M = 16
-    xs, ys = {}, {}
-    for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
-        xs[name] = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(0, 0, idx))).to(dev)
-        ys[name] = torch.empty((M, N), dtype=torch.float32, device=dev)
-    layers = [layer_problems(torch, dmq, 0, layer, M, xs, ys) for layer in range(8)]
-    per = time_graph(torch, dmq.dmq_gemm_group, [g for g, _ in layers], 20, per_replay=True)
-    us = float(np.median(per)) * 1e3
-    print(json.dumps({"sweep": "layer GEMMs M=16 (grouped small-M launch, 8 rotating layers, graph replay)",
-                      "us_per_layer": round(us, 2), "weight_GB/s": round(weight_bytes() / us / 1e3, 1),
-                      "TFLOP/s": round(flops_of(M) / us / 1e6, 2), "ms_per_layer": stats(per)}), flush=True)
-    del layers
-
+    # one layer's seven projections at M = 16, 2 and 3 in one grouped launch
+    # (M = 2 on the two-row decode kernel, the others on the small-M kernel),
+    # 8 rotating layers, graph replay
+    for M, kern in ((16, "small-M"), (2, "two-row decode"), (3, "small-M")):
+        xs, ys = {}, {}
+        for idx, (name, fmt, N, K) in enumerate(synthetic.LAYER_PROJECTIONS):
+            xs[name] = torch.from_numpy(synthetic.activations(M, K, seed=synthetic.act_seed(0, 0, idx))).to(dev)
+            ys[name] = torch.empty((M, N), dtype=torch.float32, device=dev)
+        layers = [layer_problems(torch, dmq, 0, layer, M, xs, ys) for layer in range(8)]
+        per = time_graph(torch, dmq.dmq_gemm_group, [g for g, _ in layers], 20, per_replay=True)
+        us = float(np.median(per)) * 1e3
+        print(json.dumps({"sweep": f"layer GEMMs M={M} (grouped {kern} launch, 8 rotating layers, graph replay)",
+                          "us_per_layer": round(us, 2), "weight_GB/s": round(weight_bytes() / us / 1e3, 1),
+                          "TFLOP/s": round(flops_of(M) / us / 1e6, 2), "ms_per_layer": stats(per)}), flush=True)
+        del layers
 
 
 def sweep_ffn(torch, dmq):
