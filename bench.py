@@ -46,7 +46,7 @@ SETTLE_MS = 150.0              # untimed GPU work before any timed region (clock
 # only for the kernel sources they were taken with: a changed source reports
 # traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("dequant_gemm_q4_amd/csrc/gemm.hip", "dequant_gemm_q4_amd/csrc/dmq_common.h")
-TRAFFIC = {"sources_sha256": "6a4f02d21326477b5e6f84783a4881ff2b4a68b7b54094bc2c73716fdbef2d0a", "bytes_per_launch": 622238126}
+TRAFFIC = {"sources_sha256": "1033dacbb2758a9c331803b657681d1bfaab1b5f342691ebb532f7982cc0340d", "bytes_per_launch": 619616247}
 COPY_PROBE_BYTES = 256 << 20
 
 
