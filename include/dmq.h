@@ -167,7 +167,11 @@ typedef struct {
  * same kernel kind: all M = 1 (decode), or all M > 1.  Results meet the same
  * bound as dmq_gemm_q4k / dmq_gemm_q6k per entry; they are the same bits as
  * those calls except where the group's launch plan splits a problem's K
- * differently (tiled kernel only), which changes the fp32 summation order.
+ * differently (tiled kernel only), which changes the fp32 summation order,
+ * or where the group runs another kernel than the single call would: the
+ * kernel is chosen from the group's largest M and K, its SwiGLU pairs and
+ * its total size (e.g. an M = 2 problem beside an M = 3 one takes the
+ * small-M kernel, not the two-row decode kernel).
  */
 int dmq_gemm_group(const dmq_gemm_desc* descs, int32_t count, void* stream);
 
